@@ -1,0 +1,361 @@
+"""Pins of the fp64 oracle against what the pages and mathematics fix.
+
+Every check here compares the oracle with something other than itself: values worked
+out by hand from the pages' block definition (tests/golden), numpy's IEEE half and f32
+arithmetic, closed forms, an independent word-level decode feeding numpy's matmul, and
+the page's description of the reference quantizer.
+"""
+
+import math
+import os
+import struct
+
+import numpy as np
+import pytest
+
+import oracle
+from ternary_bit_quantized_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _same_bits(a, b):
+    a = np.asarray(a, dtype=np.float32)
+    b = np.asarray(b, dtype=np.float32)
+    nan = np.isnan(a) & np.isnan(b)
+    return bool(np.all(nan | (a.view(np.uint32) == b.view(np.uint32))))
+
+
+def _block(d_bits, words):
+    """One block built straight from the format paragraph: LE half, then four LE u32."""
+    return struct.pack("<H4I", d_bits, *words)
+
+
+def _word_with(codes16):
+    """A 32-bit word whose code i (bits 2i..2i+1) is codes16[i]."""
+    w = 0
+    for i, c in enumerate(codes16):
+        w |= (int(c) & 3) << (2 * i)
+    return w
+
+
+# --------------------------------------------------------------------------- sizes
+
+def _golden_kv(name):
+    out = {}
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            k, v = line.split()
+            out[k] = float(v)
+    return out
+
+
+def test_block_size_and_bpw():
+    g = _golden_kv("file_sizes.txt")
+    assert oracle.BLOCK_BYTES == 18 and oracle.BLOCK_WEIGHTS == 64
+    assert oracle.BLOCK_BYTES * 8 / oracle.BLOCK_WEIGHTS == g["bpw_g64"]
+    g128_bytes = 2 + 128 // 4       # same scale, 2 bits per code, group of 128
+    assert g128_bytes == 34 and g128_bytes * 8 / 128 == g["bpw_g128"]
+    assert round(100 * (g["bpw_g64"] / g["bpw_g128"] - 1), 1) == g["g64_vs_g128_percent"]
+
+
+def test_file_sizes_reproduce_pages():
+    g = _golden_kv("file_sizes.txt")
+    per_layer = sum(M * K for M, K in synth.QWEN3_8B.values())
+    params = synth.QWEN3_8B_LAYERS * per_layer + 2 * synth.VOCAB * synth.HIDDEN_8B
+    gib = 2.0 ** 30
+    blocks = params // 64
+    assert params % 64 == 0
+    assert round(blocks * oracle.BLOCK_BYTES / gib, 2) == g["size_8b_q2_0_g64"]
+    assert round(params // 128 * 34 / gib, 2) == g["size_8b_q2_0_g128"]
+    assert round(params * 2 / gib, 2) == g["size_8b_f16"]
+    assert round(16 / g["bpw_g64"], 1) == g["ratio_f16_over_q2_0"]
+
+
+# --------------------------------------------------------------------------- half precision
+
+def test_half_decode_exhaustive():
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.half_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_half_encode_matches_numpy_rounding():
+    rng = np.random.default_rng(123)
+    vals = np.concatenate([
+        rng.uniform(0, 70000, 4000),
+        np.exp(rng.uniform(np.log(1e-9), np.log(7e4), 4000)),
+        # exact midpoints between neighbouring halves (ties to even), incl. subnormals
+        (np.arange(0, 2048, dtype=np.uint16).view(np.float16).astype(np.float64)[1:]
+         + np.arange(1, 2048, dtype=np.uint16).view(np.float16).astype(np.float64)) / 2,
+        np.array([0.0, 2.0 ** -25, 2.0 ** -24, 3 * 2.0 ** -26, 65504.0, 65519.99, 65520.0, 1e6]),
+    ])
+    vals = np.concatenate([vals, -vals[:100]])
+    ref = vals.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.double_to_half(float(v)) for v in vals], dtype=np.uint16)
+    assert np.array_equal(got, ref)
+
+
+# --------------------------------------------------------------------------- block decode
+
+def _parse_golden_blocks():
+    cases, block = [], None
+    for line in open(os.path.join(GOLDEN, "q2_0_blocks.txt")):
+        t = line.split()
+        if not t or t[0].startswith("#"):
+            continue
+        if t[0] == "block":
+            block = bytes.fromhex(t[1])
+        elif t[0] == "values":
+            vals = []
+            for tok in t[1:]:
+                v, n = tok.split("*")
+                x = float(v) if v in ("inf", "-inf", "nan") else float.fromhex(v)
+                vals += [x] * int(n)
+            cases.append((block, np.array(vals, dtype=np.float64)))
+    return cases
+
+
+def test_golden_blocks_decode():
+    cases = _parse_golden_blocks()
+    assert len(cases) == 7
+    for block, vals in cases:
+        w = np.frombuffer(block, dtype=np.uint8)
+        deq = oracle.dequant(w, 1, 64)[0]
+        nan = np.isnan(vals)
+        assert np.array_equal(np.isnan(deq), nan)
+        assert np.array_equal(deq[~nan], vals[~nan])
+        assert np.array_equal(np.signbit(deq[~nan]), np.signbit(vals[~nan]))
+        rows = oracle.get_rows(w, 1, 64, np.array([0]))
+        assert _same_bits(rows[0], vals.astype(np.float32))
+
+
+def test_layout_one_hot():
+    """Weight j alone carries code 2 (value +1 with d = 1): x = e_j gives 1, x = arange gives j."""
+    blocks = []
+    for j in range(64):
+        words = [0x55555555] * 4
+        codes = [1] * 16
+        codes[j % 16] = 2
+        words[j // 16] = _word_with(codes)
+        blocks.append(_block(0x3C00, words))
+    w = np.frombuffer(b"".join(blocks), dtype=np.uint8)
+    deq = oracle.dequant(w, 64, 64)
+    assert np.array_equal(deq, np.eye(64))
+    x = np.concatenate([np.eye(64, dtype=np.float32), np.arange(64, dtype=np.float32)[None]])
+    y, bound = oracle.mul_mat(w, 64, 64, x)
+    assert np.array_equal(y[:64], np.eye(64))
+    assert np.array_equal(y[64], np.arange(64, dtype=np.float64))
+    assert np.array_equal(bound[64], np.arange(64, dtype=np.float64))
+
+
+def test_word_order_inside_block():
+    """Words are consecutive 32-bit groups after the scale: one code 3 in word w, code 15."""
+    for wi in range(4):
+        words = [0x55555555] * 4
+        words[wi] = 0x55555555 | (3 << 30)        # code 15 -> 3 (0b11)
+        w = np.frombuffer(_block(0x3C00, words), dtype=np.uint8)
+        deq = oracle.dequant(w, 1, 64)[0]
+        expect = np.zeros(64)
+        expect[16 * wi + 15] = 2.0
+        assert np.array_equal(deq, expect)
+
+
+# --------------------------------------------------------------------------- products
+
+def _uniform_codes_matrix(M, K, code, d_bits):
+    nb = K // 64
+    word = _word_with([code] * 16)
+    blocks = [_block(int(d_bits[m, b]), [word] * 4) for m in range(M) for b in range(nb)]
+    return np.frombuffer(b"".join(blocks), dtype=np.uint8)
+
+
+@pytest.mark.parametrize("code,factor", [(1, 0), (2, 1), (0, -1), (3, 2)])
+def test_closed_forms_exact(code, factor):
+    """All codes equal: y = (code - 1) * sum_b d_b * sum_(x in block b); exact with integer x
+    and power-of-two scales, so fp64 must reproduce it bit for bit."""
+    rng = np.random.default_rng(7)
+    M, K, N = 5, 320, 3
+    exps = rng.integers(-12, 4, size=(M, K // 64))
+    d = (2.0 ** exps) * rng.choice([-1, 1], size=exps.shape)
+    d_bits = d.astype(np.float16).view(np.uint16)
+    w = _uniform_codes_matrix(M, K, code, d_bits)
+    x = rng.integers(-50, 51, size=(N, K)).astype(np.float32)
+    y, bound = oracle.mul_mat(w, M, K, x)
+    xs = x.astype(np.float64).reshape(N, K // 64, 64).sum(-1)          # (N, nb)
+    expect = factor * (xs @ d.T)
+    assert np.array_equal(y, expect)
+    if factor == 0:
+        assert np.all(bound == 0) and np.all(y == 0) and not np.any(np.signbit(y))
+
+
+def test_all_code_one_zero_for_any_input():
+    rng = np.random.default_rng(8)
+    M, K, N = 7, 512, 4
+    d_bits = rng.uniform(0.001, 10, size=(M, K // 64)).astype(np.float16).view(np.uint16)
+    w = _uniform_codes_matrix(M, K, 1, d_bits)
+    x = rng.standard_normal((N, K), dtype=np.float32) * 1e3
+    y, bound = oracle.mul_mat(w, M, K, x)
+    assert np.all(y == 0) and np.all(bound == 0)
+
+
+def _independent_dense(w_bytes, M, K):
+    """Dense fp64 dequant by a different route: little-endian u32 words and shifts."""
+    nb = K // 64
+    blk = w_bytes.reshape(M, nb, 18)
+    d = np.ascontiguousarray(blk[:, :, 0:2]).view("<f2").reshape(M, nb).astype(np.float64)
+    words = np.ascontiguousarray(blk[:, :, 2:]).view("<u4").reshape(M, nb, 4).astype(np.uint64)
+    shifts = (2 * np.arange(16, dtype=np.uint64))
+    q = (words[..., None] >> shifts) & 3                       # (M, nb, 4, 16)
+    q = q.reshape(M, nb, 64).astype(np.float64)
+    return ((q - 1.0) * d[..., None]).reshape(M, K)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 64, 1), (3, 128, 2), (17, 192, 5), (64, 256, 8), (33, 64, 3)])
+def test_brute_force_tiny(M, K, N):
+    rng = np.random.default_rng(M * 1000 + K + N)
+    w = synth.random_blocks(rng, M, K // 64)
+    # finite scales only (a random NaN/inf scale makes every product non-finite)
+    blk = w.reshape(M, K // 64, 18)
+    blk[:, :, 1] &= 0xFB  # clear the lowest exponent bit: exponent 31 (inf/NaN) cannot occur
+    x = rng.standard_normal((N, K), dtype=np.float32)
+    dense = _independent_dense(w, M, K)
+    assert np.all(np.isfinite(dense))
+    np.testing.assert_array_equal(oracle.dequant(w, M, K), dense)
+    y, bound = oracle.mul_mat(w, M, K, x)
+    ref = x.astype(np.float64) @ dense.T
+    absref = np.abs(x.astype(np.float64)) @ np.abs(dense).T
+    assert np.all(np.abs(y - ref) <= 1e-12 * absref + 1e-300)
+    np.testing.assert_allclose(bound, absref, rtol=1e-12, atol=0)
+
+
+def test_row_subset_matches_full():
+    rng = np.random.default_rng(3)
+    M, K, N = 40, 256, 3
+    w = synth.weight(9, 0, 0, M, K, "quad", synth.ScaleDist("uniform", 0.01, 0.1))
+    x = rng.standard_normal((N, K), dtype=np.float32)
+    y, b = oracle.mul_mat(w, M, K, x)
+    rows = np.array([39, 0, 17, 17, 5])
+    ys, bs = oracle.mul_mat(w, M, K, x, rows=rows)
+    assert np.array_equal(ys, y[:, rows]) and np.array_equal(bs, b[:, rows])
+
+
+# --------------------------------------------------------------------------- get_rows
+
+def test_get_rows_every_scale_and_code():
+    """All 65536 half scales x 4 codes: the f32 output equals numpy's IEEE f32 product
+    float32(q - 1) * float32(d), bit for bit (zero signs, subnormals, inf, NaN included)."""
+    bits = np.arange(65536, dtype=np.uint16)
+    # one block per scale; each word carries codes 0,0,0,0,1,1,1,1,2,2,2,2,3,3,3,3
+    word = _word_with([0] * 4 + [1] * 4 + [2] * 4 + [3] * 4)
+    blocks = b"".join(_block(int(b), [word] * 4) for b in bits)
+    w = np.frombuffer(blocks, dtype=np.uint8)
+    out = oracle.get_rows(w, 65536, 64, np.arange(65536, dtype=np.int32))
+    q = np.repeat(np.arange(4), 4)
+    q = np.tile(q, 4).astype(np.float32)                    # code per weight
+    d32 = bits.view(np.float16).astype(np.float32)
+    ref = (q[None, :] - np.float32(1)) * d32[:, None]
+    assert ref.dtype == np.float32
+    assert _same_bits(out, ref)
+
+
+def test_get_rows_out_of_range_ids_nan():
+    w = synth.weight(1, 0, 0, 8, 128, "tern", synth.ScaleDist("uniform", 0.01, 0.1))
+    ids = np.array([3, -1, 8, 7, 2 ** 31 - 1], dtype=np.int32)
+    out = oracle.get_rows(w, 8, 128, ids)
+    assert np.all(np.isnan(out[[1, 2, 4]]))
+    assert np.all(np.isfinite(out[[0, 3]]))
+    assert _same_bits(out[0], oracle.get_rows(w, 8, 128, np.array([3]))[0])
+
+
+# --------------------------------------------------------------------------- quantizer
+
+def test_quantizer_reproduces_ternary_exactly():
+    rng = np.random.default_rng(11)
+    M, K = 32, 512
+    nb = K // 64
+    d = rng.uniform(1e-3, 3.0, size=(M, nb)).astype(np.float16).astype(np.float32)
+    t = rng.integers(-1, 2, size=(M, nb, 64)).astype(np.float32)
+    t[:, :, 0] = rng.choice([-1.0, 1.0], size=(M, nb))   # at least one nonzero per block
+    t[0, 0, :] = 0.0                                       # one all-zero block
+    wf = (t * d[..., None]).reshape(M, K)
+    packed = oracle.quantize_ref(wf)
+    back = oracle.dequant(packed, M, K).astype(np.float32)
+    assert np.array_equal(back.view(np.uint32), wf.view(np.uint32))
+    dense_codes = _codes_of(packed, M, K)
+    assert not np.any(dense_codes == 3)
+    assert np.all(dense_codes[0, :64] == 1)
+    assert packed[0, 0] == 0 and packed[0, 1] == 0     # zero block -> d = 0
+
+
+def _codes_of(packed, M, K):
+    words = np.ascontiguousarray(packed.reshape(M, K // 64, 18)[:, :, 2:]).view("<u4")
+    words = words.reshape(M, K // 64, 4).astype(np.uint64)
+    q = (words[..., None] >> (2 * np.arange(16, dtype=np.uint64))) & 3
+    return q.reshape(M, K)
+
+
+def test_quantizer_picks_a_nearest_level():
+    rng = np.random.default_rng(12)
+    M, K = 16, 256
+    wf = rng.standard_normal((M, K)).astype(np.float32) * np.float32(0.05)
+    packed = oracle.quantize_ref(wf)
+    blk = packed.reshape(M, K // 64, 18)
+    d = np.ascontiguousarray(blk[:, :, 0:2]).view("<f2").reshape(M, K // 64).astype(np.float64)
+    amax = np.abs(wf.astype(np.float64)).reshape(M, K // 64, 64).max(-1)
+    assert np.array_equal(d, amax.astype(np.float16).astype(np.float64))
+    q = _codes_of(packed, M, K).astype(np.float64).reshape(M, K // 64, 64)
+    levels = (np.arange(4)[None, None, None, :] - 1.0) * d[..., None, None]
+    dist = np.abs(wf.astype(np.float64).reshape(M, K // 64, 64, 1) - levels)
+    chosen = np.take_along_axis(dist, q[..., None].astype(np.int64), axis=-1)[..., 0]
+    assert np.all(chosen <= dist.min(-1))
+    assert not np.any(q == 3)
+
+
+def test_quantizer_tie_goes_to_level_nearer_zero():
+    """Reading of the pages (no worked example): a weight at exactly d/2 or -d/2 takes 0."""
+    wf = np.zeros((1, 64), dtype=np.float32)
+    wf[0, 0] = 1.0
+    wf[0, 1] = 0.5
+    wf[0, 2] = -0.5
+    wf[0, 3] = -1.0
+    q = _codes_of(oracle.quantize_ref(wf), 1, 64)[0]
+    assert list(q[:4]) == [2, 1, 1, 0]
+
+
+# --------------------------------------------------------------------------- synthetic inputs
+
+def test_synth_pack_matches_format_paragraph():
+    rng = np.random.default_rng(5)
+    M, K = 3, 192
+    codes = rng.integers(0, 4, size=(M, K), dtype=np.uint8)
+    d = rng.uniform(-2, 2, size=(M, K // 64)).astype(np.float16)
+    packed = synth.pack(codes, d)
+    manual = b"".join(
+        _block(int(d.view(np.uint16)[m, b]),
+               [_word_with(codes[m, 64 * b + 16 * wi: 64 * b + 16 * wi + 16]) for wi in range(4)])
+        for m in range(M) for b in range(K // 64))
+    assert packed.tobytes() == manual
+
+
+def test_synth_distributions_and_determinism():
+    a = synth.weight(1, 2, 3, 64, 4096, "tern_c3", synth.ScaleDist("uniform", 0.005, 0.05))
+    b = synth.weight(1, 2, 3, 64, 4096, "tern_c3", synth.ScaleDist("uniform", 0.005, 0.05))
+    assert np.array_equal(a, b)
+    q = _codes_of(a, 64, 4096)
+    frac = np.bincount(q.ravel(), minlength=4) / q.size
+    assert abs(frac[3] - 0.005) < 0.001
+    assert all(abs(frac[i] - 0.995 / 3) < 0.01 for i in range(3))
+    t = _codes_of(synth.weight(0, 0, 0, 64, 4096, "tern", synth.ScaleDist("uniform", 0.01, 0.1)), 64, 4096)
+    ft = np.bincount(t.ravel(), minlength=4) / t.size
+    assert ft[3] == 0 and all(abs(ft[i] - 1 / 3) < 0.01 for i in range(3))
+    v = synth.weight(4, 0, 0, 512, 4096, "quad", synth.ScaleDist("loguniform", 1e-3, 1e-1, 0.01))
+    dv = np.ascontiguousarray(v.reshape(512, 64, 18)[:, :, 0:2]).view("<f2").astype(np.float64)
+    assert abs((dv == 0).mean() - 0.01) < 0.003
+    nz = dv[dv != 0]
+    assert nz.min() >= np.float16(1e-3) and nz.max() <= np.float16(1e-1)
