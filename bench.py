@@ -1,0 +1,275 @@
+"""Benchmark of the Q2_0 hot path on one MI355X.
+
+Workload: a Qwen3-8B-shaped ternary model's linear work -- the 36-layer stack of
+q/o 4096x4096, k/v 1024x4096, gate/up 12288x4096 and down 4096x12288 Q2_0 matrices
+(1.95 GB) plus a 151936x4096 Q2_0 vocabulary tensor used both as the embedding
+(get_rows) and as the LM head -- with seeded synthetic weights and activations.
+
+One step is one pass of the whole hot path:
+  prefill: get_rows of 512 token ids, then the 252 stack matrices at N = 512 on the
+           fp16-MFMA GEMM;
+  decode : get_rows of 1 token id, then the 252 stack matrices and the LM head at
+           N = 1 on the mat-vec (one token, weights streamed from HBM).
+Each part is captured once in a HIP graph and replayed, so the timed region holds
+GPU work only.  Inputs are resident in HBM before timing starts.
+
+Printed: one JSON line.  `value` is the decode mat-vec stream rate in GB/s
+(algorithmic bytes: Q2_0 weights + f32 activations + f32 outputs, over the time of
+the 253 mat-vec launches).  Extra fields give decode and prefill tokens/s, the
+prefill GEMM TFLOP/s, the roofline fractions and the CPU oracle's rate on a
+bounded sample of the same work.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Q2_0 mat-vec GB/s (% HBM peak) at N=1; prefill GEMM TFLOP/s; tokens/s"
+HBM_PEAK_GBS = 8000.0
+F16_MFMA_PEAK_TFLOPS = 2500.0
+PREFILL_N = 512
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--layers", type=int, default=36, help="stack layers (36 = the full model)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-prefill-row-stride", type=int, default=64)
+    return p.parse_args()
+
+
+def mat_bytes(M, K, N):
+    return M * (K // 64) * 18 + 4 * K * N + 4 * M * N
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from ternary_bit_quantized_amd import q2_0 as B
+    from ternary_bit_quantized_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    B.lib()
+
+    wl, vwl = synth.STACK_8B, synth.VOCAB_8B
+    layers = list(range(args.layers))
+    t0 = time.time()
+    host_w = synth.stack_weights(wl, layers, threads=min(16, os.cpu_count() or 8))
+    emb_host = synth.workload_weight(vwl, "emb")
+    log("generated %d matrices + vocab tensor in %.1f s" % (len(host_w), time.time() - t0))
+
+    W = {k: torch.from_numpy(v).to(dev) for k, v in host_w.items()}
+    emb = torch.from_numpy(emb_host).to(dev)
+    VM, VK = vwl.shapes["emb"]
+    Ks = sorted({K for (_, K) in wl.shapes.values()})
+    Ms = sorted({M for (M, _) in wl.shapes.values()} | {VM})
+    x1 = {K: torch.from_numpy(synth.activations(wl.seed, 0, synth.stack_x_matrix_index(K), 1, K)).to(dev)
+          for K in Ks}
+    xP = {K: torch.from_numpy(synth.activations(wl.seed, 1, synth.stack_x_matrix_index(K), PREFILL_N, K)).to(dev)
+          for K in Ks}
+    y1 = {M: torch.empty((1, M), dtype=torch.float32, device=dev) for M in Ms}
+    yP = {M: torch.empty((PREFILL_N, M), dtype=torch.float32, device=dev) for M in Ms}
+    ids_p = torch.from_numpy(synth.row_ids(vwl.seed, 0, 0, PREFILL_N, VM)).to(dev)
+    ids_d = torch.from_numpy(synth.row_ids(vwl.seed, 1, 0, 1, VM)).to(dev)
+    emb_out_p = torch.empty((PREFILL_N, VK), dtype=torch.float32, device=dev)
+    emb_out_d = torch.empty((1, VK), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log("inputs resident on the GPU")
+
+    order = [(l, n) for l in layers for n in synth.MATS]
+
+    def check(st, what):
+        if st != 0:
+            raise RuntimeError("%s failed: %s" % (what, B.lib().q2_0_status_string(st).decode()))
+
+    def s():
+        return torch.cuda.current_stream().cuda_stream
+
+    def run_get_rows(ids, out):
+        check(B.get_rows_raw(emb.data_ptr(), VM, VK, ids.data_ptr(), ids.numel(), out.data_ptr(), VK, s()),
+              "get_rows")
+
+    def run_decode_matvecs():
+        st = s()
+        for key in order:
+            M, K = wl.shapes[key[1]]
+            check(B.mul_mat_vec_raw(W[key].data_ptr(), M, K, x1[K].data_ptr(), K, 1,
+                                    y1[M].data_ptr(), M, st), "mat_vec")
+        check(B.mul_mat_vec_raw(emb.data_ptr(), VM, VK, x1[VK].data_ptr(), VK, 1, y1[VM].data_ptr(), VM, st),
+              "lm_head")
+
+    def run_prefill_gemms(precision=B.Q2_0_PREC_F16_MFMA):
+        st = s()
+        for key in order:
+            M, K = wl.shapes[key[1]]
+            check(B.mul_mat_raw(W[key].data_ptr(), M, K, xP[K].data_ptr(), K, PREFILL_N,
+                                yP[M].data_ptr(), M, precision, 0, 0, st), "mul_mat")
+
+    # ---- capture the four parts as graphs
+    parts = {
+        "prefill_get_rows": lambda: run_get_rows(ids_p, emb_out_p),
+        "prefill_gemm": run_prefill_gemms,
+        "decode_get_rows": lambda: run_get_rows(ids_d, emb_out_d),
+        "decode_mat_vec": run_decode_matvecs,
+    }
+    graphs = {}
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        for name, fn in parts.items():   # eager warm-up on the capture stream
+            fn()
+    torch.cuda.synchronize()
+    for name, fn in parts.items():
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        graphs[name] = g
+    torch.cuda.synchronize()
+    log("graphs captured")
+
+    ev = {n: [] for n in parts}
+
+    def step(record):
+        for name, g in graphs.items():
+            if record:
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                g.replay()
+                b.record()
+                ev[name].append((a, b))
+            else:
+                g.replay()
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log("warm-up done (%d steps)" % args.warmup)
+
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    log("timed %d steps in %.3f s" % (args.steps, t_total))
+
+    ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in parts}
+
+    # ---- algorithmic work
+    dec_bytes = sum(mat_bytes(*wl.shapes[n], 1) for (_, n) in order) + mat_bytes(VM, VK, 1)
+    n_dec_launches = len(order) + 1
+    pre_flops = sum(2.0 * M * K * PREFILL_N for (_, n) in order for (M, K) in [wl.shapes[n]])
+    pre_bytes = sum(mat_bytes(*wl.shapes[n], PREFILL_N) for (_, n) in order)
+    matvec_gbs = dec_bytes / (ms["decode_mat_vec"] * 1e-3) / 1e9
+    gemm_tflops = pre_flops / (ms["prefill_gemm"] * 1e-3) / 1e12
+    dec_tok_s = 1.0 / ((ms["decode_mat_vec"] + ms["decode_get_rows"]) * 1e-3)
+    pre_tok_s = PREFILL_N / ((ms["prefill_gemm"] + ms["prefill_get_rows"]) * 1e-3)
+    weight_bytes = sum(host_w[k].nbytes for k in order)
+
+    result = {
+        "metric": METRIC,
+        "value": round(matvec_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_total * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded Q2_0 ternary weights, x ~ N(0,1))",
+        "config": {
+            "workload": "qwen3_8b_stack_%dx7_plus_vocab151936x4096" % args.layers,
+            "layers": args.layers, "decode_N": 1, "prefill_N": PREFILL_N,
+            "stack_weight_bytes": weight_bytes, "vocab_bytes": int(emb_host.nbytes),
+        },
+        "hbm_frac": round(matvec_gbs / HBM_PEAK_GBS, 4),
+        "decode_tokens_per_s": round(dec_tok_s, 1),
+        "prefill_tokens_per_s": round(pre_tok_s, 1),
+        "prefill_gemm_tflops": round(gemm_tflops, 2),
+        "ms": {k: round(v, 4) for k, v in ms.items()},
+        "roofline": {
+            "kernel": "mat_vec (N=1, 253 launches per decode token)",
+            "bound": "hbm", "achieved": round(matvec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(matvec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "bytes_per_launch_avg": int(dec_bytes / n_dec_launches),
+            "avg_launch_us": round(ms["decode_mat_vec"] * 1e3 / n_dec_launches, 3),
+        },
+        "roofline_gemm": {
+            "kernel": "gemm_f16 (N=512, 252 launches per prefill)",
+            "bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": F16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(gemm_tflops / F16_MFMA_PEAK_TFLOPS, 4),
+            "traffic": None, "algorithmic_bytes": int(pre_bytes),
+        },
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(host_w, order, wl, args)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(host_w, order, wl, args):
+    """The fp64 oracle, as it stands, on the host cores: the decode mat-vec over the whole
+    stack at N = 1 and the prefill product on every S-th row of every matrix at N = 512."""
+    import oracle
+    from ternary_bit_quantized_amd import synth
+    oracle.build()
+    threads = oracle.num_threads()
+    xs1 = {K: synth.activations(wl.seed, 0, synth.stack_x_matrix_index(K), 1, K) for K in (4096, 12288)}
+    xsP = {K: synth.activations(wl.seed, 1, synth.stack_x_matrix_index(K), PREFILL_N, K) for K in (4096, 12288)}
+    t = time.perf_counter()
+    nbytes = 0
+    for key in order:
+        M, K = wl.shapes[key[1]]
+        oracle.mul_mat(host_w[key], M, K, xs1[K])
+        nbytes += mat_bytes(M, K, 1)
+    t_dec = time.perf_counter() - t
+    log("cpu oracle decode: %.2f s" % t_dec)
+    S = args.cpu_prefill_row_stride
+    t = time.perf_counter()
+    flops = 0.0
+    for key in order:
+        M, K = wl.shapes[key[1]]
+        rows = np.arange(0, M, S)
+        oracle.mul_mat(host_w[key], M, K, xsP[K], rows=rows)
+        flops += 2.0 * rows.size * K * PREFILL_N
+    t_pre = time.perf_counter() - t
+    log("cpu oracle prefill sample: %.2f s" % t_pre)
+    return {
+        "value": round(nbytes / t_dec / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": "decode mat-vec N=1 over all %d stack matrices (%d B); prefill N=512 on every "
+                  "%dth row of each matrix" % (len(order), nbytes, S),
+        "decode_s": round(t_dec, 3), "prefill_sample_s": round(t_pre, 3),
+        "prefill_tflops": round(flops / t_pre / 1e12, 6),
+        "decode_tokens_per_s": round(1.0 / t_dec, 4),
+    }
+
+
+if __name__ == "__main__":
+    main()

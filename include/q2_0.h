@@ -1,0 +1,129 @@
+/*
+ * q2_0.h -- C ABI of the MI355X (gfx950) Q2_0 x F32 library (libq2_0.so).
+ *
+ * Q2_0 storage (bisque.today, "WebGPU: add Q2_0 support" (llama.cpp PR 30914),
+ * the paragraph on the block format; aisvetem.cz, "Llama.cpp umi dvoubitovy Q2_0
+ * i na kartach NVIDIA", section "Osmnact bajtu na ctyriasedesat vah"):
+ *   - a block is 18 bytes holding 64 weights (2.25 bits per weight);
+ *   - bytes 0-1: the scale d, IEEE half precision, little-endian;
+ *   - bytes 2-17: four little-endian 32-bit words; code i of word w is bits
+ *     2i..2i+1 and belongs to weight 16w+i;
+ *   - a code q decodes to (q - 1) * d, i.e. -d, 0, d, 2d (code 3 is reserved by
+ *     the model card but decodes to 2d and is accepted).
+ *
+ * Matrix layout used by every entry point:
+ *   w : M rows, each K/64 consecutive blocks; row m starts at byte m*(K/64)*18.
+ *   x : N activation columns of K contiguous floats; column n starts at x + n*ldx.
+ *   y : N output columns of M contiguous floats;     column n starts at y + n*ldy.
+ * so y[n][m] = sum_k W[m][k] * x[n][k]  (W times each activation column).
+ *
+ * Conventions shared by all calls:
+ *   - Every pointer is a DEVICE pointer owned by the caller.  The library never
+ *     allocates device memory, keeps no reference after the call returns and has
+ *     no global state besides a thread-local copy of the last HIP error.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *     work; the caller keeps buffers alive until the stream has passed them.
+ *   - Arguments are validated on the host before anything is launched; on any
+ *     error nothing is written and nothing is launched.  Check order: SHAPE,
+ *     then the empty no-op (M, N or n_ids == 0 returns Q2_0_OK), then NULL,
+ *     LAYOUT, ALIGN, UNSUPPORTED, WORKSPACE.
+ *   - No call prints, throws across the ABI or aborts.
+ */
+#ifndef Q2_0_H
+#define Q2_0_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q2_0_BLOCK_WEIGHTS 64
+#define Q2_0_BLOCK_BYTES 18
+
+typedef enum {
+    Q2_0_OK = 0,
+    Q2_0_ERR_NULL = 1,        /* a required pointer is NULL */
+    Q2_0_ERR_SHAPE = 2,       /* K <= 0, K % 64 != 0, a negative size, or a size beyond the limits */
+    Q2_0_ERR_LAYOUT = 3,      /* ldx < K, ldy < M or ld_out < K */
+    Q2_0_ERR_ALIGN = 4,       /* w not 2-byte aligned, or x / y / out / ids not 4-byte aligned */
+    Q2_0_ERR_UNSUPPORTED = 5, /* N > 8 for the mat-vec, or an unknown precision */
+    Q2_0_ERR_WORKSPACE = 6,   /* workspace smaller than q2_0_mul_mat_workspace_bytes() */
+    Q2_0_ERR_HIP = 7          /* a HIP launch failed; see q2_0_last_hip_error() */
+} q2_0_status;
+
+typedef enum {
+    Q2_0_PREC_F16_MFMA = 0,   /* W tiles as fp16 d*(q-1) (exact), x rounded to fp16, MFMA, f32 accumulate */
+    Q2_0_PREC_F32 = 1         /* W as f32 (q-1) and d, x in f32, f32 FMA with fp64 across blocks */
+} q2_0_precision;
+
+/* Largest activation-column count of q2_0_mul_mat_vec. */
+#define Q2_0_MAT_VEC_MAX_N 8
+
+/*
+ * get_rows: gather rows of a Q2_0 matrix and dequantize them to f32
+ * (bisque.today "WebGPU: add Q2_0 support": the get-rows shader copies rows out
+ * of a Q2_0 tensor and writes 64 floats per block).
+ *   w      : M x K Q2_0 matrix (layout above), 2-byte aligned.
+ *   ids    : n_ids int32 row indices, device memory, 4-byte aligned.
+ *   out    : n_ids rows of K floats; row r starts at out + r*ld_out (ld_out >= K).
+ * out[r][k] is the IEEE f32 product f32(q - 1) * f32(d) of weight k of row
+ * ids[r] -- bit-exact, zero signs included.  An id outside [0, M) fills its row's
+ * first K floats with quiet NaN and reads nothing.  Columns K..ld_out-1 are not
+ * written.
+ */
+int q2_0_get_rows(const void *w, int64_t M, int64_t K, const int32_t *ids, int64_t n_ids,
+                  float *out, int64_t ld_out, void *stream);
+
+/*
+ * mul_mat_vec: y = W x for 1 <= N <= 8 activation columns, fp32-grade
+ * (bisque.today "WebGPU: add Q2_0 support", the matrix-vector paragraph: each
+ * block's sum of (q - 1) * x is formed first and the scale applied once).
+ *   w : M x K Q2_0 matrix, 2-byte aligned (16-byte aligned rows take the fast path).
+ *   x : N columns of K floats at x + n*ldx, ldx >= K, 4-byte aligned.
+ *   y : N columns of M floats at y + n*ldy, ldy >= M, 4-byte aligned; y[n][m] is
+ *       overwritten.  x and y must not overlap.
+ * Accuracy: |y - y_exact| <= 1e-5 * sum_k |W[m][k] * x[n][k]|, and exactly 0 when
+ * that sum is 0, for finite inputs with |x| < 2^100.
+ * N > 8 returns Q2_0_ERR_UNSUPPORTED (use q2_0_mul_mat).
+ */
+int q2_0_mul_mat_vec(const void *w, int64_t M, int64_t K, const float *x, int64_t ldx, int64_t N,
+                     float *y, int64_t ldy, void *stream);
+
+/*
+ * mul_mat: y = W x for any N (batched prefill GEMM).
+ * (bisque.today "WebGPU: add Q2_0 support": the tiled matrix multiply unpacks 16
+ * codes per thread into shared memory as half precision.)
+ *   Layouts and alignment as for q2_0_mul_mat_vec; precision is a q2_0_precision.
+ *   N <= 8 is routed to the mat-vec for either precision (fp32-grade result).
+ *   Otherwise Q2_0_PREC_F16_MFMA stages each weight tile in LDS as fp16 d*(q-1),
+ *   which is exact for |d| <= 32752, rounds x to fp16 (nearest-even) and
+ *   accumulates in f32 on the matrix cores: |y - y_exact| <= 2e-3 * sum|W x| for
+ *   |x| <= 65504 and |d| <= 32752.  Q2_0_PREC_F32 is the fp32-grade fallback
+ *   (same bound as the mat-vec).
+ *   workspace / ws_bytes: scratch the caller provides; at least
+ *   q2_0_mul_mat_workspace_bytes(M, K, N, precision) bytes (it may be 0, and then
+ *   workspace may be NULL).
+ */
+int q2_0_mul_mat(const void *w, int64_t M, int64_t K, const float *x, int64_t ldx, int64_t N,
+                 float *y, int64_t ldy, int precision, void *workspace, size_t ws_bytes,
+                 void *stream);
+
+/* Workspace q2_0_mul_mat needs for these sizes (0 when none); 0 for invalid sizes. */
+size_t q2_0_mul_mat_workspace_bytes(int64_t M, int64_t K, int64_t N, int precision);
+
+/* A static, human-readable name for a status code. */
+const char *q2_0_status_string(int status);
+
+/* The hipError_t of the last Q2_0_ERR_HIP returned on the calling thread (0 if none). */
+int q2_0_last_hip_error(void);
+
+/* Library version string, e.g. "q2_0 0.1.0 gfx950". */
+const char *q2_0_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q2_0_H */

@@ -1,0 +1,119 @@
+// C ABI of libq2_0.so: argument validation and dispatch.  Declared in include/q2_0.h.
+//
+// Validation runs entirely on the host and returns before any HIP call, so a bad
+// argument never reaches a kernel.  The kernels themselves assume what is checked
+// here: K a positive multiple of 64, strides at least the row length, 2-byte
+// aligned weights, 4-byte aligned floats and ids, and sizes within the grid limits.
+#include "../../include/q2_0.h"
+#include "q2_0_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+// Largest sizes the launch geometry covers (grid.y limit times the tile, and
+// 32-bit in-row offsets).
+constexpr int64_t kMaxK = (int64_t)1 << 24;          // 16 Mi weights per row
+constexpr int64_t kMaxRows = ((int64_t)1 << 31) - 1;  // M and n_ids
+constexpr int64_t kMaxGemmN = (int64_t)65535 * 64;
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return Q2_0_OK;
+    g_last_hip_error = (int)e;
+    return Q2_0_ERR_HIP;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_shape(int64_t M, int64_t K, int64_t N) {
+    if (K <= 0 || K % Q2_0_BLOCK_WEIGHTS != 0 || K > kMaxK) return Q2_0_ERR_SHAPE;
+    if (M < 0 || N < 0 || M > kMaxRows) return Q2_0_ERR_SHAPE;
+    return Q2_0_OK;
+}
+
+// Common checks of mul_mat_vec and mul_mat after the empty no-op.
+int check_product(const void *w, int64_t M, int64_t K, const float *x, int64_t ldx, const float *y,
+                  int64_t ldy) {
+    if (!w || !x || !y) return Q2_0_ERR_NULL;
+    if (ldx < K || ldy < M) return Q2_0_ERR_LAYOUT;
+    if (!aligned(w, 2) || !aligned(x, 4) || !aligned(y, 4)) return Q2_0_ERR_ALIGN;
+    return Q2_0_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int q2_0_get_rows(const void *w, int64_t M, int64_t K, const int32_t *ids, int64_t n_ids,
+                  float *out, int64_t ld_out, void *stream) {
+    int st = check_shape(M, K, 0);
+    if (st) return st;
+    if (n_ids < 0 || n_ids > kMaxRows) return Q2_0_ERR_SHAPE;
+    if (n_ids == 0) return Q2_0_OK;
+    if (!w || !ids || !out) return Q2_0_ERR_NULL;
+    if (ld_out < K) return Q2_0_ERR_LAYOUT;
+    if (!aligned(w, 2) || !aligned(ids, 4) || !aligned(out, 4)) return Q2_0_ERR_ALIGN;
+    return hip_status(q2_0::launch_get_rows(static_cast<const uint8_t *>(w), M,
+                                            (int)(K / Q2_0_BLOCK_WEIGHTS), ids, n_ids, out, ld_out,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int q2_0_mul_mat_vec(const void *w, int64_t M, int64_t K, const float *x, int64_t ldx, int64_t N,
+                     float *y, int64_t ldy, void *stream) {
+    int st = check_shape(M, K, N);
+    if (st) return st;
+    if (M == 0 || N == 0) return Q2_0_OK;
+    st = check_product(w, M, K, x, ldx, y, ldy);
+    if (st) return st;
+    if (N > Q2_0_MAT_VEC_MAX_N) return Q2_0_ERR_UNSUPPORTED;
+    return hip_status(q2_0::launch_mat_vec(static_cast<const uint8_t *>(w), M,
+                                           (int)(K / Q2_0_BLOCK_WEIGHTS), x, ldx, (int)N, y, ldy,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+size_t q2_0_mul_mat_workspace_bytes(int64_t M, int64_t K, int64_t N, int precision) {
+    (void)M; (void)K; (void)N; (void)precision;
+    return 0;
+}
+
+int q2_0_mul_mat(const void *w, int64_t M, int64_t K, const float *x, int64_t ldx, int64_t N,
+                 float *y, int64_t ldy, int precision, void *workspace, size_t ws_bytes,
+                 void *stream) {
+    int st = check_shape(M, K, N);
+    if (st) return st;
+    if (N > kMaxGemmN) return Q2_0_ERR_SHAPE;
+    if (M == 0 || N == 0) return Q2_0_OK;
+    st = check_product(w, M, K, x, ldx, y, ldy);
+    if (st) return st;
+    if (precision != Q2_0_PREC_F16_MFMA && precision != Q2_0_PREC_F32) return Q2_0_ERR_UNSUPPORTED;
+    if (ws_bytes < q2_0_mul_mat_workspace_bytes(M, K, N, precision)) return Q2_0_ERR_WORKSPACE;
+    (void)workspace;
+    const uint8_t *wb = static_cast<const uint8_t *>(w);
+    const int nb = (int)(K / Q2_0_BLOCK_WEIGHTS);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (N <= Q2_0_MAT_VEC_MAX_N)
+        return hip_status(q2_0::launch_mat_vec(wb, M, nb, x, ldx, (int)N, y, ldy, s));
+    if (precision == Q2_0_PREC_F16_MFMA)
+        return hip_status(q2_0::launch_gemm_f16(wb, M, nb, x, ldx, N, y, ldy, s));
+    return hip_status(q2_0::launch_gemm_f32(wb, M, nb, x, ldx, N, y, ldy, s));
+}
+
+const char *q2_0_status_string(int status) {
+    switch (status) {
+        case Q2_0_OK: return "Q2_0_OK";
+        case Q2_0_ERR_NULL: return "Q2_0_ERR_NULL: a required pointer is NULL";
+        case Q2_0_ERR_SHAPE: return "Q2_0_ERR_SHAPE: K must be a positive multiple of 64 and sizes non-negative and within limits";
+        case Q2_0_ERR_LAYOUT: return "Q2_0_ERR_LAYOUT: a leading dimension is smaller than the row length";
+        case Q2_0_ERR_ALIGN: return "Q2_0_ERR_ALIGN: w must be 2-byte aligned and float/int32 buffers 4-byte aligned";
+        case Q2_0_ERR_UNSUPPORTED: return "Q2_0_ERR_UNSUPPORTED: N > 8 for mat-vec, or unknown precision";
+        case Q2_0_ERR_WORKSPACE: return "Q2_0_ERR_WORKSPACE: workspace too small";
+        case Q2_0_ERR_HIP: return "Q2_0_ERR_HIP: a HIP launch failed";
+        default: return "unknown q2_0 status";
+    }
+}
+
+int q2_0_last_hip_error(void) { return g_last_hip_error; }
+
+const char *q2_0_version(void) { return "q2_0 0.1.0 gfx950"; }
+
+}  // extern "C"

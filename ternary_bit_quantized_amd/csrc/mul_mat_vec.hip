@@ -1,0 +1,93 @@
+// mul_mat_vec: y = W x for N = 1..8 activation columns, fp32-grade.
+//
+// bisque.today, "WebGPU: add Q2_0 support", the matrix-vector paragraph: a block's
+// 64 weights are split over four threads of 16 weights each; a thread loads the
+// block's scale and one 32-bit word, accumulates (q - 1) * x over its 16 codes and
+// multiplies that partial sum by the scale once.
+//
+// Generic kernel (any row alignment, any K): one wave per output row; lane l takes
+// code words l, l+64, ... of the row, forms the 16-term partial sum per column in
+// f32, scales it by d and accumulates; the 64 lane sums are combined with a
+// butterfly.  Summation depth per output: 16 + K/1024 + 6, far below what the
+// 1e-5 relative bound allows (about 160 f32 roundings).
+#include "q2_0_internal.h"
+
+namespace q2_0 {
+
+template <int NC, bool kVecX>
+__global__ __launch_bounds__(256) void mat_vec_generic(const uint8_t *__restrict__ w, int64_t M,
+                                                       int nb, const float *__restrict__ x,
+                                                       int64_t ldx, float *__restrict__ y,
+                                                       int64_t ldy) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;
+    const uint8_t *wr = w + row * (int64_t)nb * kBlockBytes;
+    const int words = nb * 4;
+    float acc[NC];
+#pragma unroll
+    for (int n = 0; n < NC; ++n) acc[n] = 0.f;
+    for (int t = lane; t < words; t += 64) {
+        const uint16_t *blk16 = reinterpret_cast<const uint16_t *>(wr + (t >> 2) * kBlockBytes);
+        const float d = half_bits_to_float(blk16[0]);
+        const uint32_t q = load_word_u16x2(blk16, t & 3);
+        float qm1[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) qm1[i] = (float)((int)((q >> (2 * i)) & 3u) - 1);
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+            const float *xp = x + n * ldx + t * 16;
+            float xv[16];
+            if (kVecX) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float4_t v = reinterpret_cast<const float4_t *>(xp)[j];
+                    xv[4 * j] = v.x; xv[4 * j + 1] = v.y; xv[4 * j + 2] = v.z; xv[4 * j + 3] = v.w;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) xv[i] = xp[i];
+            }
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s = __builtin_fmaf(qm1[i], xv[i], s);
+            acc[n] = __builtin_fmaf(d, s, acc[n]);
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        float v = acc[n];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+        if (lane == 0) y[n * ldy + row] = v;
+    }
+}
+
+template <int NC>
+static void launch_generic_nc(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx,
+                              float *y, int64_t ldy, hipStream_t s, bool vec) {
+    dim3 grid((unsigned)((M + 3) / 4));
+    if (vec)
+        mat_vec_generic<NC, true><<<grid, 256, 0, s>>>(w, M, nb, x, ldx, y, ldy);
+    else
+        mat_vec_generic<NC, false><<<grid, 256, 0, s>>>(w, M, nb, x, ldx, y, ldy);
+}
+
+hipError_t launch_mat_vec(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx, int N,
+                          float *y, int64_t ldy, hipStream_t s) {
+    const bool vec = ((uintptr_t)x % 16 == 0) && (ldx % 4 == 0);
+    switch (N) {
+        case 1: launch_generic_nc<1>(w, M, nb, x, ldx, y, ldy, s, vec); break;
+        case 2: launch_generic_nc<2>(w, M, nb, x, ldx, y, ldy, s, vec); break;
+        case 3: launch_generic_nc<3>(w, M, nb, x, ldx, y, ldy, s, vec); break;
+        case 4: launch_generic_nc<4>(w, M, nb, x, ldx, y, ldy, s, vec); break;
+        case 5: launch_generic_nc<5>(w, M, nb, x, ldx, y, ldy, s, vec); break;
+        case 6: launch_generic_nc<6>(w, M, nb, x, ldx, y, ldy, s, vec); break;
+        case 7: launch_generic_nc<7>(w, M, nb, x, ldx, y, ldy, s, vec); break;
+        case 8: launch_generic_nc<8>(w, M, nb, x, ldx, y, ldy, s, vec); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace q2_0

@@ -1,0 +1,39 @@
+// Internal declarations shared by the HIP sources of libq2_0.so (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q2_0 {
+
+constexpr int kBlockWeights = 64;
+constexpr int kBlockBytes = 18;
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+
+// IEEE half bits -> f32 (v_cvt_f32_f16: exact for every half, subnormals included).
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+// Scale and one 32-bit code word of block `blk` from a 2-byte aligned block base.
+// Word w sits at byte 2 + 4w: 4-byte aligned only for odd blocks of an aligned row,
+// so it is read as two half-words.
+__device__ __forceinline__ uint32_t load_word_u16x2(const uint16_t *blk16, int w) {
+    return (uint32_t)blk16[1 + 2 * w] | ((uint32_t)blk16[2 + 2 * w] << 16);
+}
+
+// Launchers (return the HIP error of the launch).
+hipError_t launch_get_rows(const uint8_t *w, int64_t M, int nb, const int32_t *ids, int64_t n_ids,
+                           float *out, int64_t ld_out, hipStream_t s);
+hipError_t launch_mat_vec(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx, int N,
+                          float *y, int64_t ldy, hipStream_t s);
+hipError_t launch_gemm_f16(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx,
+                           int64_t N, float *y, int64_t ldy, hipStream_t s);
+hipError_t launch_gemm_f32(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx,
+                           int64_t N, float *y, int64_t ldy, hipStream_t s);
+
+}  // namespace q2_0

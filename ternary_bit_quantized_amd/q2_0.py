@@ -1,0 +1,162 @@
+"""Python binding of libq2_0.so (ctypes).  Argument marshalling only.
+
+Every computation happens in the HIP kernels behind the C ABI declared in
+include/q2_0.h.  PyTorch supplies device memory and the current stream; there is
+no fallback of any kind: if the library is missing or a call fails, an exception
+is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libq2_0.so")
+
+Q2_0_OK = 0
+Q2_0_ERR_NULL = 1
+Q2_0_ERR_SHAPE = 2
+Q2_0_ERR_LAYOUT = 3
+Q2_0_ERR_ALIGN = 4
+Q2_0_ERR_UNSUPPORTED = 5
+Q2_0_ERR_WORKSPACE = 6
+Q2_0_ERR_HIP = 7
+Q2_0_PREC_F16_MFMA = 0
+Q2_0_PREC_F32 = 1
+BLOCK_WEIGHTS = 64
+BLOCK_BYTES = 18
+MAT_VEC_MAX_N = 8
+
+EXPORTS = ("q2_0_get_rows", "q2_0_mul_mat_vec", "q2_0_mul_mat", "q2_0_mul_mat_workspace_bytes",
+           "q2_0_status_string", "q2_0_last_hip_error", "q2_0_version")
+
+
+class Q2_0Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        msg = lib().q2_0_status_string(status).decode()
+        if status == Q2_0_ERR_HIP:
+            msg += " (hipError %d)" % lib().q2_0_last_hip_error()
+        super().__init__("%s: %s" % (what, msg))
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libq2_0.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libq2_0.so is not built (%s); run `python -m "
+                               "ternary_bit_quantized_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64 = ctypes.c_void_p, ctypes.c_int64
+        L.q2_0_get_rows.argtypes = [P, I64, I64, P, I64, P, I64, P]
+        L.q2_0_mul_mat_vec.argtypes = [P, I64, I64, P, I64, I64, P, I64, P]
+        L.q2_0_mul_mat.argtypes = [P, I64, I64, P, I64, I64, P, I64, ctypes.c_int, P,
+                                   ctypes.c_size_t, P]
+        L.q2_0_mul_mat_workspace_bytes.argtypes = [I64, I64, I64, ctypes.c_int]
+        L.q2_0_mul_mat_workspace_bytes.restype = ctypes.c_size_t
+        L.q2_0_status_string.argtypes = [ctypes.c_int]
+        L.q2_0_status_string.restype = ctypes.c_char_p
+        L.q2_0_version.restype = ctypes.c_char_p
+        for f in (L.q2_0_get_rows, L.q2_0_mul_mat_vec, L.q2_0_mul_mat, L.q2_0_last_hip_error):
+            f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != Q2_0_OK:
+        raise Q2_0Error(status, what)
+
+
+# ----------------------------------------------------------------------------- raw (pointers)
+
+def get_rows_raw(w: int, M: int, K: int, ids: int, n_ids: int, out: int, ld_out: int,
+                 stream: int = 0) -> int:
+    return lib().q2_0_get_rows(w, M, K, ids, n_ids, out, ld_out, stream)
+
+
+def mul_mat_vec_raw(w: int, M: int, K: int, x: int, ldx: int, N: int, y: int, ldy: int,
+                    stream: int = 0) -> int:
+    return lib().q2_0_mul_mat_vec(w, M, K, x, ldx, N, y, ldy, stream)
+
+
+def mul_mat_raw(w: int, M: int, K: int, x: int, ldx: int, N: int, y: int, ldy: int, precision: int,
+                workspace: int, ws_bytes: int, stream: int = 0) -> int:
+    return lib().q2_0_mul_mat(w, M, K, x, ldx, N, y, ldy, precision, workspace, ws_bytes, stream)
+
+
+def mul_mat_workspace_bytes(M: int, K: int, N: int, precision: int) -> int:
+    return int(lib().q2_0_mul_mat_workspace_bytes(M, K, N, precision))
+
+
+def version() -> str:
+    return lib().q2_0_version().decode()
+
+
+# ----------------------------------------------------------------------------- torch tensors
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _cols(t, K, name):
+    """A (N, >=K) float32 device tensor with unit column stride -> (ptr, N, ld)."""
+    import torch
+    if t.dtype != torch.float32 or not t.is_cuda or t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("%s must be a 2-D float32 CUDA tensor with unit inner stride" % name)
+    if t.shape[1] < K:
+        raise ValueError("%s must have at least %d columns" % (name, K))
+    ld = t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
+    return t.data_ptr(), t.shape[0], ld
+
+
+def q2_0_get_rows(w, M: int, K: int, ids, out=None, stream=None):
+    """out[r, :K] = dequantized row ids[r] of the (M, K) Q2_0 matrix w (uint8 device tensor)."""
+    import torch
+    n = ids.numel()
+    if out is None:
+        out = torch.empty((n, K), dtype=torch.float32, device=w.device)
+    ptr, rows, ld = _cols(out, K, "out")
+    if ids.dtype != torch.int32 or not ids.is_contiguous():
+        raise ValueError("ids must be a contiguous int32 tensor")
+    _check(get_rows_raw(w.data_ptr(), M, K, ids.data_ptr(), n, ptr, ld, _stream(stream)),
+           "q2_0_get_rows")
+    return out
+
+
+def q2_0_mul_mat_vec(w, M: int, K: int, x, y=None, stream=None):
+    """y (N, M) = W x for x (N, K), N <= 8."""
+    import torch
+    xp, N, ldx = _cols(x, K, "x")
+    if y is None:
+        y = torch.empty((N, M), dtype=torch.float32, device=x.device)
+    yp, _, ldy = _cols(y, M, "y")
+    _check(mul_mat_vec_raw(w.data_ptr(), M, K, xp, ldx, N, yp, ldy, _stream(stream)),
+           "q2_0_mul_mat_vec")
+    return y
+
+
+def q2_0_mul_mat(w, M: int, K: int, x, precision: int = Q2_0_PREC_F16_MFMA, y=None, workspace=None,
+                 stream=None):
+    """y (N, M) = W x for x (N, K), any N."""
+    import torch
+    xp, N, ldx = _cols(x, K, "x")
+    if y is None:
+        y = torch.empty((N, M), dtype=torch.float32, device=x.device)
+    yp, _, ldy = _cols(y, M, "y")
+    need = mul_mat_workspace_bytes(M, K, N, precision)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wsp = workspace.data_ptr() if workspace is not None else 0
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(mul_mat_raw(w.data_ptr(), M, K, xp, ldx, N, yp, ldy, precision, wsp, wsb, _stream(stream)),
+           "q2_0_mul_mat")
+    return y

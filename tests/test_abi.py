@@ -1,0 +1,101 @@
+"""The C ABI on the host: the library loads, exports what include/q2_0.h declares, and
+rejects bad arguments with the documented status before touching the GPU.
+
+No call here launches a kernel: every call either fails validation or is an empty
+no-op, which returns before any HIP call, so these run without a GPU.
+"""
+
+import os
+import re
+
+import pytest
+
+from ternary_bit_quantized_amd import q2_0 as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q2_0.h")
+
+# Fake but aligned device addresses: validation never dereferences them.
+P16, P4 = 1 << 20, (1 << 20) + 4
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(q2_0_[a-z_]+)\s*\(", text))
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    declared = _declared()
+    assert declared == set(B.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in B.version()
+    for s in range(8):
+        assert B.lib().q2_0_status_string(s).decode().startswith("Q2_0_")
+    assert B.lib().q2_0_status_string(99) == b"unknown q2_0 status"
+    assert B.lib().q2_0_last_hip_error() == 0
+
+
+@pytest.mark.parametrize("K", [0, -64, 100, 63, 1 << 25])
+def test_shape_errors(K):
+    assert B.get_rows_raw(P16, 10, K, P4, 1, P16, max(K, 1)) == B.Q2_0_ERR_SHAPE
+    assert B.mul_mat_vec_raw(P16, 10, K, P16, max(K, 1), 1, P16, 10) == B.Q2_0_ERR_SHAPE
+    assert B.mul_mat_raw(P16, 10, K, P16, max(K, 1), 16, P16, 10, 0, 0, 0) == B.Q2_0_ERR_SHAPE
+
+
+def test_negative_sizes():
+    assert B.get_rows_raw(P16, -1, 64, P4, 1, P16, 64) == B.Q2_0_ERR_SHAPE
+    assert B.get_rows_raw(P16, 1, 64, P4, -1, P16, 64) == B.Q2_0_ERR_SHAPE
+    assert B.mul_mat_vec_raw(P16, 1, 64, P16, 64, -1, P16, 1) == B.Q2_0_ERR_SHAPE
+    assert B.mul_mat_raw(P16, -5, 64, P16, 64, 16, P16, 1, 0, 0, 0) == B.Q2_0_ERR_SHAPE
+    assert B.mul_mat_raw(P16, 5, 64, P16, 64, 65535 * 64 + 1, P16, 5, 0, 0, 0) == B.Q2_0_ERR_SHAPE
+
+
+def test_empty_is_ok_even_with_null_pointers():
+    assert B.get_rows_raw(0, 10, 64, 0, 0, 0, 64) == B.Q2_0_OK
+    assert B.mul_mat_vec_raw(0, 0, 64, 0, 64, 1, 0, 0) == B.Q2_0_OK
+    assert B.mul_mat_vec_raw(0, 10, 64, 0, 64, 0, 0, 10) == B.Q2_0_OK
+    assert B.mul_mat_raw(0, 0, 64, 0, 64, 100, 0, 0, 0, 0, 0) == B.Q2_0_OK
+    assert B.mul_mat_raw(0, 10, 64, 0, 64, 0, 0, 10, 1, 0, 0) == B.Q2_0_OK
+
+
+def test_null_pointers():
+    assert B.get_rows_raw(0, 10, 64, P4, 1, P16, 64) == B.Q2_0_ERR_NULL
+    assert B.get_rows_raw(P16, 10, 64, 0, 1, P16, 64) == B.Q2_0_ERR_NULL
+    assert B.get_rows_raw(P16, 10, 64, P4, 1, 0, 64) == B.Q2_0_ERR_NULL
+    for args in [(0, P16, P16), (P16, 0, P16), (P16, P16, 0)]:
+        w, x, y = args
+        assert B.mul_mat_vec_raw(w, 10, 64, x, 64, 1, y, 10) == B.Q2_0_ERR_NULL
+        assert B.mul_mat_raw(w, 10, 64, x, 64, 32, y, 10, 0, 0, 0) == B.Q2_0_ERR_NULL
+
+
+def test_layout_errors():
+    assert B.get_rows_raw(P16, 10, 128, P4, 1, P16, 127) == B.Q2_0_ERR_LAYOUT
+    assert B.mul_mat_vec_raw(P16, 10, 128, P16, 127, 2, P16, 10) == B.Q2_0_ERR_LAYOUT
+    assert B.mul_mat_vec_raw(P16, 10, 128, P16, 128, 2, P16, 9) == B.Q2_0_ERR_LAYOUT
+    assert B.mul_mat_raw(P16, 10, 128, P16, 64, 20, P16, 10, 0, 0, 0) == B.Q2_0_ERR_LAYOUT
+
+
+def test_alignment_errors():
+    assert B.get_rows_raw(P16 + 1, 10, 64, P4, 1, P16, 64) == B.Q2_0_ERR_ALIGN
+    assert B.get_rows_raw(P16, 10, 64, P4 + 2, 1, P16, 64) == B.Q2_0_ERR_ALIGN
+    assert B.get_rows_raw(P16, 10, 64, P4, 1, P16 + 2, 64) == B.Q2_0_ERR_ALIGN
+    assert B.mul_mat_vec_raw(P16 + 1, 10, 64, P16, 64, 1, P16, 10) == B.Q2_0_ERR_ALIGN
+    assert B.mul_mat_vec_raw(P16, 10, 64, P16 + 2, 64, 1, P16, 10) == B.Q2_0_ERR_ALIGN
+    assert B.mul_mat_raw(P16, 10, 64, P16, 64, 20, P16 + 1, 10, 0, 0, 0) == B.Q2_0_ERR_ALIGN
+
+
+def test_unsupported():
+    assert B.mul_mat_vec_raw(P16, 10, 64, P16, 64, 9, P16, 10) == B.Q2_0_ERR_UNSUPPORTED
+    assert B.mul_mat_raw(P16, 10, 64, P16, 64, 20, P16, 10, 2, 0, 0) == B.Q2_0_ERR_UNSUPPORTED
+    assert B.mul_mat_raw(P16, 10, 64, P16, 64, 20, P16, 10, -1, 0, 0) == B.Q2_0_ERR_UNSUPPORTED
+
+
+def test_workspace_query():
+    for p in (B.Q2_0_PREC_F16_MFMA, B.Q2_0_PREC_F32):
+        assert B.mul_mat_workspace_bytes(4096, 4096, 512, p) >= 0

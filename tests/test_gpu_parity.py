@@ -1,0 +1,321 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+get_rows must match bit for bit (NaN matches NaN).  Products must satisfy
+|y - y_ref| <= rel * sum|W x| elementwise with rel = 1e-5 on the fp32 paths (mat-vec
+and the fp32 GEMM) and 2e-3 on the fp16-MFMA GEMM; a non-finite y fails where y_ref is
+finite, and a zero bound demands y == 0 exactly.  Large workloads run at full size on
+the GPU and are compared on sampled rows the oracle computes one by one.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from ternary_bit_quantized_amd import q2_0 as B
+from ternary_bit_quantized_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+REL_F32 = 1e-5
+REL_F16 = 2e-3
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def dev(a):
+    torch = _torch()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    _torch().cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def same_bits(a, b):
+    a = np.asarray(a, dtype=np.float32)
+    b = np.asarray(b, dtype=np.float32)
+    nan = np.isnan(a) & np.isnan(b)
+    eq = nan | (a.view(np.uint32) == b.view(np.uint32))
+    return bool(eq.all()), int((~eq).sum())
+
+
+def assert_products(y, w, M, K, x, rel, rows=None, what=""):
+    y_ref, bound = oracle.mul_mat(w, M, K, x, rows=rows)
+    yy = y if rows is None else y[:, rows]
+    r = oracle.check_products(yy, y_ref, bound, rel)
+    assert r["ok"], "%s: %d/%d outside %.0e*bound, worst %.3g, first %s" % (
+        what, r["n_bad"], r["n"], rel, r["max_err_over_bound"], r["first_bad"])
+    return r
+
+
+def run_mat_vec(w_d, M, K, x, ldx=None, ldy=None):
+    torch = _torch()
+    N = x.shape[0]
+    ldx = ldx or K
+    ldy = ldy or M
+    xb = np.zeros((N, ldx), dtype=np.float32)
+    xb[:, :K] = x
+    xd = dev(xb)
+    yd = torch.full((N, ldy), float("nan"), dtype=torch.float32, device="cuda")
+    st = B.mul_mat_vec_raw(w_d.data_ptr(), M, K, xd.data_ptr(), ldx, N, yd.data_ptr(), ldy,
+                           torch.cuda.current_stream().cuda_stream)
+    assert st == 0, B.lib().q2_0_status_string(st)
+    y = host(yd)
+    if ldy > M:
+        assert np.all(np.isnan(y[:, M:])), "mat-vec wrote past M"
+    return y[:, :M]
+
+
+def run_mul_mat(w_d, M, K, x, precision, ldx=None, ldy=None):
+    torch = _torch()
+    N = x.shape[0]
+    ldx = ldx or K
+    ldy = ldy or M
+    xb = np.zeros((N, ldx), dtype=np.float32)
+    xb[:, :K] = x
+    xd = dev(xb)
+    yd = torch.full((N, ldy), float("nan"), dtype=torch.float32, device="cuda")
+    ws = B.mul_mat_workspace_bytes(M, K, N, precision)
+    wsd = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
+    st = B.mul_mat_raw(w_d.data_ptr(), M, K, xd.data_ptr(), ldx, N, yd.data_ptr(), ldy, precision,
+                       wsd.data_ptr(), ws, torch.cuda.current_stream().cuda_stream)
+    assert st == 0, B.lib().q2_0_status_string(st)
+    y = host(yd)
+    if ldy > M:
+        assert np.all(np.isnan(y[:, M:])), "mul_mat wrote past M"
+    return y[:, :M]
+
+
+def run_get_rows(w_d, M, K, ids, ld_out=None, offset=0):
+    torch = _torch()
+    ld = ld_out or K
+    n = ids.size
+    buf = torch.full((n * ld + offset + 16,), float("nan"), dtype=torch.float32, device="cuda")
+    sentinel = np.float32(-12345.5)
+    buf.fill_(float(sentinel))
+    idd = dev(ids.astype(np.int32))
+    st = B.get_rows_raw(w_d.data_ptr(), M, K, idd.data_ptr(), n, buf.data_ptr() + 4 * offset, ld,
+                        torch.cuda.current_stream().cuda_stream)
+    assert st == 0, B.lib().q2_0_status_string(st)
+    flat = host(buf)
+    assert np.all(flat[:offset] == sentinel) and np.all(flat[offset + n * ld:] == sentinel)
+    out = flat[offset:offset + n * ld].reshape(n, ld)
+    if ld > K:
+        assert np.all(out[:, K:] == sentinel), "get_rows wrote past K"
+    return out[:, :K]
+
+
+def ws(wl, name="w", layer=0):
+    return synth.workload_weight(wl, name, layer)
+
+
+# =============================================================================== get_rows
+
+def test_get_rows_tiny_workload():
+    M, K = synth.TINY.shapes["w"]
+    w = ws(synth.TINY)
+    ids = synth.row_ids(synth.TINY.seed, 0, 0, synth.TINY_IDS, M)
+    out = run_get_rows(dev(w), M, K, ids)
+    ok, nbad = same_bits(out, oracle.get_rows(w, M, K, ids))
+    assert ok, nbad
+
+
+def test_get_rows_every_half_scale():
+    rng = np.random.default_rng(0)
+    M, K = 65536, 64
+    w = synth.random_blocks(rng, M, 1)
+    w[:, 0] = (np.arange(M) & 0xFF).astype(np.uint8)
+    w[:, 1] = (np.arange(M) >> 8).astype(np.uint8)
+    ids = np.arange(M, dtype=np.int32)
+    out = run_get_rows(dev(w), M, K, ids)
+    ok, nbad = same_bits(out, oracle.get_rows(w, M, K, ids))
+    assert ok, nbad
+
+
+@pytest.mark.parametrize("M,K,n,ld,off", [(300, 192, 14000, 192, 0), (77, 64, 500, 70, 1),
+                                          (1000, 4096, 64, 4100, 3), (5, 128, 33, 128, 2)])
+def test_get_rows_random_bytes_fuzz(M, K, n, ld, off):
+    rng = np.random.default_rng(M + K + n)
+    w = synth.random_blocks(rng, M, K // 64)
+    ids = rng.integers(-3, M + 3, size=n).astype(np.int32)
+    ids[:4] = [0, M - 1, -1, M]
+    out = run_get_rows(dev(w), M, K, ids, ld_out=ld, offset=off)
+    ok, nbad = same_bits(out, oracle.get_rows(w, M, K, ids))
+    assert ok, nbad
+    assert np.all(np.isnan(out[(ids < 0) | (ids >= M)]))
+
+
+def test_get_rows_vocab_workload():
+    wl = synth.VOCAB_8B
+    M, K = wl.shapes["emb"]
+    w = ws(wl, "emb")
+    ids = synth.row_ids(wl.seed, 0, 0, synth.VOCAB_IDS, M)
+    out = run_get_rows(dev(w), M, K, ids)
+    ok, nbad = same_bits(out, oracle.get_rows(w, M, K, ids))
+    assert ok, nbad
+
+
+# =============================================================================== mat-vec
+
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_mat_vec_tiny_all_n(N):
+    M, K = synth.TINY.shapes["w"]
+    w = ws(synth.TINY)
+    x = synth.activations(synth.TINY.seed, 0, 0, N, K)
+    y = run_mat_vec(dev(w), M, K, x)
+    assert_products(y, w, M, K, x, REL_F32, what="tiny N=%d" % N)
+
+
+@pytest.mark.parametrize("M,K,N,ldx,ldy,codes", [
+    (1, 64, 1, 64, 1, "quad"), (257, 192, 3, 200, 300, "quad"), (63, 576, 8, 577, 64, "tern"),
+    (129, 4096, 2, 4096, 129, "quad"), (31, 12288, 5, 12288, 40, "tern_c3"), (1000, 64 * 9, 1, 577, 1000, "quad"),
+    (4095, 2048, 8, 2048, 4095, "quad"), (16, 512 + 64, 4, 600, 16, "quad")])
+def test_mat_vec_ragged_and_strided(M, K, N, ldx, ldy, codes):
+    w = synth.weight(11, M, K // 64, M, K, codes, synth.ScaleDist("loguniform", 1e-3, 1e-1, 0.02))
+    x = synth.activations(11, M, K // 64, N, K)
+    y = run_mat_vec(dev(w), M, K, x, ldx=ldx, ldy=ldy)
+    assert_products(y, w, M, K, x, REL_F32, what="M=%d K=%d N=%d" % (M, K, N))
+
+
+@pytest.mark.parametrize("code,factor", [(1, 0.0), (2, 1.0), (0, -1.0), (3, 2.0)])
+def test_mat_vec_closed_forms(code, factor):
+    rng = np.random.default_rng(code)
+    M, K, N = 96, 2048, 4
+    d = rng.uniform(0.001, 0.1, size=(M, K // 64)).astype(np.float16)
+    codes = np.full((M, K), code, dtype=np.uint8)
+    w = synth.pack(codes, d)
+    x = rng.standard_normal((N, K), dtype=np.float32)
+    y = run_mat_vec(dev(w), M, K, x)
+    if factor == 0.0:
+        assert np.all(y == 0.0)
+    expect = factor * (x.astype(np.float64).reshape(N, K // 64, 64).sum(-1) @ d.astype(np.float64).T)
+    _, bound = oracle.mul_mat(w, M, K, x)
+    assert np.all(np.abs(y - expect) <= REL_F32 * bound)
+
+
+def test_mat_vec_decode_1p7b_workload():
+    wl = synth.DECODE_1P7B
+    for name, (M, K) in wl.shapes.items():
+        w = ws(wl, name)
+        wd = dev(w)
+        for N in wl.ns:
+            x = synth.activations(wl.seed, 0, synth.MATS.index(name), N, K)
+            y = run_mat_vec(wd, M, K, x)
+            assert_products(y, w, M, K, x, REL_F32, what="%s N=%d" % (name, N))
+
+
+def test_mat_vec_stack_8b_layer_workload():
+    wl = synth.STACK_8B
+    rng = np.random.default_rng(3)
+    for name, (M, K) in wl.shapes.items():
+        w = ws(wl, name, layer=35)
+        x = synth.activations(wl.seed, 0, synth.stack_x_matrix_index(K), 1, K)
+        y = run_mat_vec(dev(w), M, K, x)
+        rows = np.unique(np.concatenate([rng.integers(0, M, 512), [0, M - 1]]))
+        assert_products(y, w, M, K, x, REL_F32, rows=rows, what=name)
+
+
+@pytest.mark.parametrize("N", [1, 4])
+def test_mat_vec_vocab_head_workload(N):
+    wl = synth.VOCAB_8B
+    M, K = wl.shapes["emb"]
+    w = ws(wl, "emb")
+    x = synth.activations(wl.seed, 0, 0, N, K)
+    y = run_mat_vec(dev(w), M, K, x)
+    rows = np.unique(np.concatenate([np.random.default_rng(N).integers(0, M, 2048), [0, M - 1]]))
+    assert_products(y, w, M, K, x, REL_F32, rows=rows, what="head N=%d" % N)
+
+
+def test_mat_vec_metamorphic_scale_and_permute():
+    rng = np.random.default_rng(21)
+    M, K, N = 200, 1024, 3
+    codes = rng.integers(0, 4, size=(M, K), dtype=np.uint8)
+    d = rng.uniform(0.01, 0.1, size=(M, K // 64)).astype(np.float16)
+    x = rng.standard_normal((N, K), dtype=np.float32)
+    y = run_mat_vec(dev(synth.pack(codes, d)), M, K, x)
+    y4 = run_mat_vec(dev(synth.pack(codes, (d.astype(np.float32) * 4).astype(np.float16))), M, K, x)
+    assert np.array_equal(y4, 4 * y)
+    perm = rng.permutation(M)
+    yp = run_mat_vec(dev(synth.pack(codes[perm], d[perm])), M, K, x)
+    assert np.array_equal(yp, y[:, perm])
+    for n in range(N):
+        y1 = run_mat_vec(dev(synth.pack(codes, d)), M, K, x[n:n + 1])
+        _, bound = oracle.mul_mat(synth.pack(codes, d), M, K, x[n:n + 1])
+        assert np.all(np.abs(y1[0] - y[n]) <= 2 * REL_F32 * bound[0])
+
+
+# =============================================================================== GEMM
+
+@pytest.mark.parametrize("precision,rel", [(B.Q2_0_PREC_F16_MFMA, REL_F16), (B.Q2_0_PREC_F32, REL_F32)])
+@pytest.mark.parametrize("M,K,N,ldx,ldy", [
+    (64, 64, 64, 64, 64), (1, 64, 9, 64, 1), (65, 192, 63, 200, 70), (200, 512, 130, 512, 203),
+    (127, 2048, 65, 2050, 127), (33, 576, 100, 576, 33)])
+def test_mul_mat_ragged(precision, rel, M, K, N, ldx, ldy):
+    w = synth.weight(12, M, N, M, K, "quad", synth.ScaleDist("loguniform", 1e-3, 1e-1, 0.02))
+    x = synth.activations(12, M, N, N, K)
+    y = run_mul_mat(dev(w), M, K, x, precision, ldx=ldx, ldy=ldy)
+    assert_products(y, w, M, K, x, rel, what="p=%d M=%d K=%d N=%d" % (precision, M, K, N))
+
+
+@pytest.mark.parametrize("precision,rel", [(B.Q2_0_PREC_F16_MFMA, REL_F16), (B.Q2_0_PREC_F32, REL_F32)])
+def test_mul_mat_prefill_1p7b_workload(precision, rel):
+    wl = synth.PREFILL_1P7B
+    rng = np.random.default_rng(2)
+    for name, (M, K) in wl.shapes.items():
+        w = ws(wl, name)
+        x = synth.activations(wl.seed, 0, synth.MATS.index(name), 512, K)
+        y = run_mul_mat(dev(w), M, K, x, precision)
+        rows = np.unique(np.concatenate([rng.integers(0, M, 96), [0, M - 1]]))
+        assert_products(y, w, M, K, x, rel, rows=rows, what=name)
+
+
+@pytest.mark.parametrize("precision,rel", [(B.Q2_0_PREC_F16_MFMA, REL_F16), (B.Q2_0_PREC_F32, REL_F32)])
+def test_mul_mat_stack_8b_workload(precision, rel):
+    wl = synth.STACK_8B
+    rng = np.random.default_rng(4)
+    for name in ("k", "down"):
+        M, K = wl.shapes[name]
+        w = ws(wl, name, layer=0)
+        x = synth.activations(wl.seed, 0, synth.stack_x_matrix_index(K) + 10, 512, K)
+        y = run_mul_mat(dev(w), M, K, x, precision)
+        rows = np.unique(np.concatenate([rng.integers(0, M, 48), [0, M - 1]]))
+        assert_products(y, w, M, K, x, rel, rows=rows, what=name)
+
+
+def test_mul_mat_small_n_routes_to_mat_vec():
+    M, K = 300, 1024
+    w = synth.weight(13, 0, 0, M, K, "quad", synth.ScaleDist("uniform", 0.01, 0.1))
+    wd = dev(w)
+    for N in (1, 5, 8):
+        x = synth.activations(13, 0, N, N, K)
+        a = run_mat_vec(wd, M, K, x)
+        for p in (B.Q2_0_PREC_F16_MFMA, B.Q2_0_PREC_F32):
+            assert np.array_equal(run_mul_mat(wd, M, K, x, p), a)
+
+
+@pytest.mark.parametrize("precision", [B.Q2_0_PREC_F16_MFMA, B.Q2_0_PREC_F32])
+def test_mul_mat_all_code_one_is_exactly_zero(precision):
+    rng = np.random.default_rng(5)
+    M, K, N = 130, 1024, 70
+    d = rng.uniform(0.01, 1.0, size=(M, K // 64)).astype(np.float16)
+    w = synth.pack(np.ones((M, K), dtype=np.uint8), d)
+    x = rng.standard_normal((N, K), dtype=np.float32)
+    y = run_mul_mat(dev(w), M, K, x, precision)
+    assert np.all(y == 0.0)
+
+
+@pytest.mark.parametrize("precision", [B.Q2_0_PREC_F16_MFMA, B.Q2_0_PREC_F32])
+def test_mul_mat_metamorphic_scale(precision):
+    rng = np.random.default_rng(6)
+    M, K, N = 100, 512, 40
+    codes = rng.integers(0, 4, size=(M, K), dtype=np.uint8)
+    d = rng.uniform(0.01, 0.1, size=(M, K // 64)).astype(np.float16)
+    x = rng.standard_normal((N, K), dtype=np.float32)
+    y = run_mul_mat(dev(synth.pack(codes, d)), M, K, x, precision)
+    y8 = run_mul_mat(dev(synth.pack(codes, (d.astype(np.float32) * 8).astype(np.float16))), M, K, x,
+                     precision)
+    assert np.array_equal(y8, 8 * y)
