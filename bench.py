@@ -9,15 +9,19 @@ One step is one pass of the whole hot path:
   prefill: get_rows of 512 token ids, then the 252 stack matrices at N = 512 on the
            fp16-MFMA GEMM;
   decode : get_rows of 1 token id, then the 252 stack matrices and the LM head at
-           N = 1 on the mat-vec (one token, weights streamed from HBM).
+           N = 1 on the mat-vec (one token, weights streamed from HBM), launched as a
+           transformer layer would: per layer one grouped launch for q/k/v (they share
+           the attention input), one for o, one grouped launch for gate/up, one for
+           down -- 4 launches per layer plus the head.
 Each part is captured once in a HIP graph and replayed, so the timed region holds
 GPU work only.  Inputs are resident in HBM before timing starts.
 
 Printed: one JSON line.  `value` is the decode mat-vec stream rate in GB/s
 (algorithmic bytes: Q2_0 weights + f32 activations + f32 outputs, over the time of
-the 253 mat-vec launches).  Extra fields give decode and prefill tokens/s, the
-prefill GEMM TFLOP/s, the roofline fractions and the CPU oracle's rate on a
-bounded sample of the same work.
+the decode mat-vec launches).  Extra fields give decode and prefill tokens/s, the
+prefill GEMM TFLOP/s, the roofline fractions, the same decode launched one matrix at
+a time and grouped by activation, and the CPU oracle's rate on a bounded sample of
+the same work.
 """
 
 from __future__ import annotations
@@ -112,14 +116,43 @@ def main():
         check(B.get_rows_raw(emb.data_ptr(), VM, VK, ids.data_ptr(), ids.numel(), out.data_ptr(), VK, s()),
               "get_rows")
 
-    def run_decode_matvecs():
+    # one output buffer per matrix so grouped launches never share a y
+    yd = {key: torch.empty((1, wl.shapes[key[1]][0]), dtype=torch.float32, device=dev) for key in order}
+
+    def head(st):
+        check(B.mul_mat_vec_raw(emb.data_ptr(), VM, VK, x1[VK].data_ptr(), VK, 1, y1[VM].data_ptr(), VM, st),
+              "lm_head")
+
+    def run_decode_per_matrix():
         st = s()
         for key in order:
             M, K = wl.shapes[key[1]]
             check(B.mul_mat_vec_raw(W[key].data_ptr(), M, K, x1[K].data_ptr(), K, 1,
-                                    y1[M].data_ptr(), M, st), "mat_vec")
-        check(B.mul_mat_vec_raw(emb.data_ptr(), VM, VK, x1[VK].data_ptr(), VK, 1, y1[VM].data_ptr(), VM, st),
-              "lm_head")
+                                    yd[key].data_ptr(), M, st), "mat_vec")
+        head(st)
+
+    def group_items(keys):
+        return B.make_items([(W[k].data_ptr(), wl.shapes[k[1]][0], yd[k].data_ptr(), wl.shapes[k[1]][0])
+                             for k in keys])
+
+    layer_groups = []
+    for l in layers:
+        for names in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
+            keys = [(l, n) for n in names]
+            layer_groups.append((group_items(keys), len(keys), wl.shapes[names[0]][1]))
+    by_k = {}
+    for key in order:
+        by_k.setdefault(wl.shapes[key[1]][1], []).append(key)
+    act_groups = [(group_items(keys), len(keys), K) for K, keys in sorted(by_k.items())]
+
+    def run_groups(groups):
+        st = s()
+        for items, n, K in groups:
+            check(B.mul_mat_vec_group_raw(items, n, K, x1[K].data_ptr(), K, 1, st), "mat_vec_group")
+        head(st)
+
+    def run_decode_matvecs():
+        run_groups(layer_groups)
 
     def run_prefill_gemms(precision=B.Q2_0_PREC_F16_MFMA):
         st = s()
@@ -134,6 +167,8 @@ def main():
         "prefill_gemm": run_prefill_gemms,
         "decode_get_rows": lambda: run_get_rows(ids_d, emb_out_d),
         "decode_mat_vec": run_decode_matvecs,
+        "decode_mat_vec_per_matrix": run_decode_per_matrix,
+        "decode_mat_vec_by_activation": lambda: run_groups(act_groups),
     }
     graphs = {}
     side = torch.cuda.Stream()
@@ -149,10 +184,13 @@ def main():
     torch.cuda.synchronize()
     log("graphs captured")
 
+    step_parts = ("prefill_get_rows", "prefill_gemm", "decode_get_rows", "decode_mat_vec")
+    compare_parts = ("decode_mat_vec_per_matrix", "decode_mat_vec_by_activation")
     ev = {n: [] for n in parts}
 
-    def step(record):
-        for name, g in graphs.items():
+    def replay(names, record):
+        for name in names:
+            g = graphs[name]
             if record:
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
@@ -164,23 +202,29 @@ def main():
                 g.replay()
 
     for _ in range(args.warmup):
-        step(False)
+        replay(step_parts, False)
     torch.cuda.synchronize()
     log("warm-up done (%d steps)" % args.warmup)
 
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for _ in range(args.steps):
-        step(True)
+        replay(step_parts, True)
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
     log("timed %d steps in %.3f s" % (args.steps, t_total))
+
+    # the same decode under two other launch schedules, for comparison (not part of the step)
+    replay(compare_parts, False)
+    for _ in range(args.steps):
+        replay(compare_parts, True)
+    torch.cuda.synchronize()
 
     ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in parts}
 
     # ---- algorithmic work
     dec_bytes = sum(mat_bytes(*wl.shapes[n], 1) for (_, n) in order) + mat_bytes(VM, VK, 1)
-    n_dec_launches = len(order) + 1
+    n_dec_launches = len(layer_groups) + 1
     pre_flops = sum(2.0 * M * K * PREFILL_N for (_, n) in order for (M, K) in [wl.shapes[n]])
     pre_bytes = sum(mat_bytes(*wl.shapes[n], PREFILL_N) for (_, n) in order)
     matvec_gbs = dec_bytes / (ms["decode_mat_vec"] * 1e-3) / 1e9
@@ -212,8 +256,15 @@ def main():
         "prefill_tokens_per_s": round(pre_tok_s, 1),
         "prefill_gemm_tflops": round(gemm_tflops, 2),
         "ms": {k: round(v, 4) for k, v in ms.items()},
+        "decode_schedules_GBps": {
+            "per_layer_groups (%d launches)" % (len(layer_groups) + 1): round(matvec_gbs, 1),
+            "per_matrix (%d launches)" % (len(order) + 1):
+                round(dec_bytes / (ms["decode_mat_vec_per_matrix"] * 1e-3) / 1e9, 1),
+            "by_activation (%d group calls)" % (len(act_groups) + 1):
+                round(dec_bytes / (ms["decode_mat_vec_by_activation"] * 1e-3) / 1e9, 1),
+        },
         "roofline": {
-            "kernel": "mat_vec (N=1, 253 launches per decode token)",
+            "kernel": "mat_vec_stream (N=1, %d launches per decode token)" % n_dec_launches,
             "bound": "hbm", "achieved": round(matvec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(matvec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
             "bytes_per_launch_avg": int(dec_bytes / n_dec_launches),

@@ -91,6 +91,29 @@ int q2_0_get_rows(const void *w, int64_t M, int64_t K, const int32_t *ids, int64
 int q2_0_mul_mat_vec(const void *w, int64_t M, int64_t K, const float *x, int64_t ldx, int64_t N,
                      float *y, int64_t ldy, void *stream);
 
+/* One matrix of a grouped mat-vec (see q2_0_mul_mat_vec_group). */
+typedef struct {
+    const void *w;   /* M x K Q2_0 matrix (device), 2-byte aligned */
+    int64_t M;       /* rows; 0 is allowed and writes nothing */
+    float *y;        /* device: N columns of M floats at y + n*ldy, 4-byte aligned */
+    int64_t ldy;     /* >= M */
+} q2_0_mat_vec_item;
+
+/*
+ * mul_mat_vec_group: several mat-vecs that share K and the activation x, in as
+ * few launches as possible: y_i = W_i x for i < n_items (for example the q, k and
+ * v projections of one layer, or gate and up).  Same arithmetic, accuracy and
+ * layouts as q2_0_mul_mat_vec; each y_i meets the same bound and does not
+ * depend on the other items or on how they are grouped.
+ *   items  : HOST array of n_items descriptors; read during the call only.
+ *   x, ldx, N, stream: as for q2_0_mul_mat_vec (1 <= N <= 8).
+ * The y_i must not overlap each other or x.  Errors are those of
+ * q2_0_mul_mat_vec, checked for every item before anything is launched
+ * (NULL also for items == NULL with n_items > 0); n_items < 0 is SHAPE.
+ */
+int q2_0_mul_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K,
+                           const float *x, int64_t ldx, int64_t N, void *stream);
+
 /*
  * mul_mat: y = W x for any N (batched prefill GEMM).
  * (bisque.today "WebGPU: add Q2_0 support": the tiled matrix multiply unpacks 16

@@ -71,6 +71,30 @@ int q2_0_mul_mat_vec(const void *w, int64_t M, int64_t K, const float *x, int64_
                                            static_cast<hipStream_t>(stream)));
 }
 
+int q2_0_mul_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K,
+                           const float *x, int64_t ldx, int64_t N, void *stream) {
+    int st = check_shape(0, K, N);
+    if (st) return st;
+    if (n_items < 0) return Q2_0_ERR_SHAPE;
+    if (n_items == 0 || N == 0) return Q2_0_OK;
+    if (!items) return Q2_0_ERR_NULL;
+    for (int64_t i = 0; i < n_items; ++i) {
+        st = check_shape(items[i].M, K, N);
+        if (st) return st;
+    }
+    bool any = false;
+    for (int64_t i = 0; i < n_items; ++i) {
+        if (items[i].M == 0) continue;
+        any = true;
+        st = check_product(items[i].w, items[i].M, K, x, ldx, items[i].y, items[i].ldy);
+        if (st) return st;
+    }
+    if (!any) return Q2_0_OK;
+    if (N > Q2_0_MAT_VEC_MAX_N) return Q2_0_ERR_UNSUPPORTED;
+    return hip_status(q2_0::launch_mat_vec_group(items, n_items, (int)(K / Q2_0_BLOCK_WEIGHTS), x, ldx,
+                                                 (int)N, static_cast<hipStream_t>(stream)));
+}
+
 size_t q2_0_mul_mat_workspace_bytes(int64_t M, int64_t K, int64_t N, int precision) {
     (void)M; (void)K; (void)N; (void)precision;
     return 0;

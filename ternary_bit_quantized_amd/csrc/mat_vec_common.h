@@ -1,0 +1,179 @@
+// Device building blocks shared by the MFMA mat-vec kernels (gfx950).
+//
+// Arithmetic (bisque.today "WebGPU: add Q2_0 support", the matrix-vector
+// paragraph): each 64-weight block contributes d * sum (q - 1) * x, the scale
+// applied once to the block's sum.  On gfx950 the block sum runs on the matrix
+// cores: v_mfma_f32_16x16x32_f16 with the activation as the A operand (A row 2n =
+// fp16(x_n), row 2n+1 = fp16(x_n - fp16(x_n)), so hi + lo carries ~22 bits of x)
+// and the exact fp16 values q - 1 as B (16 weight rows as the 16 B columns).  D
+// lane (j, g) then holds, for weight row j, x rows 4g..4g+3 = columns 2g and 2g+1
+// as (hi, lo) pairs.
+//
+// Weight layout in the wave's LDS tile: rows are 16-byte aligned, so a block pair
+// is 9 dwords D0..D8: D0 = [d_b | h0], D1..D3 = [h1|h2] [h3|h4] [h5|h6], D4 =
+// [h7 | d_b+1], D5..D8 = [h0|h1] .. [h6|h7] of block b+1 (h_i = the 8 codes of
+// weights 8i..8i+7).  Lane group g takes one code dword per block: even blocks
+// (h0,h7) (h1,h2) (h3,h4) (h5,h6), odd blocks (h0,h1) .. (h6,h7).  The A operand
+// is staged in the same pairing, so B element 2e+h multiplies the x of the same
+// weight.
+#pragma once
+
+#include "q2_0_internal.h"
+
+namespace q2_0 {
+
+constexpr int kMvTile = 16;        // weight rows per MFMA tile
+constexpr int kMvStreamSB = 16;    // blocks per stage in the streaming kernel
+constexpr int kMvMaxGroup = 64;    // matrices per grouped launch (kernel argument size)
+
+struct MvProblem {
+    const uint8_t *w;
+    float *y;
+    int64_t ldy;
+    int M;
+    int tile0;   // first tile number of this matrix within the group
+};
+
+struct MvGroup {
+    MvProblem p[kMvMaxGroup];
+    int n;
+    int total_tiles;
+};
+
+__device__ __forceinline__ int find_problem(const MvGroup &grp, int tile) {
+    int idx = 0;
+    for (int i = 1; i < grp.n; ++i)
+        if (tile >= grp.p[i].tile0) idx = i;
+    return idx;
+}
+
+__device__ __forceinline__ half8_t as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(half8_t, u4{a, b, c, d});
+}
+
+// (a & mask) | orv as one v_and_or_b32.  gfx9 VOP3 encodings take no literal and
+// read at most one SGPR, so the mask must sit in a VGPR for the compiler to select
+// the fused form; otherwise it splits the expression into a v_and and a v_or.
+// The masks are therefore materialised once through an opaque v_mov (which keeps
+// the compiler from folding them back into literals), and the AND-OR itself is
+// plain code, so the compiler's own hazard tracking covers it (it does not see
+// into inline asm, which matters next to MFMAs writing VGPRs).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t orv) {
+    return (a & mask) | orv;
+}
+
+// Masks selecting code s (s = 0..4) of both 16-bit halves, held in VGPRs.
+struct PairMasks {
+    uint32_t m[5];
+    __device__ __forceinline__ PairMasks() {
+        asm volatile("v_mov_b32 %0, 0x30003" : "=v"(m[0]));
+        asm volatile("v_mov_b32 %0, 0xc000c" : "=v"(m[1]));
+        asm volatile("v_mov_b32 %0, 0x300030" : "=v"(m[2]));
+        asm volatile("v_mov_b32 %0, 0xc000c0" : "=v"(m[3]));
+        asm volatile("v_mov_b32 %0, 0x3000300" : "=v"(m[4]));
+    }
+};
+
+// fp16 pair (q_s - 1 of the low half, q_s - 1 of the high half) of a code dword, for
+// codes at mantissa bits 2s, 2s+1 (s = 0..4).  OR-ing the code under the exponent
+// 25 - 2s gives the half 2^(10-2s) + q exactly; subtracting 2^(10-2s) + 1 leaves
+// q - 1 exactly.
+template <int S>
+__device__ __forceinline__ uint32_t pair_qm1(uint32_t cd, const PairMasks &pm) {
+    constexpr uint32_t magic = (uint32_t)(25 - 2 * S) << 10;
+    constexpr float off = (float)((1 << (10 - 2 * S)) + 1);
+    const uint32_t t = and_or(cd, pm.m[S], magic | (magic << 16));
+    half2_t h = __builtin_bit_cast(half2_t, t);
+    h = h - half2_t{(_Float16)off, (_Float16)off};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// The 8 pairs of a code dword: pairs 0..3 feed the block's first MFMA, 4..7 the
+// second.  Pair s takes code s of both halves.
+__device__ __forceinline__ void decode_dword(uint32_t cd, const PairMasks &pm, half8_t &b0,
+                                             half8_t &b1) {
+    const uint32_t hi = cd >> 10;   // codes 5..7 of each half down to bits 0..5
+    b0 = as_half8(pair_qm1<0>(cd, pm), pair_qm1<1>(cd, pm), pair_qm1<2>(cd, pm), pair_qm1<3>(cd, pm));
+    b1 = as_half8(pair_qm1<4>(cd, pm), pair_qm1<0>(hi, pm), pair_qm1<1>(hi, pm), pair_qm1<2>(hi, pm));
+}
+
+__device__ __forceinline__ int half_lo(int g, int odd) { return odd ? 2 * g : (g == 0 ? 0 : 2 * g - 1); }
+__device__ __forceinline__ int half_hi(int g, int odd) { return odd ? 2 * g + 1 : (g == 0 ? 7 : 2 * g); }
+
+// One A-operand item: column n, lane group gg, MFMA mu of block blk.  Loaded as the
+// two runs of 4 consecutive x the item pairs, then written as two LDS entries (hi
+// row 2n, lo row 2n+1) of 8 halves each.
+struct XItem {
+    float4_t a, c;
+};
+
+__device__ __forceinline__ XItem load_x_item(const float *__restrict__ x, int64_t ldx, int blk, int mu,
+                                             int gg, int n) {
+    const int odd = blk & 1;
+    const float *xb = x + n * ldx + (int64_t)blk * kBlockWeights + 4 * mu;
+    return XItem{*reinterpret_cast<const float4_t *>(xb + 8 * half_lo(gg, odd)),
+                 *reinterpret_cast<const float4_t *>(xb + 8 * half_hi(gg, odd))};
+}
+
+__device__ __forceinline__ void store_x_item(const XItem &it, half8_t *dst) {
+    uint32_t hiw[4], low[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const _Float16 ha = (_Float16)it.a[e], hc = (_Float16)it.c[e];
+        const _Float16 la = (_Float16)(it.a[e] - (float)ha), lc = (_Float16)(it.c[e] - (float)hc);
+        hiw[e] = __builtin_bit_cast(uint32_t, half2_t{ha, hc});
+        low[e] = __builtin_bit_cast(uint32_t, half2_t{la, lc});
+    }
+    dst[0] = as_half8(hiw[0], hiw[1], hiw[2], hiw[3]);
+    dst[1] = as_half8(low[0], low[1], low[2], low[3]);
+}
+
+// Stage x for blocks 0..nb-1: entry ((b*2 + mu)*4 + g)*2NC + row.
+template <int NC>
+__device__ __forceinline__ void stage_x_all(const float *__restrict__ x, int64_t ldx, int nb,
+                                            half8_t *lds_x, int tid, int nthreads) {
+    const int items = nb * 2 * 4 * NC;
+    for (int q = tid; q < items; q += nthreads) {
+        const int n = q % NC, gg = (q / NC) % 4, mu = (q / (4 * NC)) % 2, b = q / (8 * NC);
+        store_x_item(load_x_item(x, ldx, b, mu, gg, n), lds_x + (q / NC) * (2 * NC) + 2 * n);
+    }
+}
+
+// One block pair: lp points at the pair's 36 bytes of this lane's row in LDS, a at
+// the A entry of (even block, mu = 0) for this lane; entries of (block, mu) are
+// 4*2NC apart.  acc0/acc1 accumulate even/odd blocks for columns 2g, 2g+1.
+template <int NC>
+__device__ __forceinline__ void mv_block_pair(const uint8_t *lp, const half8_t *a, int g, uint32_t sel,
+                                              const PairMasks &pm, float acc0[2], float acc1[2]) {
+    constexpr int NR = 2 * NC;
+    const uint32_t X = *reinterpret_cast<const uint32_t *>(lp + 4 * g);
+    const uint32_t Y = *reinterpret_cast<const uint32_t *>(lp + 16);
+    const uint32_t Z = *reinterpret_cast<const uint32_t *>(lp + 20 + 4 * g);
+    uint32_t D0 = X;   // group 0 reads D0 anyway; only columns of group 0 exist for NC <= 2
+    if (NC > 2) D0 = *reinterpret_cast<const uint32_t *>(lp);
+    // even block: group 0 pairs h0 (high half of D0) with h7 (low half of D4)
+    const uint32_t cde = __builtin_amdgcn_perm(Y, X, sel);
+    half8_t b0, b1, c0, c1;
+    decode_dword(cde, pm, b0, b1);
+    decode_dword(Z, pm, c0, c1);
+    float4_t ce = {0.f, 0.f, 0.f, 0.f}, co = {0.f, 0.f, 0.f, 0.f};
+    ce = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], b0, ce, 0, 0, 0);
+    ce = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[4 * NR], b1, ce, 0, 0, 0);
+    co = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[8 * NR], c0, co, 0, 0, 0);
+    co = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[12 * NR], c1, co, 0, 0, 0);
+    const float de = half_bits_to_float(D0 & 0xffffu);
+    const float dd = half_bits_to_float(Y >> 16);
+    acc0[0] = __builtin_fmaf(de, ce[0] + ce[1], acc0[0]);
+    acc1[0] = __builtin_fmaf(dd, co[0] + co[1], acc1[0]);
+    if (NC > 1) {
+        acc0[1] = __builtin_fmaf(de, ce[2] + ce[3], acc0[1]);
+        acc1[1] = __builtin_fmaf(dd, co[2] + co[3], acc1[1]);
+    }
+}
+
+size_t mat_vec_stream_lds(int N, int nb);
+hipError_t launch_mat_vec_stream(const MvGroup &grp, int nb, const float *x, int64_t ldx, int N,
+                                 hipStream_t s);
+
+}  // namespace q2_0

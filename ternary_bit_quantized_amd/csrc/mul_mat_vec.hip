@@ -11,6 +11,7 @@
 // butterfly.  Summation depth per output: 16 + K/1024 + 6, far below what the
 // 1e-5 relative bound allows (about 160 f32 roundings).
 #include "q2_0_internal.h"
+#include "mat_vec_common.h"
 
 namespace q2_0 {
 
@@ -73,8 +74,26 @@ static void launch_generic_nc(const uint8_t *w, int64_t M, int nb, const float *
         mat_vec_generic<NC, false><<<grid, 256, 0, s>>>(w, M, nb, x, ldx, y, ldy);
 }
 
+// Fast-path choice.  Rows 16-byte aligned and x 16-byte aligned: the MFMA kernels.
+// Matrices with at least kStreamTiles 16-row tiles stream with whole-K waves; smaller
+// ones split K over the waves of a workgroup to fill the chip.  Anything else takes
+// the generic kernel.
+constexpr int64_t kStreamTiles = 1024;
+
+static bool stream_fits(int N, int nb) { return mat_vec_stream_lds(N, nb) <= 160 * 1024; }
+
 hipError_t launch_mat_vec(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx, int N,
                           float *y, int64_t ldy, hipStream_t s) {
+    if (mat_vec_mfma_eligible(w, M, nb, x, ldx)) {
+        if ((M + kMvTile - 1) / kMvTile >= kStreamTiles && stream_fits(N, nb)) {
+            MvGroup grp;
+            grp.n = 1;
+            grp.p[0] = MvProblem{w, y, ldy, (int)M, 0};
+            grp.total_tiles = (int)((M + kMvTile - 1) / kMvTile);
+            return launch_mat_vec_stream(grp, nb, x, ldx, N, s);
+        }
+        return launch_mat_vec_mfma(w, M, nb, x, ldx, N, y, ldy, s);
+    }
     const bool vec = ((uintptr_t)x % 16 == 0) && (ldx % 4 == 0);
     switch (N) {
         case 1: launch_generic_nc<1>(w, M, nb, x, ldx, y, ldy, s, vec); break;
@@ -88,6 +107,40 @@ hipError_t launch_mat_vec(const uint8_t *w, int64_t M, int nb, const float *x, i
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items, int nb,
+                                const float *x, int64_t ldx, int N, hipStream_t s) {
+    int64_t i = 0;
+    while (i < n_items) {
+        // Gather up to kMvMaxGroup consecutive stream-eligible matrices into one launch.
+        MvGroup grp;
+        grp.n = 0;
+        int tiles = 0;
+        while (i < n_items && grp.n < kMvMaxGroup) {
+            const q2_0_mat_vec_item &it = items[i];
+            const uint8_t *w = static_cast<const uint8_t *>(it.w);
+            if (it.M == 0) { ++i; continue; }
+            const bool ok = mat_vec_mfma_eligible(w, it.M, nb, x, ldx) && stream_fits(N, nb) &&
+                            tiles + (it.M + kMvTile - 1) / kMvTile < 0x7fffffff;
+            if (!ok) {
+                if (grp.n) break;   // launch what is gathered first
+                hipError_t e = launch_mat_vec(w, it.M, nb, x, ldx, N, it.y, it.ldy, s);
+                if (e != hipSuccess) return e;
+                ++i;
+                continue;
+            }
+            grp.p[grp.n++] = MvProblem{w, it.y, it.ldy, (int)it.M, tiles};
+            tiles += (int)((it.M + kMvTile - 1) / kMvTile);
+            ++i;
+        }
+        if (grp.n) {
+            grp.total_tiles = tiles;
+            hipError_t e = launch_mat_vec_stream(grp, nb, x, ldx, N, s);
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
 }
 
 }  // namespace q2_0

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/q2_0.h"
+
 namespace q2_0 {
 
 constexpr int kBlockWeights = 64;
@@ -13,6 +15,7 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // IEEE half bits -> f32 (v_cvt_f32_f16: exact for every half, subnormals included).
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
@@ -31,6 +34,11 @@ hipError_t launch_get_rows(const uint8_t *w, int64_t M, int nb, const int32_t *i
                            float *out, int64_t ld_out, hipStream_t s);
 hipError_t launch_mat_vec(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx, int N,
                           float *y, int64_t ldy, hipStream_t s);
+hipError_t launch_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items, int nb,
+                                const float *x, int64_t ldx, int N, hipStream_t s);
+bool mat_vec_mfma_eligible(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx);
+hipError_t launch_mat_vec_mfma(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx,
+                               int N, float *y, int64_t ldy, hipStream_t s);
 hipError_t launch_gemm_f16(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx,
                            int64_t N, float *y, int64_t ldy, hipStream_t s);
 hipError_t launch_gemm_f32(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx,

@@ -28,8 +28,23 @@ BLOCK_WEIGHTS = 64
 BLOCK_BYTES = 18
 MAT_VEC_MAX_N = 8
 
-EXPORTS = ("q2_0_get_rows", "q2_0_mul_mat_vec", "q2_0_mul_mat", "q2_0_mul_mat_workspace_bytes",
+EXPORTS = ("q2_0_get_rows", "q2_0_mul_mat_vec", "q2_0_mul_mat_vec_group", "q2_0_mul_mat",
+           "q2_0_mul_mat_workspace_bytes",
            "q2_0_status_string", "q2_0_last_hip_error", "q2_0_version")
+
+
+class MatVecItem(ctypes.Structure):
+    """q2_0_mat_vec_item: one matrix of a grouped mat-vec."""
+    _fields_ = [("w", ctypes.c_void_p), ("M", ctypes.c_int64), ("y", ctypes.c_void_p),
+                ("ldy", ctypes.c_int64)]
+
+
+def make_items(entries):
+    """[(w_ptr, M, y_ptr, ldy), ...] -> a ctypes array to pass to mul_mat_vec_group_raw."""
+    arr = (MatVecItem * len(entries))()
+    for i, (w, M, y, ldy) in enumerate(entries):
+        arr[i] = MatVecItem(w, M, y, ldy)
+    return arr
 
 
 class Q2_0Error(RuntimeError):
@@ -55,6 +70,8 @@ def lib() -> ctypes.CDLL:
         P, I64 = ctypes.c_void_p, ctypes.c_int64
         L.q2_0_get_rows.argtypes = [P, I64, I64, P, I64, P, I64, P]
         L.q2_0_mul_mat_vec.argtypes = [P, I64, I64, P, I64, I64, P, I64, P]
+        L.q2_0_mul_mat_vec_group.argtypes = [P, I64, I64, P, I64, I64, P]
+        L.q2_0_mul_mat_vec_group.restype = ctypes.c_int
         L.q2_0_mul_mat.argtypes = [P, I64, I64, P, I64, I64, P, I64, ctypes.c_int, P,
                                    ctypes.c_size_t, P]
         L.q2_0_mul_mat_workspace_bytes.argtypes = [I64, I64, I64, ctypes.c_int]
@@ -83,6 +100,13 @@ def get_rows_raw(w: int, M: int, K: int, ids: int, n_ids: int, out: int, ld_out:
 def mul_mat_vec_raw(w: int, M: int, K: int, x: int, ldx: int, N: int, y: int, ldy: int,
                     stream: int = 0) -> int:
     return lib().q2_0_mul_mat_vec(w, M, K, x, ldx, N, y, ldy, stream)
+
+
+def mul_mat_vec_group_raw(items, n_items: int, K: int, x: int, ldx: int, N: int,
+                          stream: int = 0) -> int:
+    """items: a ctypes array from make_items (or None with n_items == 0)."""
+    return lib().q2_0_mul_mat_vec_group(ctypes.cast(items, ctypes.c_void_p) if items is not None else None,
+                                        n_items, K, x, ldx, N, stream)
 
 
 def mul_mat_raw(w: int, M: int, K: int, x: int, ldx: int, N: int, y: int, ldy: int, precision: int,
@@ -142,6 +166,22 @@ def q2_0_mul_mat_vec(w, M: int, K: int, x, y=None, stream=None):
     _check(mul_mat_vec_raw(w.data_ptr(), M, K, xp, ldx, N, yp, ldy, _stream(stream)),
            "q2_0_mul_mat_vec")
     return y
+
+
+def q2_0_mul_mat_vec_group(mats, K: int, x, ys=None, stream=None):
+    """mats: [(w, M), ...] sharing K; returns [y_i (N, M_i)] with y_i = W_i x."""
+    import torch
+    xp, N, ldx = _cols(x, K, "x")
+    if ys is None:
+        ys = [torch.empty((N, M), dtype=torch.float32, device=x.device) for (_, M) in mats]
+    entries = []
+    for (w, M), y in zip(mats, ys):
+        yp, _, ldy = _cols(y, M, "y")
+        entries.append((w.data_ptr(), M, yp, ldy))
+    items = make_items(entries)
+    _check(mul_mat_vec_group_raw(items, len(entries), K, xp, ldx, N, _stream(stream)),
+           "q2_0_mul_mat_vec_group")
+    return ys
 
 
 def q2_0_mul_mat(w, M: int, K: int, x, precision: int = Q2_0_PREC_F16_MFMA, y=None, workspace=None,

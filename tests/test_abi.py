@@ -99,3 +99,20 @@ def test_unsupported():
 def test_workspace_query():
     for p in (B.Q2_0_PREC_F16_MFMA, B.Q2_0_PREC_F32):
         assert B.mul_mat_workspace_bytes(4096, 4096, 512, p) >= 0
+
+
+def test_group_validation():
+    items = B.make_items([(P16, 10, P16, 10), (P16, 5, P16 + 2, 5)])
+    assert B.mul_mat_vec_group_raw(items, 2, 64, P16, 64, 1) == B.Q2_0_ERR_ALIGN
+    assert B.mul_mat_vec_group_raw(items, 2, 100, P16, 100, 1) == B.Q2_0_ERR_SHAPE
+    assert B.mul_mat_vec_group_raw(items, -1, 64, P16, 64, 1) == B.Q2_0_ERR_SHAPE
+    assert B.mul_mat_vec_group_raw(None, 0, 64, P16, 64, 1) == B.Q2_0_OK
+    assert B.mul_mat_vec_group_raw(None, 3, 64, P16, 64, 1) == B.Q2_0_ERR_NULL
+    ok = B.make_items([(P16, 10, P16, 10), (0, 0, 0, 0)])
+    assert B.mul_mat_vec_group_raw(ok, 2, 64, P16, 64, 9) == B.Q2_0_ERR_UNSUPPORTED
+    assert B.mul_mat_vec_group_raw(ok, 2, 64, P16, 63, 1) == B.Q2_0_ERR_LAYOUT
+    assert B.mul_mat_vec_group_raw(ok, 2, 64, 0, 64, 1) == B.Q2_0_ERR_NULL
+    bad_ldy = B.make_items([(P16, 10, P16, 9)])
+    assert B.mul_mat_vec_group_raw(bad_ldy, 1, 64, P16, 64, 1) == B.Q2_0_ERR_LAYOUT
+    empty = B.make_items([(0, 0, 0, 0)])
+    assert B.mul_mat_vec_group_raw(empty, 1, 64, 0, 64, 1) == B.Q2_0_OK

@@ -319,3 +319,93 @@ def test_mul_mat_metamorphic_scale(precision):
     y8 = run_mul_mat(dev(synth.pack(codes, (d.astype(np.float32) * 8).astype(np.float16))), M, K, x,
                      precision)
     assert np.array_equal(y8, 8 * y)
+
+
+# =============================================================================== grouped mat-vec
+
+def run_group(mats, K, x, ldx=None):
+    """mats: [(w_bytes or None, M, codes)]; runs q2_0_mul_mat_vec_group, returns [y_i]."""
+    torch = _torch()
+    N = x.shape[0]
+    ldx = ldx or K
+    xb = np.zeros((N, ldx), dtype=np.float32)
+    xb[:, :K] = x
+    xd = dev(xb)
+    keep, entries, ys = [], [], []
+    for w, M in mats:
+        wd = dev(w) if M else None
+        yd = torch.full((N, M + 3), float("nan"), dtype=torch.float32, device="cuda")
+        keep.append(wd)
+        ys.append(yd)
+        entries.append((wd.data_ptr() if wd is not None else 0, M, yd.data_ptr(), M + 3))
+    items = B.make_items(entries)
+    st = B.mul_mat_vec_group_raw(items, len(entries), K, xd.data_ptr(), ldx, N,
+                                 torch.cuda.current_stream().cuda_stream)
+    assert st == 0, B.lib().q2_0_status_string(st)
+    out = []
+    for (w, M), yd in zip(mats, ys):
+        y = host(yd)
+        assert np.all(np.isnan(y[:, M:])), "group wrote past M"
+        out.append(y[:, :M])
+    return out
+
+
+@pytest.mark.parametrize("N", [1, 2, 5, 8])
+def test_mat_vec_group_qkv_like(N):
+    K = 2048
+    shapes = [4096, 1024, 1024, 0, 37, 16, 1]
+    mats = [(synth.weight(20, i, N, M, K, "quad", synth.ScaleDist("loguniform", 1e-3, 1e-1, 0.02))
+             if M else None, M) for i, M in enumerate(shapes)]
+    x = synth.activations(20, N, 0, N, K)
+    ys = run_group(mats, K, x)
+    for (w, M), y in zip(mats, ys):
+        if M:
+            assert_products(y, w, M, K, x, REL_F32, what="group M=%d N=%d" % (M, N))
+
+
+def test_mat_vec_group_many_items_chunks_and_matches_single():
+    rng = np.random.default_rng(31)
+    K, N = 512, 1
+    Ms = [int(m) for m in rng.integers(1, 300, size=70)]
+    mats = [(synth.weight(21, i, 0, M, K, "tern", synth.ScaleDist("uniform", 0.01, 0.1)), M)
+            for i, M in enumerate(Ms)]
+    x = synth.activations(21, 0, 0, N, K)
+    ys = run_group(mats, K, x)
+    for (w, M), y in zip(mats, ys):
+        assert_products(y, w, M, K, x, REL_F32, what="many M=%d" % M)
+    # grouping does not change results: the same matrix alone in a group of one
+    for (w, M), y in list(zip(mats, ys))[:5]:
+        (y1,) = run_group([(w, M)], K, x)
+        assert np.array_equal(y1, y)
+
+
+def test_mat_vec_group_mixed_eligibility():
+    """K/64 % 8 != 0 rows (not 16-byte aligned) take the generic kernel inside a group."""
+    K, N = 64 * 12, 3
+    mats = [(synth.weight(22, i, 0, M, K, "quad", synth.ScaleDist("uniform", 0.01, 0.1)), M)
+            for i, M in enumerate([100, 2000, 5])]
+    x = synth.activations(22, 0, 0, N, K)
+    for (w, M), y in zip(mats, run_group(mats, K, x, ldx=K + 5)):
+        assert_products(y, w, M, K, x, REL_F32, what="mixed M=%d" % M)
+
+
+@pytest.mark.parametrize("N", [1, 3, 8])
+def test_mat_vec_stream_path_full_oracle(N):
+    """M large enough for the whole-K streaming kernel on a single call; every row checked."""
+    M, K = 20000 + 7, 1024
+    w = synth.weight(23, N, 0, M, K, "quad", synth.ScaleDist("loguniform", 1e-3, 1e-1, 0.01))
+    x = synth.activations(23, N, 0, N, K)
+    y = run_mat_vec(dev(w), M, K, x, ldy=M + 9)
+    assert_products(y, w, M, K, x, REL_F32, what="stream N=%d" % N)
+
+
+def test_mat_vec_group_stack_8b_layer_workload():
+    wl = synth.STACK_8B
+    K = 4096
+    names = ["q", "k", "v", "o", "gate", "up"]
+    mats = [(ws(wl, n, layer=1), wl.shapes[n][0]) for n in names]
+    x = synth.activations(wl.seed, 0, synth.stack_x_matrix_index(K), 1, K)
+    rng = np.random.default_rng(7)
+    for (w, M), y, n in zip(mats, run_group(mats, K, x), names):
+        rows = np.unique(np.concatenate([rng.integers(0, M, 256), [0, M - 1]]))
+        assert_products(y, w, M, K, x, REL_F32, rows=rows, what=n)
