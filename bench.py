@@ -154,12 +154,16 @@ def main():
     def run_decode_matvecs():
         run_groups(layer_groups)
 
+    ws_bytes = max(B.mul_mat_workspace_bytes(M, K, PREFILL_N, B.Q2_0_PREC_F16_MFMA)
+                   for (M, K) in wl.shapes.values())
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+
     def run_prefill_gemms(precision=B.Q2_0_PREC_F16_MFMA):
         st = s()
         for key in order:
             M, K = wl.shapes[key[1]]
             check(B.mul_mat_raw(W[key].data_ptr(), M, K, xP[K].data_ptr(), K, PREFILL_N,
-                                yP[M].data_ptr(), M, precision, 0, 0, st), "mul_mat")
+                                yP[M].data_ptr(), M, precision, ws.data_ptr(), ws_bytes, st), "mul_mat")
 
     # ---- capture the four parts as graphs
     parts = {

@@ -49,7 +49,7 @@ typedef enum {
     Q2_0_ERR_LAYOUT = 3,      /* ldx < K, ldy < M or ld_out < K */
     Q2_0_ERR_ALIGN = 4,       /* w not 2-byte aligned, or x / y / out / ids not 4-byte aligned */
     Q2_0_ERR_UNSUPPORTED = 5, /* N > 8 for the mat-vec, or an unknown precision */
-    Q2_0_ERR_WORKSPACE = 6,   /* workspace smaller than q2_0_mul_mat_workspace_bytes() */
+    Q2_0_ERR_WORKSPACE = 6,   /* workspace smaller than q2_0_mul_mat_workspace_bytes(), or not 16-byte aligned */
     Q2_0_ERR_HIP = 7          /* a HIP launch failed; see q2_0_last_hip_error() */
 } q2_0_status;
 
@@ -125,15 +125,18 @@ int q2_0_mul_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items, int6
  *   accumulates in f32 on the matrix cores: |y - y_exact| <= 2e-3 * sum|W x| for
  *   |x| <= 65504 and |d| <= 32752.  Q2_0_PREC_F32 is the fp32-grade fallback
  *   (same bound as the mat-vec).
- *   workspace / ws_bytes: scratch the caller provides; at least
- *   q2_0_mul_mat_workspace_bytes(M, K, N, precision) bytes (it may be 0, and then
- *   workspace may be NULL).
+ *   workspace / ws_bytes: device scratch the caller provides, 16-byte aligned, at
+ *   least q2_0_mul_mat_workspace_bytes(M, K, N, precision) bytes: for
+ *   Q2_0_PREC_F16_MFMA with N > 8, x as fp16 (N*K*2) plus, when the output tile grid
+ *   is too small to fill the GPU, f32 partial sums of a K split (splits*N*M*4, split
+ *   count <= 8, added in a fixed order); otherwise 0 (then workspace may be NULL).
+ *   Its contents are overwritten; it must not overlap w, x or y.
  */
 int q2_0_mul_mat(const void *w, int64_t M, int64_t K, const float *x, int64_t ldx, int64_t N,
                  float *y, int64_t ldy, int precision, void *workspace, size_t ws_bytes,
                  void *stream);
 
-/* Workspace q2_0_mul_mat needs for these sizes (0 when none); 0 for invalid sizes. */
+/* Workspace bytes q2_0_mul_mat needs for these sizes (0 when none, and for invalid sizes). */
 size_t q2_0_mul_mat_workspace_bytes(int64_t M, int64_t K, int64_t N, int precision);
 
 /* A static, human-readable name for a status code. */

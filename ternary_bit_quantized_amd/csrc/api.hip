@@ -96,8 +96,9 @@ int q2_0_mul_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items, int6
 }
 
 size_t q2_0_mul_mat_workspace_bytes(int64_t M, int64_t K, int64_t N, int precision) {
-    (void)M; (void)K; (void)N; (void)precision;
-    return 0;
+    if (check_shape(M, K, N) || N > kMaxGemmN) return 0;
+    if (precision != Q2_0_PREC_F16_MFMA || N <= Q2_0_MAT_VEC_MAX_N) return 0;
+    return q2_0::gemm_f16_workspace_bytes(M, K, N);   // x as fp16 (+ split-K partials)
 }
 
 int q2_0_mul_mat(const void *w, int64_t M, int64_t K, const float *x, int64_t ldx, int64_t N,
@@ -110,15 +111,15 @@ int q2_0_mul_mat(const void *w, int64_t M, int64_t K, const float *x, int64_t ld
     st = check_product(w, M, K, x, ldx, y, ldy);
     if (st) return st;
     if (precision != Q2_0_PREC_F16_MFMA && precision != Q2_0_PREC_F32) return Q2_0_ERR_UNSUPPORTED;
-    if (ws_bytes < q2_0_mul_mat_workspace_bytes(M, K, N, precision)) return Q2_0_ERR_WORKSPACE;
-    (void)workspace;
+    const size_t need = q2_0_mul_mat_workspace_bytes(M, K, N, precision);
+    if (ws_bytes < need || (need && (!workspace || !aligned(workspace, 16)))) return Q2_0_ERR_WORKSPACE;
     const uint8_t *wb = static_cast<const uint8_t *>(w);
     const int nb = (int)(K / Q2_0_BLOCK_WEIGHTS);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (N <= Q2_0_MAT_VEC_MAX_N)
         return hip_status(q2_0::launch_mat_vec(wb, M, nb, x, ldx, (int)N, y, ldy, s));
     if (precision == Q2_0_PREC_F16_MFMA)
-        return hip_status(q2_0::launch_gemm_f16(wb, M, nb, x, ldx, N, y, ldy, s));
+        return hip_status(q2_0::launch_gemm_f16_v2(wb, M, nb, x, ldx, N, y, ldy, workspace, s));
     return hip_status(q2_0::launch_gemm_f32(wb, M, nb, x, ldx, N, y, ldy, s));
 }
 
@@ -130,7 +131,7 @@ const char *q2_0_status_string(int status) {
         case Q2_0_ERR_LAYOUT: return "Q2_0_ERR_LAYOUT: a leading dimension is smaller than the row length";
         case Q2_0_ERR_ALIGN: return "Q2_0_ERR_ALIGN: w must be 2-byte aligned and float/int32 buffers 4-byte aligned";
         case Q2_0_ERR_UNSUPPORTED: return "Q2_0_ERR_UNSUPPORTED: N > 8 for mat-vec, or unknown precision";
-        case Q2_0_ERR_WORKSPACE: return "Q2_0_ERR_WORKSPACE: workspace too small";
+        case Q2_0_ERR_WORKSPACE: return "Q2_0_ERR_WORKSPACE: workspace missing, too small or not 16-byte aligned";
         case Q2_0_ERR_HIP: return "Q2_0_ERR_HIP: a HIP launch failed";
         default: return "unknown q2_0 status";
     }

@@ -39,8 +39,9 @@ hipError_t launch_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items,
 bool mat_vec_mfma_eligible(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx);
 hipError_t launch_mat_vec_mfma(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx,
                                int N, float *y, int64_t ldy, hipStream_t s);
-hipError_t launch_gemm_f16(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx,
-                           int64_t N, float *y, int64_t ldy, hipStream_t s);
+size_t gemm_f16_workspace_bytes(int64_t M, int64_t K, int64_t N);
+hipError_t launch_gemm_f16_v2(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx,
+                              int64_t N, float *y, int64_t ldy, void *workspace, hipStream_t s);
 hipError_t launch_gemm_f32(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx,
                            int64_t N, float *y, int64_t ldy, hipStream_t s);
 

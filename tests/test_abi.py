@@ -96,9 +96,19 @@ def test_unsupported():
     assert B.mul_mat_raw(P16, 10, 64, P16, 64, 20, P16, 10, -1, 0, 0) == B.Q2_0_ERR_UNSUPPORTED
 
 
-def test_workspace_query():
-    for p in (B.Q2_0_PREC_F16_MFMA, B.Q2_0_PREC_F32):
-        assert B.mul_mat_workspace_bytes(4096, 4096, 512, p) >= 0
+def test_workspace_query_and_checks():
+    # fp16 GEMM stages x as fp16: N*K*2 bytes (rounded up to 256), plus split-K partials
+    # when the tile grid is small; nothing else needs any
+    assert B.mul_mat_workspace_bytes(65536, 4096, 512, B.Q2_0_PREC_F16_MFMA) == 512 * 4096 * 2
+    assert B.mul_mat_workspace_bytes(1024, 4096, 512, B.Q2_0_PREC_F16_MFMA) > 512 * 4096 * 2
+    assert B.mul_mat_workspace_bytes(4096, 4096, 512, B.Q2_0_PREC_F32) == 0
+    assert B.mul_mat_workspace_bytes(4096, 4096, 8, B.Q2_0_PREC_F16_MFMA) == 0
+    assert B.mul_mat_workspace_bytes(4096, 100, 512, B.Q2_0_PREC_F16_MFMA) == 0
+    need = B.mul_mat_workspace_bytes(10, 64, 20, B.Q2_0_PREC_F16_MFMA)
+    assert need >= 20 * 64 * 2
+    assert B.mul_mat_raw(P16, 10, 64, P16, 64, 20, P16, 10, 0, P16, need - 1) == B.Q2_0_ERR_WORKSPACE
+    assert B.mul_mat_raw(P16, 10, 64, P16, 64, 20, P16, 10, 0, 0, need) == B.Q2_0_ERR_WORKSPACE
+    assert B.mul_mat_raw(P16, 10, 64, P16, 64, 20, P16, 10, 0, P16 + 8, need) == B.Q2_0_ERR_WORKSPACE
 
 
 def test_group_validation():
