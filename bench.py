@@ -9,19 +9,29 @@ One step is one pass of the whole hot path:
   prefill: get_rows of 512 token ids, then the 252 stack matrices at N = 512 on the
            fp16-MFMA GEMM;
   decode : get_rows of 1 token id, then the 252 stack matrices and the LM head at
-           N = 1 on the mat-vec (one token, weights streamed from HBM), launched as a
-           transformer layer would: per layer one grouped launch for q/k/v (they share
-           the attention input), one for o, one grouped launch for gate/up, one for
-           down -- 4 launches per layer plus the head.
+           N = 1 on the mat-vec (one token, weights streamed from HBM).  The stack's
+           matrices use one activation per distinct K, so they are launched grouped by
+           activation: all K = 4096 matrices, all K = 12288 matrices, then the head.
 Each part is captured once in a HIP graph and replayed, so the timed region holds
 GPU work only.  Inputs are resident in HBM before timing starts.
+
+The same decode is also timed, outside the step, under two other launch schedules:
+per layer as a transformer with layer-to-layer dependencies would run it (grouped
+q/k/v, o, grouped gate/up, down: 4 launches per layer + head) and one launch per
+matrix.  Every launch here costs a few microseconds of ramp-up and drain, which
+bounds those schedules whatever the kernel does.
 
 Printed: one JSON line.  `value` is the decode mat-vec stream rate in GB/s
 (algorithmic bytes: Q2_0 weights + f32 activations + f32 outputs, over the time of
 the decode mat-vec launches).  Extra fields give decode and prefill tokens/s, the
-prefill GEMM TFLOP/s, the roofline fractions, the same decode launched one matrix at
-a time and grouped by activation, and the CPU oracle's rate on a bounded sample of
+prefill GEMM TFLOP/s, the roofline fractions, the other decode schedules, the fp32
+fallback GEMM's rate on one layer, and the CPU oracle's rate on a bounded sample of
 the same work.
+
+Profiling: --eager launches the selected --parts directly (no graphs), and
+--copy-calibration-mib runs one elementwise copy-like kernel (torch.neg) of known
+size first, whose counter readings scale the kernels' FETCH_SIZE / WRITE_SIZE to
+bytes.
 """
 
 from __future__ import annotations
@@ -54,7 +64,12 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--layers", type=int, default=36, help="stack layers (36 = the full model)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-prefill-row-stride", type=int, default=64)
+    p.add_argument("--cpu-prefill-row-stride", type=int, default=16)
+    p.add_argument("--cpu-decode-repeats", type=int, default=8)
+    p.add_argument("--eager", action="store_true", help="launch parts directly, without HIP graphs")
+    p.add_argument("--parts", default="", help="comma-separated subset of parts to run (profiling)")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="one device-to-device copy of this size before the parts (counter scaling)")
     return p.parse_args()
 
 
@@ -152,15 +167,15 @@ def main():
         head(st)
 
     def run_decode_matvecs():
-        run_groups(layer_groups)
+        run_groups(act_groups)
 
     ws_bytes = max(B.mul_mat_workspace_bytes(M, K, PREFILL_N, B.Q2_0_PREC_F16_MFMA)
                    for (M, K) in wl.shapes.values())
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
 
-    def run_prefill_gemms(precision=B.Q2_0_PREC_F16_MFMA):
+    def run_prefill_gemms(precision=B.Q2_0_PREC_F16_MFMA, layer_keys=None):
         st = s()
-        for key in order:
+        for key in (layer_keys or order):
             M, K = wl.shapes[key[1]]
             check(B.mul_mat_raw(W[key].data_ptr(), M, K, xP[K].data_ptr(), K, PREFILL_N,
                                 yP[M].data_ptr(), M, precision, ws.data_ptr(), ws_bytes, st), "mul_mat")
@@ -171,10 +186,29 @@ def main():
         "prefill_gemm": run_prefill_gemms,
         "decode_get_rows": lambda: run_get_rows(ids_d, emb_out_d),
         "decode_mat_vec": run_decode_matvecs,
+        "decode_mat_vec_per_layer": lambda: run_groups(layer_groups),
         "decode_mat_vec_per_matrix": run_decode_per_matrix,
-        "decode_mat_vec_by_activation": lambda: run_groups(act_groups),
+        "prefill_gemm_f32_layer0": lambda: run_prefill_gemms(B.Q2_0_PREC_F32, layer_keys=order[:7]),
     }
+    if args.parts:
+        keep = args.parts.split(",")
+        parts = {k: v for k, v in parts.items() if k in keep}
+    if args.copy_calibration_mib:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)      # one elementwise kernel: reads and writes nbytes each
+        torch.cuda.synchronize()
+        log("calibration kernel over %d bytes done" % nbytes)
+        del src, dst
     graphs = {}
+    if args.eager:
+        for name, fn in parts.items():
+            fn()
+        torch.cuda.synchronize()
+        log("eager parts done: %s" % ",".join(parts))
+        return
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
         for name, fn in parts.items():   # eager warm-up on the capture stream
@@ -188,8 +222,10 @@ def main():
     torch.cuda.synchronize()
     log("graphs captured")
 
-    step_parts = ("prefill_get_rows", "prefill_gemm", "decode_get_rows", "decode_mat_vec")
-    compare_parts = ("decode_mat_vec_per_matrix", "decode_mat_vec_by_activation")
+    step_parts = [p for p in ("prefill_get_rows", "prefill_gemm", "decode_get_rows", "decode_mat_vec")
+                  if p in graphs]
+    compare_parts = [p for p in ("decode_mat_vec_per_layer", "decode_mat_vec_per_matrix",
+                                 "prefill_gemm_f32_layer0") if p in graphs]
     ev = {n: [] for n in parts}
 
     def replay(names, record):
@@ -218,17 +254,21 @@ def main():
     t_total = time.perf_counter() - t_start
     log("timed %d steps in %.3f s" % (args.steps, t_total))
 
-    # the same decode under two other launch schedules, for comparison (not part of the step)
+    # the other decode schedules and the fp32 fallback, for comparison (not part of the step)
     replay(compare_parts, False)
     for _ in range(args.steps):
         replay(compare_parts, True)
     torch.cuda.synchronize()
 
-    ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in parts}
+    ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in parts if ev[n]}
+    if set(step_parts) != {"prefill_get_rows", "prefill_gemm", "decode_get_rows", "decode_mat_vec"}:
+        print(json.dumps({"partial_run": True, "ms": ms}), flush=True)
+        return
 
     # ---- algorithmic work
     dec_bytes = sum(mat_bytes(*wl.shapes[n], 1) for (_, n) in order) + mat_bytes(VM, VK, 1)
-    n_dec_launches = len(layer_groups) + 1
+    n_dec_launches = sum((n + 63) // 64 for (_, n, _) in act_groups) + 1
+    f32_flops = sum(2.0 * M * K * PREFILL_N for (_, n) in order[:7] for (M, K) in [wl.shapes[n]])
     pre_flops = sum(2.0 * M * K * PREFILL_N for (_, n) in order for (M, K) in [wl.shapes[n]])
     pre_bytes = sum(mat_bytes(*wl.shapes[n], PREFILL_N) for (_, n) in order)
     matvec_gbs = dec_bytes / (ms["decode_mat_vec"] * 1e-3) / 1e9
@@ -261,21 +301,24 @@ def main():
         "prefill_gemm_tflops": round(gemm_tflops, 2),
         "ms": {k: round(v, 4) for k, v in ms.items()},
         "decode_schedules_GBps": {
-            "per_layer_groups (%d launches)" % (len(layer_groups) + 1): round(matvec_gbs, 1),
+            "by_activation (%d launches, the step)" % n_dec_launches: round(matvec_gbs, 1),
+            "per_layer_groups (%d launches)" % (len(layer_groups) + 1):
+                round(dec_bytes / (ms["decode_mat_vec_per_layer"] * 1e-3) / 1e9, 1),
             "per_matrix (%d launches)" % (len(order) + 1):
                 round(dec_bytes / (ms["decode_mat_vec_per_matrix"] * 1e-3) / 1e9, 1),
-            "by_activation (%d group calls)" % (len(act_groups) + 1):
-                round(dec_bytes / (ms["decode_mat_vec_by_activation"] * 1e-3) / 1e9, 1),
         },
+        "decode_tokens_per_s_per_layer_schedule": round(
+            1.0 / ((ms["decode_mat_vec_per_layer"] + ms["decode_get_rows"]) * 1e-3), 1),
+        "f32_fallback_gemm_tflops_layer0": round(f32_flops / (ms["prefill_gemm_f32_layer0"] * 1e-3) / 1e12, 2),
         "roofline": {
-            "kernel": "mat_vec_stream (N=1, %d launches per decode token)" % n_dec_launches,
+            "kernel": "mat_vec_stream (N=1; %d grouped launches per decode token)" % n_dec_launches,
             "bound": "hbm", "achieved": round(matvec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(matvec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
             "bytes_per_launch_avg": int(dec_bytes / n_dec_launches),
             "avg_launch_us": round(ms["decode_mat_vec"] * 1e3 / n_dec_launches, 3),
         },
         "roofline_gemm": {
-            "kernel": "gemm_f16 (N=512, 252 launches per prefill)",
+            "kernel": "gemm_f16_mfma (N=512; 252 GEMMs per prefill, each an fp16 x conversion + GEMM (+ split-K reduce))",
             "bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": F16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(gemm_tflops / F16_MFMA_PEAK_TFLOPS, 4),
             "traffic": None, "algorithmic_bytes": int(pre_bytes),
@@ -300,11 +343,13 @@ def cpu_baseline(host_w, order, wl, args):
     xsP = {K: synth.activations(wl.seed, 1, synth.stack_x_matrix_index(K), PREFILL_N, K) for K in (4096, 12288)}
     t = time.perf_counter()
     nbytes = 0
-    for key in order:
-        M, K = wl.shapes[key[1]]
-        oracle.mul_mat(host_w[key], M, K, xs1[K])
-        nbytes += mat_bytes(M, K, 1)
-    t_dec = time.perf_counter() - t
+    for _ in range(args.cpu_decode_repeats):
+        for key in order:
+            M, K = wl.shapes[key[1]]
+            oracle.mul_mat(host_w[key], M, K, xs1[K])
+            nbytes += mat_bytes(M, K, 1)
+    t_dec = (time.perf_counter() - t) / args.cpu_decode_repeats
+    nbytes //= args.cpu_decode_repeats
     log("cpu oracle decode: %.2f s" % t_dec)
     S = args.cpu_prefill_row_stride
     t = time.perf_counter()
@@ -318,8 +363,8 @@ def cpu_baseline(host_w, order, wl, args):
     log("cpu oracle prefill sample: %.2f s" % t_pre)
     return {
         "value": round(nbytes / t_dec / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-        "sample": "decode mat-vec N=1 over all %d stack matrices (%d B); prefill N=512 on every "
-                  "%dth row of each matrix" % (len(order), nbytes, S),
+        "sample": "decode mat-vec N=1 over all %d stack matrices (%d B), mean of %d passes; prefill "
+                  "N=512 on every %dth row of each matrix" % (len(order), nbytes, args.cpu_decode_repeats, S),
         "decode_s": round(t_dec, 3), "prefill_sample_s": round(t_pre, 3),
         "prefill_tflops": round(flops / t_pre / 1e12, 6),
         "decode_tokens_per_s": round(1.0 / t_dec, 4),

@@ -208,20 +208,24 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_mfma(const uint8_t *__restric
     load_x(2, xA);
     __syncthreads();
 
-    // Two steps per iteration so that the register sets alternate statically.
-    for (int s = 0; s < nbs; s += 2) {
+    // Two steps per iteration so that the register sets alternate statically.  The loop
+    // has no exit in the middle (an exit there makes the compiler keep the
+    // accumulators in two register sets and copy between them every iteration); an
+    // odd last step runs after it.
+    int s = 0;
+    for (; s + 1 < nbs; s += 2) {
         mma_stage(0);
-        store_stage(1, wB, xB);          // step s+1 (a clamped duplicate past the end)
+        store_stage(1, wB, xB);          // step s+1
         load_w(s + 3, wB);
         load_x(s + 3, xB);
         __syncthreads();
-        if (s + 1 >= nbs) break;
         mma_stage(1);
-        store_stage(0, wA, xA);          // step s+2
+        store_stage(0, wA, xA);          // step s+2 (a clamped duplicate past the end)
         load_w(s + 4, wA);
         load_x(s + 4, xA);
         __syncthreads();
     }
+    if (s < nbs) mma_stage(0);
 
     // ---- epilogue: D lane l, register v -> row 8*(v/4) + 4*(l/32) + v%4, column l%32
 #pragma unroll
