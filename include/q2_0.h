@@ -121,15 +121,18 @@ int q2_0_mul_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items, int6
  *   Layouts and alignment as for q2_0_mul_mat_vec; precision is a q2_0_precision.
  *   N <= 8 is routed to the mat-vec for either precision (fp32-grade result).
  *   Otherwise Q2_0_PREC_F16_MFMA stages each weight tile in LDS as fp16 d*(q-1),
- *   which is exact for |d| <= 32752, rounds x to fp16 (nearest-even) and
- *   accumulates in f32 on the matrix cores: |y - y_exact| <= 2e-3 * sum|W x| for
- *   |x| <= 65504 and |d| <= 32752.  Q2_0_PREC_F32 is the fp32-grade fallback
- *   (same bound as the mat-vec).
+ *   which is exact for |d| <= 32752, rounds x to fp16 (nearest-even) after
+ *   scaling each column by a power of two that puts its max |x| in [2^14, 2^15)
+ *   (undone exactly on the results), and accumulates in f32 on the matrix cores:
+ *   |y - y_exact| <= 2e-3 * sum|W x| for finite x with |x| < 2^100 and
+ *   |d| <= 32752.  Q2_0_PREC_F32 is the fp32-grade fallback (same bound as the
+ *   mat-vec).
  *   workspace / ws_bytes: device scratch the caller provides, 16-byte aligned, at
  *   least q2_0_mul_mat_workspace_bytes(M, K, N, precision) bytes: for
- *   Q2_0_PREC_F16_MFMA with N > 8, x as fp16 (N*K*2) plus, when the output tile grid
- *   is too small to fill the GPU, f32 partial sums of a K split (splits*N*M*4, split
- *   count <= 8, added in a fixed order); otherwise 0 (then workspace may be NULL).
+ *   Q2_0_PREC_F16_MFMA with N > 8, x as fp16 (N*K*2) and N column exponents, plus,
+ *   when the output tile grid is too small to fill the GPU, f32 partial sums of a K
+ *   split (splits*N*M*4, split count <= 8, added in a fixed order); otherwise 0
+ *   (then workspace may be NULL).
  *   Its contents are overwritten; it must not overlap w, x or y.
  */
 int q2_0_mul_mat(const void *w, int64_t M, int64_t K, const float *x, int64_t ldx, int64_t N,

@@ -8,10 +8,11 @@
 // fp16-pair decode of the mat-vec (OR the code under a magic exponent, one packed
 // subtract) and one packed multiply by d.
 //
-//  * x is converted once per call into the caller's workspace as fp16, and within
-//    every group of 16 k its order is permuted to (0, 8, 1, 9, ..., 7, 15): the order
-//    in which the pair decode emits a word's 16 weights.  A and B then share the k
-//    order without any shuffling.
+//  * x is converted once per call into the caller's workspace as fp16, each column
+//    scaled by a power of two that keeps it inside fp16's normal range (undone on
+//    the results), and within every group of 16 k its order is permuted to (0, 8,
+//    1, 9, ..., 7, 15): the order in which the pair decode emits a word's 16
+//    weights.  A and B then share the k order without any shuffling.
 //  * Workgroup tile 128 (m) x 128 (n), four waves of 64 x 64, each a 2 x 2 grid of
 //    v_mfma_f32_32x32x16_f16; one Q2_0 block (64 k) per step.
 //  * LDS is double buffered (one barrier per step); the next step's code words and
@@ -29,15 +30,38 @@ namespace {
 constexpr int GM = 128, GN = 128, GK = 64;
 constexpr int GLD = GK + 8;   // fp16 row stride in LDS (144 B): 8 consecutive rows hit distinct banks
 
-// x (N columns of K floats) -> fp16, k permuted inside each 16-group.
+// x (N columns of K floats) -> fp16, k permuted inside each 16-group, one workgroup
+// per column.  The column is scaled by 2^e (e = xe[n]) so that its max |x| lands in
+// [2^14, 2^15): fp16 then neither overflows (|x| > 65504) nor falls into its
+// subnormal range, where the relative error would exceed 2^-11.  The GEMM multiplies
+// the column's results by 2^-e.
 template <bool kVec>
 __global__ __launch_bounds__(256) void x_to_f16_perm(const float *__restrict__ x, int64_t ldx, int K,
-                                                     int64_t N, _Float16 *__restrict__ x16) {
-    const int64_t groups = N * (K / 16);
-    for (int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x; gi < groups; gi += (int64_t)gridDim.x * 256) {
-        const int64_t n = gi / (K / 16);
-        const int k0 = (int)(gi - n * (K / 16)) * 16;
-        const float *src = x + n * ldx + k0;
+                                                     _Float16 *__restrict__ x16, int *__restrict__ xe) {
+    __shared__ float red[4];
+    const int tid = threadIdx.x;
+    const int64_t n = blockIdx.x;
+    const float *col = x + n * ldx;
+    const int groups = K / 16;
+    float m = 0.f;
+    for (int gi = tid; gi < groups; gi += 256) {
+        const float *src = col + 16 * gi;
+        if (kVec) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) m = fmaxf(m, max_abs4(reinterpret_cast<const float4_t *>(src)[q]));
+        } else {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) m = fmaxf(m, fabsf(src[q]));
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    const int e = column_exponent(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+    if (tid == 0) xe[n] = e;
+    for (int gi = tid; gi < groups; gi += 256) {
+        const float *src = col + 16 * gi;
         float v[16];
         if (kVec) {
 #pragma unroll
@@ -52,8 +76,9 @@ __global__ __launch_bounds__(256) void x_to_f16_perm(const float *__restrict__ x
         uint32_t o[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s)
-            o[s] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)v[s], (_Float16)v[s + 8]});
-        u32x4_t *dst = reinterpret_cast<u32x4_t *>(x16 + n * K + k0);
+            o[s] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)__builtin_amdgcn_ldexpf(v[s], e),
+                                                        (_Float16)__builtin_amdgcn_ldexpf(v[s + 8], e)});
+        u32x4_t *dst = reinterpret_cast<u32x4_t *>(x16 + n * K + 16 * gi);
         dst[0] = u32x4_t{o[0], o[1], o[2], o[3]};
         dst[1] = u32x4_t{o[4], o[5], o[6], o[7]};
     }
@@ -84,7 +109,8 @@ struct WRegs {
 // splits > 1: workgroup (tile, split) covers blocks [split*nbs, (split+1)*nbs) and writes
 // its partial sum to part + split*N*M (column n at n*M); the reduce kernel adds them.
 __global__ __launch_bounds__(256, 2) void gemm_f16_mfma(const uint8_t *__restrict__ w, int M, int nb,
-                                                        const _Float16 *__restrict__ x16, int N,
+                                                        const _Float16 *__restrict__ x16,
+                                                        const int *__restrict__ xe, int N,
                                                         float *__restrict__ y, int64_t ldy,
                                                         int tiles_m, int tiles_n, int xcd_map,
                                                         int splits, float *__restrict__ part) {
@@ -235,11 +261,13 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_mfma(const uint8_t *__restric
             const int n = n0 + wn * 64 + jj * 32 + (lane & 31);
             if (n >= N) continue;
             float *yc = (splits > 1) ? part + ((int64_t)split * N + n) * M : y + (int64_t)n * ldy;
+            const int ye = -xe[n];   // undo the column's staging scale
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) {
                 const int m = m0 + wm * 64 + i * 32 + 8 * v4 + 4 * (lane >> 5);
-                const float4_t val = {acc[i][jj][4 * v4], acc[i][jj][4 * v4 + 1], acc[i][jj][4 * v4 + 2],
-                                      acc[i][jj][4 * v4 + 3]};
+                float4_t val;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) val[e] = __builtin_amdgcn_ldexpf(acc[i][jj][4 * v4 + e], ye);
                 if (m + 3 < M && ((((uintptr_t)(yc + m)) & 15) == 0)) {
                     *reinterpret_cast<float4_t *>(yc + m) = val;
                 } else {
@@ -278,29 +306,30 @@ size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 }  // namespace
 
+// Workspace: fp16 x (N*K halves), the column exponents (N ints), then split-K partials.
 size_t gemm_f16_workspace_bytes(int64_t M, int64_t K, int64_t N) {
     const int sp = gemm_splits(M, N, (int)(K / kBlockWeights));
-    return align256((size_t)N * K * 2) + (sp > 1 ? align256((size_t)sp * N * M * 4) : 0);
+    return align256((size_t)N * K * 2) + align256((size_t)N * 4) + (sp > 1 ? align256((size_t)sp * N * M * 4) : 0);
 }
 
 hipError_t launch_gemm_f16_v2(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx,
                               int64_t N, float *y, int64_t ldy, void *workspace, hipStream_t s) {
     const int K = nb * kBlockWeights;
-    _Float16 *x16 = static_cast<_Float16 *>(workspace);
-    float *part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + align256((size_t)N * K * 2));
-    const int64_t groups = N * (K / 16);
-    const int pgrid = (int)((groups + 255) / 256 < 4096 ? (groups + 255) / 256 : 4096);
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    _Float16 *x16 = reinterpret_cast<_Float16 *>(ws);
+    int *xe = reinterpret_cast<int *>(ws + align256((size_t)N * K * 2));
+    float *part = reinterpret_cast<float *>(ws + align256((size_t)N * K * 2) + align256((size_t)N * 4));
     if (((uintptr_t)x % 16 == 0) && (ldx % 4 == 0))
-        x_to_f16_perm<true><<<pgrid, 256, 0, s>>>(x, ldx, K, N, x16);
+        x_to_f16_perm<true><<<(unsigned)N, 256, 0, s>>>(x, ldx, K, x16, xe);
     else
-        x_to_f16_perm<false><<<pgrid, 256, 0, s>>>(x, ldx, K, N, x16);
+        x_to_f16_perm<false><<<(unsigned)N, 256, 0, s>>>(x, ldx, K, x16, xe);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int tiles_m = (int)((M + GM - 1) / GM), tiles_n = (int)((N + GN - 1) / GN);
     const int per = (tiles_n <= 8 && 8 % tiles_n == 0) ? 8 / tiles_n : 0;
     const int splits = gemm_splits(M, N, nb);
     const int xcd_map = (splits == 1 && per != 0 && tiles_m % per == 0) ? 1 : 0;
-    gemm_f16_mfma<<<tiles_m * tiles_n * splits, 256, 0, s>>>(w, (int)M, nb, x16, (int)N, y, ldy, tiles_m,
+    gemm_f16_mfma<<<tiles_m * tiles_n * splits, 256, 0, s>>>(w, (int)M, nb, x16, xe, (int)N, y, ldy, tiles_m,
                                                               tiles_n, xcd_map, splits, part);
     e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;

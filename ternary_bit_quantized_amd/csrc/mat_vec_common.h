@@ -25,6 +25,7 @@ namespace q2_0 {
 constexpr int kMvTile = 16;        // weight rows per MFMA tile
 constexpr int kMvStreamSB = 16;    // blocks per stage in the streaming kernel
 constexpr int kMvMaxGroup = 64;    // matrices per grouped launch (kernel argument size)
+constexpr size_t kMvStreamStaticLds = 512;   // static LDS bound of the streaming kernel
 
 struct MvProblem {
     const uint8_t *w;
@@ -34,16 +35,22 @@ struct MvProblem {
     int tile0;   // first tile number of this matrix within the group
 };
 
+// A launch's matrices.  tile0 repeats the problems' first tiles contiguously (entries
+// past n hold INT_MAX), so that a tile's matrix is found by a binary search of
+// log2(kMvMaxGroup) scalar loads.
 struct MvGroup {
     MvProblem p[kMvMaxGroup];
+    int tile0[kMvMaxGroup];
     int n;
     int total_tiles;
 };
 
 __device__ __forceinline__ int find_problem(const MvGroup &grp, int tile) {
+    // binary search: the last i with tile0[i] <= tile (tile0 ascends, INT_MAX past n)
     int idx = 0;
-    for (int i = 1; i < grp.n; ++i)
-        if (tile >= grp.p[i].tile0) idx = i;
+#pragma unroll
+    for (int step = kMvMaxGroup / 2; step >= 1; step >>= 1)
+        if (grp.tile0[idx + step] <= tile) idx += step;
     return idx;
 }
 
@@ -101,6 +108,52 @@ __device__ __forceinline__ void decode_dword(uint32_t cd, const PairMasks &pm, h
 __device__ __forceinline__ int half_lo(int g, int odd) { return odd ? 2 * g : (g == 0 ? 0 : 2 * g - 1); }
 __device__ __forceinline__ int half_hi(int g, int odd) { return odd ? 2 * g + 1 : (g == 0 ? 7 : 2 * g); }
 
+// Activation range.  fp16 holds x to ~22 bits as hi + lo only for |x| in about
+// [2^-3, 2^15]: above 65504 hi overflows, and below 2^-3 lo loses bits to fp16's
+// subnormal spacing (2^-24).  Each column n is therefore staged as x * 2^e_n, with
+// the power of two chosen so that the column's max |x| lands in [2^14, 2^15), and
+// its results are multiplied by 2^-e_n on the way out (v_ldexp_f32 both times, exact
+// barring f32 under/overflow).  Elements within 2^18 of the column maximum keep
+// 2^-22 relative accuracy; smaller ones err by at most 2^-40 of the maximum.
+// An all-zero (or non-finite) maximum keeps e = 0.
+__device__ __forceinline__ int column_exponent(float amax) {
+    if (!(amax > 0.f) || amax > 3.4028234663852886e38f) return 0;
+    return 15 - __builtin_amdgcn_frexp_expf(amax);
+}
+
+__device__ __forceinline__ float max_abs4(float4_t v) {
+    return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+// Column exponents of x (NC columns of K floats, 16-byte aligned, ldx % 4 == 0) into
+// lds_e[0..NC), computed by the whole workgroup; lds_tmp holds NC floats per wave.
+// Contains two workgroup barriers, so every thread must call it.
+template <int NC>
+__device__ __forceinline__ void column_exponents(const float *__restrict__ x, int64_t ldx, int K,
+                                                 int *lds_e, float *lds_tmp, int tid, int nthreads) {
+    float m[NC];
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        m[n] = 0.f;
+        const float4_t *xc = reinterpret_cast<const float4_t *>(x + n * ldx);
+        for (int i = tid; i < K / 4; i += nthreads) m[n] = fmaxf(m[n], max_abs4(xc[i]));
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) m[n] = fmaxf(m[n], __shfl_xor(m[n], off));
+    }
+    const int wave = tid >> 6;
+    if ((tid & 63) == 0) {
+#pragma unroll
+        for (int n = 0; n < NC; ++n) lds_tmp[wave * NC + n] = m[n];
+    }
+    __syncthreads();
+    if (tid < NC) {
+        float a = 0.f;
+        for (int wv = 0; wv < nthreads / 64; ++wv) a = fmaxf(a, lds_tmp[wv * NC + tid]);
+        lds_e[tid] = column_exponent(a);
+    }
+    __syncthreads();
+}
+
 // One A-operand item: column n, lane group gg, MFMA mu of block blk.  Loaded as the
 // two runs of 4 consecutive x the item pairs, then written as two LDS entries (hi
 // row 2n, lo row 2n+1) of 8 halves each.
@@ -116,12 +169,14 @@ __device__ __forceinline__ XItem load_x_item(const float *__restrict__ x, int64_
                  *reinterpret_cast<const float4_t *>(xb + 8 * half_hi(gg, odd))};
 }
 
-__device__ __forceinline__ void store_x_item(const XItem &it, half8_t *dst) {
+// xe: the column's exponent (x is staged as x * 2^xe).
+__device__ __forceinline__ void store_x_item(const XItem &it, int xe, half8_t *dst) {
     uint32_t hiw[4], low[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const _Float16 ha = (_Float16)it.a[e], hc = (_Float16)it.c[e];
-        const _Float16 la = (_Float16)(it.a[e] - (float)ha), lc = (_Float16)(it.c[e] - (float)hc);
+        const float va = __builtin_amdgcn_ldexpf(it.a[e], xe), vc = __builtin_amdgcn_ldexpf(it.c[e], xe);
+        const _Float16 ha = (_Float16)va, hc = (_Float16)vc;
+        const _Float16 la = (_Float16)(va - (float)ha), lc = (_Float16)(vc - (float)hc);
         hiw[e] = __builtin_bit_cast(uint32_t, half2_t{ha, hc});
         low[e] = __builtin_bit_cast(uint32_t, half2_t{la, lc});
     }
@@ -129,14 +184,15 @@ __device__ __forceinline__ void store_x_item(const XItem &it, half8_t *dst) {
     dst[1] = as_half8(low[0], low[1], low[2], low[3]);
 }
 
-// Stage x for blocks 0..nb-1: entry ((b*2 + mu)*4 + g)*2NC + row.
+// Stage x for blocks 0..nb-1: entry ((b*2 + mu)*4 + g)*2NC + row; lds_e holds the
+// column exponents.
 template <int NC>
 __device__ __forceinline__ void stage_x_all(const float *__restrict__ x, int64_t ldx, int nb,
-                                            half8_t *lds_x, int tid, int nthreads) {
+                                            const int *lds_e, half8_t *lds_x, int tid, int nthreads) {
     const int items = nb * 2 * 4 * NC;
     for (int q = tid; q < items; q += nthreads) {
         const int n = q % NC, gg = (q / NC) % 4, mu = (q / (4 * NC)) % 2, b = q / (8 * NC);
-        store_x_item(load_x_item(x, ldx, b, mu, gg, n), lds_x + (q / NC) * (2 * NC) + 2 * n);
+        store_x_item(load_x_item(x, ldx, b, mu, gg, n), lds_e[n], lds_x + (q / NC) * (2 * NC) + 2 * n);
     }
 }
 

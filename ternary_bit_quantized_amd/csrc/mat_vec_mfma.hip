@@ -28,10 +28,11 @@
 //  * K split.  The four waves of a workgroup cover RG row tiles x KS slices of K;
 //    slice partials are added in LDS in a fixed order (deterministic).
 //
-// Accuracy: x's hi/lo split errs <= 2^-22 |x| for |x| >= 2^-3 (absolute 2^-25
-// below), MFMA products are exact, and the f32 chain is the MFMA sum plus
-// K/128/KS block partials per accumulator (two accumulators alternate over
-// blocks) -- inside the 1e-5 * sum|W x| bound for |x| < 2^15.
+// Accuracy: each column is staged scaled by a power of two that takes its max |x|
+// to [2^14, 2^15); the hi/lo split then errs <= 2^-22 |x| (at most 2^-40 of the
+// column maximum for elements far below it), MFMA products are exact, and the f32
+// chain is the MFMA sum plus K/128/KS block partials per accumulator (two
+// accumulators alternate over blocks) -- inside the 1e-5 * sum|W x| bound.
 #include "q2_0_internal.h"
 #include "mat_vec_common.h"
 
@@ -57,6 +58,8 @@ __global__ __launch_bounds__(256) void mat_vec_mfma(const uint8_t *__restrict__ 
     __shared__ __attribute__((aligned(16))) uint8_t lds_w[4][kTile * RSB];
     __shared__ __attribute__((aligned(16))) half8_t lds_x[KS * SB * 2 * 4 * NR];
     __shared__ float lds_red[(KS > 1) ? 4 * kTile * NC : 1];
+    __shared__ int lds_e[NC];
+    __shared__ float lds_tmp[4 * NC];
 
     const int tid = threadIdx.x;
     // the wave index is uniform: keep it (and all tile bookkeeping) in SGPRs
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(256) void mat_vec_mfma(const uint8_t *__restrict__ 
             const int q = t * 256 + tid;
             const int b = (q / (8 * NC)) % SB;
             if (q < XITEMS && b < sb) {
-                store_x_item(xreg[t], lds_x + (q / NC) * NR + 2 * (q % NC));
+                store_x_item(xreg[t], lds_e[q % NC], lds_x + (q / NC) * NR + 2 * (q % NC));
             }
         }
     };
@@ -129,6 +132,7 @@ __global__ __launch_bounds__(256) void mat_vec_mfma(const uint8_t *__restrict__ 
     const uint32_t sel = (g == 0) ? 0x05040302u : 0x03020100u;
 
     issue_loads(0);
+    column_exponents<NC>(x, ldx, nb * kBlockWeights, lds_e, lds_tmp, tid, 256);
     for (int st = 0; st < nstage; ++st) {
         park(st);
         __syncthreads();
@@ -142,13 +146,15 @@ __global__ __launch_bounds__(256) void mat_vec_mfma(const uint8_t *__restrict__ 
     }
 
     // Lane (j, g) holds rows m0 + j for columns 2g (index 0) and 2g + 1 (index 1).
+    // (results leave as acc * 2^-e of their column)
     const float r0 = acc0[0] + acc1[0];
     const float r1 = acc0[1] + acc1[1];
     const int row = m0 + j;
     if (KS == 1) {
         if (row < M) {
-            if (2 * g < NC) y[(int64_t)(2 * g) * ldy + row] = r0;
-            if (2 * g + 1 < NC) y[(int64_t)(2 * g + 1) * ldy + row] = r1;
+            if (2 * g < NC) y[(int64_t)(2 * g) * ldy + row] = __builtin_amdgcn_ldexpf(r0, -lds_e[2 * g]);
+            if (2 * g + 1 < NC)
+                y[(int64_t)(2 * g + 1) * ldy + row] = __builtin_amdgcn_ldexpf(r1, -lds_e[2 * g + 1]);
         }
     } else {
         // slice partials -> LDS, then a fixed-order sum over the KS slices
@@ -161,7 +167,7 @@ __global__ __launch_bounds__(256) void mat_vec_mfma(const uint8_t *__restrict__ 
 #pragma unroll
             for (int k = 0; k < KS; ++k) sum += lds_red[((k * RG + tg) * kTile + rr) * NC + n];
             const int orow = (blockIdx.x * RG + tg) * kTile + rr;
-            if (orow < M) y[(int64_t)n * ldy + orow] = sum;
+            if (orow < M) y[(int64_t)n * ldy + orow] = __builtin_amdgcn_ldexpf(sum, -lds_e[n]);
         }
     }
 }

@@ -52,14 +52,20 @@ __global__ __launch_bounds__(512) void mat_vec_stream(MvGroup grp, int nb, const
                                                       int64_t ldx) {
     constexpr int NR = 2 * NC;
     constexpr int RSB = SB * kBlockBytes + 16;
-    constexpr int CPR = SB * kBlockBytes / 16;
-    constexpr int CH = (kMvTile * CPR + 63) / 64;
+    constexpr int CPR = SB * kBlockBytes / 16;        // 16-byte chunks per row of a full stage
+    constexpr int NCHUNK = kMvTile * CPR;             // chunks of a full stage
+    constexpr int CH = (NCHUNK + 63) / 64;            // chunks per lane
+    constexpr int LAST_LANES = NCHUNK - 64 * (CH - 1);  // lanes whose last chunk is real
     constexpr int WAVES = 8;
-    static_assert(RSB % 16 == 0 && SB % 8 == 0, "stage geometry");
+    static_assert(RSB % 16 == 0 && SB % 16 == 0, "stage geometry");
 
+    constexpr int DUMMY = (64 - LAST_LANES) * 16;     // park slots for the lanes past the tile
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint8_t *lds_w = smem;                                                       // WAVES x 16 x RSB
-    half8_t *lds_x = reinterpret_cast<half8_t *>(smem + WAVES * kMvTile * RSB);  // nb x 2 x 4 x NR
+    uint8_t *lds_w = smem;   // WAVES x (16 x RSB + DUMMY)
+    half8_t *lds_x = reinterpret_cast<half8_t *>(smem + WAVES * (kMvTile * RSB + DUMMY));  // nb x 2 x 4 x NR
+    __shared__ int lds_e[NC];
+    __shared__ float lds_tmp[WAVES * NC];
+    static_assert(sizeof(lds_e) + sizeof(lds_tmp) <= kMvStreamStaticLds, "static LDS reserve");
 
     const int tid = threadIdx.x;
     // the wave index is uniform: keep it (and all tile bookkeeping) in SGPRs
@@ -69,16 +75,41 @@ __global__ __launch_bounds__(512) void mat_vec_stream(MvGroup grp, int nb, const
     const int tw = gridDim.x * WAVES;
     const int first = blockIdx.x * WAVES + wave;
     const int ns = (nb + SB - 1) / SB;
-    const int64_t rowbytes = (int64_t)nb * kBlockBytes;
+    const uint32_t rowbytes = (uint32_t)nb * kBlockBytes;
+    const bool ragged = (nb % SB) != 0;   // the last stage of a row holds SB/2 blocks
 
-    // Per-lane chunk geometry of a full stage: chunk q*64 + lane -> row r, 16-byte
-    // column cc.  Chunks past the tile (r >= 16) load a duplicate and are not parked.
-    int cr[CH], ccol[CH];
+    // Per-lane chunk geometry of a stage: chunk q*64 + lane -> tile row cr, 16-byte column
+    // cc, parked at lds_off.  In a half stage (SB/2 blocks) the chunks past its end load a
+    // clamped duplicate, parked into the unused tail of the row.
+    int cr[CH], cc[CH];
+    uint32_t lds_off[CH];
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
         const int c = q * 64 + lane;
-        cr[q] = c / CPR;
-        ccol[q] = c % CPR;
+        cr[q] = min(c / CPR, kMvTile - 1);
+        cc[q] = c % CPR;
+        // chunks past the tile (lanes >= LAST_LANES of the last one) park in the wave's
+        // dummy slots, so that every park is an unconditional store
+        lds_off[q] = (uint32_t)(wave * (kMvTile * RSB + DUMMY) +
+                                (c < NCHUNK ? (c / CPR) * RSB + 16 * cc[q] : kMvTile * RSB + 16 * (c - NCHUNK)));
+    }
+
+    // Byte offsets of this lane's chunks from the first row of the tile being loaded;
+    // rows past the matrix end are clamped to its last row (their outputs are never
+    // stored).  Recomputed whenever the loads move to a new tile.
+    // (Macros rather than lambdas: a lambda writing a captured register array makes
+    // the compiler keep the array in scratch.)
+    uint32_t off[CH];
+    const uint8_t *ld_base = nullptr;   // first byte of the tile being loaded (uniform)
+    int ld_tile = -1;
+#define Q2_0_SET_LOAD_TILE(TILE)                                                                   \
+    {                                                                                              \
+        const TileRef tr_ = tile_ref(grp, (TILE));                                                 \
+        ld_base = tr_.w + (int64_t)tr_.m0 * rowbytes;                                              \
+        const int rows_ = tr_.M - tr_.m0;                                                          \
+        _Pragma("unroll") for (int q = 0; q < CH; ++q)                                            \
+            off[q] = (uint32_t)min(cr[q], rows_ - 1) * rowbytes + 16u * (uint32_t)cc[q];           \
+        ld_tile = (TILE);                                                                          \
     }
 
     // work item i of this wave = (tile first + (i / ns) * tw, stage i % ns)
@@ -87,62 +118,74 @@ __global__ __launch_bounds__(512) void mat_vec_stream(MvGroup grp, int nb, const
         if (n.st == ns) { n.st = 0; n.tile += tw; }
         return n;
     };
-    auto issue = [&](Item it, const TileRef &tr, u32x4_t (&reg)[CH]) {
-        const int sb = min(SB, nb - it.st * SB);
-        const int cpr = sb * kBlockBytes / 16;
-        const uint8_t *base = tr.w + (int64_t)it.st * SB * kBlockBytes;
-#pragma unroll
-        for (int q = 0; q < CH; ++q) {
-            const int row = min(tr.m0 + min(cr[q], kMvTile - 1), tr.M - 1);
-            const int cc = min(ccol[q], cpr - 1);
-            reg[q] = *reinterpret_cast<const u32x4_t *>(base + (int64_t)row * rowbytes + 16 * cc);
-        }
-    };
-    uint8_t *lw = lds_w + wave * kMvTile * RSB;
-    auto park = [&](Item it, const u32x4_t (&reg)[CH]) {
-        const int sb = min(SB, nb - it.st * SB);
-        const int cpr = sb * kBlockBytes / 16;
-#pragma unroll
-        for (int q = 0; q < CH; ++q)
-            if (cr[q] < kMvTile && ccol[q] < cpr)
-                *reinterpret_cast<u32x4_t *>(lw + cr[q] * RSB + 16 * ccol[q]) = reg[q];
-    };
+    // Every call issues exactly CH loads (items past the end reload the last real one),
+    // so the wait counts before each park stay exact.
+#define Q2_0_ISSUE(IT, REG)                                                                    \
+    {                                                                                          \
+        if ((IT).tile != ld_tile) Q2_0_SET_LOAD_TILE((IT).tile)                               \
+        const uint8_t *sbase = ld_base + (uint32_t)(IT).st * (uint32_t)(SB * kBlockBytes);     \
+        if (ragged && (IT).st == ns - 1) {                                                     \
+            _Pragma("unroll") for (int q = 0; q < CH; ++q) {                                   \
+                const uint32_t o = off[q] - 16u * (uint32_t)max(cc[q] - (CPR / 2 - 1), 0);     \
+                REG[q] = *reinterpret_cast<const u32x4_t *>(sbase + o);                        \
+            }                                                                                  \
+        } else {                                                                               \
+            _Pragma("unroll") for (int q = 0; q < CH; ++q)                                     \
+                REG[q] = *reinterpret_cast<const u32x4_t *>(sbase + off[q]);                   \
+        }                                                                                      \
+    }
+#define Q2_0_PARK(REG)                                                                          \
+    {                                                                                           \
+        _Pragma("unroll") for (int q = 0; q < CH; ++q)                                         \
+            *reinterpret_cast<u32x4_t *>(lds_w + lds_off[q]) = REG[q];                          \
+    }
 
-    // Prefetch the first two stages before staging x, so their latency overlaps it.
-    Item cur{first, 0};
-    Item nxt = next_item(cur);
-    TileRef tr_cur = tile_ref(grp, first < total ? first : 0);
-    TileRef tr_nxt = (nxt.st == 0 && nxt.tile < total) ? tile_ref(grp, nxt.tile) : tr_cur;
-    u32x4_t regA[CH], regB[CH];
-    if (first < total) issue(cur, tr_cur, regA);
-    if (nxt.tile < total) issue(nxt, tr_nxt, regB);
-
-    stage_x_all<NC>(x, ldx, nb, lds_x, tid, WAVES * 64);
+    column_exponents<NC>(x, ldx, nb * kBlockWeights, lds_e, lds_tmp, tid, WAVES * 64);
+    stage_x_all<NC>(x, ldx, nb, lds_e, lds_x, tid, WAVES * 64);
     __syncthreads();
     if (first >= total) return;
 
-    const uint8_t *lw_row = lw + j * RSB;
+    // The first two stages are issued only now, so that on entering the loop exactly
+    // these two sets of loads are in flight, as on every later iteration; the
+    // compiler's wait counts at the loop head are then the two-deep ones.
+    Item cur{first, 0};
+    Item nxt = next_item(cur);
+    u32x4_t regA[CH], regB[CH];
+    Q2_0_ISSUE(cur, regA)
+    {
+        const Item load = nxt.tile < total ? nxt : cur;
+        Q2_0_ISSUE(load, regB)
+    }
+    // results leave as acc * 2^-e of their column
+    const int ye0 = -lds_e[min(2 * g, NC - 1)], ye1 = -lds_e[min(2 * g + 1, NC - 1)];
+
+    const uint8_t *lw_row = lds_w + wave * (kMvTile * RSB + DUMMY) + j * RSB;
     const int arow = g * NR + (j % NR);
     const uint32_t sel = (g == 0) ? 0x05040302u : 0x03020100u;
     const PairMasks pm;
     float acc0[2] = {0.f, 0.f}, acc1[2] = {0.f, 0.f};
+    TileRef tr_out = tile_ref(grp, cur.tile);   // matrix and rows of the tile being computed
 
-    auto compute_and_store = [&](Item it, const TileRef &tr) {
+    auto compute_and_store = [&](Item it) {
         const int sb = min(SB, nb - it.st * SB);
         const half8_t *ax = lds_x + (it.st * SB * 2 * 4) * NR + arow;
+        // first half of the stage, then the second unless the stage is a half one
+#pragma unroll
+        for (int pp = 0; pp < SB / 4; ++pp)
+            mv_block_pair<NC>(lw_row + 36 * pp, ax + (2 * pp) * 2 * 4 * NR, g, sel, pm, acc0, acc1);
         if (sb == SB) {
 #pragma unroll
-            for (int pp = 0; pp < SB / 2; ++pp)
-                mv_block_pair<NC>(lw_row + 36 * pp, ax + (2 * pp) * 2 * 4 * NR, g, sel, pm, acc0, acc1);
-        } else {
-            for (int pp = 0; pp < sb / 2; ++pp)
+            for (int pp = SB / 4; pp < SB / 2; ++pp)
                 mv_block_pair<NC>(lw_row + 36 * pp, ax + (2 * pp) * 2 * 4 * NR, g, sel, pm, acc0, acc1);
         }
         if (it.st == ns - 1) {
+            const TileRef &tr = tr_out;
             const int row = tr.m0 + j;
             if (row < tr.M) {
-                if (2 * g < NC) tr.y[(int64_t)(2 * g) * tr.ldy + row] = acc0[0] + acc1[0];
-                if (2 * g + 1 < NC) tr.y[(int64_t)(2 * g + 1) * tr.ldy + row] = acc0[1] + acc1[1];
+                if (2 * g < NC)
+                    tr.y[(int64_t)(2 * g) * tr.ldy + row] = __builtin_amdgcn_ldexpf(acc0[0] + acc1[0], ye0);
+                if (2 * g + 1 < NC)
+                    tr.y[(int64_t)(2 * g + 1) * tr.ldy + row] = __builtin_amdgcn_ldexpf(acc0[1] + acc1[1], ye1);
             }
             acc0[0] = acc0[1] = acc1[0] = acc1[1] = 0.f;
         }
@@ -153,29 +196,40 @@ __global__ __launch_bounds__(512) void mat_vec_stream(MvGroup grp, int nb, const
     // compiler would otherwise keep in scratch.)
 #define Q2_0_HALF_STEP(REG)                                                        \
     {                                                                              \
-        park(cur, REG);                                                            \
+        Q2_0_PARK(REG)                                                             \
         __builtin_amdgcn_wave_barrier();                                           \
         const Item ahead = next_item(nxt);                                         \
-        TileRef tr_ahead = tr_nxt;                                                 \
-        if (ahead.st == 0 && ahead.tile < total) tr_ahead = tile_ref(grp, ahead.tile); \
-        if (ahead.tile < total) issue(ahead, tr_ahead, REG);                       \
-        compute_and_store(cur, tr_cur);                                            \
+        const Item load = ahead.tile < total ? ahead : cur;                        \
+        Q2_0_ISSUE(load, REG)                                                      \
+        compute_and_store(cur);                                                    \
         __builtin_amdgcn_wave_barrier();                                           \
-        if (nxt.tile >= total) break;                                              \
+        if (nxt.tile < total && nxt.tile != cur.tile) tr_out = tile_ref(grp, nxt.tile); \
         cur = nxt;                                                                 \
-        tr_cur = tr_nxt;                                                           \
         nxt = ahead;                                                               \
-        tr_nxt = tr_ahead;                                                         \
     }
-    while (true) {
+    // The wave's items, counted up front so that the loop is a plain counted one with
+    // no exit in the middle (which keeps the compiler's wait counts exact).
+    const int n_items = ns * ((total - first + tw - 1) / tw);
+    int i = 0;
+    for (; i + 2 <= n_items; i += 2) {
         Q2_0_HALF_STEP(regA)
         Q2_0_HALF_STEP(regB)
     }
+    if (i < n_items) Q2_0_HALF_STEP(regA)
 #undef Q2_0_HALF_STEP
+#undef Q2_0_PARK
+#undef Q2_0_ISSUE
+#undef Q2_0_SET_LOAD_TILE
 }
 
+// Dynamic LDS of one workgroup: 8 wave tiles (with their dummy park slots) + the
+// staged activation.  Its static
+// LDS (column exponents and their reduction, under kMvStreamStaticLds bytes) comes
+// on top.
 size_t mat_vec_stream_lds(int N, int nb) {
-    return (size_t)8 * kMvTile * (kMvStreamSB * kBlockBytes + 16) + (size_t)nb * 2 * 4 * 2 * N * 16;
+    constexpr int nchunk = kMvTile * kMvStreamSB * kBlockBytes / 16;
+    constexpr int dummy = (64 - (nchunk - 64 * ((nchunk + 63) / 64 - 1))) * 16;
+    return (size_t)8 * (kMvTile * (kMvStreamSB * kBlockBytes + 16) + dummy) + (size_t)nb * 2 * 4 * 2 * N * 16;
 }
 
 template <int NC>
@@ -190,8 +244,12 @@ static hipError_t launch_stream_nc(const MvGroup &grp, int nb, const float *x, i
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= 64 || !configured[dev]) {
+        // the cap on dynamic LDS is what the kernel's static LDS leaves of 160 KiB
+        hipFuncAttributes fa;
+        e = hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(kern));
+        if (e != hipSuccess) return e;
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)(160 * 1024 - fa.sharedSizeBytes));
         if (e != hipSuccess) return e;
         if (dev >= 0 && dev < 64) configured[dev] = true;
     }
@@ -201,7 +259,7 @@ static hipError_t launch_stream_nc(const MvGroup &grp, int nb, const float *x, i
 
 hipError_t launch_mat_vec_stream(const MvGroup &grp, int nb, const float *x, int64_t ldx, int N,
                                  hipStream_t s) {
-    const size_t lds = mat_vec_stream_lds(N, nb);
+    const size_t lds = mat_vec_stream_lds(N, nb) + kMvStreamStaticLds;
     const int per_cu = (int)((160 * 1024) / lds);
     const int max_grid = 256 * (per_cu < 1 ? 1 : per_cu);
     const int need = (grp.total_tiles + 7) / 8;

@@ -10,6 +10,8 @@
 // f32, scales it by d and accumulates; the 64 lane sums are combined with a
 // butterfly.  Summation depth per output: 16 + K/1024 + 6, far below what the
 // 1e-5 relative bound allows (about 160 f32 roundings).
+#include <climits>
+
 #include "q2_0_internal.h"
 #include "mat_vec_common.h"
 
@@ -80,7 +82,7 @@ static void launch_generic_nc(const uint8_t *w, int64_t M, int nb, const float *
 // the generic kernel.
 constexpr int64_t kStreamTiles = 1024;
 
-static bool stream_fits(int N, int nb) { return mat_vec_stream_lds(N, nb) <= 160 * 1024; }
+static bool stream_fits(int N, int nb) { return mat_vec_stream_lds(N, nb) + kMvStreamStaticLds <= 160 * 1024; }
 
 hipError_t launch_mat_vec(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx, int N,
                           float *y, int64_t ldy, hipStream_t s) {
@@ -89,6 +91,7 @@ hipError_t launch_mat_vec(const uint8_t *w, int64_t M, int nb, const float *x, i
             MvGroup grp;
             grp.n = 1;
             grp.p[0] = MvProblem{w, y, ldy, (int)M, 0};
+            for (int i = 0; i < kMvMaxGroup; ++i) grp.tile0[i] = i ? INT_MAX : 0;
             grp.total_tiles = (int)((M + kMvTile - 1) / kMvTile);
             return launch_mat_vec_stream(grp, nb, x, ldx, N, s);
         }
@@ -130,11 +133,13 @@ hipError_t launch_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items,
                 ++i;
                 continue;
             }
+            grp.tile0[grp.n] = tiles;
             grp.p[grp.n++] = MvProblem{w, it.y, it.ldy, (int)it.M, tiles};
             tiles += (int)((it.M + kMvTile - 1) / kMvTile);
             ++i;
         }
         if (grp.n) {
+            for (int k = grp.n; k < kMvMaxGroup; ++k) grp.tile0[k] = INT_MAX;
             grp.total_tiles = tiles;
             hipError_t e = launch_mat_vec_stream(grp, nb, x, ldx, N, s);
             if (e != hipSuccess) return e;

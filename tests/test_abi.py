@@ -97,9 +97,10 @@ def test_unsupported():
 
 
 def test_workspace_query_and_checks():
-    # fp16 GEMM stages x as fp16: N*K*2 bytes (rounded up to 256), plus split-K partials
-    # when the tile grid is small; nothing else needs any
-    assert B.mul_mat_workspace_bytes(65536, 4096, 512, B.Q2_0_PREC_F16_MFMA) == 512 * 4096 * 2
+    # fp16 GEMM stages x as fp16: N*K*2 bytes and N int32 column exponents (each rounded
+    # up to 256), plus split-K partials when the tile grid is small; nothing else needs any
+    assert B.mul_mat_workspace_bytes(65536, 4096, 512, B.Q2_0_PREC_F16_MFMA) == 512 * 4096 * 2 + 2048
+    assert B.mul_mat_workspace_bytes(65536, 4096, 100, B.Q2_0_PREC_F16_MFMA) == 100 * 4096 * 2 + 512
     assert B.mul_mat_workspace_bytes(1024, 4096, 512, B.Q2_0_PREC_F16_MFMA) > 512 * 4096 * 2
     assert B.mul_mat_workspace_bytes(4096, 4096, 512, B.Q2_0_PREC_F32) == 0
     assert B.mul_mat_workspace_bytes(4096, 4096, 8, B.Q2_0_PREC_F16_MFMA) == 0

@@ -248,6 +248,43 @@ def test_mat_vec_metamorphic_scale_and_permute():
         assert np.all(np.abs(y1[0] - y[n]) <= 2 * REL_F32 * bound[0])
 
 
+# Activation magnitudes far from 1: fp16 staging must neither overflow (|x| > 65504)
+# nor lose the small end to fp16 subnormals, so each column is scaled into range.
+MAGS = [1e-30, 1e-8, 1e-5, 1e-3, 1.0, 3e3, 1e5, 1e8, 1e30]
+
+
+def _ranged_x(seed, N, K, mags, spread=False):
+    x = synth.activations(seed, 0, 9, N, K).astype(np.float64)
+    x *= np.array([mags[n % len(mags)] for n in range(N)])[:, None]
+    if spread:   # every other element 1e4 times smaller: dynamic range inside a column
+        x[:, 1::2] *= 1e-4
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("M,K", [(300, 1024), (16400, 512)])   # K-split kernel, streaming kernel
+@pytest.mark.parametrize("N,first", [(1, 0), (1, 2), (1, 7), (1, 8), (4, 0), (8, 1)])
+def test_mat_vec_activation_range(M, K, N, first):
+    w = synth.weight(13, M, K // 64, M, K, "tern_c3", synth.ScaleDist("uniform", 0.005, 0.05))
+    mags = MAGS[first:] + MAGS[:first]
+    for spread in (False, True):
+        x = _ranged_x(13, N, K, mags, spread)
+        y = run_mat_vec(dev(w), M, K, x)
+        rows = None if M < 1000 else np.arange(0, M, 7)
+        assert_products(y, w, M, K, x, REL_F32, rows=rows,
+                        what="M=%d N=%d mags from %g spread=%s" % (M, N, mags[0], spread))
+
+
+def test_mat_vec_group_activation_range():
+    K, N = 512, 3
+    mats = [synth.weight(14, i, 0, M, K, "quad", synth.ScaleDist("uniform", 0.005, 0.05))
+            for i, M in enumerate((16384, 80, 4096))]
+    x = _ranged_x(14, N, K, [1e-9, 7e4, 1e12])
+    ys = run_group([(w, w.shape[0]) for w in mats], K, x)
+    for w, y in zip(mats, ys):
+        M = w.shape[0]
+        assert_products(y, w, M, K, x, REL_F32, rows=np.arange(0, M, 5), what="group M=%d" % M)
+
+
 # =============================================================================== GEMM
 
 @pytest.mark.parametrize("precision,rel", [(B.Q2_0_PREC_F16_MFMA, REL_F16), (B.Q2_0_PREC_F32, REL_F32)])
@@ -295,6 +332,16 @@ def test_mul_mat_small_n_routes_to_mat_vec():
         a = run_mat_vec(wd, M, K, x)
         for p in (B.Q2_0_PREC_F16_MFMA, B.Q2_0_PREC_F32):
             assert np.array_equal(run_mul_mat(wd, M, K, x, p), a)
+
+
+@pytest.mark.parametrize("precision,rel", [(B.Q2_0_PREC_F16_MFMA, REL_F16), (B.Q2_0_PREC_F32, REL_F32)])
+@pytest.mark.parametrize("M,K,N", [(200, 640, 9), (1024, 4096, 27), (129, 12288, 18)])
+def test_mul_mat_activation_range(precision, rel, M, K, N):
+    w = synth.weight(15, M, K // 64, M, K, "tern", synth.ScaleDist("uniform", 0.002, 0.02))
+    for spread in (False, True):
+        x = _ranged_x(15, N, K, MAGS, spread)
+        y = run_mul_mat(dev(w), M, K, x, precision)
+        assert_products(y, w, M, K, x, rel, what="M=%d K=%d N=%d spread=%s" % (M, K, N, spread))
 
 
 @pytest.mark.parametrize("precision", [B.Q2_0_PREC_F16_MFMA, B.Q2_0_PREC_F32])
