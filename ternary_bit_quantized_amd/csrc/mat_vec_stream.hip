@@ -1,25 +1,31 @@
 // Persistent streaming mat-vec for N = 1..8 on the gfx950 matrix cores.
 //
-// Same arithmetic as mat_vec_mfma.hip (block sums of (q - 1) * x formed on the
-// matrix cores from exact fp16 (q - 1) and an fp16 hi/lo split of x, one multiply
-// by the block scale per block; bisque.today "WebGPU: add Q2_0 support", the
-// matrix-vector paragraph), organised for throughput on large or grouped launches:
+// What is computed follows the matrix-vector paragraph of bisque.today "WebGPU: add
+// Q2_0 support": per block the sum of (q - 1) * x, then one multiply by the block
+// scale.  The block sums run on the matrix cores as S - T: S = sum q * x from the
+// codes decoded as exact fp16 subnormals (one AND per two weights), T = sum x from
+// the same MFMA chain with every code 1, formed once per block and workgroup (the
+// offset-free decode in mat_vec_common.h); x enters as an fp16 hi/lo pair.  The
+// kernel is organised for throughput on large or grouped launches:
 //
 //  * The activation columns for the whole of K are converted once per workgroup
 //    into LDS, laid out as the MFMA A operand, behind a single barrier.
-//  * After that each wave streams on its own, with no workgroup barrier: it walks
-//    16-row tiles (tile = wave id, + total waves, ...), each over all of K in
-//    stages of SB blocks.  Two stages are in flight in registers (coalesced
-//    16-byte loads, consecutive lanes on consecutive bytes of a row) while a third
-//    is decoded, so HBM latency hides behind the decode.  Weight bytes pass
-//    through a wave-private LDS tile only to be regrouped per lane.
-//  * Loads are branch-free: rows past the end of a matrix are clamped to its last
-//    row (their outputs are never stored).
+//  * Work is a list of items (16-row tile, stage of SB blocks), tile-major.  Each
+//    workgroup owns a contiguous run of tiles and each of its 8 waves a contiguous
+//    eighth of that run's items, so every wave streams the same number of stages
+//    to within one: no tail where a few waves finish a last round alone.
+//  * A wave streams on its own, with no barrier: two stages are in flight in
+//    registers (coalesced 16-byte loads, consecutive lanes on consecutive bytes of
+//    a row) while a third is decoded.  Weight bytes pass through a wave-private LDS
+//    tile only to be regrouped per lane.  Loads are branch-free: rows past the end
+//    of a matrix are clamped to its last row (their outputs are never stored).
+//  * A tile whose stages are split between waves is finished after one barrier at
+//    the end: the waves that hold its earlier stages leave their partial sums in
+//    LDS, and the wave that holds its last stage adds them in stage order.  The
+//    split depends only on the sizes and the grid, so results are deterministic.
 //  * One launch may cover several matrices that share K and the activation (for
 //    example the q, k, v projections, or gate and up): tiles are numbered across
 //    the group and a wave looks its matrix up once per tile.
-//  * Every output is produced by one wave over the full K (no split), so results
-//    are deterministic and independent of the group and grid.
 #include "q2_0_internal.h"
 #include "mat_vec_common.h"
 
@@ -63,20 +69,30 @@ __global__ __launch_bounds__(512) void mat_vec_stream(MvGroup grp, int nb, const
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint8_t *lds_w = smem;   // WAVES x (16 x RSB + DUMMY)
     half8_t *lds_x = reinterpret_cast<half8_t *>(smem + WAVES * (kMvTile * RSB + DUMMY));  // nb x 2 x 4 x NR
+    float4_t *lds_T = reinterpret_cast<float4_t *>(lds_x + nb * 2 * 4 * NR);               // nb/2 x 4
     __shared__ int lds_e[NC];
     __shared__ float lds_tmp[WAVES * NC];
-    static_assert(sizeof(lds_e) + sizeof(lds_tmp) <= kMvStreamStaticLds, "static LDS reserve");
+    __shared__ float2_t lds_part[WAVES][64];   // a wave's unfinished last tile, per lane
+    __shared__ int lds_part_tile[WAVES];
+    static_assert(sizeof(lds_e) + sizeof(lds_tmp) + sizeof(lds_part) + sizeof(lds_part_tile) <=
+                      kMvStreamStaticLds, "static LDS reserve");
 
     const int tid = threadIdx.x;
     // the wave index is uniform: keep it (and all tile bookkeeping) in SGPRs
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 15, g = lane >> 4;
     const int total = grp.total_tiles;
-    const int tw = gridDim.x * WAVES;
-    const int first = blockIdx.x * WAVES + wave;
     const int ns = (nb + SB - 1) / SB;
     const uint32_t rowbytes = (uint32_t)nb * kBlockBytes;
     const bool ragged = (nb % SB) != 0;   // the last stage of a row holds SB/2 blocks
+
+    // This workgroup's tiles [tb0, tb1) and this wave's items [i0, i1) among them.
+    const int tb0 = (int)((int64_t)total * blockIdx.x / gridDim.x);
+    const int tb1 = (int)((int64_t)total * (blockIdx.x + 1) / gridDim.x);
+    const int64_t n_wg = (int64_t)(tb1 - tb0) * ns;
+    const int64_t i0 = n_wg * wave / WAVES, i1 = n_wg * (wave + 1) / WAVES;
+    const int n_items = (int)(i1 - i0);
+    const Item first{tb0 + (int)(i0 / ns), (int)(i0 % ns)};
 
     // Per-lane chunk geometry of a stage: chunk q*64 + lane -> tile row cr, 16-byte column
     // cc, parked at lds_off.  In a half stage (SB/2 blocks) the chunks past its end load a
@@ -112,14 +128,13 @@ __global__ __launch_bounds__(512) void mat_vec_stream(MvGroup grp, int nb, const
         ld_tile = (TILE);                                                                          \
     }
 
-    // work item i of this wave = (tile first + (i / ns) * tw, stage i % ns)
     auto next_item = [&](Item it) {
         Item n{it.tile, it.st + 1};
-        if (n.st == ns) { n.st = 0; n.tile += tw; }
+        if (n.st == ns) { n.st = 0; n.tile += 1; }
         return n;
     };
-    // Every call issues exactly CH loads (items past the end reload the last real one),
-    // so the wait counts before each park stay exact.
+    // Every call issues exactly CH loads (items past the wave's range reload the current
+    // one), so the wait counts before each park stay exact.
 #define Q2_0_ISSUE(IT, REG)                                                                    \
     {                                                                                          \
         if ((IT).tile != ld_tile) Q2_0_SET_LOAD_TILE((IT).tile)                               \
@@ -140,96 +155,124 @@ __global__ __launch_bounds__(512) void mat_vec_stream(MvGroup grp, int nb, const
             *reinterpret_cast<u32x4_t *>(lds_w + lds_off[q]) = REG[q];                          \
     }
 
-    column_exponents<NC>(x, ldx, nb * kBlockWeights, lds_e, lds_tmp, tid, WAVES * 64);
-    stage_x_all<NC>(x, ldx, nb, lds_e, lds_x, tid, WAVES * 64);
+    column_exponents<NC, 11>(x, ldx, nb * kBlockWeights, lds_e, lds_tmp, tid, WAVES * 64);
+    stage_x_all_q<NC>(x, ldx, nb, lds_e, lds_x, tid, WAVES * 64);
     __syncthreads();
-    if (first >= total) return;
+    block_ones_sums<NC>(lds_x, nb, lds_T, lane, wave, WAVES);
+    __syncthreads();
 
-    // The first two stages are issued only now, so that on entering the loop exactly
-    // these two sets of loads are in flight, as on every later iteration; the
-    // compiler's wait counts at the loop head are then the two-deep ones.
-    Item cur{first, 0};
-    Item nxt = next_item(cur);
-    u32x4_t regA[CH], regB[CH];
-    Q2_0_ISSUE(cur, regA)
-    {
-        const Item load = nxt.tile < total ? nxt : cur;
-        Q2_0_ISSUE(load, regB)
-    }
-    // results leave as acc * 2^-e of their column
-    const int ye0 = -lds_e[min(2 * g, NC - 1)], ye1 = -lds_e[min(2 * g + 1, NC - 1)];
-
+    // block sums are in units of 2^-16 x 2^e of their column: results leave as
+    // acc * 2^(16 - e)
+    const int ye0 = 16 - lds_e[min(2 * g, NC - 1)], ye1 = 16 - lds_e[min(2 * g + 1, NC - 1)];
     const uint8_t *lw_row = lds_w + wave * (kMvTile * RSB + DUMMY) + j * RSB;
     const int arow = g * NR + (j % NR);
     const uint32_t sel = (g == 0) ? 0x05040302u : 0x03020100u;
-    const PairMasks pm;
     float acc0[2] = {0.f, 0.f}, acc1[2] = {0.f, 0.f};
-    TileRef tr_out = tile_ref(grp, cur.tile);   // matrix and rows of the tile being computed
+    float2_t pend = {0.f, 0.f};   // the first tile, when it started in an earlier wave
+    bool has_pend = false;
 
+    auto store_tile = [&](const TileRef &tr, float r0, float r1) {
+        const int row = tr.m0 + j;
+        if (row < tr.M) {
+            if (2 * g < NC) tr.y[(int64_t)(2 * g) * tr.ldy + row] = __builtin_amdgcn_ldexpf(r0, ye0);
+            if (2 * g + 1 < NC) tr.y[(int64_t)(2 * g + 1) * tr.ldy + row] = __builtin_amdgcn_ldexpf(r1, ye1);
+        }
+    };
+
+    TileRef tr_out = tile_ref(grp, first.tile);   // matrix and rows of the tile being computed
     auto compute_and_store = [&](Item it) {
         const int sb = min(SB, nb - it.st * SB);
         const half8_t *ax = lds_x + (it.st * SB * 2 * 4) * NR + arow;
+        const float4_t *tp = lds_T + (it.st * SB / 2) * 4 + g;
         // first half of the stage, then the second unless the stage is a half one
 #pragma unroll
         for (int pp = 0; pp < SB / 4; ++pp)
-            mv_block_pair<NC>(lw_row + 36 * pp, ax + (2 * pp) * 2 * 4 * NR, g, sel, pm, acc0, acc1);
+            mv_block_pair_q<NC>(lw_row + 36 * pp, ax + (2 * pp) * 2 * 4 * NR, tp + 4 * pp, g, sel, acc0, acc1);
         if (sb == SB) {
 #pragma unroll
             for (int pp = SB / 4; pp < SB / 2; ++pp)
-                mv_block_pair<NC>(lw_row + 36 * pp, ax + (2 * pp) * 2 * 4 * NR, g, sel, pm, acc0, acc1);
+                mv_block_pair_q<NC>(lw_row + 36 * pp, ax + (2 * pp) * 2 * 4 * NR, tp + 4 * pp, g, sel, acc0,
+                                    acc1);
         }
         if (it.st == ns - 1) {
-            const TileRef &tr = tr_out;
-            const int row = tr.m0 + j;
-            if (row < tr.M) {
-                if (2 * g < NC)
-                    tr.y[(int64_t)(2 * g) * tr.ldy + row] = __builtin_amdgcn_ldexpf(acc0[0] + acc1[0], ye0);
-                if (2 * g + 1 < NC)
-                    tr.y[(int64_t)(2 * g + 1) * tr.ldy + row] = __builtin_amdgcn_ldexpf(acc0[1] + acc1[1], ye1);
+            const float r0 = acc0[0] + acc1[0], r1 = acc0[1] + acc1[1];
+            if (it.tile == first.tile && first.st != 0) {
+                pend = float2_t{r0, r1};
+                has_pend = true;
+            } else {
+                store_tile(tr_out, r0, r1);
             }
             acc0[0] = acc0[1] = acc1[0] = acc1[1] = 0.f;
         }
     };
 
+    Item cur = first;
+    Item nxt = next_item(cur);
+    u32x4_t regA[CH], regB[CH];
+    if (n_items > 0) {
+        Q2_0_ISSUE(cur, regA)
+        const Item load = n_items > 1 ? nxt : cur;
+        Q2_0_ISSUE(load, regB)
+    }
+
     // Two register buffers alternate: park A, refill A two items ahead, compute; then B.
     // (Written out rather than as a lambda over a register-array reference, which the
-    // compiler would otherwise keep in scratch.)
+    // compiler would otherwise keep in scratch.)  k counts the items done.
 #define Q2_0_HALF_STEP(REG)                                                        \
     {                                                                              \
         Q2_0_PARK(REG)                                                             \
         __builtin_amdgcn_wave_barrier();                                           \
         const Item ahead = next_item(nxt);                                         \
-        const Item load = ahead.tile < total ? ahead : cur;                        \
+        const Item load = (k + 2 < n_items) ? ahead : cur;                         \
         Q2_0_ISSUE(load, REG)                                                      \
         compute_and_store(cur);                                                    \
         __builtin_amdgcn_wave_barrier();                                           \
-        if (nxt.tile < total && nxt.tile != cur.tile) tr_out = tile_ref(grp, nxt.tile); \
+        if (k + 1 < n_items && nxt.tile != cur.tile) tr_out = tile_ref(grp, nxt.tile); \
         cur = nxt;                                                                 \
         nxt = ahead;                                                               \
+        ++k;                                                                       \
     }
-    // The wave's items, counted up front so that the loop is a plain counted one with
-    // no exit in the middle (which keeps the compiler's wait counts exact).
-    const int n_items = ns * ((total - first + tw - 1) / tw);
-    int i = 0;
-    for (; i + 2 <= n_items; i += 2) {
+    // A plain counted loop with no exit in the middle, which keeps the compiler's
+    // wait counts exact.
+    int k = 0;
+    while (k + 2 <= n_items) {
         Q2_0_HALF_STEP(regA)
         Q2_0_HALF_STEP(regB)
     }
-    if (i < n_items) Q2_0_HALF_STEP(regA)
+    if (k < n_items) Q2_0_HALF_STEP(regA)
 #undef Q2_0_HALF_STEP
 #undef Q2_0_PARK
 #undef Q2_0_ISSUE
 #undef Q2_0_SET_LOAD_TILE
+
+    // An unfinished last tile leaves its partial sums for the wave that holds the
+    // tile's last stage; that wave adds the earlier waves' partials in order.
+    const bool open_end = n_items > 0 && ((int)((i1 - 1) % ns) != ns - 1);
+    if (open_end) lds_part[wave][lane] = float2_t{acc0[0] + acc1[0], acc0[1] + acc1[1]};
+    if (lane == 0) lds_part_tile[wave] = open_end ? (tb0 + (int)((i1 - 1) / ns)) : -1;
+    __syncthreads();
+    if (has_pend) {
+        float r0 = 0.f, r1 = 0.f;
+        for (int w = 0; w < wave; ++w) {
+            if (lds_part_tile[w] == first.tile) {
+                const float2_t p = lds_part[w][lane];
+                r0 += p.x;
+                r1 += p.y;
+            }
+        }
+        store_tile(tile_ref(grp, first.tile), r0 + pend.x, r1 + pend.y);
+    }
 }
 
 // Dynamic LDS of one workgroup: 8 wave tiles (with their dummy park slots) + the
-// staged activation.  Its static
+// staged activation + the blocks' weight-free sums T.  Its static
 // LDS (column exponents and their reduction, under kMvStreamStaticLds bytes) comes
 // on top.
 size_t mat_vec_stream_lds(int N, int nb) {
     constexpr int nchunk = kMvTile * kMvStreamSB * kBlockBytes / 16;
     constexpr int dummy = (64 - (nchunk - 64 * ((nchunk + 63) / 64 - 1))) * 16;
-    return (size_t)8 * (kMvTile * (kMvStreamSB * kBlockBytes + 16) + dummy) + (size_t)nb * 2 * 4 * 2 * N * 16;
+    return (size_t)8 * (kMvTile * (kMvStreamSB * kBlockBytes + 16) + dummy) + (size_t)nb * 2 * 4 * 2 * N * 16 +
+           (size_t)nb * 32;
 }
 
 template <int NC>
@@ -262,8 +305,11 @@ hipError_t launch_mat_vec_stream(const MvGroup &grp, int nb, const float *x, int
     const size_t lds = mat_vec_stream_lds(N, nb) + kMvStreamStaticLds;
     const int per_cu = (int)((160 * 1024) / lds);
     const int max_grid = 256 * (per_cu < 1 ? 1 : per_cu);
-    const int need = (grp.total_tiles + 7) / 8;
-    const int grid = need < max_grid ? need : max_grid;
+    // every wave gets at least about one stage; never more workgroups than tiles
+    const int64_t ns = (nb + kMvStreamSB - 1) / kMvStreamSB;
+    int64_t need = ((int64_t)grp.total_tiles * ns + 7) / 8;
+    if (need > grp.total_tiles) need = grp.total_tiles;
+    const int grid = (int)(need < max_grid ? need : max_grid);
     switch (N) {
         case 1: return launch_stream_nc<1>(grp, nb, x, ldx, s, grid);
         case 2: return launch_stream_nc<2>(grp, nb, x, ldx, s, grid);
