@@ -85,7 +85,11 @@ int q2_0_get_rows(const void *w, int64_t M, int64_t K, const int32_t *ids, int64
  *   y : N columns of M floats at y + n*ldy, ldy >= M, 4-byte aligned; y[n][m] is
  *       overwritten.  x and y must not overlap.
  * Accuracy: |y - y_exact| <= 1e-5 * sum_k |W[m][k] * x[n][k]|, and exactly 0 when
- * that sum is 0, for finite inputs with |x| < 2^100.
+ * that sum is 0, for finite inputs with |x| < 2^100.  x is carried as an fp16
+ * hi/lo pair after an exact power-of-two scaling per column: every element within
+ * 2^18 of its column's largest |x| keeps 2^-22 relative accuracy and smaller ones
+ * err by at most 2^-40 of that largest value, so the bound can fail only where
+ * sum|W x| is carried by elements that far below a zero-weighted neighbour.
  * N > 8 returns Q2_0_ERR_UNSUPPORTED (use q2_0_mul_mat).
  */
 int q2_0_mul_mat_vec(const void *w, int64_t M, int64_t K, const float *x, int64_t ldx, int64_t N,

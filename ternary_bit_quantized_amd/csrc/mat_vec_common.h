@@ -248,118 +248,6 @@ __device__ __forceinline__ void mv_block_pair(const uint8_t *lp, const half8_t *
     }
 }
 
-// ---- Offset-free decode (streaming kernel) ------------------------------------
-// The (q - 1) pairs above cost two VALU ops per two weights.  This variant costs one:
-// the code is AND-ed into mantissa bits 2p, 2p+1 of an fp16 with a zero exponent,
-// which reads as the subnormal q * 2^(2p - 24) exactly.  Two shifts bring every code
-// of a dword to p = 2, 3 or 4:
-//   codes 0, 1 via (cd << 4) at p = 2, 3;  codes 2, 3, 4 in place at p = 2, 3, 4;
-//   codes 5, 6, 7 via (cd >> 6) at p = 2, 3, 4.
-// The A operand carries x * 2^(8 - 2p) for the slot's p, so every product is
-// q * x * 2^-16 whatever p is.  The matrix core then yields S = sum q x; the -1 of
-// (q - 1) is the weight-free T = sum x, which is computed once per block by the same
-// MFMA chain with every code 1 (block_ones_sums): S and T are then bitwise equal
-// for an all-code-1 block, whose contribution S - T is exactly zero.
-// Position of the code behind B element pair e of the block's MFMA mu.
-__device__ __forceinline__ constexpr int code_pos(int mu, int e) {
-    return mu == 0 ? ((e & 1) ? 3 : 2) : ((e == 0 || e == 3) ? 4 : (e == 1 ? 2 : 3));
-}
-
-__device__ __forceinline__ void decode_dword_q(uint32_t cd, half8_t &b0, half8_t &b1) {
-    const uint32_t lo4 = cd << 4, hi6 = cd >> 6;
-    b0 = as_half8(lo4 & 0x00300030u, lo4 & 0x00c000c0u, cd & 0x00300030u, cd & 0x00c000c0u);
-    b1 = as_half8(cd & 0x03000300u, hi6 & 0x00300030u, hi6 & 0x00c000c0u, hi6 & 0x03000300u);
-}
-
-// Every code 1: the B operands of block_ones_sums.
-__device__ __forceinline__ void ones_q(half8_t &b0, half8_t &b1) {
-    b0 = as_half8(0x00100010u, 0x00400040u, 0x00100010u, 0x00400040u);
-    b1 = as_half8(0x01000100u, 0x00100010u, 0x00400040u, 0x01000100u);
-}
-
-// As store_x_item, with slot e of MFMA mu scaled by 2^(8 - 2 code_pos(mu, e)).
-__device__ __forceinline__ void store_x_item_q(const XItem &it, int xe, int mu, half8_t *dst) {
-    uint32_t hiw[4], low[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int f = xe + 8 - 2 * (mu == 0 ? code_pos(0, e) : code_pos(1, e));
-        const float va = __builtin_amdgcn_ldexpf(it.a[e], f), vc = __builtin_amdgcn_ldexpf(it.c[e], f);
-        const _Float16 ha = (_Float16)va, hc = (_Float16)vc;
-        const _Float16 la = (_Float16)(va - (float)ha), lc = (_Float16)(vc - (float)hc);
-        hiw[e] = __builtin_bit_cast(uint32_t, half2_t{ha, hc});
-        low[e] = __builtin_bit_cast(uint32_t, half2_t{la, lc});
-    }
-    dst[0] = as_half8(hiw[0], hiw[1], hiw[2], hiw[3]);
-    dst[1] = as_half8(low[0], low[1], low[2], low[3]);
-}
-
-template <int NC>
-__device__ __forceinline__ void stage_x_all_q(const float *__restrict__ x, int64_t ldx, int nb,
-                                              const int *lds_e, half8_t *lds_x, int tid, int nthreads) {
-    const int items = nb * 2 * 4 * NC;
-    for (int q = tid; q < items; q += nthreads) {
-        const int n = q % NC, gg = (q / NC) % 4, mu = (q / (4 * NC)) % 2, b = q / (8 * NC);
-        store_x_item_q(load_x_item(x, ldx, b, mu, gg, n), lds_e[n], mu, lds_x + (q / NC) * (2 * NC) + 2 * n);
-    }
-}
-
-// T of every block pair into lds_T[pair * 4 + g] = {T_even(2g), T_odd(2g),
-// T_even(2g+1), T_odd(2g+1)} (columns 2g, 2g+1 of lane group g), each the f32 sum of
-// the hi and lo rows exactly as mv_block_pair_q forms S.  Waves take pairs in turn.
-template <int NC>
-__device__ __forceinline__ void block_ones_sums(const half8_t *lds_x, int nb, float4_t *lds_T, int lane,
-                                                int wave, int nwaves) {
-    constexpr int NR = 2 * NC;
-    const int j = lane & 15, g = lane >> 4;
-    const int arow = g * NR + (j % NR);
-    half8_t o0, o1;
-    ones_q(o0, o1);
-    for (int pr = wave; pr < nb / 2; pr += nwaves) {
-        const half8_t *a = lds_x + (2 * pr * 2 * 4) * NR + arow;
-        float4_t te = {0.f, 0.f, 0.f, 0.f}, to = {0.f, 0.f, 0.f, 0.f};
-        te = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], o0, te, 0, 0, 0);
-        te = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[4 * NR], o1, te, 0, 0, 0);
-        to = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[8 * NR], o0, to, 0, 0, 0);
-        to = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[12 * NR], o1, to, 0, 0, 0);
-        if (j == 0) lds_T[pr * 4 + g] = float4_t{te[0] + te[1], to[0] + to[1], te[2] + te[3], to[2] + to[3]};
-    }
-}
-
-// One block pair with the offset-free decode; T points at the pair's lds_T entry of
-// this lane's group.  Block sums are (S - T), still in units of 2^-16 x.
-template <int NC>
-__device__ __forceinline__ void mv_block_pair_q(const uint8_t *lp, const half8_t *a, const float4_t *T,
-                                                int g, uint32_t sel, float acc0[2], float acc1[2]) {
-    constexpr int NR = 2 * NC;
-    const uint32_t X = *reinterpret_cast<const uint32_t *>(lp + 4 * g);
-    const uint32_t Y = *reinterpret_cast<const uint32_t *>(lp + 16);
-    const uint32_t Z = *reinterpret_cast<const uint32_t *>(lp + 20 + 4 * g);
-    uint32_t D0 = X;   // group 0 reads D0 anyway; only columns of group 0 exist for NC <= 2
-    if (NC > 2) D0 = *reinterpret_cast<const uint32_t *>(lp);
-    const uint32_t cde = __builtin_amdgcn_perm(Y, X, sel);
-    half8_t b0, b1, c0, c1;
-    decode_dword_q(cde, b0, b1);
-    decode_dword_q(Z, c0, c1);
-    float4_t ce = {0.f, 0.f, 0.f, 0.f}, co = {0.f, 0.f, 0.f, 0.f};
-    ce = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], b0, ce, 0, 0, 0);
-    ce = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[4 * NR], b1, ce, 0, 0, 0);
-    co = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[8 * NR], c0, co, 0, 0, 0);
-    co = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[12 * NR], c1, co, 0, 0, 0);
-    const float de = half_bits_to_float(D0 & 0xffffu);
-    const float dd = half_bits_to_float(Y >> 16);
-    if (NC == 1) {
-        const float2_t t = *reinterpret_cast<const float2_t *>(T);
-        acc0[0] = __builtin_fmaf(de, (ce[0] + ce[1]) - t.x, acc0[0]);
-        acc1[0] = __builtin_fmaf(dd, (co[0] + co[1]) - t.y, acc1[0]);
-    } else {
-        const float4_t t = *T;
-        acc0[0] = __builtin_fmaf(de, (ce[0] + ce[1]) - t.x, acc0[0]);
-        acc1[0] = __builtin_fmaf(dd, (co[0] + co[1]) - t.y, acc1[0]);
-        acc0[1] = __builtin_fmaf(de, (ce[2] + ce[3]) - t.z, acc0[1]);
-        acc1[1] = __builtin_fmaf(dd, (co[2] + co[3]) - t.w, acc1[1]);
-    }
-}
-
 size_t mat_vec_stream_lds(int N, int nb);
 hipError_t launch_mat_vec_stream(const MvGroup &grp, int nb, const float *x, int64_t ldx, int N,
                                  hipStream_t s);

@@ -1,12 +1,9 @@
 // Persistent streaming mat-vec for N = 1..8 on the gfx950 matrix cores.
 //
-// What is computed follows the matrix-vector paragraph of bisque.today "WebGPU: add
-// Q2_0 support": per block the sum of (q - 1) * x, then one multiply by the block
-// scale.  The block sums run on the matrix cores as S - T: S = sum q * x from the
-// codes decoded as exact fp16 subnormals (one AND per two weights), T = sum x from
-// the same MFMA chain with every code 1, formed once per block and workgroup (the
-// offset-free decode in mat_vec_common.h); x enters as an fp16 hi/lo pair.  The
-// kernel is organised for throughput on large or grouped launches:
+// Same arithmetic as mat_vec_mfma.hip (block sums of (q - 1) * x formed on the
+// matrix cores from exact fp16 (q - 1) and an fp16 hi/lo split of x, one multiply
+// by the block scale per block; bisque.today "WebGPU: add Q2_0 support", the
+// matrix-vector paragraph), organised for throughput on large or grouped launches:
 //
 //  * The activation columns for the whole of K are converted once per workgroup
 //    into LDS, laid out as the MFMA A operand, behind a single barrier.
@@ -69,7 +66,6 @@ __global__ __launch_bounds__(512) void mat_vec_stream(MvGroup grp, int nb, const
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint8_t *lds_w = smem;   // WAVES x (16 x RSB + DUMMY)
     half8_t *lds_x = reinterpret_cast<half8_t *>(smem + WAVES * (kMvTile * RSB + DUMMY));  // nb x 2 x 4 x NR
-    float4_t *lds_T = reinterpret_cast<float4_t *>(lds_x + nb * 2 * 4 * NR);               // nb/2 x 4
     __shared__ int lds_e[NC];
     __shared__ float lds_tmp[WAVES * NC];
     __shared__ float2_t lds_part[WAVES][64];   // a wave's unfinished last tile, per lane
@@ -155,18 +151,16 @@ __global__ __launch_bounds__(512) void mat_vec_stream(MvGroup grp, int nb, const
             *reinterpret_cast<u32x4_t *>(lds_w + lds_off[q]) = REG[q];                          \
     }
 
-    column_exponents<NC, 11>(x, ldx, nb * kBlockWeights, lds_e, lds_tmp, tid, WAVES * 64);
-    stage_x_all_q<NC>(x, ldx, nb, lds_e, lds_x, tid, WAVES * 64);
-    __syncthreads();
-    block_ones_sums<NC>(lds_x, nb, lds_T, lane, wave, WAVES);
+    column_exponents<NC>(x, ldx, nb * kBlockWeights, lds_e, lds_tmp, tid, WAVES * 64);
+    stage_x_all<NC>(x, ldx, nb, lds_e, lds_x, tid, WAVES * 64);
     __syncthreads();
 
-    // block sums are in units of 2^-16 x 2^e of their column: results leave as
-    // acc * 2^(16 - e)
-    const int ye0 = 16 - lds_e[min(2 * g, NC - 1)], ye1 = 16 - lds_e[min(2 * g + 1, NC - 1)];
+    // results leave as acc * 2^-e of their column
+    const int ye0 = -lds_e[min(2 * g, NC - 1)], ye1 = -lds_e[min(2 * g + 1, NC - 1)];
     const uint8_t *lw_row = lds_w + wave * (kMvTile * RSB + DUMMY) + j * RSB;
     const int arow = g * NR + (j % NR);
     const uint32_t sel = (g == 0) ? 0x05040302u : 0x03020100u;
+    const PairMasks pm;
     float acc0[2] = {0.f, 0.f}, acc1[2] = {0.f, 0.f};
     float2_t pend = {0.f, 0.f};   // the first tile, when it started in an earlier wave
     bool has_pend = false;
@@ -183,16 +177,14 @@ __global__ __launch_bounds__(512) void mat_vec_stream(MvGroup grp, int nb, const
     auto compute_and_store = [&](Item it) {
         const int sb = min(SB, nb - it.st * SB);
         const half8_t *ax = lds_x + (it.st * SB * 2 * 4) * NR + arow;
-        const float4_t *tp = lds_T + (it.st * SB / 2) * 4 + g;
         // first half of the stage, then the second unless the stage is a half one
 #pragma unroll
         for (int pp = 0; pp < SB / 4; ++pp)
-            mv_block_pair_q<NC>(lw_row + 36 * pp, ax + (2 * pp) * 2 * 4 * NR, tp + 4 * pp, g, sel, acc0, acc1);
+            mv_block_pair<NC>(lw_row + 36 * pp, ax + (2 * pp) * 2 * 4 * NR, g, sel, pm, acc0, acc1);
         if (sb == SB) {
 #pragma unroll
             for (int pp = SB / 4; pp < SB / 2; ++pp)
-                mv_block_pair_q<NC>(lw_row + 36 * pp, ax + (2 * pp) * 2 * 4 * NR, tp + 4 * pp, g, sel, acc0,
-                                    acc1);
+                mv_block_pair<NC>(lw_row + 36 * pp, ax + (2 * pp) * 2 * 4 * NR, g, sel, pm, acc0, acc1);
         }
         if (it.st == ns - 1) {
             const float r0 = acc0[0] + acc1[0], r1 = acc0[1] + acc1[1];
@@ -265,14 +257,13 @@ __global__ __launch_bounds__(512) void mat_vec_stream(MvGroup grp, int nb, const
 }
 
 // Dynamic LDS of one workgroup: 8 wave tiles (with their dummy park slots) + the
-// staged activation + the blocks' weight-free sums T.  Its static
+// staged activation.  Its static
 // LDS (column exponents and their reduction, under kMvStreamStaticLds bytes) comes
 // on top.
 size_t mat_vec_stream_lds(int N, int nb) {
     constexpr int nchunk = kMvTile * kMvStreamSB * kBlockBytes / 16;
     constexpr int dummy = (64 - (nchunk - 64 * ((nchunk + 63) / 64 - 1))) * 16;
-    return (size_t)8 * (kMvTile * (kMvStreamSB * kBlockBytes + 16) + dummy) + (size_t)nb * 2 * 4 * 2 * N * 16 +
-           (size_t)nb * 32;
+    return (size_t)8 * (kMvTile * (kMvStreamSB * kBlockBytes + 16) + dummy) + (size_t)nb * 2 * 4 * 2 * N * 16;
 }
 
 template <int NC>

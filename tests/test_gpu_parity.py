@@ -274,6 +274,25 @@ def test_mat_vec_activation_range(M, K, N, first):
                         what="M=%d N=%d mags from %g spread=%s" % (M, N, mags[0], spread))
 
 
+@pytest.mark.parametrize("M,K", [(300, 1024), (16400, 512)])   # K-split kernel, streaming kernel
+@pytest.mark.parametrize("big", [1e4, 1e6])
+def test_mat_vec_outlier_on_zero_weights(M, K, big):
+    """A huge activation whose weights are all zero must not cost the other elements
+    their accuracy: the bound is relative to sum|W x|, which the outlier does not enter."""
+    rng = synth.rng_for(16, M, K, 0)
+    codes = rng.integers(0, 3, size=(M, K), dtype=np.uint8)
+    k0 = 3 * 64 + 17
+    codes[:, k0] = 1
+    d = rng.uniform(0.005, 0.05, size=(M, K // 64)).astype(np.float16)
+    w = synth.pack(codes, d)
+    x = synth.activations(16, M, K, 2, K)
+    x[:, k0] = big
+    x[1, k0 + 5] = -big * 0.5   # a second outlier with live weights in the same block
+    y = run_mat_vec(dev(w), M, K, x)
+    rows = None if M < 1000 else np.arange(0, M, 7)
+    assert_products(y, w, M, K, x, REL_F32, rows=rows, what="outlier %g M=%d" % (big, M))
+
+
 def test_mat_vec_group_activation_range():
     K, N = 512, 3
     mats = [synth.weight(14, i, 0, M, K, "quad", synth.ScaleDist("uniform", 0.005, 0.05))
