@@ -25,7 +25,8 @@ namespace q2_0 {
 constexpr int kMvTile = 16;        // weight rows per MFMA tile
 constexpr int kMvStreamSB = 16;    // blocks per stage in the streaming kernel
 constexpr int kMvMaxGroup = 64;    // matrices per grouped launch (kernel argument size)
-constexpr size_t kMvStreamStaticLds = 4608;  // static LDS bound of the streaming kernel
+constexpr size_t kMvStreamStaticLds = 1024;  // static LDS bound of the streaming kernel
+constexpr int kMvStreamMaxWaves = 16;        // largest streaming workgroup (waves)
 
 struct MvProblem {
     const uint8_t *w;
@@ -248,7 +249,8 @@ __device__ __forceinline__ void mv_block_pair(const uint8_t *lp, const half8_t *
     }
 }
 
-size_t mat_vec_stream_lds(int N, int nb);
+size_t mat_vec_stream_lds(int N, int nb, int waves);
+int mat_vec_stream_waves(int N, int nb, int *resident);
 hipError_t launch_mat_vec_stream(const MvGroup &grp, int nb, const float *x, int64_t ldx, int N,
                                  hipStream_t s);
 

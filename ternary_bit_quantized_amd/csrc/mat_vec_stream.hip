@@ -11,9 +11,9 @@
 //    workgroup owns a contiguous run of tiles and each of its 8 waves a contiguous
 //    eighth of that run's items, so every wave streams the same number of stages
 //    to within one: no tail where a few waves finish a last round alone.
-//  * A wave streams on its own, with no barrier: two stages are in flight in
+//  * A wave streams on its own, with no barrier: one stage is in flight in
 //    registers (coalesced 16-byte loads, consecutive lanes on consecutive bytes of
-//    a row) while a third is decoded.  Weight bytes pass through a wave-private LDS
+//    a row) while the previous one is decoded.  Weight bytes pass through a wave-private LDS
 //    tile only to be regrouped per lane.  Loads are branch-free: rows past the end
 //    of a matrix are clamped to its last row (their outputs are never stored).
 //  * A tile whose stages are split between waves is finished after one barrier at
@@ -51,7 +51,8 @@ struct Item {
 }  // namespace
 
 template <int NC, int SB>
-__global__ __launch_bounds__(512) void mat_vec_stream(MvGroup grp, int nb, const float *__restrict__ x,
+__global__ __launch_bounds__(kMvStreamMaxWaves * 64)
+__attribute__((amdgpu_waves_per_eu(4))) void mat_vec_stream(MvGroup grp, int nb, const float *__restrict__ x,
                                                       int64_t ldx) {
     constexpr int NR = 2 * NC;
     constexpr int RSB = SB * kBlockBytes + 16;
@@ -59,19 +60,19 @@ __global__ __launch_bounds__(512) void mat_vec_stream(MvGroup grp, int nb, const
     constexpr int NCHUNK = kMvTile * CPR;             // chunks of a full stage
     constexpr int CH = (NCHUNK + 63) / 64;            // chunks per lane
     constexpr int LAST_LANES = NCHUNK - 64 * (CH - 1);  // lanes whose last chunk is real
-    constexpr int WAVES = 8;
+    const int WAVES = __builtin_amdgcn_readfirstlane((int)(blockDim.x >> 6));   // 4..16, chosen by the host
     static_assert(RSB % 16 == 0 && SB % 16 == 0, "stage geometry");
 
     constexpr int DUMMY = (64 - LAST_LANES) * 16;     // park slots for the lanes past the tile
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint8_t *lds_w = smem;   // WAVES x (16 x RSB + DUMMY)
-    half8_t *lds_x = reinterpret_cast<half8_t *>(smem + WAVES * (kMvTile * RSB + DUMMY));  // nb x 2 x 4 x NR
+    float2_t *lds_part = reinterpret_cast<float2_t *>(smem + WAVES * (kMvTile * RSB + DUMMY));  // WAVES x 64
+    half8_t *lds_x = reinterpret_cast<half8_t *>(lds_part + WAVES * 64);                     // nb x 2 x 4 x NR
     __shared__ int lds_e[NC];
-    __shared__ float lds_tmp[WAVES * NC];
-    __shared__ float2_t lds_part[WAVES][64];   // a wave's unfinished last tile, per lane
-    __shared__ int lds_part_tile[WAVES];
-    static_assert(sizeof(lds_e) + sizeof(lds_tmp) + sizeof(lds_part) + sizeof(lds_part_tile) <=
-                      kMvStreamStaticLds, "static LDS reserve");
+    __shared__ float lds_tmp[kMvStreamMaxWaves * NC];
+    __shared__ int lds_part_tile[kMvStreamMaxWaves];   // lds_part: a wave's unfinished last tile
+    static_assert(sizeof(lds_e) + sizeof(lds_tmp) + sizeof(lds_part_tile) <= kMvStreamStaticLds,
+                  "static LDS reserve");
 
     const int tid = threadIdx.x;
     // the wave index is uniform: keep it (and all tile bookkeeping) in SGPRs
@@ -151,6 +152,11 @@ __global__ __launch_bounds__(512) void mat_vec_stream(MvGroup grp, int nb, const
             *reinterpret_cast<u32x4_t *>(lds_w + lds_off[q]) = REG[q];                          \
     }
 
+    // The first stage is issued before x is staged, so its latency overlaps the staging;
+    // on entering the loop exactly this stage is in flight, as on every later iteration.
+    u32x4_t reg[CH];
+    if (n_items > 0) Q2_0_ISSUE(first, reg)
+
     column_exponents<NC>(x, ldx, nb * kBlockWeights, lds_e, lds_tmp, tid, WAVES * 64);
     stage_x_all<NC>(x, ldx, nb, lds_e, lds_x, tid, WAVES * 64);
     __syncthreads();
@@ -200,39 +206,24 @@ __global__ __launch_bounds__(512) void mat_vec_stream(MvGroup grp, int nb, const
 
     Item cur = first;
     Item nxt = next_item(cur);
-    u32x4_t regA[CH], regB[CH];
-    if (n_items > 0) {
-        Q2_0_ISSUE(cur, regA)
-        const Item load = n_items > 1 ? nxt : cur;
-        Q2_0_ISSUE(load, regB)
-    }
 
-    // Two register buffers alternate: park A, refill A two items ahead, compute; then B.
-    // (Written out rather than as a lambda over a register-array reference, which the
-    // compiler would otherwise keep in scratch.)  k counts the items done.
-#define Q2_0_HALF_STEP(REG)                                                        \
-    {                                                                              \
-        Q2_0_PARK(REG)                                                             \
-        __builtin_amdgcn_wave_barrier();                                           \
-        const Item ahead = next_item(nxt);                                         \
-        const Item load = (k + 2 < n_items) ? ahead : cur;                         \
-        Q2_0_ISSUE(load, REG)                                                      \
-        compute_and_store(cur);                                                    \
-        __builtin_amdgcn_wave_barrier();                                           \
-        if (k + 1 < n_items && nxt.tile != cur.tile) tr_out = tile_ref(grp, nxt.tile); \
-        cur = nxt;                                                                 \
-        nxt = ahead;                                                               \
-        ++k;                                                                       \
+    // One stage in flight: park the stage that arrived, issue the next one into the
+    // same registers, then decode the parked stage -- its decode takes several times
+    // the memory latency, and the registers saved buy a fifth wave per SIMD.  A plain
+    // counted loop with no exit in the middle, which keeps the compiler's wait counts
+    // exact.  (The step is written out rather than as a lambda over a register-array
+    // reference, which the compiler would otherwise keep in scratch.)
+    for (int k = 0; k < n_items; ++k) {
+        Q2_0_PARK(reg)
+        __builtin_amdgcn_wave_barrier();
+        const Item load = (k + 1 < n_items) ? nxt : cur;
+        Q2_0_ISSUE(load, reg)
+        compute_and_store(cur);
+        __builtin_amdgcn_wave_barrier();
+        if (k + 1 < n_items && nxt.tile != cur.tile) tr_out = tile_ref(grp, nxt.tile);
+        cur = nxt;
+        nxt = next_item(nxt);
     }
-    // A plain counted loop with no exit in the middle, which keeps the compiler's
-    // wait counts exact.
-    int k = 0;
-    while (k + 2 <= n_items) {
-        Q2_0_HALF_STEP(regA)
-        Q2_0_HALF_STEP(regB)
-    }
-    if (k < n_items) Q2_0_HALF_STEP(regA)
-#undef Q2_0_HALF_STEP
 #undef Q2_0_PARK
 #undef Q2_0_ISSUE
 #undef Q2_0_SET_LOAD_TILE
@@ -240,14 +231,14 @@ __global__ __launch_bounds__(512) void mat_vec_stream(MvGroup grp, int nb, const
     // An unfinished last tile leaves its partial sums for the wave that holds the
     // tile's last stage; that wave adds the earlier waves' partials in order.
     const bool open_end = n_items > 0 && ((int)((i1 - 1) % ns) != ns - 1);
-    if (open_end) lds_part[wave][lane] = float2_t{acc0[0] + acc1[0], acc0[1] + acc1[1]};
+    if (open_end) lds_part[wave * 64 + lane] = float2_t{acc0[0] + acc1[0], acc0[1] + acc1[1]};
     if (lane == 0) lds_part_tile[wave] = open_end ? (tb0 + (int)((i1 - 1) / ns)) : -1;
     __syncthreads();
     if (has_pend) {
         float r0 = 0.f, r1 = 0.f;
         for (int w = 0; w < wave; ++w) {
             if (lds_part_tile[w] == first.tile) {
-                const float2_t p = lds_part[w][lane];
+                const float2_t p = lds_part[w * 64 + lane];
                 r0 += p.x;
                 r1 += p.y;
             }
@@ -256,21 +247,40 @@ __global__ __launch_bounds__(512) void mat_vec_stream(MvGroup grp, int nb, const
     }
 }
 
-// Dynamic LDS of one workgroup: 8 wave tiles (with their dummy park slots) + the
-// staged activation.  Its static
-// LDS (column exponents and their reduction, under kMvStreamStaticLds bytes) comes
-// on top.
-size_t mat_vec_stream_lds(int N, int nb) {
+// Dynamic LDS of one workgroup of `waves` waves: the wave tiles (with their dummy
+// park slots), the waves' partial-tile slots and the staged activation.  Its static
+// LDS (column exponents, their reduction, the partial-tile ids; under
+// kMvStreamStaticLds bytes) comes on top.
+size_t mat_vec_stream_lds(int N, int nb, int waves) {
     constexpr int nchunk = kMvTile * kMvStreamSB * kBlockBytes / 16;
     constexpr int dummy = (64 - (nchunk - 64 * ((nchunk + 63) / 64 - 1))) * 16;
-    return (size_t)8 * (kMvTile * (kMvStreamSB * kBlockBytes + 16) + dummy) + (size_t)nb * 2 * 4 * 2 * N * 16;
+    return (size_t)waves * (kMvTile * (kMvStreamSB * kBlockBytes + 16) + dummy + 64 * 8) +
+           (size_t)nb * 2 * 4 * 2 * N * 16;
+}
+
+// Workgroup size: the wave count (4..16) that keeps the most waves resident per CU,
+// given the LDS each workgroup needs (the staged activation is per workgroup) and
+// the waves per SIMD the kernel's registers allow; ties go to fewer, larger groups.
+// 0 if even 4 waves do not fit; *resident (optional) receives the waves per CU.
+int mat_vec_stream_waves(int N, int nb, int *resident) {
+    const int per_simd = 4;   // the kernel's registers allow four waves per SIMD
+    int best = 0, best_res = 0;
+    for (int w = kMvStreamMaxWaves; w >= 4; --w) {
+        const size_t lds = mat_vec_stream_lds(N, nb, w) + kMvStreamStaticLds;
+        if (lds > 160 * 1024) continue;
+        int wgs = (int)((160 * 1024) / lds);
+        while (wgs > 0 && wgs * w > 4 * per_simd) --wgs;
+        if (wgs * w > best_res) { best_res = wgs * w; best = w; }
+    }
+    if (resident) *resident = best_res;
+    return best;
 }
 
 template <int NC>
 static hipError_t launch_stream_nc(const MvGroup &grp, int nb, const float *x, int64_t ldx,
-                                   hipStream_t s, int grid) {
+                                   hipStream_t s, int grid, int waves) {
     constexpr int SB = kMvStreamSB;
-    const size_t lds = mat_vec_stream_lds(NC, nb);
+    const size_t lds = mat_vec_stream_lds(NC, nb, waves);
     auto kern = mat_vec_stream<NC, SB>;
     // Raise the dynamic-LDS cap once per device (idempotent, so a race is harmless).
     static bool configured[64] = {};
@@ -287,29 +297,34 @@ static hipError_t launch_stream_nc(const MvGroup &grp, int nb, const float *x, i
         if (e != hipSuccess) return e;
         if (dev >= 0 && dev < 64) configured[dev] = true;
     }
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(512), lds, s, grp, nb, x, ldx);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * waves), lds, s, grp, nb, x, ldx);
     return hipGetLastError();
 }
 
 hipError_t launch_mat_vec_stream(const MvGroup &grp, int nb, const float *x, int64_t ldx, int N,
                                  hipStream_t s) {
-    const size_t lds = mat_vec_stream_lds(N, nb) + kMvStreamStaticLds;
+    int waves = mat_vec_stream_waves(N, nb, nullptr);
+    if (waves == 0) return hipErrorInvalidValue;
+    // Small launches: fewer waves per workgroup until there is a workgroup per CU.
+    const int64_t ns = (nb + kMvStreamSB - 1) / kMvStreamSB;
+    const int64_t items = (int64_t)grp.total_tiles * ns;
+    while (waves > 4 && (items + waves - 1) / waves < 256) waves = (waves + 1) / 2 < 4 ? 4 : (waves + 1) / 2;
+    const size_t lds = mat_vec_stream_lds(N, nb, waves) + kMvStreamStaticLds;
     const int per_cu = (int)((160 * 1024) / lds);
     const int max_grid = 256 * (per_cu < 1 ? 1 : per_cu);
     // every wave gets at least about one stage; never more workgroups than tiles
-    const int64_t ns = (nb + kMvStreamSB - 1) / kMvStreamSB;
-    int64_t need = ((int64_t)grp.total_tiles * ns + 7) / 8;
+    int64_t need = (items + waves - 1) / waves;
     if (need > grp.total_tiles) need = grp.total_tiles;
     const int grid = (int)(need < max_grid ? need : max_grid);
     switch (N) {
-        case 1: return launch_stream_nc<1>(grp, nb, x, ldx, s, grid);
-        case 2: return launch_stream_nc<2>(grp, nb, x, ldx, s, grid);
-        case 3: return launch_stream_nc<3>(grp, nb, x, ldx, s, grid);
-        case 4: return launch_stream_nc<4>(grp, nb, x, ldx, s, grid);
-        case 5: return launch_stream_nc<5>(grp, nb, x, ldx, s, grid);
-        case 6: return launch_stream_nc<6>(grp, nb, x, ldx, s, grid);
-        case 7: return launch_stream_nc<7>(grp, nb, x, ldx, s, grid);
-        case 8: return launch_stream_nc<8>(grp, nb, x, ldx, s, grid);
+        case 1: return launch_stream_nc<1>(grp, nb, x, ldx, s, grid, waves);
+        case 2: return launch_stream_nc<2>(grp, nb, x, ldx, s, grid, waves);
+        case 3: return launch_stream_nc<3>(grp, nb, x, ldx, s, grid, waves);
+        case 4: return launch_stream_nc<4>(grp, nb, x, ldx, s, grid, waves);
+        case 5: return launch_stream_nc<5>(grp, nb, x, ldx, s, grid, waves);
+        case 6: return launch_stream_nc<6>(grp, nb, x, ldx, s, grid, waves);
+        case 7: return launch_stream_nc<7>(grp, nb, x, ldx, s, grid, waves);
+        case 8: return launch_stream_nc<8>(grp, nb, x, ldx, s, grid, waves);
         default: return hipErrorInvalidValue;
     }
 }

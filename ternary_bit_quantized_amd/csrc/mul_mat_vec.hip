@@ -82,7 +82,12 @@ static void launch_generic_nc(const uint8_t *w, int64_t M, int nb, const float *
 // the generic kernel.
 constexpr int64_t kStreamTiles = 1024;
 
-static bool stream_fits(int N, int nb) { return mat_vec_stream_lds(N, nb) + kMvStreamStaticLds <= 160 * 1024; }
+// The streaming kernel needs the whole activation staged per workgroup; where that
+// leaves fewer than 8 resident waves per CU the K-split kernel is used instead.
+static bool stream_fits(int N, int nb) {
+    int resident = 0;
+    return mat_vec_stream_waves(N, nb, &resident) > 0 && resident >= 8;
+}
 
 hipError_t launch_mat_vec(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx, int N,
                           float *y, int64_t ldy, hipStream_t s) {
