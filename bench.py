@@ -7,7 +7,8 @@ q/o 4096x4096, k/v 1024x4096, gate/up 12288x4096 and down 4096x12288 Q2_0 matric
 
 One step is one pass of the whole hot path:
   prefill: get_rows of 512 token ids, then the 252 stack matrices at N = 512 on the
-           fp16-MFMA GEMM;
+           fp16-MFMA GEMM, per layer as the model runs them: q/k/v as one group call
+           (they share the input), o, gate/up as one group call, down;
   decode : get_rows of 1 token id, then the 252 stack matrices and the LM head at
            N = 1 on the mat-vec (one token, weights streamed from HBM).  The stack's
            matrices use one activation per distinct K, so they are launched grouped by
@@ -169,16 +170,36 @@ def main():
     def run_decode_matvecs():
         run_groups(act_groups)
 
-    ws_bytes = max(B.mul_mat_workspace_bytes(M, K, PREFILL_N, B.Q2_0_PREC_F16_MFMA)
-                   for (M, K) in wl.shapes.values())
+    # prefill: one output buffer per matrix name (grouped items never share a y); the
+    # layer's matrices that share x run as one group: q/k/v, o, gate/up, down
+    yPn = {n: torch.empty((PREFILL_N, wl.shapes[n][0]), dtype=torch.float32, device=dev) for n in synth.MATS}
+    prefill_names = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+
+    def prefill_items(l, names):
+        return B.make_items([(W[(l, n)].data_ptr(), wl.shapes[n][0], yPn[n].data_ptr(), wl.shapes[n][0])
+                             for n in names])
+
+    prefill_groups = [(prefill_items(l, names), len(names), wl.shapes[names[0]][1])
+                      for l in layers for names in prefill_names]
+    ws_bytes = max(max(B.mul_mat_group_workspace_bytes(items, n, K, PREFILL_N, B.Q2_0_PREC_F16_MFMA)
+                       for (items, n, K) in prefill_groups),
+                   max(B.mul_mat_workspace_bytes(M, K, PREFILL_N, B.Q2_0_PREC_F16_MFMA)
+                       for (M, K) in wl.shapes.values()))
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
 
-    def run_prefill_gemms(precision=B.Q2_0_PREC_F16_MFMA, layer_keys=None):
+    def run_prefill_gemms(precision=B.Q2_0_PREC_F16_MFMA, groups=None):
         st = s()
-        for key in (layer_keys or order):
+        for items, n, K in (groups or prefill_groups):
+            check(B.mul_mat_group_raw(items, n, K, xP[K].data_ptr(), K, PREFILL_N, precision,
+                                      ws.data_ptr(), ws_bytes, st), "mul_mat_group")
+
+    def run_prefill_per_matrix():
+        st = s()
+        for key in order:
             M, K = wl.shapes[key[1]]
             check(B.mul_mat_raw(W[key].data_ptr(), M, K, xP[K].data_ptr(), K, PREFILL_N,
-                                yP[M].data_ptr(), M, precision, ws.data_ptr(), ws_bytes, st), "mul_mat")
+                                yPn[key[1]].data_ptr(), M, B.Q2_0_PREC_F16_MFMA, ws.data_ptr(), ws_bytes, st),
+                  "mul_mat")
 
     # ---- capture the four parts as graphs
     parts = {
@@ -188,7 +209,8 @@ def main():
         "decode_mat_vec": run_decode_matvecs,
         "decode_mat_vec_per_layer": lambda: run_groups(layer_groups),
         "decode_mat_vec_per_matrix": run_decode_per_matrix,
-        "prefill_gemm_f32_layer0": lambda: run_prefill_gemms(B.Q2_0_PREC_F32, layer_keys=order[:7]),
+        "prefill_gemm_per_matrix": run_prefill_per_matrix,
+        "prefill_gemm_f32_layer0": lambda: run_prefill_gemms(B.Q2_0_PREC_F32, groups=prefill_groups[:4]),
     }
     if args.parts:
         keep = args.parts.split(",")
@@ -225,7 +247,7 @@ def main():
     step_parts = [p for p in ("prefill_get_rows", "prefill_gemm", "decode_get_rows", "decode_mat_vec")
                   if p in graphs]
     compare_parts = [p for p in ("decode_mat_vec_per_layer", "decode_mat_vec_per_matrix",
-                                 "prefill_gemm_f32_layer0") if p in graphs]
+                                 "prefill_gemm_per_matrix", "prefill_gemm_f32_layer0") if p in graphs]
     ev = {n: [] for n in parts}
 
     def replay(names, record):
@@ -310,6 +332,11 @@ def main():
         "decode_tokens_per_s_per_layer_schedule": round(
             1.0 / ((ms["decode_mat_vec_per_layer"] + ms["decode_get_rows"]) * 1e-3), 1),
         "f32_fallback_gemm_tflops_layer0": round(f32_flops / (ms["prefill_gemm_f32_layer0"] * 1e-3) / 1e12, 2),
+        "prefill_schedules_TFLOPs": {
+            "per_layer_groups (%d group calls, the step)" % len(prefill_groups): round(gemm_tflops, 1),
+            "per_matrix (%d calls)" % len(order):
+                round(pre_flops / (ms["prefill_gemm_per_matrix"] * 1e-3) / 1e12, 1),
+        },
         "roofline": {
             "kernel": "mat_vec_stream (N=1; %d grouped launches per decode token)" % n_dec_launches,
             "bound": "hbm", "achieved": round(matvec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -318,7 +345,7 @@ def main():
             "avg_launch_us": round(ms["decode_mat_vec"] * 1e3 / n_dec_launches, 3),
         },
         "roofline_gemm": {
-            "kernel": "gemm_f16_mfma (N=512; 252 GEMMs per prefill, each an fp16 x conversion + GEMM (+ split-K reduce))",
+            "kernel": "gemm_f16_mfma (N=512; 144 group calls per prefill, each an fp16 x conversion + one GEMM launch)",
             "bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": F16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(gemm_tflops / F16_MFMA_PEAK_TFLOPS, 4),
             "traffic": None, "algorithmic_bytes": int(pre_bytes),

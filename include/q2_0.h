@@ -134,8 +134,8 @@ int q2_0_mul_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items, int6
  *   workspace / ws_bytes: device scratch the caller provides, 16-byte aligned, at
  *   least q2_0_mul_mat_workspace_bytes(M, K, N, precision) bytes: for
  *   Q2_0_PREC_F16_MFMA with N > 8, x as fp16 (N*K*2) and N column exponents, plus,
- *   when the output tile grid is too small to fill the GPU, f32 partial sums of a K
- *   split (splits*N*M*4, split count <= 8, added in a fixed order); otherwise 0
+ *   when the output tile grid is too small to fill the GPU, the f32 partial sums of a
+ *   K split (splits*N*M*4, split count <= 8, added in a fixed order); otherwise 0
  *   (then workspace may be NULL).
  *   Its contents are overwritten; it must not overlap w, x or y.
  */
@@ -145,6 +145,32 @@ int q2_0_mul_mat(const void *w, int64_t M, int64_t K, const float *x, int64_t ld
 
 /* Workspace bytes q2_0_mul_mat needs for these sizes (0 when none, and for invalid sizes). */
 size_t q2_0_mul_mat_workspace_bytes(int64_t M, int64_t K, int64_t N, int precision);
+
+/*
+ * mul_mat_group: several q2_0_mul_mat products that share K and the activation x,
+ * y_i = W_i x (a prefill layer's q, k and v projections, or gate and up).  Same
+ * arithmetic, accuracy, layouts and routing as q2_0_mul_mat for each item; with
+ * Q2_0_PREC_F16_MFMA and N > 8, x is converted to fp16 once for all items and their
+ * tiles run in shared launches (up to 16 matrices each), so small matrices fill the
+ * GPU together.  Each y_i does not depend on the other items or on the grouping.
+ *   items  : HOST array of n_items descriptors {w, M, y, ldy} (q2_0_mat_vec_item);
+ *            read during the call only.  M = 0 items are skipped.
+ *   x, ldx, N, precision, stream: as for q2_0_mul_mat.
+ *   workspace / ws_bytes: at least q2_0_mul_mat_group_workspace_bytes() bytes,
+ *            16-byte aligned: x as fp16 and its column exponents once, plus, when the
+ *            group's tile grid is too small to fill the GPU, every item's split-K
+ *            partial sums.  Overwritten; must not overlap w, x or y.
+ * The y_i must not overlap each other or x.  Errors are those of q2_0_mul_mat,
+ * checked for every item before anything is launched (NULL also for items == NULL
+ * with n_items > 0; n_items < 0 is SHAPE).
+ */
+int q2_0_mul_mat_group(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, const float *x,
+                       int64_t ldx, int64_t N, int precision, void *workspace, size_t ws_bytes,
+                       void *stream);
+
+/* Workspace bytes q2_0_mul_mat_group needs (0 when none, and for invalid arguments). */
+size_t q2_0_mul_mat_group_workspace_bytes(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K,
+                                          int64_t N, int precision);
 
 /* A static, human-readable name for a status code. */
 const char *q2_0_status_string(int status);

@@ -21,6 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libq2_0.so")
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
+COMPILE_TIMEOUT_S = 600
 # Packed-FP32 VALU forms are switched off for all device code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -36,7 +37,8 @@ PER_FILE = {"mat_vec_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [HIPCC, *FLAGS, *PER_FILE.get(os.path.basename(src), []), "-c", src, "-o", obj]
-    r = subprocess.run(cmd, capture_output=True, text=True)
+    # a compile that runs away (the scheduler on some inputs) fails instead of hanging
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=COMPILE_TIMEOUT_S)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
     return obj
@@ -49,7 +51,7 @@ def build(verbose: bool = False) -> str:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=COMPILE_TIMEOUT_S)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
     os.replace(tmp, LIB)

@@ -98,7 +98,7 @@ int q2_0_mul_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items, int6
 size_t q2_0_mul_mat_workspace_bytes(int64_t M, int64_t K, int64_t N, int precision) {
     if (check_shape(M, K, N) || N > kMaxGemmN) return 0;
     if (precision != Q2_0_PREC_F16_MFMA || N <= Q2_0_MAT_VEC_MAX_N) return 0;
-    return q2_0::gemm_f16_workspace_bytes(M, K, N);   // x as fp16 (+ split-K partials)
+    return q2_0::gemm_f16_workspace_bytes(&M, 1, K, N);   // x as fp16 (+ split-K state)
 }
 
 int q2_0_mul_mat(const void *w, int64_t M, int64_t K, const float *x, int64_t ldx, int64_t N,
@@ -107,6 +107,7 @@ int q2_0_mul_mat(const void *w, int64_t M, int64_t K, const float *x, int64_t ld
     int st = check_shape(M, K, N);
     if (st) return st;
     if (N > kMaxGemmN) return Q2_0_ERR_SHAPE;
+    if (((M + 127) / 128) * ((N + 127) / 128) * 8 > kMaxRows) return Q2_0_ERR_SHAPE;   // launch grid
     if (M == 0 || N == 0) return Q2_0_OK;
     st = check_product(w, M, K, x, ldx, y, ldy);
     if (st) return st;
@@ -118,9 +119,74 @@ int q2_0_mul_mat(const void *w, int64_t M, int64_t K, const float *x, int64_t ld
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (N <= Q2_0_MAT_VEC_MAX_N)
         return hip_status(q2_0::launch_mat_vec(wb, M, nb, x, ldx, (int)N, y, ldy, s));
-    if (precision == Q2_0_PREC_F16_MFMA)
-        return hip_status(q2_0::launch_gemm_f16_v2(wb, M, nb, x, ldx, N, y, ldy, workspace, s));
+    if (precision == Q2_0_PREC_F16_MFMA) {
+        const q2_0::GemmMat m{wb, M, y, ldy};
+        return hip_status(q2_0::launch_gemm_f16_group(&m, 1, nb, x, ldx, N, workspace, s));
+    }
     return hip_status(q2_0::launch_gemm_f32(wb, M, nb, x, ldx, N, y, ldy, s));
+}
+
+size_t q2_0_mul_mat_group_workspace_bytes(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K,
+                                          int64_t N, int precision) {
+    if (check_shape(0, K, N) || N > kMaxGemmN || n_items < 0 || (n_items > 0 && !items)) return 0;
+    if (precision != Q2_0_PREC_F16_MFMA || N <= Q2_0_MAT_VEC_MAX_N || n_items == 0) return 0;
+    int64_t local[64];
+    int64_t *Ms = n_items <= 64 ? local : new int64_t[n_items];
+    bool ok = true;
+    for (int64_t i = 0; i < n_items; ++i) {
+        if (check_shape(items[i].M, K, N)) ok = false;
+        Ms[i] = items[i].M;
+    }
+    const size_t r = ok ? q2_0::gemm_f16_workspace_bytes(Ms, n_items, K, N) : 0;
+    if (Ms != local) delete[] Ms;
+    return r;
+}
+
+int q2_0_mul_mat_group(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, const float *x,
+                       int64_t ldx, int64_t N, int precision, void *workspace, size_t ws_bytes, void *stream) {
+    int st = check_shape(0, K, N);
+    if (st) return st;
+    if (N > kMaxGemmN || n_items < 0) return Q2_0_ERR_SHAPE;
+    if (n_items == 0 || N == 0) return Q2_0_OK;
+    if (!items) return Q2_0_ERR_NULL;
+    int64_t row_tiles = 0;
+    for (int64_t i = 0; i < n_items; ++i) {
+        st = check_shape(items[i].M, K, N);
+        if (st) return st;
+        row_tiles += (items[i].M + 127) / 128;
+    }
+    if (row_tiles * ((N + 127) / 128) * 8 > kMaxRows) return Q2_0_ERR_SHAPE;   // launch grid
+    bool any = false;
+    for (int64_t i = 0; i < n_items; ++i) {
+        if (items[i].M == 0) continue;
+        any = true;
+        st = check_product(items[i].w, items[i].M, K, x, ldx, items[i].y, items[i].ldy);
+        if (st) return st;
+    }
+    if (!any) return Q2_0_OK;
+    if (precision != Q2_0_PREC_F16_MFMA && precision != Q2_0_PREC_F32) return Q2_0_ERR_UNSUPPORTED;
+    const size_t need = q2_0_mul_mat_group_workspace_bytes(items, n_items, K, N, precision);
+    if (ws_bytes < need || (need && (!workspace || !aligned(workspace, 16)))) return Q2_0_ERR_WORKSPACE;
+    const int nb = (int)(K / Q2_0_BLOCK_WEIGHTS);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (N <= Q2_0_MAT_VEC_MAX_N)
+        return hip_status(q2_0::launch_mat_vec_group(items, n_items, nb, x, ldx, (int)N, s));
+    if (precision == Q2_0_PREC_F32) {
+        for (int64_t i = 0; i < n_items; ++i) {
+            if (items[i].M == 0) continue;
+            st = hip_status(q2_0::launch_gemm_f32(static_cast<const uint8_t *>(items[i].w), items[i].M, nb, x, ldx,
+                                                  N, items[i].y, items[i].ldy, s));
+            if (st) return st;
+        }
+        return Q2_0_OK;
+    }
+    q2_0::GemmMat local[64];
+    q2_0::GemmMat *mats = n_items <= 64 ? local : new q2_0::GemmMat[n_items];
+    for (int64_t i = 0; i < n_items; ++i)
+        mats[i] = q2_0::GemmMat{static_cast<const uint8_t *>(items[i].w), items[i].M, items[i].y, items[i].ldy};
+    st = hip_status(q2_0::launch_gemm_f16_group(mats, n_items, nb, x, ldx, N, workspace, s));
+    if (mats != local) delete[] mats;
+    return st;
 }
 
 const char *q2_0_status_string(int status) {

@@ -20,6 +20,16 @@
 //  * Tiles are ordered so that all workgroups on one XCD (dispatch is round-robin
 //    over the 8 XCDs) share one 128-column slice of x, which then stays in that
 //    XCD's L2.
+//  * A launch may cover several matrices that share K and x (q/k/v, gate/up): their
+//    row tiles are numbered across the group and x is converted once for all.
+//  * When the tile grid is too small to fill the chip, K is split (at most 8 ways);
+//    every split writes its partial tile to the workspace and a reduction kernel adds
+//    them in split order (deterministic).  Finishing the tile in the last split to
+//    arrive would save that launch, but the partials cross XCDs whose L2 caches are
+//    not coherent: device-scope stores bypass the write-back L2 and L2 flushes stall
+//    every workgroup, and both measured several times slower than the extra launch.
+#include <climits>
+
 #include "q2_0_internal.h"
 #include "mat_vec_common.h"
 
@@ -34,7 +44,35 @@ constexpr int GLD = GK + 8;   // fp16 row stride in LDS (144 B): 8 consecutive r
 // per column.  The column is scaled by 2^e (e = xe[n]) so that its max |x| lands in
 // [2^14, 2^15): fp16 then neither overflows (|x| > 65504) nor falls into its
 // subnormal range, where the relative error would exceed 2^-11.  The GEMM multiplies
-// the column's results by 2^-e.
+// the column's results by 2^-e.  Up to kPreGroups 16-value groups per thread are held
+// in registers between the max and the conversion (x is read once); longer columns
+// are read twice.
+constexpr int kPreGroups = 4;
+
+__device__ __forceinline__ void load16(const float *src, bool vec, float v[16]) {
+    if (vec) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4_t t = reinterpret_cast<const float4_t *>(src)[q];
+            v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) v[q] = src[q];
+    }
+}
+
+__device__ __forceinline__ void store16_perm(const float v[16], int e, _Float16 *dst16) {
+    uint32_t o[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+        o[s] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)__builtin_amdgcn_ldexpf(v[s], e),
+                                                    (_Float16)__builtin_amdgcn_ldexpf(v[s + 8], e)});
+    u32x4_t *dst = reinterpret_cast<u32x4_t *>(dst16);
+    dst[0] = u32x4_t{o[0], o[1], o[2], o[3]};
+    dst[1] = u32x4_t{o[4], o[5], o[6], o[7]};
+}
+
 template <bool kVec>
 __global__ __launch_bounds__(256) void x_to_f16_perm(const float *__restrict__ x, int64_t ldx, int K,
                                                      _Float16 *__restrict__ x16, int *__restrict__ xe) {
@@ -43,15 +81,25 @@ __global__ __launch_bounds__(256) void x_to_f16_perm(const float *__restrict__ x
     const int64_t n = blockIdx.x;
     const float *col = x + n * ldx;
     const int groups = K / 16;
+    const bool resident = groups <= kPreGroups * 256;
+    float v[kPreGroups][16];
     float m = 0.f;
-    for (int gi = tid; gi < groups; gi += 256) {
-        const float *src = col + 16 * gi;
-        if (kVec) {
+    if (resident) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) m = fmaxf(m, max_abs4(reinterpret_cast<const float4_t *>(src)[q]));
-        } else {
+        for (int u = 0; u < kPreGroups; ++u) {
+            const int gi = tid + 256 * u;
+            if (gi < groups) {
+                load16(col + 16 * gi, kVec, v[u]);
 #pragma unroll
-            for (int q = 0; q < 16; ++q) m = fmaxf(m, fabsf(src[q]));
+                for (int q = 0; q < 16; ++q) m = fmaxf(m, fabsf(v[u][q]));
+            }
+        }
+    } else {
+        for (int gi = tid; gi < groups; gi += 256) {
+            float t[16];
+            load16(col + 16 * gi, kVec, t);
+#pragma unroll
+            for (int q = 0; q < 16; ++q) m = fmaxf(m, fabsf(t[q]));
         }
     }
 #pragma unroll
@@ -60,27 +108,18 @@ __global__ __launch_bounds__(256) void x_to_f16_perm(const float *__restrict__ x
     __syncthreads();
     const int e = column_exponent(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
     if (tid == 0) xe[n] = e;
-    for (int gi = tid; gi < groups; gi += 256) {
-        const float *src = col + 16 * gi;
-        float v[16];
-        if (kVec) {
+    if (resident) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4_t t = reinterpret_cast<const float4_t *>(src)[q];
-                v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
-            }
-        } else {
-#pragma unroll
-            for (int q = 0; q < 16; ++q) v[q] = src[q];
+        for (int u = 0; u < kPreGroups; ++u) {
+            const int gi = tid + 256 * u;
+            if (gi < groups) store16_perm(v[u], e, x16 + n * K + 16 * gi);
         }
-        uint32_t o[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-            o[s] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)__builtin_amdgcn_ldexpf(v[s], e),
-                                                        (_Float16)__builtin_amdgcn_ldexpf(v[s + 8], e)});
-        u32x4_t *dst = reinterpret_cast<u32x4_t *>(x16 + n * K + 16 * gi);
-        dst[0] = u32x4_t{o[0], o[1], o[2], o[3]};
-        dst[1] = u32x4_t{o[4], o[5], o[6], o[7]};
+    } else {
+        for (int gi = tid; gi < groups; gi += 256) {
+            float t[16];
+            load16(col + 16 * gi, kVec, t);
+            store16_perm(t, e, x16 + n * K + 16 * gi);
+        }
     }
 }
 
@@ -106,14 +145,23 @@ struct WRegs {
 
 }  // namespace
 
+// One launch's matrices (see GemmGroup in q2_0_internal.h): row tiles are numbered
+// across the whole call; tm0 repeats the items' first row tiles contiguously (entries
+// past n hold INT_MAX) for a binary-search lookup.
+__device__ __forceinline__ int find_gemm_item(const GemmGroup &grp, int tmg) {
+    int idx = 0;
+#pragma unroll
+    for (int step = kGemmMaxGroup / 2; step >= 1; step >>= 1)
+        if (grp.tm0[idx + step] <= tmg) idx += step;
+    return idx;
+}
+
 // splits > 1: workgroup (tile, split) covers blocks [split*nbs, (split+1)*nbs) and writes
-// its partial sum to part + split*N*M (column n at n*M); the reduce kernel adds them.
-__global__ __launch_bounds__(256, 2) void gemm_f16_mfma(const uint8_t *__restrict__ w, int M, int nb,
-                                                        const _Float16 *__restrict__ x16,
-                                                        const int *__restrict__ xe, int N,
-                                                        float *__restrict__ y, int64_t ldy,
-                                                        int tiles_m, int tiles_n, int xcd_map,
-                                                        int splits, float *__restrict__ part) {
+// its partial tile to the item's part + split*N*M (column n at n*M); gemm_split_reduce
+// then adds the partials in split order.
+__global__ __launch_bounds__(256, 2) void gemm_f16_mfma(GemmGroup grp, int nb, const _Float16 *__restrict__ x16,
+                                                        const int *__restrict__ xe, int N, int tiles_n,
+                                                        int xcd_map, int splits) {
     __shared__ __attribute__((aligned(16))) _Float16 As[2][GM * GLD];
     __shared__ __attribute__((aligned(16))) _Float16 Bs[2][GN * GLD];
 
@@ -121,9 +169,9 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_mfma(const uint8_t *__restric
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;   // 64 x 64 sub-tile of this wave
 
-    // ---- tile of this workgroup.  xcd_map: XCD j = blockIdx % 8 handles column tile
-    // j % tiles_n and every (8 / tiles_n)-th row tile.
-    int tm, tn;
+    // ---- tile of this workgroup (row tile tmg counted across the call).  xcd_map: XCD
+    // j = blockIdx % 8 handles column tile j % tiles_n and every (8 / tiles_n)-th row tile.
+    int tl, tn;
     const int split = blockIdx.x % splits;
     {
         const int b = blockIdx.x / splits;
@@ -131,12 +179,17 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_mfma(const uint8_t *__restric
             const int j = b & 7, l = b >> 3;
             const int per = 8 / tiles_n;     // XCDs per column tile
             tn = j % tiles_n;
-            tm = l * per + j / tiles_n;
+            tl = l * per + j / tiles_n;
         } else {
             tn = b % tiles_n;
-            tm = b / tiles_n;
+            tl = b / tiles_n;
         }
     }
+    const int tmg = grp.tm_base + tl;
+    const GemmItem &item = grp.p[find_gemm_item(grp, tmg)];
+    const uint8_t *__restrict__ w = item.w;
+    const int M = item.M;
+    const int tm = tmg - item.tm0;
     const int m0 = tm * GM, n0 = tn * GN;
     const int K = nb * kBlockWeights;
     const int64_t rowbytes = (int64_t)nb * kBlockBytes;
@@ -240,11 +293,13 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_mfma(const uint8_t *__restric
     // odd last step runs after it.
     int s = 0;
     for (; s + 1 < nbs; s += 2) {
+        __builtin_amdgcn_iglp_opt(0);    // let the scheduler interleave MFMA with the step's other work
         mma_stage(0);
         store_stage(1, wB, xB);          // step s+1
         load_w(s + 3, wB);
         load_x(s + 3, xB);
         __syncthreads();
+        __builtin_amdgcn_iglp_opt(0);
         mma_stage(1);
         store_stage(0, wA, xA);          // step s+2 (a clamped duplicate past the end)
         load_w(s + 4, wA);
@@ -254,89 +309,169 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_mfma(const uint8_t *__restric
     if (s < nbs) mma_stage(0);
 
     // ---- epilogue: D lane l, register v -> row 8*(v/4) + 4*(l/32) + v%4, column l%32
+    // Results are scaled back by the column's 2^-e first (exact), so partials and y
+    // hold the same numbers.
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int n = n0 + wn * 64 + jj * 32 + (lane & 31);
+            const int ye = -xe[n < N ? n : 0];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][jj][v] = __builtin_amdgcn_ldexpf(acc[i][jj][v], ye);
+        }
+    // Stores of a 4-row run of column n at row m: float4 when in range and aligned.
+    auto store4 = [&](float *col, int m, const float4_t &val) {
+        if (m + 3 < M && ((((uintptr_t)(col + m)) & 15) == 0)) {
+            *reinterpret_cast<float4_t *>(col + m) = val;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (m + e < M) col[m + e] = val[e];
+        }
+    };
+    // With a K split the tile goes to this split's partial (summed by gemm_split_reduce).
+    float *const yout = (splits > 1) ? item.part + (int64_t)split * N * M : item.y;
+    const int64_t ldo = (splits > 1) ? M : item.ldy;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
             const int n = n0 + wn * 64 + jj * 32 + (lane & 31);
             if (n >= N) continue;
-            float *yc = (splits > 1) ? part + ((int64_t)split * N + n) * M : y + (int64_t)n * ldy;
-            const int ye = -xe[n];   // undo the column's staging scale
+            float *yc = yout + (int64_t)n * ldo;
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) {
                 const int m = m0 + wm * 64 + i * 32 + 8 * v4 + 4 * (lane >> 5);
-                float4_t val;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) val[e] = __builtin_amdgcn_ldexpf(acc[i][jj][4 * v4 + e], ye);
-                if (m + 3 < M && ((((uintptr_t)(yc + m)) & 15) == 0)) {
-                    *reinterpret_cast<float4_t *>(yc + m) = val;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (m + e < M) yc[m + e] = val[e];
-                }
+                store4(yc, m, float4_t{acc[i][jj][4 * v4], acc[i][jj][4 * v4 + 1], acc[i][jj][4 * v4 + 2],
+                                       acc[i][jj][4 * v4 + 3]});
             }
         }
 }
 
-// y[n][m] = sum over splits of part[split][n][m], in split order.
-__global__ __launch_bounds__(256) void gemm_split_reduce(const float *__restrict__ part, int splits, int M,
-                                                         int64_t N, float *__restrict__ y, int64_t ldy) {
-    const int64_t total = N * M;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-        const int64_t n = i / M, m = i - n * M;
-        float acc = part[i];
-        for (int sp = 1; sp < splits; ++sp) acc += part[(int64_t)sp * total + i];
-        y[n * ldy + m] = acc;
+// y_i[n][m] = sum over splits of part_i[split][n][m], in split order.  Grid: x over
+// 1024-row chunks of a column, y over the N columns (strided past 65535), z over the
+// launch's matrices;
+// each thread adds four consecutive rows (16-byte accesses when aligned).
+__global__ __launch_bounds__(256) void gemm_split_reduce(GemmGroup grp, int splits, int N) {
+    const GemmItem &it = grp.p[blockIdx.z];
+    const int M = it.M;
+    const int m = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (m >= M) return;
+    const int64_t per = (int64_t)N * M;
+    for (int n = blockIdx.y; n < N; n += gridDim.y) {
+        const float *src = it.part + (int64_t)n * M + m;
+        float *dst = it.y + (int64_t)n * it.ldy + m;
+        const bool vec = m + 3 < M && (((uintptr_t)src | (uintptr_t)dst) & 15) == 0 && (M & 3) == 0;
+        if (vec) {
+            float4_t acc = *reinterpret_cast<const float4_t *>(src);
+            for (int sp = 1; sp < splits; ++sp) acc += *reinterpret_cast<const float4_t *>(src + sp * per);
+            *reinterpret_cast<float4_t *>(dst) = acc;
+        } else {
+            for (int e = 0; e < 4 && m + e < M; ++e) {
+                float acc = src[e];
+                for (int sp = 1; sp < splits; ++sp) acc += src[e + sp * per];
+                dst[e] = acc;
+            }
+        }
     }
 }
 
 namespace {
 
-// K splits for a GEMM: enough workgroups for two per CU when the tile grid alone is
-// smaller, each split keeping at least 8 blocks; splits divide K/64.
-int gemm_splits(int64_t M, int64_t N, int nb) {
-    const int64_t tiles = ((M + GM - 1) / GM) * ((N + GN - 1) / GN);
-    int sp = 1;
-    while (tiles * sp < 512 && sp < 8 && nb % (2 * sp) == 0 && nb / (2 * sp) >= 8) sp *= 2;
-    return sp;
-}
-
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 }  // namespace
 
-// Workspace: fp16 x (N*K halves), the column exponents (N ints), then split-K partials.
-size_t gemm_f16_workspace_bytes(int64_t M, int64_t K, int64_t N) {
-    const int sp = gemm_splits(M, N, (int)(K / kBlockWeights));
-    return align256((size_t)N * K * 2) + align256((size_t)N * 4) + (sp > 1 ? align256((size_t)sp * N * M * 4) : 0);
+// Workspace of a call: fp16 x (N*K halves), the column exponents (N ints), and with
+// a K split each matrix's partials (splits * N * M floats).
+static size_t gemm_layout(const int64_t *Ms, int64_t n_items, int nb, int64_t N, int *splits_out,
+                          size_t *parts_off) {
+    int64_t tiles_m = 0;
+    for (int64_t i = 0; i < n_items; ++i) tiles_m += (Ms[i] + GM - 1) / GM;
+    const int64_t K = (int64_t)nb * kBlockWeights;
+    const int tiles_n = (int)((N + GN - 1) / GN);
+    int sp = 1;
+    while (tiles_m * tiles_n * sp < 512 && sp < 8 && nb % (2 * sp) == 0 && nb / (2 * sp) >= 8) sp *= 2;
+    size_t off = align256((size_t)N * K * 2) + align256((size_t)N * 4);
+    *parts_off = off;
+    if (sp > 1)
+        for (int64_t i = 0; i < n_items; ++i) off += align256((size_t)sp * N * Ms[i] * 4);
+    *splits_out = sp;
+    return off;
 }
 
-hipError_t launch_gemm_f16_v2(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx,
-                              int64_t N, float *y, int64_t ldy, void *workspace, hipStream_t s) {
+size_t gemm_f16_workspace_bytes(const int64_t *Ms, int64_t n_items, int64_t K, int64_t N) {
+    int sp;
+    size_t po;
+    return gemm_layout(Ms, n_items, (int)(K / kBlockWeights), N, &sp, &po);
+}
+
+hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, const float *x, int64_t ldx,
+                                 int64_t N, void *workspace, hipStream_t s) {
     const int K = nb * kBlockWeights;
+    int64_t Ms_local[64];
+    int64_t *Ms = n_items <= 64 ? Ms_local : new int64_t[n_items];
+    for (int64_t i = 0; i < n_items; ++i) Ms[i] = mats[i].M;
+    int splits;
+    size_t parts_off;
+    gemm_layout(Ms, n_items, nb, N, &splits, &parts_off);
+    if (Ms != Ms_local) delete[] Ms;
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     _Float16 *x16 = reinterpret_cast<_Float16 *>(ws);
     int *xe = reinterpret_cast<int *>(ws + align256((size_t)N * K * 2));
-    float *part = reinterpret_cast<float *>(ws + align256((size_t)N * K * 2) + align256((size_t)N * 4));
+    const int tiles_n = (int)((N + GN - 1) / GN);
+
     if (((uintptr_t)x % 16 == 0) && (ldx % 4 == 0))
         x_to_f16_perm<true><<<(unsigned)N, 256, 0, s>>>(x, ldx, K, x16, xe);
     else
         x_to_f16_perm<false><<<(unsigned)N, 256, 0, s>>>(x, ldx, K, x16, xe);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int tiles_m = (int)((M + GM - 1) / GM), tiles_n = (int)((N + GN - 1) / GN);
-    const int per = (tiles_n <= 8 && 8 % tiles_n == 0) ? 8 / tiles_n : 0;
-    const int splits = gemm_splits(M, N, nb);
-    const int xcd_map = (splits == 1 && per != 0 && tiles_m % per == 0) ? 1 : 0;
-    gemm_f16_mfma<<<tiles_m * tiles_n * splits, 256, 0, s>>>(w, (int)M, nb, x16, xe, (int)N, y, ldy, tiles_m,
-                                                              tiles_n, xcd_map, splits, part);
-    e = hipGetLastError();
-    if (e != hipSuccess || splits == 1) return e;
-    const int64_t total = N * M;
-    const int rgrid = (int)((total + 255) / 256 < 8192 ? (total + 255) / 256 : 8192);
-    gemm_split_reduce<<<rgrid, 256, 0, s>>>(part, splits, (int)M, N, y, ldy);
-    return hipGetLastError();
+
+    // one launch (plus one reduction with a K split) per kGemmMaxGroup matrices
+    float *part = reinterpret_cast<float *>(ws + parts_off);
+    int64_t tm_next = 0;
+    for (int64_t i0 = 0; i0 < n_items; i0 += kGemmMaxGroup) {
+        GemmGroup grp;
+        grp.n = 0;
+        grp.tm_base = (int)tm_next;
+        int64_t rows = 0;
+        for (int64_t i = i0; i < n_items && i < i0 + kGemmMaxGroup; ++i) {
+            const int64_t M = mats[i].M;
+            if (M == 0) continue;
+            GemmItem &it = grp.p[grp.n];
+            it.w = mats[i].w;
+            it.y = mats[i].y;
+            it.ldy = mats[i].ldy;
+            it.part = part;
+            it.M = (int)M;
+            it.tm0 = (int)tm_next;
+            grp.tm0[grp.n] = it.tm0;
+            ++grp.n;
+            tm_next += (M + GM - 1) / GM;
+            rows += M;
+            if (splits > 1) part += align256((size_t)splits * N * M * 4) / 4;
+        }
+        if (grp.n == 0) continue;
+        for (int k = grp.n; k < kGemmMaxGroup; ++k) grp.tm0[k] = INT_MAX;
+        const int tiles_m = (int)tm_next - grp.tm_base;
+        const int per = (tiles_n <= 8 && 8 % tiles_n == 0) ? 8 / tiles_n : 0;
+        const int xcd_map = (splits == 1 && per != 0 && tiles_m % per == 0) ? 1 : 0;
+        gemm_f16_mfma<<<tiles_m * tiles_n * splits, 256, 0, s>>>(grp, nb, x16, xe, (int)N, tiles_n, xcd_map,
+                                                                  splits);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        if (splits > 1) {
+            int maxM = 0;
+            for (int k = 0; k < grp.n; ++k) maxM = grp.p[k].M > maxM ? grp.p[k].M : maxM;
+            const dim3 rgrid((unsigned)((maxM + 1023) / 1024), (unsigned)(N < 65535 ? N : 65535), (unsigned)grp.n);
+            gemm_split_reduce<<<rgrid, 256, 0, s>>>(grp, splits, (int)N);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
 }
 
 }  // namespace q2_0

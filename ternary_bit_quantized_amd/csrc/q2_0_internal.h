@@ -40,9 +40,31 @@ hipError_t launch_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items,
 bool mat_vec_mfma_eligible(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx);
 hipError_t launch_mat_vec_mfma(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx,
                                int N, float *y, int64_t ldy, hipStream_t s);
-size_t gemm_f16_workspace_bytes(int64_t M, int64_t K, int64_t N);
-hipError_t launch_gemm_f16_v2(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx,
-                              int64_t N, float *y, int64_t ldy, void *workspace, hipStream_t s);
+// fp16-MFMA GEMM over one or more matrices that share K and x.
+struct GemmMat {
+    const uint8_t *w;
+    int64_t M;
+    float *y;
+    int64_t ldy;
+};
+constexpr int kGemmMaxGroup = 16;   // matrices per GEMM launch (kernel argument size)
+struct GemmItem {
+    const uint8_t *w;
+    float *y;
+    int64_t ldy;
+    float *part;   // this matrix's split-K partials (splits x N x M floats)
+    int M;
+    int tm0;       // first row tile of this matrix, counted across the call
+};
+struct GemmGroup {
+    GemmItem p[kGemmMaxGroup];
+    int tm0[kGemmMaxGroup];   // p[i].tm0 contiguously; INT_MAX past n
+    int n;
+    int tm_base;              // first row tile of this launch
+};
+size_t gemm_f16_workspace_bytes(const int64_t *Ms, int64_t n_items, int64_t K, int64_t N);
+hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, const float *x, int64_t ldx,
+                                 int64_t N, void *workspace, hipStream_t s);
 hipError_t launch_gemm_f32(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx,
                            int64_t N, float *y, int64_t ldy, hipStream_t s);
 

@@ -29,7 +29,7 @@ BLOCK_BYTES = 18
 MAT_VEC_MAX_N = 8
 
 EXPORTS = ("q2_0_get_rows", "q2_0_mul_mat_vec", "q2_0_mul_mat_vec_group", "q2_0_mul_mat",
-           "q2_0_mul_mat_workspace_bytes",
+           "q2_0_mul_mat_workspace_bytes", "q2_0_mul_mat_group", "q2_0_mul_mat_group_workspace_bytes",
            "q2_0_status_string", "q2_0_last_hip_error", "q2_0_version")
 
 
@@ -76,6 +76,10 @@ def lib() -> ctypes.CDLL:
                                    ctypes.c_size_t, P]
         L.q2_0_mul_mat_workspace_bytes.argtypes = [I64, I64, I64, ctypes.c_int]
         L.q2_0_mul_mat_workspace_bytes.restype = ctypes.c_size_t
+        L.q2_0_mul_mat_group.argtypes = [P, I64, I64, P, I64, I64, ctypes.c_int, P, ctypes.c_size_t, P]
+        L.q2_0_mul_mat_group.restype = ctypes.c_int
+        L.q2_0_mul_mat_group_workspace_bytes.argtypes = [P, I64, I64, I64, ctypes.c_int]
+        L.q2_0_mul_mat_group_workspace_bytes.restype = ctypes.c_size_t
         L.q2_0_status_string.argtypes = [ctypes.c_int]
         L.q2_0_status_string.restype = ctypes.c_char_p
         L.q2_0_version.restype = ctypes.c_char_p
@@ -116,6 +120,21 @@ def mul_mat_raw(w: int, M: int, K: int, x: int, ldx: int, N: int, y: int, ldy: i
 
 def mul_mat_workspace_bytes(M: int, K: int, N: int, precision: int) -> int:
     return int(lib().q2_0_mul_mat_workspace_bytes(M, K, N, precision))
+
+
+def _items_ptr(items):
+    return ctypes.cast(items, ctypes.c_void_p) if items is not None else None
+
+
+def mul_mat_group_raw(items, n_items: int, K: int, x: int, ldx: int, N: int, precision: int,
+                      workspace: int, ws_bytes: int, stream: int = 0) -> int:
+    """items: a ctypes array from make_items (or None with n_items == 0)."""
+    return lib().q2_0_mul_mat_group(_items_ptr(items), n_items, K, x, ldx, N, precision, workspace, ws_bytes,
+                                    stream)
+
+
+def mul_mat_group_workspace_bytes(items, n_items: int, K: int, N: int, precision: int) -> int:
+    return int(lib().q2_0_mul_mat_group_workspace_bytes(_items_ptr(items), n_items, K, N, precision))
 
 
 def version() -> str:
@@ -200,3 +219,25 @@ def q2_0_mul_mat(w, M: int, K: int, x, precision: int = Q2_0_PREC_F16_MFMA, y=No
     _check(mul_mat_raw(w.data_ptr(), M, K, xp, ldx, N, yp, ldy, precision, wsp, wsb, _stream(stream)),
            "q2_0_mul_mat")
     return y
+
+
+def q2_0_mul_mat_group(mats, K: int, x, precision: int = Q2_0_PREC_F16_MFMA, ys=None, workspace=None,
+                       stream=None):
+    """mats: [(w, M), ...] sharing K; returns [y_i (N, M_i)] with y_i = W_i x, any N."""
+    import torch
+    xp, N, ldx = _cols(x, K, "x")
+    if ys is None:
+        ys = [torch.empty((N, M), dtype=torch.float32, device=x.device) for (_, M) in mats]
+    entries = []
+    for (w, M), y in zip(mats, ys):
+        yp, _, ldy = _cols(y, M, "y")
+        entries.append((w.data_ptr(), M, yp, ldy))
+    items = make_items(entries)
+    need = mul_mat_group_workspace_bytes(items, len(entries), K, N, precision)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wsp = workspace.data_ptr() if workspace is not None else 0
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(mul_mat_group_raw(items, len(entries), K, xp, ldx, N, precision, wsp, wsb, _stream(stream)),
+           "q2_0_mul_mat_group")
+    return ys

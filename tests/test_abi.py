@@ -127,3 +127,26 @@ def test_group_validation():
     assert B.mul_mat_vec_group_raw(bad_ldy, 1, 64, P16, 64, 1) == B.Q2_0_ERR_LAYOUT
     empty = B.make_items([(0, 0, 0, 0)])
     assert B.mul_mat_vec_group_raw(empty, 1, 64, 0, 64, 1) == B.Q2_0_OK
+
+
+def test_gemm_group_validation_and_workspace():
+    items = B.make_items([(P16, 10, P16, 10), (P16, 5, P16 + 2, 5)])
+    assert B.mul_mat_group_raw(items, 2, 64, P16, 64, 20, 0, P16, 1 << 20) == B.Q2_0_ERR_ALIGN
+    assert B.mul_mat_group_raw(items, 2, 100, P16, 100, 20, 0, P16, 1 << 20) == B.Q2_0_ERR_SHAPE
+    assert B.mul_mat_group_raw(items, -1, 64, P16, 64, 20, 0, P16, 1 << 20) == B.Q2_0_ERR_SHAPE
+    assert B.mul_mat_group_raw(None, 0, 64, P16, 64, 20, 0, 0, 0) == B.Q2_0_OK
+    assert B.mul_mat_group_raw(None, 2, 64, P16, 64, 20, 0, 0, 0) == B.Q2_0_ERR_NULL
+    ok = B.make_items([(P16, 10, P16, 10), (0, 0, 0, 0), (P16, 300, P16, 300)])
+    assert B.mul_mat_group_raw(ok, 3, 64, P16, 64, 20, 7, P16, 1 << 20) == B.Q2_0_ERR_UNSUPPORTED
+    assert B.mul_mat_group_raw(ok, 3, 64, P16, 63, 20, 0, P16, 1 << 20) == B.Q2_0_ERR_LAYOUT
+    # workspace: x once for the whole group, split-K state for every item
+    need = B.mul_mat_group_workspace_bytes(ok, 3, 64, 20, B.Q2_0_PREC_F16_MFMA)
+    assert need >= 20 * 64 * 2
+    assert B.mul_mat_group_raw(ok, 3, 64, P16, 64, 20, 0, P16, need - 1) == B.Q2_0_ERR_WORKSPACE
+    assert B.mul_mat_group_raw(ok, 3, 64, P16, 64, 20, 0, 0, need) == B.Q2_0_ERR_WORKSPACE
+    assert B.mul_mat_group_workspace_bytes(ok, 3, 64, 20, B.Q2_0_PREC_F32) == 0
+    assert B.mul_mat_group_workspace_bytes(ok, 3, 64, 8, B.Q2_0_PREC_F16_MFMA) == 0
+    big = B.make_items([(P16, 4096, P16, 4096), (P16, 1024, P16, 1024), (P16, 1024, P16, 1024)])
+    g = B.mul_mat_group_workspace_bytes(big, 3, 4096, 512, B.Q2_0_PREC_F16_MFMA)
+    singles = [B.mul_mat_workspace_bytes(M, 4096, 512, B.Q2_0_PREC_F16_MFMA) for M in (4096, 1024, 1024)]
+    assert 512 * 4096 * 2 < g < sum(singles)   # x staged once, fewer splits than the small singles

@@ -475,3 +475,57 @@ def test_mat_vec_group_stack_8b_layer_workload():
     for (w, M), y, n in zip(mats, run_group(mats, K, x), names):
         rows = np.unique(np.concatenate([rng.integers(0, M, 256), [0, M - 1]]))
         assert_products(y, w, M, K, x, REL_F32, rows=rows, what=n)
+
+
+# =============================================================================== grouped GEMM
+
+def run_gemm_group(mats, K, x, precision):
+    torch = _torch()
+    N = x.shape[0]
+    xd = dev(x)
+    keep, entries, ys = [], [], []
+    for w, M in mats:
+        wd = dev(w) if M else None
+        yd = torch.full((N, M + 5), float("nan"), dtype=torch.float32, device="cuda")
+        keep.append(wd)
+        ys.append(yd)
+        entries.append((wd.data_ptr() if wd is not None else 0, M, yd.data_ptr(), M + 5))
+    items = B.make_items(entries)
+    need = B.mul_mat_group_workspace_bytes(items, len(entries), K, N, precision)
+    wsd = torch.full((max(need, 16) // 4 + 1,), float("nan"), dtype=torch.float32, device="cuda")
+    st = B.mul_mat_group_raw(items, len(entries), K, xd.data_ptr(), K, N, precision, wsd.data_ptr(), need,
+                             torch.cuda.current_stream().cuda_stream)
+    assert st == 0, B.lib().q2_0_status_string(st)
+    out = []
+    for (w, M), yd in zip(mats, ys):
+        y = host(yd)
+        assert np.all(np.isnan(y[:, M:])), "group GEMM wrote past M"
+        out.append(y[:, :M])
+    return out
+
+
+@pytest.mark.parametrize("precision,rel", [(B.Q2_0_PREC_F16_MFMA, REL_F16), (B.Q2_0_PREC_F32, REL_F32)])
+@pytest.mark.parametrize("Ms,K,N", [((4096 // 8, 1024 // 8, 1024 // 8), 2048, 96), ((300, 0, 77, 129), 576, 130),
+                                    ((64,) * 20, 192, 64), ((1000, 24), 4096, 9)])
+def test_mul_mat_group_matches_oracle(precision, rel, Ms, K, N):
+    mats = [(synth.weight(17, i, len(Ms), M, K, "quad", synth.ScaleDist("loguniform", 1e-3, 1e-1, 0.02)), M)
+            for i, M in enumerate(Ms)]
+    x = synth.activations(17, len(Ms), K, N, K)
+    ys = run_gemm_group(mats, K, x, precision)
+    for (w, M), y in zip(mats, ys):
+        if M:
+            assert_products(y, w, M, K, x, rel, what="group item M=%d K=%d N=%d" % (M, K, N))
+
+
+def test_mul_mat_group_prefill_qkv_deterministic():
+    wl = synth.PREFILL_1P7B
+    names = ["q", "k", "v"]
+    K = wl.shapes["q"][1]
+    mats = [(ws(wl, n), wl.shapes[n][0]) for n in names]
+    x = synth.activations(wl.seed, 0, 0, 512, K)
+    a = run_gemm_group(mats, K, x, B.Q2_0_PREC_F16_MFMA)
+    b = run_gemm_group(mats, K, x, B.Q2_0_PREC_F16_MFMA)
+    for (w, M), ya, yb, n in zip(mats, a, b, names):
+        assert np.array_equal(ya.view(np.uint32), yb.view(np.uint32)), "run-to-run difference in " + n
+        rows = np.unique(np.concatenate([np.arange(0, M, 97), [M - 1]]))
+        assert_products(ya, w, M, K, x, REL_F16, rows=rows, what="qkv " + n)
