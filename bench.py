@@ -54,6 +54,42 @@ F16_MFMA_PEAK_TFLOPS = 2500.0
 PREFILL_N = 512
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "mat_vec_stream_gemm_f16_hbm_traffic.md")
+
+
+def kernel_sources_sha256() -> str:
+    """sha256 over the HIP sources of libq2_0.so (sorted by name), to tell whether the
+    recorded counter readings still describe the kernels being timed."""
+    import hashlib
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "ternary_bit_quantized_amd", "csrc")
+    for name in sorted(os.listdir(src)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(src, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic() -> dict:
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE passes
+    (lines `traffic_bytes_per_launch <kernel>: <bytes>`), or {} when the kernel sources
+    changed after those passes were taken (line `sources_sha256: <hex>`)."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return {}
+    out, sha = {}, None
+    for ln in lines:
+        ln = ln.strip().strip("`")
+        if ln.startswith("sources_sha256:"):
+            sha = ln.split(":", 1)[1].strip()
+        elif ln.startswith("traffic_bytes_per_launch "):
+            key, val = ln[len("traffic_bytes_per_launch "):].split(":", 1)
+            out[key.strip()] = int(val)
+    return out if sha == kernel_sources_sha256() else {}
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -111,7 +147,6 @@ def main():
     xP = {K: torch.from_numpy(synth.activations(wl.seed, 1, synth.stack_x_matrix_index(K), PREFILL_N, K)).to(dev)
           for K in Ks}
     y1 = {M: torch.empty((1, M), dtype=torch.float32, device=dev) for M in Ms}
-    yP = {M: torch.empty((PREFILL_N, M), dtype=torch.float32, device=dev) for M in Ms}
     ids_p = torch.from_numpy(synth.row_ids(vwl.seed, 0, 0, PREFILL_N, VM)).to(dev)
     ids_d = torch.from_numpy(synth.row_ids(vwl.seed, 1, 0, 1, VM)).to(dev)
     emb_out_p = torch.empty((PREFILL_N, VK), dtype=torch.float32, device=dev)
@@ -299,6 +334,7 @@ def main():
     pre_tok_s = PREFILL_N / ((ms["prefill_gemm"] + ms["prefill_get_rows"]) * 1e-3)
     weight_bytes = sum(host_w[k].nbytes for k in order)
 
+    traffic = recorded_traffic()
     result = {
         "metric": METRIC,
         "value": round(matvec_gbs, 2),
@@ -340,15 +376,16 @@ def main():
         "roofline": {
             "kernel": "mat_vec_stream (N=1; %d grouped launches per decode token)" % n_dec_launches,
             "bound": "hbm", "achieved": round(matvec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(matvec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(matvec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic.get("mat_vec_stream"),
             "bytes_per_launch_avg": int(dec_bytes / n_dec_launches),
             "avg_launch_us": round(ms["decode_mat_vec"] * 1e3 / n_dec_launches, 3),
         },
         "roofline_gemm": {
-            "kernel": "gemm_f16_mfma (N=512; 144 group calls per prefill, each an fp16 x conversion + one GEMM launch)",
+            "kernel": "gemm_f16_mfma (N=512; %d group calls per prefill, each an fp16 x conversion, "
+                      "one GEMM launch and, where K is split, one reduction)" % len(prefill_groups),
             "bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": F16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(gemm_tflops / F16_MFMA_PEAK_TFLOPS, 4),
-            "traffic": None, "algorithmic_bytes": int(pre_bytes),
+            "traffic": traffic.get("gemm_f16_mfma"), "algorithmic_bytes": int(pre_bytes),
         },
         "cpu_baseline": None,
     }

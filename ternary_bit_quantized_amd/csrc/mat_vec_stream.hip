@@ -6,11 +6,16 @@
 // matrix-vector paragraph), organised for throughput on large or grouped launches:
 //
 //  * The activation columns for the whole of K are converted once per workgroup
-//    into LDS, laid out as the MFMA A operand, behind a single barrier.
+//    into LDS, laid out as the MFMA A operand, behind a single barrier; each
+//    column is first scaled by a power of two that puts its max |x| just below
+//    2^15, so the fp16 hi/lo split neither overflows nor loses bits to fp16's
+//    subnormal range (the scale is undone on the results).
 //  * Work is a list of items (16-row tile, stage of SB blocks), tile-major.  Each
-//    workgroup owns a contiguous run of tiles and each of its 8 waves a contiguous
-//    eighth of that run's items, so every wave streams the same number of stages
-//    to within one: no tail where a few waves finish a last round alone.
+//    workgroup owns a contiguous run of tiles and each of its W waves (4 to 16,
+//    chosen per shape so that the most waves stay resident within the LDS the
+//    activation takes) a contiguous 1/W of that run's items, so every wave streams
+//    the same number of stages to within one: no tail where a few waves finish a
+//    last round alone.
 //  * A wave streams on its own, with no barrier: one stage is in flight in
 //    registers (coalesced 16-byte loads, consecutive lanes on consecutive bytes of
 //    a row) while the previous one is decoded.  Weight bytes pass through a wave-private LDS
