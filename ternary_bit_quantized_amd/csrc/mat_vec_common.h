@@ -37,11 +37,12 @@ struct MvProblem {
 };
 
 // A launch's matrices.  tile0 repeats the problems' first tiles contiguously (entries
-// past n hold INT_MAX), so that a tile's matrix is found by a binary search of
-// log2(kMvMaxGroup) scalar loads.
+// from n on, including the extra last one, hold INT_MAX), so that a tile's matrix is
+// found by a binary search of log2(kMvMaxGroup) scalar loads, and tile0[i + 1] bounds
+// matrix i.
 struct MvGroup {
     MvProblem p[kMvMaxGroup];
-    int tile0[kMvMaxGroup];
+    int tile0[kMvMaxGroup + 1];
     int n;
     int total_tiles;
 };

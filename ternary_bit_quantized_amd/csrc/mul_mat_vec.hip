@@ -96,7 +96,7 @@ hipError_t launch_mat_vec(const uint8_t *w, int64_t M, int nb, const float *x, i
             MvGroup grp;
             grp.n = 1;
             grp.p[0] = MvProblem{w, y, ldy, (int)M, 0};
-            for (int i = 0; i < kMvMaxGroup; ++i) grp.tile0[i] = i ? INT_MAX : 0;
+            for (int i = 0; i <= kMvMaxGroup; ++i) grp.tile0[i] = i ? INT_MAX : 0;
             grp.total_tiles = (int)((M + kMvTile - 1) / kMvTile);
             return launch_mat_vec_stream(grp, nb, x, ldx, N, s);
         }
@@ -144,7 +144,7 @@ hipError_t launch_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items,
             ++i;
         }
         if (grp.n) {
-            for (int k = grp.n; k < kMvMaxGroup; ++k) grp.tile0[k] = INT_MAX;
+            for (int k = grp.n; k <= kMvMaxGroup; ++k) grp.tile0[k] = INT_MAX;
             grp.total_tiles = tiles;
             hipError_t e = launch_mat_vec_stream(grp, nb, x, ldx, N, s);
             if (e != hipSuccess) return e;

@@ -261,7 +261,8 @@ def _ranged_x(seed, N, K, mags, spread=False):
     return x.astype(np.float32)
 
 
-@pytest.mark.parametrize("M,K", [(300, 1024), (16400, 512)])   # K-split kernel, streaming kernel
+# K-split kernel; streaming kernel with a ragged half stage (K = 512) and with whole stages
+@pytest.mark.parametrize("M,K", [(300, 1024), (16400, 512), (16400, 4096)])
 @pytest.mark.parametrize("N,first", [(1, 0), (1, 2), (1, 7), (1, 8), (4, 0), (8, 1)])
 def test_mat_vec_activation_range(M, K, N, first):
     w = synth.weight(13, M, K // 64, M, K, "tern_c3", synth.ScaleDist("uniform", 0.005, 0.05))
@@ -274,7 +275,8 @@ def test_mat_vec_activation_range(M, K, N, first):
                         what="M=%d N=%d mags from %g spread=%s" % (M, N, mags[0], spread))
 
 
-@pytest.mark.parametrize("M,K", [(300, 1024), (16400, 512)])   # K-split kernel, streaming kernel
+# K-split kernel; streaming kernel with a ragged half stage (K = 512) and with whole stages
+@pytest.mark.parametrize("M,K", [(300, 1024), (16400, 512), (16400, 4096)])
 @pytest.mark.parametrize("big", [1e4, 1e6])
 def test_mat_vec_outlier_on_zero_weights(M, K, big):
     """A huge activation whose weights are all zero must not cost the other elements
@@ -463,6 +465,30 @@ def test_mat_vec_stream_path_full_oracle(N):
     x = synth.activations(23, N, 0, N, K)
     y = run_mat_vec(dev(w), M, K, x, ldy=M + 9)
     assert_products(y, w, M, K, x, REL_F32, what="stream N=%d" % N)
+
+
+# The streaming kernel across K (1, 2, 4, 6, 8 and 12 stages of 16 blocks per row, and two
+# stages plus a half stage at K = 2560, where K/64 = 8 mod 16) and N, with ragged M so that
+# the last tile is partial; every row checked.
+@pytest.mark.parametrize("K,N", [(1024, 1), (2048, 1), (2048, 4), (2560, 3), (4096, 1), (4096, 2), (4096, 4),
+                                 (6144, 2), (8192, 1), (12288, 1), (12288, 2)])
+def test_mat_vec_stream_across_k(K, N):
+    M = 16384 + 5
+    w = synth.weight(24, K // 64, N, M, K, "tern_c3", synth.ScaleDist("loguniform", 1e-3, 1e-1, 0.01))
+    x = synth.activations(24, K // 64, N, N, K)
+    y = run_mat_vec(dev(w), M, K, x, ldy=M + 3)
+    assert_products(y, w, M, K, x, REL_F32, what="stream K=%d N=%d" % (K, N))
+
+
+def test_mat_vec_group_ragged_members_long_rows():
+    """Group members whose row counts leave partial tiles, at K = 12288 (12 stages a row)."""
+    K, N = 12288, 1
+    Ms = (16384 + 1, 3, 2 + 16, 1000 + 7)
+    mats = [(synth.weight(25, i, 0, M, K, "quad", synth.ScaleDist("uniform", 0.005, 0.05)), M)
+            for i, M in enumerate(Ms)]
+    x = synth.activations(25, 0, 1, N, K)
+    for (w, M), y in zip(mats, run_group(mats, K, x)):
+        assert_products(y, w, M, K, x, REL_F32, what="group M=%d" % M)
 
 
 def test_mat_vec_group_stack_8b_layer_workload():
