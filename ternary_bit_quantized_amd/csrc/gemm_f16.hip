@@ -138,8 +138,11 @@ __device__ __forceinline__ void dequant_word_f16(uint32_t word, uint32_t d2, con
         out[s] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, out[s]) * dd);
 }
 
+// A step's code words and scales as loaded.  Nothing is computed from them until the
+// step is stored, two steps later: an ALU op on a fresh load would make the wave wait
+// for it right away.
 struct WRegs {
-    uint32_t d2[2];     // half scale in both halves
+    uint32_t d[2];      // half scale (low 16 bits)
     uint32_t word[2];
 };
 
@@ -224,8 +227,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_mfma(GemmGroup grp, int nb, c
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const uint16_t *b16 = reinterpret_cast<const uint16_t *>(wrow[i] + (int64_t)blk * kBlockBytes);
-            const uint32_t d = b16[0];
-            r.d2[i] = d | (d << 16);
+            r.d[i] = b16[0];
             r.word[i] = (uint32_t)b16[1 + 2 * g] | ((uint32_t)b16[2 + 2 * g] << 16);
         }
     };
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_mfma(GemmGroup grp, int nb, c
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             uint32_t o[8];
-            dequant_word_f16(wr.word[i], wr.d2[i], pm, o);
+            dequant_word_f16(wr.word[i], wr.d[i] | (wr.d[i] << 16), pm, o);
             u32x4_t *dst = reinterpret_cast<u32x4_t *>(&As[buf][(r0 + 64 * i) * GLD + 16 * g]);
             dst[0] = u32x4_t{o[0], o[1], o[2], o[3]};
             dst[1] = u32x4_t{o[4], o[5], o[6], o[7]};
