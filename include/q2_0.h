@@ -47,8 +47,8 @@ typedef enum {
     Q2_0_ERR_NULL = 1,        /* a required pointer is NULL */
     Q2_0_ERR_SHAPE = 2,       /* K <= 0, K % 64 != 0, a negative size, or a size beyond the limits */
     Q2_0_ERR_LAYOUT = 3,      /* ldx < K, ldy < M or ld_out < K */
-    Q2_0_ERR_ALIGN = 4,       /* w not 2-byte aligned, or x / y / out / ids not 4-byte aligned */
-    Q2_0_ERR_UNSUPPORTED = 5, /* N > 8 for the mat-vec, or an unknown precision */
+    Q2_0_ERR_ALIGN = 4,       /* w not 2-byte aligned, or x / y / out / ids not aligned to their element size */
+    Q2_0_ERR_UNSUPPORTED = 5, /* N > 8 for the mat-vec, or an unknown precision or activation type */
     Q2_0_ERR_WORKSPACE = 6,   /* workspace smaller than q2_0_mul_mat_workspace_bytes(), or not 16-byte aligned */
     Q2_0_ERR_HIP = 7          /* a HIP launch failed; see q2_0_last_hip_error() */
 } q2_0_status;
@@ -60,6 +60,20 @@ typedef enum {
 
 /* Largest activation-column count of q2_0_mul_mat_vec. */
 #define Q2_0_MAT_VEC_MAX_N 8
+
+/*
+ * Activation element types of the *_act entry points.  The WebGPU backend of
+ * bisque.today "WebGPU: add Q2_0 support" accepts only F32 activations (the
+ * paragraph on what the change leaves out); these calls add half- and
+ * bfloat16-precision activations.  Every element enters the arithmetic as its
+ * exact f32 value, so a call with F16 or BF16 x gives bit for bit the result of the
+ * F32 call on those values converted to f32.
+ */
+typedef enum {
+    Q2_0_ACT_F32 = 0,    /* IEEE single, 4-byte aligned */
+    Q2_0_ACT_F16 = 1,    /* IEEE half, 2-byte aligned */
+    Q2_0_ACT_BF16 = 2    /* bfloat16 (the upper 16 bits of an IEEE single), 2-byte aligned */
+} q2_0_act_type;
 
 /*
  * get_rows: gather rows of a Q2_0 matrix and dequantize them to f32
@@ -171,6 +185,25 @@ int q2_0_mul_mat_group(const q2_0_mat_vec_item *items, int64_t n_items, int64_t 
 /* Workspace bytes q2_0_mul_mat_group needs (0 when none, and for invalid arguments). */
 size_t q2_0_mul_mat_group_workspace_bytes(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K,
                                           int64_t N, int precision);
+
+/*
+ * The same four products with activations of element type x_type (a q2_0_act_type):
+ * x points at N columns of K elements of that type, column n at element n*ldx
+ * (ldx >= K), aligned to the element size.  Everything else -- w, y, items,
+ * precision, routing, accuracy, workspace (the *_workspace_bytes queries above hold
+ * for every x_type) and errors -- is that of the F32 call.  An unknown x_type
+ * returns Q2_0_ERR_UNSUPPORTED, checked before alignment (which depends on it).
+ * q2_0_mul_mat_vec(...) is q2_0_mul_mat_vec_act(..., Q2_0_ACT_F32, ...), and so on.
+ */
+int q2_0_mul_mat_vec_act(const void *w, int64_t M, int64_t K, const void *x, int x_type, int64_t ldx,
+                         int64_t N, float *y, int64_t ldy, void *stream);
+int q2_0_mul_mat_vec_group_act(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, const void *x,
+                               int x_type, int64_t ldx, int64_t N, void *stream);
+int q2_0_mul_mat_act(const void *w, int64_t M, int64_t K, const void *x, int x_type, int64_t ldx, int64_t N,
+                     float *y, int64_t ldy, int precision, void *workspace, size_t ws_bytes, void *stream);
+int q2_0_mul_mat_group_act(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, const void *x,
+                           int x_type, int64_t ldx, int64_t N, int precision, void *workspace,
+                           size_t ws_bytes, void *stream);
 
 /* A static, human-readable name for a status code. */
 const char *q2_0_status_string(int status);

@@ -31,14 +31,59 @@ int check_shape(int64_t M, int64_t K, int64_t N) {
     return Q2_0_OK;
 }
 
-// Common checks of mul_mat_vec and mul_mat after the empty no-op.
-int check_product(const void *w, int64_t M, int64_t K, const float *x, int64_t ldx, const float *y,
-                  int64_t ldy) {
+// Common checks of the products after the empty no-op: NULL, LAYOUT, then the
+// activation type (alignment depends on it) and ALIGN.
+int check_product(const void *w, int64_t M, int64_t K, const void *x, int x_type, int64_t ldx,
+                  const float *y, int64_t ldy) {
     if (!w || !x || !y) return Q2_0_ERR_NULL;
     if (ldx < K || ldy < M) return Q2_0_ERR_LAYOUT;
-    if (!aligned(w, 2) || !aligned(x, 4) || !aligned(y, 4)) return Q2_0_ERR_ALIGN;
+    if (x_type != Q2_0_ACT_F32 && x_type != Q2_0_ACT_F16 && x_type != Q2_0_ACT_BF16) return Q2_0_ERR_UNSUPPORTED;
+    if (!aligned(w, 2) || !aligned(x, q2_0::act_bytes((q2_0::Act)x_type)) || !aligned(y, 4)) return Q2_0_ERR_ALIGN;
     return Q2_0_OK;
 }
+
+int mul_mat_vec_impl(const void *w, int64_t M, int64_t K, const void *x, int x_type, int64_t ldx, int64_t N,
+                     float *y, int64_t ldy, void *stream) {
+    int st = check_shape(M, K, N);
+    if (st) return st;
+    if (M == 0 || N == 0) return Q2_0_OK;
+    st = check_product(w, M, K, x, x_type, ldx, y, ldy);
+    if (st) return st;
+    if (N > Q2_0_MAT_VEC_MAX_N) return Q2_0_ERR_UNSUPPORTED;
+    return hip_status(q2_0::launch_mat_vec(static_cast<const uint8_t *>(w), M, (int)(K / Q2_0_BLOCK_WEIGHTS), x,
+                                           (q2_0::Act)x_type, ldx, (int)N, y, ldy,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int mul_mat_vec_group_impl(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, const void *x,
+                           int x_type, int64_t ldx, int64_t N, void *stream) {
+    int st = check_shape(0, K, N);
+    if (st) return st;
+    if (n_items < 0) return Q2_0_ERR_SHAPE;
+    if (n_items == 0 || N == 0) return Q2_0_OK;
+    if (!items) return Q2_0_ERR_NULL;
+    for (int64_t i = 0; i < n_items; ++i) {
+        st = check_shape(items[i].M, K, N);
+        if (st) return st;
+    }
+    bool any = false;
+    for (int64_t i = 0; i < n_items; ++i) {
+        if (items[i].M == 0) continue;
+        any = true;
+        st = check_product(items[i].w, items[i].M, K, x, x_type, ldx, items[i].y, items[i].ldy);
+        if (st) return st;
+    }
+    if (!any) return Q2_0_OK;
+    if (N > Q2_0_MAT_VEC_MAX_N) return Q2_0_ERR_UNSUPPORTED;
+    return hip_status(q2_0::launch_mat_vec_group(items, n_items, (int)(K / Q2_0_BLOCK_WEIGHTS), x,
+                                                 (q2_0::Act)x_type, ldx, (int)N,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+int mul_mat_impl(const void *w, int64_t M, int64_t K, const void *x, int x_type, int64_t ldx, int64_t N,
+                 float *y, int64_t ldy, int precision, void *workspace, size_t ws_bytes, void *stream);
+int mul_mat_group_impl(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, const void *x, int x_type,
+                       int64_t ldx, int64_t N, int precision, void *workspace, size_t ws_bytes, void *stream);
 
 }  // namespace
 
@@ -60,39 +105,22 @@ int q2_0_get_rows(const void *w, int64_t M, int64_t K, const int32_t *ids, int64
 
 int q2_0_mul_mat_vec(const void *w, int64_t M, int64_t K, const float *x, int64_t ldx, int64_t N,
                      float *y, int64_t ldy, void *stream) {
-    int st = check_shape(M, K, N);
-    if (st) return st;
-    if (M == 0 || N == 0) return Q2_0_OK;
-    st = check_product(w, M, K, x, ldx, y, ldy);
-    if (st) return st;
-    if (N > Q2_0_MAT_VEC_MAX_N) return Q2_0_ERR_UNSUPPORTED;
-    return hip_status(q2_0::launch_mat_vec(static_cast<const uint8_t *>(w), M,
-                                           (int)(K / Q2_0_BLOCK_WEIGHTS), x, ldx, (int)N, y, ldy,
-                                           static_cast<hipStream_t>(stream)));
+    return mul_mat_vec_impl(w, M, K, x, Q2_0_ACT_F32, ldx, N, y, ldy, stream);
+}
+
+int q2_0_mul_mat_vec_act(const void *w, int64_t M, int64_t K, const void *x, int x_type, int64_t ldx,
+                         int64_t N, float *y, int64_t ldy, void *stream) {
+    return mul_mat_vec_impl(w, M, K, x, x_type, ldx, N, y, ldy, stream);
 }
 
 int q2_0_mul_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K,
                            const float *x, int64_t ldx, int64_t N, void *stream) {
-    int st = check_shape(0, K, N);
-    if (st) return st;
-    if (n_items < 0) return Q2_0_ERR_SHAPE;
-    if (n_items == 0 || N == 0) return Q2_0_OK;
-    if (!items) return Q2_0_ERR_NULL;
-    for (int64_t i = 0; i < n_items; ++i) {
-        st = check_shape(items[i].M, K, N);
-        if (st) return st;
-    }
-    bool any = false;
-    for (int64_t i = 0; i < n_items; ++i) {
-        if (items[i].M == 0) continue;
-        any = true;
-        st = check_product(items[i].w, items[i].M, K, x, ldx, items[i].y, items[i].ldy);
-        if (st) return st;
-    }
-    if (!any) return Q2_0_OK;
-    if (N > Q2_0_MAT_VEC_MAX_N) return Q2_0_ERR_UNSUPPORTED;
-    return hip_status(q2_0::launch_mat_vec_group(items, n_items, (int)(K / Q2_0_BLOCK_WEIGHTS), x, ldx,
-                                                 (int)N, static_cast<hipStream_t>(stream)));
+    return mul_mat_vec_group_impl(items, n_items, K, x, Q2_0_ACT_F32, ldx, N, stream);
+}
+
+int q2_0_mul_mat_vec_group_act(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, const void *x,
+                               int x_type, int64_t ldx, int64_t N, void *stream) {
+    return mul_mat_vec_group_impl(items, n_items, K, x, x_type, ldx, N, stream);
 }
 
 size_t q2_0_mul_mat_workspace_bytes(int64_t M, int64_t K, int64_t N, int precision) {
@@ -104,26 +132,12 @@ size_t q2_0_mul_mat_workspace_bytes(int64_t M, int64_t K, int64_t N, int precisi
 int q2_0_mul_mat(const void *w, int64_t M, int64_t K, const float *x, int64_t ldx, int64_t N,
                  float *y, int64_t ldy, int precision, void *workspace, size_t ws_bytes,
                  void *stream) {
-    int st = check_shape(M, K, N);
-    if (st) return st;
-    if (N > kMaxGemmN) return Q2_0_ERR_SHAPE;
-    if (((M + 127) / 128) * ((N + 127) / 128) * 8 > kMaxRows) return Q2_0_ERR_SHAPE;   // launch grid
-    if (M == 0 || N == 0) return Q2_0_OK;
-    st = check_product(w, M, K, x, ldx, y, ldy);
-    if (st) return st;
-    if (precision != Q2_0_PREC_F16_MFMA && precision != Q2_0_PREC_F32) return Q2_0_ERR_UNSUPPORTED;
-    const size_t need = q2_0_mul_mat_workspace_bytes(M, K, N, precision);
-    if (ws_bytes < need || (need && (!workspace || !aligned(workspace, 16)))) return Q2_0_ERR_WORKSPACE;
-    const uint8_t *wb = static_cast<const uint8_t *>(w);
-    const int nb = (int)(K / Q2_0_BLOCK_WEIGHTS);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (N <= Q2_0_MAT_VEC_MAX_N)
-        return hip_status(q2_0::launch_mat_vec(wb, M, nb, x, ldx, (int)N, y, ldy, s));
-    if (precision == Q2_0_PREC_F16_MFMA) {
-        const q2_0::GemmMat m{wb, M, y, ldy};
-        return hip_status(q2_0::launch_gemm_f16_group(&m, 1, nb, x, ldx, N, workspace, s));
-    }
-    return hip_status(q2_0::launch_gemm_f32(wb, M, nb, x, ldx, N, y, ldy, s));
+    return mul_mat_impl(w, M, K, x, Q2_0_ACT_F32, ldx, N, y, ldy, precision, workspace, ws_bytes, stream);
+}
+
+int q2_0_mul_mat_act(const void *w, int64_t M, int64_t K, const void *x, int x_type, int64_t ldx, int64_t N,
+                     float *y, int64_t ldy, int precision, void *workspace, size_t ws_bytes, void *stream) {
+    return mul_mat_impl(w, M, K, x, x_type, ldx, N, y, ldy, precision, workspace, ws_bytes, stream);
 }
 
 size_t q2_0_mul_mat_group_workspace_bytes(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K,
@@ -144,6 +158,65 @@ size_t q2_0_mul_mat_group_workspace_bytes(const q2_0_mat_vec_item *items, int64_
 
 int q2_0_mul_mat_group(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, const float *x,
                        int64_t ldx, int64_t N, int precision, void *workspace, size_t ws_bytes, void *stream) {
+    return mul_mat_group_impl(items, n_items, K, x, Q2_0_ACT_F32, ldx, N, precision, workspace, ws_bytes,
+                              stream);
+}
+
+int q2_0_mul_mat_group_act(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, const void *x,
+                           int x_type, int64_t ldx, int64_t N, int precision, void *workspace,
+                           size_t ws_bytes, void *stream) {
+    return mul_mat_group_impl(items, n_items, K, x, x_type, ldx, N, precision, workspace, ws_bytes, stream);
+}
+
+const char *q2_0_status_string(int status) {
+    switch (status) {
+        case Q2_0_OK: return "Q2_0_OK";
+        case Q2_0_ERR_NULL: return "Q2_0_ERR_NULL: a required pointer is NULL";
+        case Q2_0_ERR_SHAPE: return "Q2_0_ERR_SHAPE: K must be a positive multiple of 64 and sizes non-negative and within limits";
+        case Q2_0_ERR_LAYOUT: return "Q2_0_ERR_LAYOUT: a leading dimension is smaller than the row length";
+        case Q2_0_ERR_ALIGN: return "Q2_0_ERR_ALIGN: w must be 2-byte aligned and other buffers aligned to their element size";
+        case Q2_0_ERR_UNSUPPORTED: return "Q2_0_ERR_UNSUPPORTED: N > 8 for mat-vec, or unknown precision or activation type";
+        case Q2_0_ERR_WORKSPACE: return "Q2_0_ERR_WORKSPACE: workspace missing, too small or not 16-byte aligned";
+        case Q2_0_ERR_HIP: return "Q2_0_ERR_HIP: a HIP launch failed";
+        default: return "unknown q2_0 status";
+    }
+}
+
+int q2_0_last_hip_error(void) { return g_last_hip_error; }
+
+const char *q2_0_version(void) { return "q2_0 0.1.0 gfx950"; }
+
+}  // extern "C"
+
+namespace {
+
+int mul_mat_impl(const void *w, int64_t M, int64_t K, const void *x, int x_type, int64_t ldx, int64_t N,
+                 float *y, int64_t ldy, int precision, void *workspace, size_t ws_bytes, void *stream) {
+    int st = check_shape(M, K, N);
+    if (st) return st;
+    if (N > kMaxGemmN) return Q2_0_ERR_SHAPE;
+    if (((M + 127) / 128) * ((N + 127) / 128) * 8 > kMaxRows) return Q2_0_ERR_SHAPE;   // launch grid
+    if (M == 0 || N == 0) return Q2_0_OK;
+    st = check_product(w, M, K, x, x_type, ldx, y, ldy);
+    if (st) return st;
+    if (precision != Q2_0_PREC_F16_MFMA && precision != Q2_0_PREC_F32) return Q2_0_ERR_UNSUPPORTED;
+    const size_t need = q2_0_mul_mat_workspace_bytes(M, K, N, precision);
+    if (ws_bytes < need || (need && (!workspace || !aligned(workspace, 16)))) return Q2_0_ERR_WORKSPACE;
+    const uint8_t *wb = static_cast<const uint8_t *>(w);
+    const int nb = (int)(K / Q2_0_BLOCK_WEIGHTS);
+    const q2_0::Act xt = (q2_0::Act)x_type;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (N <= Q2_0_MAT_VEC_MAX_N)
+        return hip_status(q2_0::launch_mat_vec(wb, M, nb, x, xt, ldx, (int)N, y, ldy, s));
+    if (precision == Q2_0_PREC_F16_MFMA) {
+        const q2_0::GemmMat m{wb, M, y, ldy};
+        return hip_status(q2_0::launch_gemm_f16_group(&m, 1, nb, x, xt, ldx, N, workspace, s));
+    }
+    return hip_status(q2_0::launch_gemm_f32(wb, M, nb, x, xt, ldx, N, y, ldy, s));
+}
+
+int mul_mat_group_impl(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, const void *x, int x_type,
+                       int64_t ldx, int64_t N, int precision, void *workspace, size_t ws_bytes, void *stream) {
     int st = check_shape(0, K, N);
     if (st) return st;
     if (N > kMaxGemmN || n_items < 0) return Q2_0_ERR_SHAPE;
@@ -160,7 +233,7 @@ int q2_0_mul_mat_group(const q2_0_mat_vec_item *items, int64_t n_items, int64_t 
     for (int64_t i = 0; i < n_items; ++i) {
         if (items[i].M == 0) continue;
         any = true;
-        st = check_product(items[i].w, items[i].M, K, x, ldx, items[i].y, items[i].ldy);
+        st = check_product(items[i].w, items[i].M, K, x, x_type, ldx, items[i].y, items[i].ldy);
         if (st) return st;
     }
     if (!any) return Q2_0_OK;
@@ -168,14 +241,15 @@ int q2_0_mul_mat_group(const q2_0_mat_vec_item *items, int64_t n_items, int64_t 
     const size_t need = q2_0_mul_mat_group_workspace_bytes(items, n_items, K, N, precision);
     if (ws_bytes < need || (need && (!workspace || !aligned(workspace, 16)))) return Q2_0_ERR_WORKSPACE;
     const int nb = (int)(K / Q2_0_BLOCK_WEIGHTS);
+    const q2_0::Act xt = (q2_0::Act)x_type;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (N <= Q2_0_MAT_VEC_MAX_N)
-        return hip_status(q2_0::launch_mat_vec_group(items, n_items, nb, x, ldx, (int)N, s));
+        return hip_status(q2_0::launch_mat_vec_group(items, n_items, nb, x, xt, ldx, (int)N, s));
     if (precision == Q2_0_PREC_F32) {
         for (int64_t i = 0; i < n_items; ++i) {
             if (items[i].M == 0) continue;
-            st = hip_status(q2_0::launch_gemm_f32(static_cast<const uint8_t *>(items[i].w), items[i].M, nb, x, ldx,
-                                                  N, items[i].y, items[i].ldy, s));
+            st = hip_status(q2_0::launch_gemm_f32(static_cast<const uint8_t *>(items[i].w), items[i].M, nb, x, xt,
+                                                  ldx, N, items[i].y, items[i].ldy, s));
             if (st) return st;
         }
         return Q2_0_OK;
@@ -184,27 +258,9 @@ int q2_0_mul_mat_group(const q2_0_mat_vec_item *items, int64_t n_items, int64_t 
     q2_0::GemmMat *mats = n_items <= 64 ? local : new q2_0::GemmMat[n_items];
     for (int64_t i = 0; i < n_items; ++i)
         mats[i] = q2_0::GemmMat{static_cast<const uint8_t *>(items[i].w), items[i].M, items[i].y, items[i].ldy};
-    st = hip_status(q2_0::launch_gemm_f16_group(mats, n_items, nb, x, ldx, N, workspace, s));
+    st = hip_status(q2_0::launch_gemm_f16_group(mats, n_items, nb, x, xt, ldx, N, workspace, s));
     if (mats != local) delete[] mats;
     return st;
 }
 
-const char *q2_0_status_string(int status) {
-    switch (status) {
-        case Q2_0_OK: return "Q2_0_OK";
-        case Q2_0_ERR_NULL: return "Q2_0_ERR_NULL: a required pointer is NULL";
-        case Q2_0_ERR_SHAPE: return "Q2_0_ERR_SHAPE: K must be a positive multiple of 64 and sizes non-negative and within limits";
-        case Q2_0_ERR_LAYOUT: return "Q2_0_ERR_LAYOUT: a leading dimension is smaller than the row length";
-        case Q2_0_ERR_ALIGN: return "Q2_0_ERR_ALIGN: w must be 2-byte aligned and float/int32 buffers 4-byte aligned";
-        case Q2_0_ERR_UNSUPPORTED: return "Q2_0_ERR_UNSUPPORTED: N > 8 for mat-vec, or unknown precision";
-        case Q2_0_ERR_WORKSPACE: return "Q2_0_ERR_WORKSPACE: workspace missing, too small or not 16-byte aligned";
-        case Q2_0_ERR_HIP: return "Q2_0_ERR_HIP: a HIP launch failed";
-        default: return "unknown q2_0 status";
-    }
-}
-
-int q2_0_last_hip_error(void) { return g_last_hip_error; }
-
-const char *q2_0_version(void) { return "q2_0 0.1.0 gfx950"; }
-
-}  // extern "C"
+}  // namespace

@@ -49,16 +49,17 @@ constexpr int GLD = GK + 8;   // fp16 row stride in LDS (144 B): 8 consecutive r
 // are read twice.
 constexpr int kPreGroups = 4;
 
-__device__ __forceinline__ void load16(const float *src, bool vec, float v[16]) {
+template <typename XT>
+__device__ __forceinline__ void load16(const XT *src, bool vec, float v[16]) {
     if (vec) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const float4_t t = reinterpret_cast<const float4_t *>(src)[q];
+            const float4_t t = load_act4(src + 4 * q);
             v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
         }
     } else {
 #pragma unroll
-        for (int q = 0; q < 16; ++q) v[q] = src[q];
+        for (int q = 0; q < 16; ++q) v[q] = act_to_f32(src[q]);
     }
 }
 
@@ -73,13 +74,13 @@ __device__ __forceinline__ void store16_perm(const float v[16], int e, _Float16 
     dst[1] = u32x4_t{o[4], o[5], o[6], o[7]};
 }
 
-template <bool kVec>
-__global__ __launch_bounds__(256) void x_to_f16_perm(const float *__restrict__ x, int64_t ldx, int K,
+template <bool kVec, typename XT>
+__global__ __launch_bounds__(256) void x_to_f16_perm(const XT *__restrict__ x, int64_t ldx, int K,
                                                      _Float16 *__restrict__ x16, int *__restrict__ xe) {
     __shared__ float red[4];
     const int tid = threadIdx.x;
     const int64_t n = blockIdx.x;
-    const float *col = x + n * ldx;
+    const XT *col = x + n * ldx;
     const int groups = K / 16;
     const bool resident = groups <= kPreGroups * 256;
     float v[kPreGroups][16];
@@ -409,8 +410,8 @@ size_t gemm_f16_workspace_bytes(const int64_t *Ms, int64_t n_items, int64_t K, i
     return gemm_layout(Ms, n_items, (int)(K / kBlockWeights), N, &sp, &po);
 }
 
-hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, const float *x, int64_t ldx,
-                                 int64_t N, void *workspace, hipStream_t s) {
+hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, const void *x, Act xt,
+                                 int64_t ldx, int64_t N, void *workspace, hipStream_t s) {
     const int K = nb * kBlockWeights;
     int64_t Ms_local[64];
     int64_t *Ms = n_items <= 64 ? Ms_local : new int64_t[n_items];
@@ -424,11 +425,16 @@ hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, c
     int *xe = reinterpret_cast<int *>(ws + align256((size_t)N * K * 2));
     const int tiles_n = (int)((N + GN - 1) / GN);
 
-    if (((uintptr_t)x % 16 == 0) && (ldx % 4 == 0))
-        x_to_f16_perm<true><<<(unsigned)N, 256, 0, s>>>(x, ldx, K, x16, xe);
-    else
-        x_to_f16_perm<false><<<(unsigned)N, 256, 0, s>>>(x, ldx, K, x16, xe);
-    hipError_t e = hipGetLastError();
+    const bool vec = ((uintptr_t)x % (4 * act_bytes(xt)) == 0) && (ldx % 4 == 0);
+    hipError_t e = with_act(xt, [&](auto tag) -> hipError_t {
+        using XT = decltype(tag);
+        const XT *xp = static_cast<const XT *>(x);
+        if (vec)
+            x_to_f16_perm<true, XT><<<(unsigned)N, 256, 0, s>>>(xp, ldx, K, x16, xe);
+        else
+            x_to_f16_perm<false, XT><<<(unsigned)N, 256, 0, s>>>(xp, ldx, K, x16, xe);
+        return hipGetLastError();
+    });
     if (e != hipSuccess) return e;
 
     // one launch (plus one reduction with a K split) per kGemmMaxGroup matrices

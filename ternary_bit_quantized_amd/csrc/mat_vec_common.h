@@ -129,13 +129,13 @@ __device__ __forceinline__ float max_abs4(float4_t v) {
     return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 }
 
-// Column exponents of x (NC columns of K floats, 16-byte aligned, ldx % 4 == 0) into
-// lds_e[0..NC), computed by the whole workgroup; lds_tmp holds NC floats per wave.
-// Each pass issues up to 8 independent 16-byte loads per thread before reducing, so
-// the scan costs about one memory latency per 8 * nthreads * 16 bytes.  Contains
-// two workgroup barriers, so every thread must call it.
-template <int NC, int TOP = 15>
-__device__ __forceinline__ void column_exponents(const float *__restrict__ x, int64_t ldx, int K,
+// Column exponents of x (NC columns of K activations of type XT, aligned to four
+// elements, ldx % 4 == 0) into lds_e[0..NC), computed by the whole workgroup; lds_tmp
+// holds NC floats per wave.  Each pass issues up to 8 independent 4-element loads per
+// thread before reducing, so the scan costs about one memory latency per pass.
+// Contains two workgroup barriers, so every thread must call it.
+template <int NC, int TOP = 15, typename XT = float>
+__device__ __forceinline__ void column_exponents(const XT *__restrict__ x, int64_t ldx, int K,
                                                  int *lds_e, float *lds_tmp, int tid, int nthreads) {
     constexpr int U = (NC >= 8) ? 1 : 8 / NC;   // loads per column per pass
     const int k4 = K / 4;
@@ -146,11 +146,11 @@ __device__ __forceinline__ void column_exponents(const float *__restrict__ x, in
         float4_t v[NC][U];
 #pragma unroll
         for (int n = 0; n < NC; ++n) {
-            const float4_t *xc = reinterpret_cast<const float4_t *>(x + n * ldx);
+            const XT *xc = x + n * ldx;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int i = base + u * nthreads;
-                v[n][u] = (i < k4) ? xc[i] : float4_t{0.f, 0.f, 0.f, 0.f};
+                v[n][u] = (i < k4) ? load_act4(xc + 4 * i) : float4_t{0.f, 0.f, 0.f, 0.f};
             }
         }
 #pragma unroll
@@ -183,12 +183,12 @@ struct XItem {
     float4_t a, c;
 };
 
-__device__ __forceinline__ XItem load_x_item(const float *__restrict__ x, int64_t ldx, int blk, int mu,
+template <typename XT>
+__device__ __forceinline__ XItem load_x_item(const XT *__restrict__ x, int64_t ldx, int blk, int mu,
                                              int gg, int n) {
     const int odd = blk & 1;
-    const float *xb = x + n * ldx + (int64_t)blk * kBlockWeights + 4 * mu;
-    return XItem{*reinterpret_cast<const float4_t *>(xb + 8 * half_lo(gg, odd)),
-                 *reinterpret_cast<const float4_t *>(xb + 8 * half_hi(gg, odd))};
+    const XT *xb = x + n * ldx + (int64_t)blk * kBlockWeights + 4 * mu;
+    return XItem{load_act4(xb + 8 * half_lo(gg, odd)), load_act4(xb + 8 * half_hi(gg, odd))};
 }
 
 // xe: the column's exponent (x is staged as x * 2^xe).
@@ -208,8 +208,8 @@ __device__ __forceinline__ void store_x_item(const XItem &it, int xe, half8_t *d
 
 // Stage x for blocks 0..nb-1: entry ((b*2 + mu)*4 + g)*2NC + row; lds_e holds the
 // column exponents.
-template <int NC>
-__device__ __forceinline__ void stage_x_all(const float *__restrict__ x, int64_t ldx, int nb,
+template <int NC, typename XT>
+__device__ __forceinline__ void stage_x_all(const XT *__restrict__ x, int64_t ldx, int nb,
                                             const int *lds_e, half8_t *lds_x, int tid, int nthreads) {
     const int items = nb * 2 * 4 * NC;
     for (int q = tid; q < items; q += nthreads) {
@@ -252,7 +252,7 @@ __device__ __forceinline__ void mv_block_pair(const uint8_t *lp, const half8_t *
 
 size_t mat_vec_stream_lds(int N, int nb, int waves);
 int mat_vec_stream_waves(int N, int nb, int *resident);
-hipError_t launch_mat_vec_stream(const MvGroup &grp, int nb, const float *x, int64_t ldx, int N,
+hipError_t launch_mat_vec_stream(const MvGroup &grp, int nb, const void *x, Act xt, int64_t ldx, int N,
                                  hipStream_t s);
 
 }  // namespace q2_0

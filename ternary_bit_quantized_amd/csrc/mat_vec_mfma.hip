@@ -42,9 +42,9 @@ constexpr int kTile = kMvTile;
 
 // NC: activation columns; KS: K slices per workgroup (RG = 4 / KS row tiles);
 // SB: blocks per stage.
-template <int NC, int KS, int SB>
+template <int NC, int KS, int SB, typename XT>
 __global__ __launch_bounds__(256) void mat_vec_mfma(const uint8_t *__restrict__ w, int M, int nb,
-                                                    const float *__restrict__ x, int64_t ldx,
+                                                    const XT *__restrict__ x, int64_t ldx,
                                                     float *__restrict__ y, int64_t ldy) {
     constexpr int RG = 4 / KS;
     constexpr int NR = 2 * NC;                      // A rows that carry data
@@ -174,8 +174,8 @@ __global__ __launch_bounds__(256) void mat_vec_mfma(const uint8_t *__restrict__ 
 
 // Host-side choice of K slices: prefer whole-K waves (cheapest activation staging)
 // while the grid still has at least two workgroups per CU.
-template <int NC>
-static hipError_t launch_nc(const uint8_t *w, int M, int nb, const float *x, int64_t ldx, float *y,
+template <int NC, typename XT>
+static hipError_t launch_nc(const uint8_t *w, int M, int nb, const XT *x, int64_t ldx, float *y,
                             int64_t ldy, hipStream_t s) {
     const int tiles = (M + kTile - 1) / kTile;
     int ks = 1;
@@ -188,33 +188,39 @@ static hipError_t launch_nc(const uint8_t *w, int M, int nb, const float *x, int
     constexpr int SB2 = (NC <= 2) ? 32 : 16;
     constexpr int SB4 = (NC <= 1) ? 32 : ((NC <= 2) ? 16 : 8);
     if (ks == 1)
-        mat_vec_mfma<NC, 1, SB1><<<grid, 256, 0, s>>>(w, M, nb, x, ldx, y, ldy);
+        mat_vec_mfma<NC, 1, SB1, XT><<<grid, 256, 0, s>>>(w, M, nb, x, ldx, y, ldy);
     else if (ks == 2)
-        mat_vec_mfma<NC, 2, SB2><<<grid, 256, 0, s>>>(w, M, nb, x, ldx, y, ldy);
+        mat_vec_mfma<NC, 2, SB2, XT><<<grid, 256, 0, s>>>(w, M, nb, x, ldx, y, ldy);
     else if constexpr (NC <= 4)
-        mat_vec_mfma<NC, 4, SB4><<<grid, 256, 0, s>>>(w, M, nb, x, ldx, y, ldy);
+        mat_vec_mfma<NC, 4, SB4, XT><<<grid, 256, 0, s>>>(w, M, nb, x, ldx, y, ldy);
     return hipGetLastError();
 }
 
-bool mat_vec_mfma_eligible(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx) {
-    return ((uintptr_t)w % 16 == 0) && (nb % 8 == 0) && ((uintptr_t)x % 16 == 0) && (ldx % 4 == 0) &&
-           M <= 0x7fffffff - 64;
+// Rows 16-byte aligned (K/64 % 8 == 0 and w aligned) and x aligned to four elements
+// with ldx % 4 == 0, so that weight chunks and activation quads load as vectors.
+bool mat_vec_mfma_eligible(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx) {
+    return ((uintptr_t)w % 16 == 0) && (nb % 8 == 0) && ((uintptr_t)x % (4 * act_bytes(xt)) == 0) &&
+           (ldx % 4 == 0) && M <= 0x7fffffff - 64;
 }
 
-hipError_t launch_mat_vec_mfma(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx,
+hipError_t launch_mat_vec_mfma(const uint8_t *w, int64_t M, int nb, const void *xv, Act xt, int64_t ldx,
                                int N, float *y, int64_t ldy, hipStream_t s) {
     const int m = (int)M;
-    switch (N) {
-        case 1: return launch_nc<1>(w, m, nb, x, ldx, y, ldy, s);
-        case 2: return launch_nc<2>(w, m, nb, x, ldx, y, ldy, s);
-        case 3: return launch_nc<3>(w, m, nb, x, ldx, y, ldy, s);
-        case 4: return launch_nc<4>(w, m, nb, x, ldx, y, ldy, s);
-        case 5: return launch_nc<5>(w, m, nb, x, ldx, y, ldy, s);
-        case 6: return launch_nc<6>(w, m, nb, x, ldx, y, ldy, s);
-        case 7: return launch_nc<7>(w, m, nb, x, ldx, y, ldy, s);
-        case 8: return launch_nc<8>(w, m, nb, x, ldx, y, ldy, s);
-        default: return hipErrorInvalidValue;
-    }
+    return with_act(xt, [&](auto tag) -> hipError_t {
+        using XT = decltype(tag);
+        const XT *x = static_cast<const XT *>(xv);
+        switch (N) {
+            case 1: return launch_nc<1>(w, m, nb, x, ldx, y, ldy, s);
+            case 2: return launch_nc<2>(w, m, nb, x, ldx, y, ldy, s);
+            case 3: return launch_nc<3>(w, m, nb, x, ldx, y, ldy, s);
+            case 4: return launch_nc<4>(w, m, nb, x, ldx, y, ldy, s);
+            case 5: return launch_nc<5>(w, m, nb, x, ldx, y, ldy, s);
+            case 6: return launch_nc<6>(w, m, nb, x, ldx, y, ldy, s);
+            case 7: return launch_nc<7>(w, m, nb, x, ldx, y, ldy, s);
+            case 8: return launch_nc<8>(w, m, nb, x, ldx, y, ldy, s);
+            default: return hipErrorInvalidValue;
+        }
+    });
 }
 
 }  // namespace q2_0

@@ -90,9 +90,9 @@ struct Item {
 
 }  // namespace
 
-template <int NC, int SB>
+template <int NC, int SB, typename XT>
 __global__ __launch_bounds__(kMvStreamMaxWaves * 64)
-__attribute__((amdgpu_waves_per_eu(4))) void mat_vec_stream(MvGroup grp, int nb, const float *__restrict__ x,
+__attribute__((amdgpu_waves_per_eu(4))) void mat_vec_stream(MvGroup grp, int nb, const XT *__restrict__ x,
                                                       int64_t ldx) {
     constexpr int NR = 2 * NC;
     constexpr int RSB = SB * kBlockBytes + 16;
@@ -323,12 +323,12 @@ int mat_vec_stream_waves(int N, int nb, int *resident) {
     return best;
 }
 
-template <int NC>
-static hipError_t launch_stream_nc(const MvGroup &grp, int nb, const float *x, int64_t ldx,
+template <int NC, typename XT>
+static hipError_t launch_stream_nc(const MvGroup &grp, int nb, const XT *x, int64_t ldx,
                                    hipStream_t s, int grid, int waves) {
     constexpr int SB = kMvStreamSB;
     const size_t lds = mat_vec_stream_lds(NC, nb, waves);
-    auto kern = mat_vec_stream<NC, SB>;
+    auto kern = mat_vec_stream<NC, SB, XT>;
     // Raise the dynamic-LDS cap once per device (idempotent, so a race is harmless).
     static bool configured[64] = {};
     int dev = 0;
@@ -348,7 +348,7 @@ static hipError_t launch_stream_nc(const MvGroup &grp, int nb, const float *x, i
     return hipGetLastError();
 }
 
-hipError_t launch_mat_vec_stream(const MvGroup &grp, int nb, const float *x, int64_t ldx, int N,
+hipError_t launch_mat_vec_stream(const MvGroup &grp, int nb, const void *xv, Act xt, int64_t ldx, int N,
                                  hipStream_t s) {
     int waves = mat_vec_stream_waves(N, nb, nullptr);
     if (waves == 0) return hipErrorInvalidValue;
@@ -363,17 +363,21 @@ hipError_t launch_mat_vec_stream(const MvGroup &grp, int nb, const float *x, int
     int64_t need = (items + waves - 1) / waves;
     if (need > grp.total_tiles) need = grp.total_tiles;
     const int grid = (int)(need < max_grid ? need : max_grid);
-    switch (N) {
-        case 1: return launch_stream_nc<1>(grp, nb, x, ldx, s, grid, waves);
-        case 2: return launch_stream_nc<2>(grp, nb, x, ldx, s, grid, waves);
-        case 3: return launch_stream_nc<3>(grp, nb, x, ldx, s, grid, waves);
-        case 4: return launch_stream_nc<4>(grp, nb, x, ldx, s, grid, waves);
-        case 5: return launch_stream_nc<5>(grp, nb, x, ldx, s, grid, waves);
-        case 6: return launch_stream_nc<6>(grp, nb, x, ldx, s, grid, waves);
-        case 7: return launch_stream_nc<7>(grp, nb, x, ldx, s, grid, waves);
-        case 8: return launch_stream_nc<8>(grp, nb, x, ldx, s, grid, waves);
-        default: return hipErrorInvalidValue;
-    }
+    return with_act(xt, [&](auto tag) -> hipError_t {
+        using XT = decltype(tag);
+        const XT *x = static_cast<const XT *>(xv);
+        switch (N) {
+            case 1: return launch_stream_nc<1>(grp, nb, x, ldx, s, grid, waves);
+            case 2: return launch_stream_nc<2>(grp, nb, x, ldx, s, grid, waves);
+            case 3: return launch_stream_nc<3>(grp, nb, x, ldx, s, grid, waves);
+            case 4: return launch_stream_nc<4>(grp, nb, x, ldx, s, grid, waves);
+            case 5: return launch_stream_nc<5>(grp, nb, x, ldx, s, grid, waves);
+            case 6: return launch_stream_nc<6>(grp, nb, x, ldx, s, grid, waves);
+            case 7: return launch_stream_nc<7>(grp, nb, x, ldx, s, grid, waves);
+            case 8: return launch_stream_nc<8>(grp, nb, x, ldx, s, grid, waves);
+            default: return hipErrorInvalidValue;
+        }
+    });
 }
 
 }  // namespace q2_0

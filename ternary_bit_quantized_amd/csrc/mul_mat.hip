@@ -24,8 +24,9 @@ constexpr int BM = 64, BN = 64, BK = 64;
 
 constexpr int LDF = BM + 4;   // f32 k-major row stride (16-byte multiple)
 
+template <typename XT>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const uint8_t *__restrict__ w, int64_t M,
-                                                       int nb, const float *__restrict__ x,
+                                                       int nb, const XT *__restrict__ x,
                                                        int64_t ldx, int64_t N,
                                                        float *__restrict__ y, int64_t ldy) {
     __shared__ __attribute__((aligned(16))) float Wt[BK][LDF];   // (q-1), k-major
@@ -39,7 +40,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const uint8_t *__restrict
 
     const int64_t lm = m0 + r, ln = n0 + r;
     const uint8_t *wrow = w + (lm < M ? lm : 0) * (int64_t)nb * kBlockBytes;
-    const float *xcol = x + (ln < N ? ln : 0) * ldx;
+    const XT *xcol = x + (ln < N ? ln : 0) * ldx;
 
     double acc[4][4];
 #pragma unroll
@@ -60,9 +61,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const uint8_t *__restrict
             if (wi == 0) Ds[r] = 0.f;
         }
         if (ln < N) {
-            const float *xp = xcol + (int64_t)b * BK + 16 * wi;
+            const XT *xp = xcol + (int64_t)b * BK + 16 * wi;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) Xt[16 * wi + i][r] = xp[i];
+            for (int i = 0; i < 16; ++i) Xt[16 * wi + i][r] = act_to_f32(xp[i]);
         } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i) Xt[16 * wi + i][r] = 0.f;
@@ -104,11 +105,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const uint8_t *__restrict
     }
 }
 
-hipError_t launch_gemm_f32(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx,
+hipError_t launch_gemm_f32(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx,
                            int64_t N, float *y, int64_t ldy, hipStream_t s) {
     dim3 grid((unsigned)((M + BM - 1) / BM), (unsigned)((N + BN - 1) / BN));
-    gemm_f32_kernel<<<grid, 256, 0, s>>>(w, M, nb, x, ldx, N, y, ldy);
-    return hipGetLastError();
+    return with_act(xt, [&](auto tag) -> hipError_t {
+        using XT = decltype(tag);
+        gemm_f32_kernel<XT><<<grid, 256, 0, s>>>(w, M, nb, static_cast<const XT *>(x), ldx, N, y, ldy);
+        return hipGetLastError();
+    });
 }
 
 }  // namespace q2_0

@@ -17,9 +17,9 @@
 
 namespace q2_0 {
 
-template <int NC, bool kVecX>
+template <int NC, bool kVecX, typename XT>
 __global__ __launch_bounds__(256) void mat_vec_generic(const uint8_t *__restrict__ w, int64_t M,
-                                                       int nb, const float *__restrict__ x,
+                                                       int nb, const XT *__restrict__ x,
                                                        int64_t ldx, float *__restrict__ y,
                                                        int64_t ldy) {
     const int lane = threadIdx.x & 63;
@@ -39,17 +39,17 @@ __global__ __launch_bounds__(256) void mat_vec_generic(const uint8_t *__restrict
         for (int i = 0; i < 16; ++i) qm1[i] = (float)((int)((q >> (2 * i)) & 3u) - 1);
 #pragma unroll
         for (int n = 0; n < NC; ++n) {
-            const float *xp = x + n * ldx + t * 16;
+            const XT *xp = x + n * ldx + t * 16;
             float xv[16];
             if (kVecX) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    float4_t v = reinterpret_cast<const float4_t *>(xp)[j];
+                    const float4_t v = load_act4(xp + 4 * j);
                     xv[4 * j] = v.x; xv[4 * j + 1] = v.y; xv[4 * j + 2] = v.z; xv[4 * j + 3] = v.w;
                 }
             } else {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) xv[i] = xp[i];
+                for (int i = 0; i < 16; ++i) xv[i] = act_to_f32(xp[i]);
             }
             float s = 0.f;
 #pragma unroll
@@ -66,14 +66,14 @@ __global__ __launch_bounds__(256) void mat_vec_generic(const uint8_t *__restrict
     }
 }
 
-template <int NC>
-static void launch_generic_nc(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx,
+template <int NC, typename XT>
+static void launch_generic_nc(const uint8_t *w, int64_t M, int nb, const XT *x, int64_t ldx,
                               float *y, int64_t ldy, hipStream_t s, bool vec) {
     dim3 grid((unsigned)((M + 3) / 4));
     if (vec)
-        mat_vec_generic<NC, true><<<grid, 256, 0, s>>>(w, M, nb, x, ldx, y, ldy);
+        mat_vec_generic<NC, true, XT><<<grid, 256, 0, s>>>(w, M, nb, x, ldx, y, ldy);
     else
-        mat_vec_generic<NC, false><<<grid, 256, 0, s>>>(w, M, nb, x, ldx, y, ldy);
+        mat_vec_generic<NC, false, XT><<<grid, 256, 0, s>>>(w, M, nb, x, ldx, y, ldy);
 }
 
 // Fast-path choice.  Rows 16-byte aligned and x 16-byte aligned: the MFMA kernels.
@@ -89,36 +89,40 @@ static bool stream_fits(int N, int nb) {
     return mat_vec_stream_waves(N, nb, &resident) > 0 && resident >= 8;
 }
 
-hipError_t launch_mat_vec(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx, int N,
+hipError_t launch_mat_vec(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx, int N,
                           float *y, int64_t ldy, hipStream_t s) {
-    if (mat_vec_mfma_eligible(w, M, nb, x, ldx)) {
+    if (mat_vec_mfma_eligible(w, M, nb, x, xt, ldx)) {
         if ((M + kMvTile - 1) / kMvTile >= kStreamTiles && stream_fits(N, nb)) {
             MvGroup grp;
             grp.n = 1;
             grp.p[0] = MvProblem{w, y, ldy, (int)M, 0};
             for (int i = 0; i <= kMvMaxGroup; ++i) grp.tile0[i] = i ? INT_MAX : 0;
             grp.total_tiles = (int)((M + kMvTile - 1) / kMvTile);
-            return launch_mat_vec_stream(grp, nb, x, ldx, N, s);
+            return launch_mat_vec_stream(grp, nb, x, xt, ldx, N, s);
         }
-        return launch_mat_vec_mfma(w, M, nb, x, ldx, N, y, ldy, s);
+        return launch_mat_vec_mfma(w, M, nb, x, xt, ldx, N, y, ldy, s);
     }
-    const bool vec = ((uintptr_t)x % 16 == 0) && (ldx % 4 == 0);
-    switch (N) {
-        case 1: launch_generic_nc<1>(w, M, nb, x, ldx, y, ldy, s, vec); break;
-        case 2: launch_generic_nc<2>(w, M, nb, x, ldx, y, ldy, s, vec); break;
-        case 3: launch_generic_nc<3>(w, M, nb, x, ldx, y, ldy, s, vec); break;
-        case 4: launch_generic_nc<4>(w, M, nb, x, ldx, y, ldy, s, vec); break;
-        case 5: launch_generic_nc<5>(w, M, nb, x, ldx, y, ldy, s, vec); break;
-        case 6: launch_generic_nc<6>(w, M, nb, x, ldx, y, ldy, s, vec); break;
-        case 7: launch_generic_nc<7>(w, M, nb, x, ldx, y, ldy, s, vec); break;
-        case 8: launch_generic_nc<8>(w, M, nb, x, ldx, y, ldy, s, vec); break;
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    const bool vec = ((uintptr_t)x % (4 * act_bytes(xt)) == 0) && (ldx % 4 == 0);
+    return with_act(xt, [&](auto tag) -> hipError_t {
+        using XT = decltype(tag);
+        const XT *xp = static_cast<const XT *>(x);
+        switch (N) {
+            case 1: launch_generic_nc<1>(w, M, nb, xp, ldx, y, ldy, s, vec); break;
+            case 2: launch_generic_nc<2>(w, M, nb, xp, ldx, y, ldy, s, vec); break;
+            case 3: launch_generic_nc<3>(w, M, nb, xp, ldx, y, ldy, s, vec); break;
+            case 4: launch_generic_nc<4>(w, M, nb, xp, ldx, y, ldy, s, vec); break;
+            case 5: launch_generic_nc<5>(w, M, nb, xp, ldx, y, ldy, s, vec); break;
+            case 6: launch_generic_nc<6>(w, M, nb, xp, ldx, y, ldy, s, vec); break;
+            case 7: launch_generic_nc<7>(w, M, nb, xp, ldx, y, ldy, s, vec); break;
+            case 8: launch_generic_nc<8>(w, M, nb, xp, ldx, y, ldy, s, vec); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    });
 }
 
 hipError_t launch_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items, int nb,
-                                const float *x, int64_t ldx, int N, hipStream_t s) {
+                                const void *x, Act xt, int64_t ldx, int N, hipStream_t s) {
     int64_t i = 0;
     while (i < n_items) {
         // Gather up to kMvMaxGroup consecutive stream-eligible matrices into one launch.
@@ -129,11 +133,11 @@ hipError_t launch_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items,
             const q2_0_mat_vec_item &it = items[i];
             const uint8_t *w = static_cast<const uint8_t *>(it.w);
             if (it.M == 0) { ++i; continue; }
-            const bool ok = mat_vec_mfma_eligible(w, it.M, nb, x, ldx) && stream_fits(N, nb) &&
+            const bool ok = mat_vec_mfma_eligible(w, it.M, nb, x, xt, ldx) && stream_fits(N, nb) &&
                             tiles + (it.M + kMvTile - 1) / kMvTile < 0x7fffffff;
             if (!ok) {
                 if (grp.n) break;   // launch what is gathered first
-                hipError_t e = launch_mat_vec(w, it.M, nb, x, ldx, N, it.y, it.ldy, s);
+                hipError_t e = launch_mat_vec(w, it.M, nb, x, xt, ldx, N, it.y, it.ldy, s);
                 if (e != hipSuccess) return e;
                 ++i;
                 continue;
@@ -146,7 +150,7 @@ hipError_t launch_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items,
         if (grp.n) {
             for (int k = grp.n; k <= kMvMaxGroup; ++k) grp.tile0[k] = INT_MAX;
             grp.total_tiles = tiles;
-            hipError_t e = launch_mat_vec_stream(grp, nb, x, ldx, N, s);
+            hipError_t e = launch_mat_vec_stream(grp, nb, x, xt, ldx, N, s);
             if (e != hipSuccess) return e;
         }
     }

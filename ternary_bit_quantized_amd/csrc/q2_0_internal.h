@@ -23,6 +23,56 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
 }
 
+// ---- activation element types (Q2_0_ACT_*).  Every kernel reads activations through
+// these helpers and computes on the exact f32 value of each element.
+enum class Act { F32 = Q2_0_ACT_F32, F16 = Q2_0_ACT_F16, BF16 = Q2_0_ACT_BF16 };
+
+struct bf16_t {   // bfloat16: the upper 16 bits of an IEEE single
+    uint16_t bits;
+};
+
+inline int act_bytes(Act a) { return a == Act::F32 ? 4 : 2; }
+
+__device__ __forceinline__ float act_to_f32(float v) { return v; }
+__device__ __forceinline__ float act_to_f32(_Float16 v) { return (float)v; }
+__device__ __forceinline__ float act_to_f32(bf16_t v) { return __builtin_bit_cast(float, (uint32_t)v.bits << 16); }
+
+// Four consecutive activations as f32; p is aligned to four elements (16 bytes for
+// f32, 8 bytes for the 16-bit types).
+template <typename XT>
+__device__ __forceinline__ float4_t load_act4(const XT *p);
+
+template <>
+__device__ __forceinline__ float4_t load_act4<float>(const float *p) {
+    return *reinterpret_cast<const float4_t *>(p);
+}
+
+template <>
+__device__ __forceinline__ float4_t load_act4<_Float16>(const _Float16 *p) {
+    typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+    const half4_t v = *reinterpret_cast<const half4_t *>(p);
+    return float4_t{(float)v.x, (float)v.y, (float)v.z, (float)v.w};
+}
+
+template <>
+__device__ __forceinline__ float4_t load_act4<bf16_t>(const bf16_t *p) {
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    const u32x2_t v = *reinterpret_cast<const u32x2_t *>(p);
+    return float4_t{__builtin_bit_cast(float, v.x << 16), __builtin_bit_cast(float, v.x & 0xffff0000u),
+                    __builtin_bit_cast(float, v.y << 16), __builtin_bit_cast(float, v.y & 0xffff0000u)};
+}
+
+// Runs f(XT{}) with XT the element type of a (host side).
+template <typename F>
+inline hipError_t with_act(Act a, F &&f) {
+    switch (a) {
+        case Act::F32: return f(float{});
+        case Act::F16: return f(_Float16{});
+        case Act::BF16: return f(bf16_t{});
+    }
+    return hipErrorInvalidValue;
+}
+
 // Scale and one 32-bit code word of block `blk` from a 2-byte aligned block base.
 // Word w sits at byte 2 + 4w: 4-byte aligned only for odd blocks of an aligned row,
 // so it is read as two half-words.
@@ -33,12 +83,13 @@ __device__ __forceinline__ uint32_t load_word_u16x2(const uint16_t *blk16, int w
 // Launchers (return the HIP error of the launch).
 hipError_t launch_get_rows(const uint8_t *w, int64_t M, int nb, const int32_t *ids, int64_t n_ids,
                            float *out, int64_t ld_out, hipStream_t s);
-hipError_t launch_mat_vec(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx, int N,
+// x points at activations of element type xt; ldx counts elements.
+hipError_t launch_mat_vec(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx, int N,
                           float *y, int64_t ldy, hipStream_t s);
 hipError_t launch_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items, int nb,
-                                const float *x, int64_t ldx, int N, hipStream_t s);
-bool mat_vec_mfma_eligible(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx);
-hipError_t launch_mat_vec_mfma(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx,
+                                const void *x, Act xt, int64_t ldx, int N, hipStream_t s);
+bool mat_vec_mfma_eligible(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx);
+hipError_t launch_mat_vec_mfma(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx,
                                int N, float *y, int64_t ldy, hipStream_t s);
 // fp16-MFMA GEMM over one or more matrices that share K and x.
 struct GemmMat {
@@ -63,9 +114,9 @@ struct GemmGroup {
     int tm_base;              // first row tile of this launch
 };
 size_t gemm_f16_workspace_bytes(const int64_t *Ms, int64_t n_items, int64_t K, int64_t N);
-hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, const float *x, int64_t ldx,
-                                 int64_t N, void *workspace, hipStream_t s);
-hipError_t launch_gemm_f32(const uint8_t *w, int64_t M, int nb, const float *x, int64_t ldx,
+hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, const void *x, Act xt,
+                                 int64_t ldx, int64_t N, void *workspace, hipStream_t s);
+hipError_t launch_gemm_f32(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx,
                            int64_t N, float *y, int64_t ldy, hipStream_t s);
 
 }  // namespace q2_0

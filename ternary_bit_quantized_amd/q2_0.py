@@ -24,12 +24,16 @@ Q2_0_ERR_WORKSPACE = 6
 Q2_0_ERR_HIP = 7
 Q2_0_PREC_F16_MFMA = 0
 Q2_0_PREC_F32 = 1
+Q2_0_ACT_F32 = 0
+Q2_0_ACT_F16 = 1
+Q2_0_ACT_BF16 = 2
 BLOCK_WEIGHTS = 64
 BLOCK_BYTES = 18
 MAT_VEC_MAX_N = 8
 
 EXPORTS = ("q2_0_get_rows", "q2_0_mul_mat_vec", "q2_0_mul_mat_vec_group", "q2_0_mul_mat",
            "q2_0_mul_mat_workspace_bytes", "q2_0_mul_mat_group", "q2_0_mul_mat_group_workspace_bytes",
+           "q2_0_mul_mat_vec_act", "q2_0_mul_mat_vec_group_act", "q2_0_mul_mat_act", "q2_0_mul_mat_group_act",
            "q2_0_status_string", "q2_0_last_hip_error", "q2_0_version")
 
 
@@ -80,6 +84,14 @@ def lib() -> ctypes.CDLL:
         L.q2_0_mul_mat_group.restype = ctypes.c_int
         L.q2_0_mul_mat_group_workspace_bytes.argtypes = [P, I64, I64, I64, ctypes.c_int]
         L.q2_0_mul_mat_group_workspace_bytes.restype = ctypes.c_size_t
+        C = ctypes.c_int
+        L.q2_0_mul_mat_vec_act.argtypes = [P, I64, I64, P, C, I64, I64, P, I64, P]
+        L.q2_0_mul_mat_vec_group_act.argtypes = [P, I64, I64, P, C, I64, I64, P]
+        L.q2_0_mul_mat_act.argtypes = [P, I64, I64, P, C, I64, I64, P, I64, C, P, ctypes.c_size_t, P]
+        L.q2_0_mul_mat_group_act.argtypes = [P, I64, I64, P, C, I64, I64, C, P, ctypes.c_size_t, P]
+        for f in (L.q2_0_mul_mat_vec_act, L.q2_0_mul_mat_vec_group_act, L.q2_0_mul_mat_act,
+                  L.q2_0_mul_mat_group_act):
+            f.restype = ctypes.c_int
         L.q2_0_status_string.argtypes = [ctypes.c_int]
         L.q2_0_status_string.restype = ctypes.c_char_p
         L.q2_0_version.restype = ctypes.c_char_p
@@ -137,6 +149,27 @@ def mul_mat_group_workspace_bytes(items, n_items: int, K: int, N: int, precision
     return int(lib().q2_0_mul_mat_group_workspace_bytes(_items_ptr(items), n_items, K, N, precision))
 
 
+def mul_mat_vec_act_raw(w: int, M: int, K: int, x: int, x_type: int, ldx: int, N: int, y: int, ldy: int,
+                        stream: int = 0) -> int:
+    return lib().q2_0_mul_mat_vec_act(w, M, K, x, x_type, ldx, N, y, ldy, stream)
+
+
+def mul_mat_vec_group_act_raw(items, n_items: int, K: int, x: int, x_type: int, ldx: int, N: int,
+                              stream: int = 0) -> int:
+    return lib().q2_0_mul_mat_vec_group_act(_items_ptr(items), n_items, K, x, x_type, ldx, N, stream)
+
+
+def mul_mat_act_raw(w: int, M: int, K: int, x: int, x_type: int, ldx: int, N: int, y: int, ldy: int,
+                    precision: int, workspace: int, ws_bytes: int, stream: int = 0) -> int:
+    return lib().q2_0_mul_mat_act(w, M, K, x, x_type, ldx, N, y, ldy, precision, workspace, ws_bytes, stream)
+
+
+def mul_mat_group_act_raw(items, n_items: int, K: int, x: int, x_type: int, ldx: int, N: int, precision: int,
+                          workspace: int, ws_bytes: int, stream: int = 0) -> int:
+    return lib().q2_0_mul_mat_group_act(_items_ptr(items), n_items, K, x, x_type, ldx, N, precision,
+                                        workspace, ws_bytes, stream)
+
+
 def version() -> str:
     return lib().q2_0_version().decode()
 
@@ -161,6 +194,19 @@ def _cols(t, K, name):
     return t.data_ptr(), t.shape[0], ld
 
 
+def _xcols(t, K, name):
+    """An activation tensor (N, >=K) of float32, float16 or bfloat16 with unit inner stride
+    -> (ptr, N, ld, x_type)."""
+    import torch
+    types = {torch.float32: Q2_0_ACT_F32, torch.float16: Q2_0_ACT_F16, torch.bfloat16: Q2_0_ACT_BF16}
+    if t.dtype not in types or not t.is_cuda or t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("%s must be a 2-D float32/float16/bfloat16 CUDA tensor with unit inner stride" % name)
+    if t.shape[1] < K:
+        raise ValueError("%s must have at least %d columns" % (name, K))
+    ld = t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
+    return t.data_ptr(), t.shape[0], ld, types[t.dtype]
+
+
 def q2_0_get_rows(w, M: int, K: int, ids, out=None, stream=None):
     """out[r, :K] = dequantized row ids[r] of the (M, K) Q2_0 matrix w (uint8 device tensor)."""
     import torch
@@ -176,21 +222,22 @@ def q2_0_get_rows(w, M: int, K: int, ids, out=None, stream=None):
 
 
 def q2_0_mul_mat_vec(w, M: int, K: int, x, y=None, stream=None):
-    """y (N, M) = W x for x (N, K), N <= 8."""
+    """y (N, M) = W x for x (N, K) of float32, float16 or bfloat16, N <= 8; y is float32."""
     import torch
-    xp, N, ldx = _cols(x, K, "x")
+    xp, N, ldx, xt = _xcols(x, K, "x")
     if y is None:
         y = torch.empty((N, M), dtype=torch.float32, device=x.device)
     yp, _, ldy = _cols(y, M, "y")
-    _check(mul_mat_vec_raw(w.data_ptr(), M, K, xp, ldx, N, yp, ldy, _stream(stream)),
-           "q2_0_mul_mat_vec")
+    _check(mul_mat_vec_act_raw(w.data_ptr(), M, K, xp, xt, ldx, N, yp, ldy, _stream(stream)),
+           "q2_0_mul_mat_vec_act")
     return y
 
 
 def q2_0_mul_mat_vec_group(mats, K: int, x, ys=None, stream=None):
-    """mats: [(w, M), ...] sharing K; returns [y_i (N, M_i)] with y_i = W_i x."""
+    """mats: [(w, M), ...] sharing K; returns [y_i (N, M_i)] with y_i = W_i x (x float32, float16
+    or bfloat16)."""
     import torch
-    xp, N, ldx = _cols(x, K, "x")
+    xp, N, ldx, xt = _xcols(x, K, "x")
     if ys is None:
         ys = [torch.empty((N, M), dtype=torch.float32, device=x.device) for (_, M) in mats]
     entries = []
@@ -198,16 +245,16 @@ def q2_0_mul_mat_vec_group(mats, K: int, x, ys=None, stream=None):
         yp, _, ldy = _cols(y, M, "y")
         entries.append((w.data_ptr(), M, yp, ldy))
     items = make_items(entries)
-    _check(mul_mat_vec_group_raw(items, len(entries), K, xp, ldx, N, _stream(stream)),
-           "q2_0_mul_mat_vec_group")
+    _check(mul_mat_vec_group_act_raw(items, len(entries), K, xp, xt, ldx, N, _stream(stream)),
+           "q2_0_mul_mat_vec_group_act")
     return ys
 
 
 def q2_0_mul_mat(w, M: int, K: int, x, precision: int = Q2_0_PREC_F16_MFMA, y=None, workspace=None,
                  stream=None):
-    """y (N, M) = W x for x (N, K), any N."""
+    """y (N, M) = W x for x (N, K) of float32, float16 or bfloat16, any N; y is float32."""
     import torch
-    xp, N, ldx = _cols(x, K, "x")
+    xp, N, ldx, xt = _xcols(x, K, "x")
     if y is None:
         y = torch.empty((N, M), dtype=torch.float32, device=x.device)
     yp, _, ldy = _cols(y, M, "y")
@@ -216,16 +263,17 @@ def q2_0_mul_mat(w, M: int, K: int, x, precision: int = Q2_0_PREC_F16_MFMA, y=No
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wsp = workspace.data_ptr() if workspace is not None else 0
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(mul_mat_raw(w.data_ptr(), M, K, xp, ldx, N, yp, ldy, precision, wsp, wsb, _stream(stream)),
-           "q2_0_mul_mat")
+    _check(mul_mat_act_raw(w.data_ptr(), M, K, xp, xt, ldx, N, yp, ldy, precision, wsp, wsb, _stream(stream)),
+           "q2_0_mul_mat_act")
     return y
 
 
 def q2_0_mul_mat_group(mats, K: int, x, precision: int = Q2_0_PREC_F16_MFMA, ys=None, workspace=None,
                        stream=None):
-    """mats: [(w, M), ...] sharing K; returns [y_i (N, M_i)] with y_i = W_i x, any N."""
+    """mats: [(w, M), ...] sharing K; returns [y_i (N, M_i)] with y_i = W_i x, any N (x float32,
+    float16 or bfloat16)."""
     import torch
-    xp, N, ldx = _cols(x, K, "x")
+    xp, N, ldx, xt = _xcols(x, K, "x")
     if ys is None:
         ys = [torch.empty((N, M), dtype=torch.float32, device=x.device) for (_, M) in mats]
     entries = []
@@ -238,6 +286,6 @@ def q2_0_mul_mat_group(mats, K: int, x, precision: int = Q2_0_PREC_F16_MFMA, ys=
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wsp = workspace.data_ptr() if workspace is not None else 0
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(mul_mat_group_raw(items, len(entries), K, xp, ldx, N, precision, wsp, wsb, _stream(stream)),
-           "q2_0_mul_mat_group")
+    _check(mul_mat_group_act_raw(items, len(entries), K, xp, xt, ldx, N, precision, wsp, wsb, _stream(stream)),
+           "q2_0_mul_mat_group_act")
     return ys

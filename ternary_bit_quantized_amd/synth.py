@@ -141,6 +141,23 @@ def activations(seed: int, layer: int, matrix: int, N: int, K: int) -> np.ndarra
     return rng_for(seed, layer, matrix, STREAM_X).standard_normal((N, K), dtype=np.float32)
 
 
+def to_f16(x: np.ndarray) -> np.ndarray:
+    """Activations as IEEE half (round to nearest even), for the 16-bit activation inputs."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16)
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Finite f32 activations rounded to bfloat16 (nearest, ties to even), as uint16 bits."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """The exact f32 value of bfloat16 bit patterns (the upper half of an IEEE single)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
 def row_ids(seed: int, layer: int, matrix: int, n: int, M: int) -> np.ndarray:
     return rng_for(seed, layer, matrix, STREAM_IDS).integers(0, M, size=n, dtype=np.int64).astype(np.int32)
 

@@ -150,3 +150,32 @@ def test_gemm_group_validation_and_workspace():
     g = B.mul_mat_group_workspace_bytes(big, 3, 4096, 512, B.Q2_0_PREC_F16_MFMA)
     singles = [B.mul_mat_workspace_bytes(M, 4096, 512, B.Q2_0_PREC_F16_MFMA) for M in (4096, 1024, 1024)]
     assert 512 * 4096 * 2 < g < sum(singles)   # x staged once, fewer splits than the small singles
+
+
+def test_activation_type_validation():
+    """The *_act entry points: an unknown activation type is UNSUPPORTED (checked before the
+    alignment, which depends on it), 16-bit activations need 2-byte alignment only, and
+    everything else is validated as for the F32 calls."""
+    F16, BF16 = B.Q2_0_ACT_F16, B.Q2_0_ACT_BF16
+    for bad in (-1, 3, 99):
+        assert B.mul_mat_vec_act_raw(P16, 10, 64, P16 + 1, bad, 64, 1, P16, 10) == B.Q2_0_ERR_UNSUPPORTED
+        assert B.mul_mat_act_raw(P16, 10, 64, P16, bad, 64, 20, P16, 10, 0, P16, 1 << 20) == B.Q2_0_ERR_UNSUPPORTED
+    for xt in (F16, BF16):
+        # a 2-byte offset is fine for 16-bit activations (passes validation), an odd address is not
+        assert B.mul_mat_vec_act_raw(P16, 10, 64, P16 + 1, xt, 64, 1, P16, 10) == B.Q2_0_ERR_ALIGN
+        assert B.mul_mat_act_raw(P16, 10, 64, P16 + 1, xt, 64, 20, P16, 10, 0, P16, 1 << 20) == B.Q2_0_ERR_ALIGN
+        assert B.mul_mat_vec_act_raw(P16, 10, 64, P16 + 2, xt, 64, 9, P16, 10) == B.Q2_0_ERR_UNSUPPORTED
+        assert B.mul_mat_vec_act_raw(P16, 10, 64, P16 + 2, xt, 63, 1, P16, 10) == B.Q2_0_ERR_LAYOUT
+        assert B.mul_mat_vec_act_raw(P16, 10, 100, P16, xt, 100, 1, P16, 10) == B.Q2_0_ERR_SHAPE
+        assert B.mul_mat_vec_act_raw(P16, 0, 64, 0, xt, 64, 1, 0, 0) == B.Q2_0_OK
+        assert B.mul_mat_vec_act_raw(P16, 10, 64, 0, xt, 64, 1, P16, 10) == B.Q2_0_ERR_NULL
+        need = B.mul_mat_workspace_bytes(10, 64, 20, B.Q2_0_PREC_F16_MFMA)
+        assert B.mul_mat_act_raw(P16, 10, 64, P16 + 2, xt, 64, 20, P16, 10, 0, P16, need - 1) == B.Q2_0_ERR_WORKSPACE
+        items = B.make_items([(P16, 10, P16, 10), (P16, 5, P16 + 2, 5)])
+        assert B.mul_mat_vec_group_act_raw(items, 2, 64, P16 + 2, xt, 64, 1) == B.Q2_0_ERR_ALIGN   # y of item 1
+        assert B.mul_mat_group_act_raw(items, 2, 64, P16 + 2, xt, 64, 20, 0, P16, 1 << 20) == B.Q2_0_ERR_ALIGN
+        ok = B.make_items([(P16, 10, P16, 10)])
+        assert B.mul_mat_vec_group_act_raw(ok, 1, 64, P16 + 1, xt, 64, 1) == B.Q2_0_ERR_ALIGN
+        assert B.mul_mat_group_act_raw(ok, 1, 64, P16, 7, 64, 20, 0, P16, 1 << 20) == B.Q2_0_ERR_UNSUPPORTED
+    # F32 through the *_act entry keeps the 4-byte rule
+    assert B.mul_mat_vec_act_raw(P16, 10, 64, P16 + 2, B.Q2_0_ACT_F32, 64, 1, P16, 10) == B.Q2_0_ERR_ALIGN

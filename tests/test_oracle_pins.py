@@ -359,3 +359,28 @@ def test_synth_distributions_and_determinism():
     assert abs((dv == 0).mean() - 0.01) < 0.003
     nz = dv[dv != 0]
     assert nz.min() >= np.float16(1e-3) and nz.max() <= np.float16(1e-1)
+
+
+# --------------------------------------------------------------- 16-bit activation inputs
+
+def test_bf16_input_helpers_against_known_patterns_and_torch():
+    """The bfloat16 input helpers: known bit patterns decode to their textbook values, and
+    rounding f32 -> bf16 is round-to-nearest-even as torch's own CPU conversion."""
+    import torch
+    bits = np.array([0x3F80, 0xC000, 0x0000, 0x8000, 0x7F7F, 0x0001, 0x4049], dtype=np.uint16)
+    vals = synth.bf16_bits_to_f32(bits)
+    assert vals[0] == 1.0 and vals[1] == -2.0 and vals[2] == 0.0 and np.signbit(vals[3])
+    assert vals[4] == np.float32(2.0 ** 127 * (1 + 127 / 128))   # largest finite bf16
+    assert vals[5] == np.float32(2.0 ** -133)                     # smallest subnormal bf16
+    assert vals[6] == np.float32(3.140625)
+    # ties: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 -> even (1.0); 1 + 3*2^-8 -> 1 + 2^-6
+    ties = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8)], dtype=np.float32)
+    assert list(synth.bf16_bits_to_f32(synth.to_bf16_bits(ties))) == [1.0, 1 + 2.0 ** -6, -1.0]
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(20000) * np.exp(rng.uniform(-30, 30, 20000))).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(synth.to_bf16_bits(x), ref)
+    # every bf16 value is exact in f32 and round-trips
+    allb = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    fin = np.isfinite(synth.bf16_bits_to_f32(allb))
+    assert np.array_equal(synth.to_bf16_bits(synth.bf16_bits_to_f32(allb[fin])), allb[fin])
