@@ -205,6 +205,37 @@ int q2_0_mul_mat_group_act(const q2_0_mat_vec_item *items, int64_t n_items, int6
                            int x_type, int64_t ldx, int64_t N, int precision, void *workspace,
                            size_t ws_bytes, void *stream);
 
+/*
+ * quantize: f32 weights -> Q2_0 by the reference quantizer (aisvetem.cz, "Llama.cpp
+ * umi dvoubitovy Q2_0 i na kartach NVIDIA", section "Na bezny model to neni": the
+ * block's largest |w| is the scale and each weight goes to the nearest level).
+ * Per block of 64: d = max|w| rounded to the nearest half (ties to even; at or
+ * above 65520 it is +inf); each weight takes the nearest of -d, 0, d, 2d, a weight
+ * exactly between two levels the one nearer zero; a block whose d is 0 (or inf) is
+ * code 1 everywhere.  Code 3 is therefore never produced.
+ *   src   : M rows of K floats (device), row m at src + m*ld_src, ld_src >= K,
+ *           4-byte aligned; finite values (NaN / inf inputs are out of contract).
+ *   w     : M x K Q2_0 output (device, layout above), 2-byte aligned; must not
+ *           overlap src.
+ * Errors: SHAPE, the M == 0 no-op, NULL, LAYOUT (ld_src < K), ALIGN.
+ */
+int q2_0_quantize(const float *src, int64_t M, int64_t K, int64_t ld_src, void *w, void *stream);
+
+/*
+ * repack_g128: the older group-128 packing (34 bytes per 128 weights; aisvetem.cz,
+ * same article, sections "Sest procent, o ktera se vedl spor" and the closing
+ * paragraph on the two kinds of files) -> Q2_0 with group 64, losslessly.  Read as
+ * the group-64 block extended: a little-endian half scale d, then eight
+ * little-endian 32-bit words, code i of word w belonging to weight 16w+i.  Legacy
+ * block j of a row becomes blocks 2j and 2j+1 of the output row, both with scale d,
+ * holding words 0..3 and 4..7.
+ *   w128  : M rows of K/128 legacy blocks (device), row m at byte m*(K/128)*34,
+ *           2-byte aligned.
+ *   w     : M x K Q2_0 output (device), 2-byte aligned; must not overlap w128.
+ * Errors: SHAPE (also K % 128 != 0), the M == 0 no-op, NULL, ALIGN.
+ */
+int q2_0_repack_g128(const void *w128, int64_t M, int64_t K, void *w, void *stream);
+
 /* A static, human-readable name for a status code. */
 const char *q2_0_status_string(int status);
 

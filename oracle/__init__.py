@@ -55,10 +55,13 @@ def lib():
         L.oracle_get_rows.argtypes = [P, I64, I64, P, I64, P, I64]
         L.oracle_mul_mat_rows.argtypes = [P, I64, I64, P, I64, I64, P, I64, P, P, I64]
         L.oracle_quantize_ref.argtypes = [P, I64, I64, P]
+        L.oracle_dequant_g128_row.argtypes = [P, I64, I64, P]
+        L.oracle_repack_g128.argtypes = [P, I64, I64, P]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_set_num_threads.argtypes = [ctypes.c_int]
         for f in (L.oracle_dequant_row, L.oracle_get_rows, L.oracle_mul_mat_rows,
-                  L.oracle_quantize_ref, L.oracle_set_num_threads):
+                  L.oracle_quantize_ref, L.oracle_set_num_threads, L.oracle_dequant_g128_row,
+                  L.oracle_repack_g128):
             f.restype = None
         _lib = L
     return _lib
@@ -132,6 +135,25 @@ def quantize_ref(wf: np.ndarray) -> np.ndarray:
     assert K % BLOCK_WEIGHTS == 0
     out = np.zeros((M, K // BLOCK_WEIGHTS * BLOCK_BYTES), dtype=np.uint8)
     lib().oracle_quantize_ref(_p(wf), M, K, _p(out))
+    return out
+
+
+def dequant_g128(w128: np.ndarray, M: int, K: int) -> np.ndarray:
+    """Legacy group-128 matrix (M rows of K/128 34-byte blocks) -> dense fp64 (M, K)."""
+    w128 = np.ascontiguousarray(w128, dtype=np.uint8)
+    assert K % 128 == 0 and w128.size == M * (K // 128) * 34
+    out = np.zeros((M, K), dtype=np.float64)
+    for m in range(M):
+        lib().oracle_dequant_g128_row(_p(w128), K, m, _p(out[m]))
+    return out
+
+
+def repack_g128(w128: np.ndarray, M: int, K: int) -> np.ndarray:
+    """Legacy group-128 matrix -> Q2_0 group 64 (M, K/64*18) uint8."""
+    w128 = np.ascontiguousarray(w128, dtype=np.uint8)
+    assert K % 128 == 0 and w128.size == M * (K // 128) * 34
+    out = np.zeros((M, K // BLOCK_WEIGHTS * BLOCK_BYTES), dtype=np.uint8)
+    lib().oracle_repack_g128(_p(w128), M, K, _p(out))
     return out
 
 

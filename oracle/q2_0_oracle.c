@@ -29,6 +29,9 @@
  *  - Quantizer: the scale is the half nearest (ties to even) to max |w|; codes
  *    are chosen against that rounded scale; a tie goes to the level nearer zero;
  *    a block whose rounded scale is 0 gets code 1 everywhere.
+ *  - The older group-128 packing ([P3], section "Sest procent, o ktera se vedl
+ *    spor": 34 bytes per 128 weights) is the group-64 block extended: a half scale,
+ *    then eight little-endian words, code i of word w for weight 16w+i.
  *
  * Every function is a direct loop over the definition; parallelism is only
  * across independent output rows (OpenMP), never inside a sum.
@@ -211,6 +214,39 @@ void oracle_quantize_ref(const float *src, int64_t M, int64_t K, uint8_t *dst) {
             }
         }
     }
+}
+
+/* Legacy group-128 packing: dequantize row m (K/128 blocks of 34 bytes) into
+ * out[0..K) as (q - 1) * d in fp64.  Weight j of a block is code j%16 of word j/16:
+ * byte 2 + 4*(j/16) + (j%16)/4, bits 2*(j%4)..2*(j%4)+1. */
+void oracle_dequant_g128_row(const uint8_t *w128, int64_t K, int64_t m, double *out) {
+    int64_t nb = K / 128;
+    for (int64_t blk = 0; blk < nb; ++blk) {
+        const uint8_t *b = w128 + (m * nb + blk) * 34;
+        double d = oracle_half_to_double((uint16_t)(b[0] | (b[1] << 8)));
+        for (int j = 0; j < 128; ++j) {
+            int w = j / 16, i = j % 16;
+            int q = (b[2 + 4 * w + i / 4] >> (2 * (i % 4))) & 3;
+            out[blk * 128 + j] = (double)(q - 1) * d;
+        }
+    }
+}
+
+/* Legacy group-128 -> group 64: block j of a row becomes blocks 2j and 2j+1, each
+ * with the legacy scale bytes, holding the code bytes of weights 0..63 and
+ * 64..127 (bytes 2..17 and 18..33 of the legacy block). */
+void oracle_repack_g128(const uint8_t *w128, int64_t M, int64_t K, uint8_t *dst) {
+    int64_t nb = K / 128;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t blk = 0; blk < nb; ++blk) {
+            const uint8_t *b = w128 + (m * nb + blk) * 34;
+            for (int h = 0; h < 2; ++h) {
+                uint8_t *o = dst + ((m * nb + blk) * 2 + h) * O_BLOCK_BYTES;
+                o[0] = b[0];
+                o[1] = b[1];
+                memcpy(o + 2, b + 2 + 16 * h, 16);
+            }
+        }
 }
 
 int oracle_num_threads(void) {

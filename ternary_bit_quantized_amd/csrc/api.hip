@@ -168,6 +168,28 @@ int q2_0_mul_mat_group_act(const q2_0_mat_vec_item *items, int64_t n_items, int6
     return mul_mat_group_impl(items, n_items, K, x, x_type, ldx, N, precision, workspace, ws_bytes, stream);
 }
 
+int q2_0_quantize(const float *src, int64_t M, int64_t K, int64_t ld_src, void *w, void *stream) {
+    int st = check_shape(M, K, 0);
+    if (st) return st;
+    if (M == 0) return Q2_0_OK;
+    if (!src || !w) return Q2_0_ERR_NULL;
+    if (ld_src < K) return Q2_0_ERR_LAYOUT;
+    if (!aligned(src, 4) || !aligned(w, 2)) return Q2_0_ERR_ALIGN;
+    return hip_status(q2_0::launch_quantize(src, M, (int)(K / Q2_0_BLOCK_WEIGHTS), ld_src,
+                                            static_cast<uint8_t *>(w), static_cast<hipStream_t>(stream)));
+}
+
+int q2_0_repack_g128(const void *w128, int64_t M, int64_t K, void *w, void *stream) {
+    int st = check_shape(M, K, 0);
+    if (st) return st;
+    if (K % 128 != 0) return Q2_0_ERR_SHAPE;
+    if (M == 0) return Q2_0_OK;
+    if (!w128 || !w) return Q2_0_ERR_NULL;
+    if (!aligned(w128, 2) || !aligned(w, 2)) return Q2_0_ERR_ALIGN;
+    return hip_status(q2_0::launch_repack_g128(static_cast<const uint8_t *>(w128), M, K, static_cast<uint8_t *>(w),
+                                               static_cast<hipStream_t>(stream)));
+}
+
 const char *q2_0_status_string(int status) {
     switch (status) {
         case Q2_0_OK: return "Q2_0_OK";

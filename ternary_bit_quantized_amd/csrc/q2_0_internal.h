@@ -119,4 +119,7 @@ hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, c
 hipError_t launch_gemm_f32(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx,
                            int64_t N, float *y, int64_t ldy, hipStream_t s);
 
+hipError_t launch_quantize(const float *src, int64_t M, int nb, int64_t ld, uint8_t *w, hipStream_t s);
+hipError_t launch_repack_g128(const uint8_t *w128, int64_t M, int64_t K, uint8_t *w, hipStream_t s);
+
 }  // namespace q2_0

@@ -34,6 +34,7 @@ MAT_VEC_MAX_N = 8
 EXPORTS = ("q2_0_get_rows", "q2_0_mul_mat_vec", "q2_0_mul_mat_vec_group", "q2_0_mul_mat",
            "q2_0_mul_mat_workspace_bytes", "q2_0_mul_mat_group", "q2_0_mul_mat_group_workspace_bytes",
            "q2_0_mul_mat_vec_act", "q2_0_mul_mat_vec_group_act", "q2_0_mul_mat_act", "q2_0_mul_mat_group_act",
+           "q2_0_quantize", "q2_0_repack_g128",
            "q2_0_status_string", "q2_0_last_hip_error", "q2_0_version")
 
 
@@ -89,8 +90,10 @@ def lib() -> ctypes.CDLL:
         L.q2_0_mul_mat_vec_group_act.argtypes = [P, I64, I64, P, C, I64, I64, P]
         L.q2_0_mul_mat_act.argtypes = [P, I64, I64, P, C, I64, I64, P, I64, C, P, ctypes.c_size_t, P]
         L.q2_0_mul_mat_group_act.argtypes = [P, I64, I64, P, C, I64, I64, C, P, ctypes.c_size_t, P]
+        L.q2_0_quantize.argtypes = [P, I64, I64, I64, P, P]
+        L.q2_0_repack_g128.argtypes = [P, I64, I64, P, P]
         for f in (L.q2_0_mul_mat_vec_act, L.q2_0_mul_mat_vec_group_act, L.q2_0_mul_mat_act,
-                  L.q2_0_mul_mat_group_act):
+                  L.q2_0_mul_mat_group_act, L.q2_0_quantize, L.q2_0_repack_g128):
             f.restype = ctypes.c_int
         L.q2_0_status_string.argtypes = [ctypes.c_int]
         L.q2_0_status_string.restype = ctypes.c_char_p
@@ -170,6 +173,14 @@ def mul_mat_group_act_raw(items, n_items: int, K: int, x: int, x_type: int, ldx:
                                         workspace, ws_bytes, stream)
 
 
+def quantize_raw(src: int, M: int, K: int, ld_src: int, w: int, stream: int = 0) -> int:
+    return lib().q2_0_quantize(src, M, K, ld_src, w, stream)
+
+
+def repack_g128_raw(w128: int, M: int, K: int, w: int, stream: int = 0) -> int:
+    return lib().q2_0_repack_g128(w128, M, K, w, stream)
+
+
 def version() -> str:
     return lib().q2_0_version().decode()
 
@@ -205,6 +216,26 @@ def _xcols(t, K, name):
         raise ValueError("%s must have at least %d columns" % (name, K))
     ld = t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
     return t.data_ptr(), t.shape[0], ld, types[t.dtype]
+
+
+def q2_0_quantize(src, w=None, stream=None):
+    """Q2_0 (uint8 device tensor (M, K/64*18)) of the float32 weights src (M, K) by the reference quantizer."""
+    import torch
+    M, K = src.shape
+    ptr, _, ld = _cols(src, K, "src")
+    if w is None:
+        w = torch.empty((M, K // BLOCK_WEIGHTS * BLOCK_BYTES), dtype=torch.uint8, device=src.device)
+    _check(quantize_raw(ptr, M, K, ld, w.data_ptr(), _stream(stream)), "q2_0_quantize")
+    return w
+
+
+def q2_0_repack_g128(w128, M: int, K: int, w=None, stream=None):
+    """The group-64 Q2_0 tensor of a legacy group-128 tensor w128 (uint8, M rows of K/128*34 bytes)."""
+    import torch
+    if w is None:
+        w = torch.empty((M, K // BLOCK_WEIGHTS * BLOCK_BYTES), dtype=torch.uint8, device=w128.device)
+    _check(repack_g128_raw(w128.data_ptr(), M, K, w.data_ptr(), _stream(stream)), "q2_0_repack_g128")
+    return w
 
 
 def q2_0_get_rows(w, M: int, K: int, ids, out=None, stream=None):

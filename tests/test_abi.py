@@ -22,7 +22,7 @@ P16, P4 = 1 << 20, (1 << 20) + 4
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return set(re.findall(r"\b(q2_0_[a-z_]+)\s*\(", text))
+    return set(re.findall(r"\b(q2_0_[a-z0-9_]+)\s*\(", text))
 
 
 def test_library_exports_every_declared_symbol():
@@ -179,3 +179,18 @@ def test_activation_type_validation():
         assert B.mul_mat_group_act_raw(ok, 1, 64, P16, 7, 64, 20, 0, P16, 1 << 20) == B.Q2_0_ERR_UNSUPPORTED
     # F32 through the *_act entry keeps the 4-byte rule
     assert B.mul_mat_vec_act_raw(P16, 10, 64, P16 + 2, B.Q2_0_ACT_F32, 64, 1, P16, 10) == B.Q2_0_ERR_ALIGN
+
+
+def test_quantize_and_repack_validation():
+    assert B.quantize_raw(P16, 10, 100, 100, P16) == B.Q2_0_ERR_SHAPE
+    assert B.quantize_raw(P16, -1, 64, 64, P16) == B.Q2_0_ERR_SHAPE
+    assert B.quantize_raw(0, 0, 64, 64, 0) == B.Q2_0_OK
+    assert B.quantize_raw(0, 10, 64, 64, P16) == B.Q2_0_ERR_NULL
+    assert B.quantize_raw(P16, 10, 64, 63, P16) == B.Q2_0_ERR_LAYOUT
+    assert B.quantize_raw(P16 + 2, 10, 64, 64, P16) == B.Q2_0_ERR_ALIGN
+    assert B.quantize_raw(P16, 10, 64, 64, P16 + 1) == B.Q2_0_ERR_ALIGN
+    assert B.repack_g128_raw(P16, 10, 64, P16) == B.Q2_0_ERR_SHAPE      # K % 128 != 0
+    assert B.repack_g128_raw(P16, 10, 100, P16) == B.Q2_0_ERR_SHAPE
+    assert B.repack_g128_raw(0, 0, 128, 0) == B.Q2_0_OK
+    assert B.repack_g128_raw(P16, 10, 128, 0) == B.Q2_0_ERR_NULL
+    assert B.repack_g128_raw(P16 + 1, 10, 128, P16) == B.Q2_0_ERR_ALIGN

@@ -384,3 +384,42 @@ def test_bf16_input_helpers_against_known_patterns_and_torch():
     allb = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
     fin = np.isfinite(synth.bf16_bits_to_f32(allb))
     assert np.array_equal(synth.to_bf16_bits(synth.bf16_bits_to_f32(allb[fin])), allb[fin])
+
+
+# --------------------------------------------------------------- legacy group-128 packing
+
+def test_g128_hand_built_block_decodes_by_definition():
+    """A legacy block written out by hand (LE half, eight LE words; code i of word w is
+    weight 16w+i): every weight takes its own code, times the scale."""
+    rng = np.random.default_rng(9)
+    codes = rng.integers(0, 4, size=128)
+    d_bits = 0x3E00                      # 1.5
+    words = [_word_with(codes[16 * w:16 * w + 16]) for w in range(8)]
+    blk = np.frombuffer(struct.pack("<H8I", d_bits, *words), dtype=np.uint8)
+    assert blk.size == 34
+    got = oracle.dequant_g128(blk, 1, 128)[0]
+    assert np.array_equal(got, (codes - 1) * 1.5)
+    # one-hot: weight j code 2 (others 1) -> only position j is nonzero
+    for j in (0, 15, 16, 63, 64, 100, 127):
+        c = np.ones(128, dtype=int)
+        c[j] = 2
+        wb = [_word_with(c[16 * w:16 * w + 16]) for w in range(8)]
+        one = oracle.dequant_g128(np.frombuffer(struct.pack("<H8I", 0x3C00, *wb), dtype=np.uint8), 1, 128)[0]
+        assert np.flatnonzero(one).tolist() == [j] and one[j] == 1.0
+
+
+def test_g128_repack_preserves_every_weight():
+    """Two independent decoders agree: the group-64 decode of the repacked matrix equals the
+    group-128 decode of the legacy one, weight for weight (random bytes: every scale)."""
+    rng = np.random.default_rng(10)
+    M, K = 37, 640
+    w128 = rng.integers(0, 256, size=(M, K // 128 * 34), dtype=np.uint8)
+    w64 = oracle.repack_g128(w128, M, K)
+    a = oracle.dequant_g128(w128, M, K)
+    b = oracle.dequant(w64, M, K)
+    assert _same_bits(a.astype(np.float32), b.astype(np.float32))
+    assert np.array_equal(np.isnan(a), np.isnan(b))
+    # the two group-64 blocks of a legacy block carry its scale bytes
+    v = w64.reshape(M, K // 64, 18)
+    l = w128.reshape(M, K // 128, 34)
+    assert np.array_equal(v[:, 0::2, :2], l[:, :, :2]) and np.array_equal(v[:, 1::2, :2], l[:, :, :2])
