@@ -206,6 +206,41 @@ int q2_0_mul_mat_group_act(const q2_0_mat_vec_item *items, int64_t n_items, int6
                            size_t ws_bytes, void *stream);
 
 /*
+ * mul_mat_id: the expert ("mixture of experts") product, which the WebGPU backend of
+ * bisque.today "WebGPU: add Q2_0 support" leaves out for Q2_0 (the paragraph on what
+ * the change does not cover).  For token t < n_tokens and slot u < n_used:
+ *     y[t][u] = W_{ids[t][u]} x[t][u mod x_slots]
+ * with W_e the e-th of n_expert M x K Q2_0 matrices.
+ *   w       : n_expert matrices back to back (device), expert e at byte
+ *             e*M*(K/64)*18, 2-byte aligned (16-byte aligned rows are faster).
+ *   x       : activations of element type x_type (a q2_0_act_type); column (t, s)
+ *             for s < x_slots at element (t*x_slots + s)*ldx, ldx >= K.  x_slots is 1
+ *             (every slot of a token multiplies the token's activation, like an
+ *             expert layer's gate and up projections) or n_used (one activation per
+ *             slot, like its down projection).
+ *   ids     : DEVICE int32 [n_tokens][n_used] expert indices, 4-byte aligned.  An id
+ *             outside [0, n_expert) makes its y column quiet NaN and reads nothing.
+ *   y       : f32 column (t, u) at y + (t*n_used + u)*ldy, ldy >= M.
+ *   precision: as for q2_0_mul_mat: Q2_0_PREC_F16_MFMA (x rounded to fp16 as there,
+ *             2e-3 bound) or Q2_0_PREC_F32 (fp32-grade, 1e-5 bound).
+ *   workspace / ws_bytes: at least q2_0_mul_mat_id_workspace_bytes() bytes, 16-byte
+ *             aligned: the routing tables (the pairs sorted by expert, stably) and,
+ *             for Q2_0_PREC_F16_MFMA, x as fp16 in expert order.  Overwritten.
+ * The routing runs on the GPU; the result does not depend on timing or on how the
+ * pairs fall to the experts beyond the products themselves.
+ * Errors: SHAPE (also n_expert < 1 or > 8192, n_tokens*n_used > 2^20, x_slots not 1
+ * or n_used), the no-op for M == 0 or no pairs, NULL, LAYOUT, UNSUPPORTED (unknown
+ * x_type, checked before alignment, or precision), ALIGN, WORKSPACE.
+ */
+int q2_0_mul_mat_id(const void *w, int64_t n_expert, int64_t M, int64_t K, const void *x, int x_type,
+                    int64_t ldx, int64_t x_slots, const int32_t *ids, int64_t n_used, int64_t n_tokens,
+                    float *y, int64_t ldy, int precision, void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes q2_0_mul_mat_id needs (0 for invalid sizes). */
+size_t q2_0_mul_mat_id_workspace_bytes(int64_t n_expert, int64_t M, int64_t K, int64_t n_used, int64_t n_tokens,
+                                       int precision);
+
+/*
  * quantize: f32 weights -> Q2_0 by the reference quantizer (aisvetem.cz, "Llama.cpp
  * umi dvoubitovy Q2_0 i na kartach NVIDIA", section "Na bezny model to neni": the
  * block's largest |w| is the scale and each weight goes to the nearest level).

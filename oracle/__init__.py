@@ -157,6 +157,34 @@ def repack_g128(w128: np.ndarray, M: int, K: int) -> np.ndarray:
     return out
 
 
+def mul_mat_id(w: np.ndarray, n_expert: int, M: int, K: int, x: np.ndarray, ids: np.ndarray):
+    """Expert product, by its definition: pair (t, u) is W_{ids[t, u]} times activation
+    x[t * x_slots + u % x_slots] (x_slots = x rows / n_tokens, 1 or n_used).  Returns
+    (y, bound) of shape (n_tokens * n_used, M), pair order; pairs with an id outside
+    [0, n_expert) get NaN in y and 0 in bound."""
+    ids = np.asarray(ids)
+    n_tokens, n_used = ids.shape
+    x = np.asarray(x, dtype=np.float32)
+    x_slots = x.shape[0] // n_tokens
+    assert x_slots in (1, n_used) and x.shape[0] == n_tokens * x_slots
+    eb = M * (K // BLOCK_WEIGHTS) * BLOCK_BYTES
+    wall = np.ascontiguousarray(w, dtype=np.uint8).reshape(-1)
+    assert wall.size == n_expert * eb
+    y = np.full((n_tokens * n_used, M), np.nan)
+    bound = np.zeros((n_tokens * n_used, M))
+    pairs = np.arange(n_tokens * n_used)
+    flat = ids.reshape(-1)
+    for e in range(n_expert):
+        sel = pairs[flat == e]
+        if sel.size == 0:
+            continue
+        cols = (sel // n_used) if x_slots == 1 else sel
+        ye, be = mul_mat(wall[e * eb:(e + 1) * eb], M, K, x[cols])
+        y[sel] = ye
+        bound[sel] = be
+    return y, bound
+
+
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
 

@@ -168,6 +168,74 @@ int q2_0_mul_mat_group_act(const q2_0_mat_vec_item *items, int64_t n_items, int6
     return mul_mat_group_impl(items, n_items, K, x, x_type, ldx, N, precision, workspace, ws_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+constexpr int64_t kMaxExperts = 8192;
+constexpr int64_t kMaxPairs = (int64_t)1 << 20;
+
+int check_moe_shape(int64_t n_expert, int64_t M, int64_t K, int64_t n_used, int64_t n_tokens, int precision) {
+    int st = check_shape(M, K, 0);
+    if (st) return st;
+    if (n_expert < 1 || n_expert > kMaxExperts || n_used < 0 || n_tokens < 0) return Q2_0_ERR_SHAPE;
+    if (n_used > kMaxPairs || n_tokens > kMaxPairs || n_used * n_tokens > kMaxPairs) return Q2_0_ERR_SHAPE;
+    const int64_t n_pairs = n_used * n_tokens;
+    // launch grids: the fp32 path has one workgroup row per tile-list entry (grid.y)
+    if (precision == Q2_0_PREC_F32 && q2_0::moe_max_tiles(n_expert, n_pairs, 64) > 65535) return Q2_0_ERR_SHAPE;
+    if ((M + 127) / 128 * q2_0::moe_max_tiles(n_expert, n_pairs, 128) > kMaxRows) return Q2_0_ERR_SHAPE;
+    return Q2_0_OK;
+}
+
+int moe_tile_w(int precision) { return precision == Q2_0_PREC_F32 ? 64 : 128; }
+
+}  // namespace
+
+extern "C" {
+
+size_t q2_0_mul_mat_id_workspace_bytes(int64_t n_expert, int64_t M, int64_t K, int64_t n_used, int64_t n_tokens,
+                                       int precision) {
+    if (check_moe_shape(n_expert, M, K, n_used, n_tokens, precision)) return 0;
+    if (precision != Q2_0_PREC_F16_MFMA && precision != Q2_0_PREC_F32) return 0;
+    const int64_t n_pairs = n_used * n_tokens;
+    size_t b = q2_0::moe_route_bytes(n_expert, n_pairs, moe_tile_w(precision));
+    if (precision == Q2_0_PREC_F16_MFMA) b += q2_0::gemm_f16_moe_scratch_bytes(K, n_pairs);
+    return b;
+}
+
+int q2_0_mul_mat_id(const void *w, int64_t n_expert, int64_t M, int64_t K, const void *x, int x_type,
+                    int64_t ldx, int64_t x_slots, const int32_t *ids, int64_t n_used, int64_t n_tokens,
+                    float *y, int64_t ldy, int precision, void *workspace, size_t ws_bytes, void *stream) {
+    int st = check_moe_shape(n_expert, M, K, n_used, n_tokens, precision);
+    if (st) return st;
+    if (x_slots != 1 && x_slots != n_used) return Q2_0_ERR_SHAPE;
+    const int64_t n_pairs = n_used * n_tokens;
+    if (M == 0 || n_pairs == 0) return Q2_0_OK;
+    if (!ids) return Q2_0_ERR_NULL;
+    st = check_product(w, M, K, x, x_type, ldx, y, ldy);
+    if (st) return st;
+    if (!aligned(ids, 4)) return Q2_0_ERR_ALIGN;
+    if (precision != Q2_0_PREC_F16_MFMA && precision != Q2_0_PREC_F32) return Q2_0_ERR_UNSUPPORTED;
+    const size_t need = q2_0_mul_mat_id_workspace_bytes(n_expert, M, K, n_used, n_tokens, precision);
+    if (ws_bytes < need || !workspace || !aligned(workspace, 16)) return Q2_0_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint8_t *wb = static_cast<const uint8_t *>(w);
+    const int nb = (int)(K / Q2_0_BLOCK_WEIGHTS);
+    const q2_0::Act xt = (q2_0::Act)x_type;
+    q2_0::MoeRoute r;
+    st = hip_status(q2_0::launch_moe_route(ids, (int)n_pairs, (int)n_expert, (int)n_used, (int)x_slots,
+                                           moe_tile_w(precision), workspace, &r, s));
+    if (st) return st;
+    if (precision == Q2_0_PREC_F16_MFMA) {
+        void *scratch = static_cast<uint8_t *>(workspace) + q2_0::moe_route_bytes(n_expert, n_pairs, 128);
+        st = hip_status(q2_0::launch_gemm_f16_moe(wb, M, nb, x, xt, ldx, r, y, ldy, scratch, s));
+    } else {
+        st = hip_status(q2_0::launch_gemm_f32_moe(wb, M, nb, x, xt, ldx, r, y, ldy, s));
+    }
+    if (st) return st;
+    return hip_status(q2_0::launch_moe_fill_bad(r, M, y, ldy, s));
+}
+
 int q2_0_quantize(const float *src, int64_t M, int64_t K, int64_t ld_src, void *w, void *stream) {
     int st = check_shape(M, K, 0);
     if (st) return st;

@@ -74,13 +74,27 @@ __device__ __forceinline__ void store16_perm(const float v[16], int e, _Float16 
     dst[1] = u32x4_t{o[4], o[5], o[6], o[7]};
 }
 
+// gather (expert routing): output column n converts x column of pair perm[n] (pair
+// p = t * n_used + u reads column t when x_slots == 1, else column p).
+struct XGather {
+    const int *perm;   // nullptr: column n is x column n
+    int n_used;
+    int x_slots;
+};
+
 template <bool kVec, typename XT>
 __global__ __launch_bounds__(256) void x_to_f16_perm(const XT *__restrict__ x, int64_t ldx, int K,
-                                                     _Float16 *__restrict__ x16, int *__restrict__ xe) {
+                                                     _Float16 *__restrict__ x16, int *__restrict__ xe,
+                                                     XGather gather) {
     __shared__ float red[4];
     const int tid = threadIdx.x;
     const int64_t n = blockIdx.x;
-    const XT *col = x + n * ldx;
+    int64_t src_col = n;
+    if (gather.perm) {
+        const int p = gather.perm[n];
+        src_col = gather.x_slots == 1 ? p / gather.n_used : p;
+    }
+    const XT *col = x + src_col * ldx;
     const int groups = K / 16;
     const bool resident = groups <= kPreGroups * 256;
     float v[kPreGroups][16];
@@ -189,12 +203,31 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_mfma(GemmGroup grp, int nb, c
             tl = b / tiles_n;
         }
     }
-    const int tmg = grp.tm_base + tl;
-    const GemmItem &item = grp.p[find_gemm_item(grp, tmg)];
-    const uint8_t *__restrict__ w = item.w;
-    const int M = item.M;
-    const int tm = tmg - item.tm0;
-    const int m0 = tm * GM, n0 = tn * GN;
+    // matrix, rows and columns of this workgroup's tile: all N columns of the call, or
+    // (expert routing) a column tile of one expert's own run of x16
+    const uint8_t *__restrict__ w;
+    int M, m0, n0, col0 = 0, Nv = N;
+    const GemmItem *itp;
+    if (!grp.moe_off) {
+        const int tmg = grp.tm_base + tl;
+        itp = &grp.p[find_gemm_item(grp, tmg)];
+        w = itp->w;
+        M = itp->M;
+        m0 = (tmg - itp->tm0) * GM;
+        n0 = tn * GN;
+    } else {
+        const int t = blockIdx.x / grp.moe_tiles_m;
+        if (t >= *grp.moe_ntiles) return;   // the whole workgroup: no tile here
+        const int e = grp.moe_tiles[2 * t];
+        itp = &grp.p[0];
+        w = itp->w + e * grp.moe_expert_bytes;
+        M = itp->M;
+        m0 = (blockIdx.x % grp.moe_tiles_m) * GM;
+        n0 = grp.moe_tiles[2 * t + 1] * GN;
+        col0 = grp.moe_off[e];
+        Nv = grp.moe_off[e + 1] - col0;
+    }
+    const GemmItem &item = *itp;
     const int K = nb * kBlockWeights;
     const int64_t rowbytes = (int64_t)nb * kBlockBytes;
     const int nbs = nb / splits;                 // blocks of this split
@@ -218,7 +251,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_mfma(GemmGroup grp, int nb, c
         xn[q] = c >> 3;
         xpart[q] = c & 7;
         const int n = n0 + xn[q];
-        xcol[q] = x16 + (int64_t)(n < N ? n : 0) * K + (int64_t)kb0 * GK + 8 * xpart[q];
+        xcol[q] = x16 + (int64_t)(col0 + (n < Nv ? n : 0)) * K + (int64_t)kb0 * GK + 8 * xpart[q];
     }
 
     // Loads of a step past the last are clamped to the last block (harmless reloads),
@@ -319,7 +352,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_mfma(GemmGroup grp, int nb, c
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
             const int n = n0 + wn * 64 + jj * 32 + (lane & 31);
-            const int ye = -xe[n < N ? n : 0];
+            const int ye = -xe[col0 + (n < Nv ? n : 0)];
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][jj][v] = __builtin_amdgcn_ldexpf(acc[i][jj][v], ye);
         }
@@ -341,8 +374,8 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_mfma(GemmGroup grp, int nb, c
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
             const int n = n0 + wn * 64 + jj * 32 + (lane & 31);
-            if (n >= N) continue;
-            float *yc = yout + (int64_t)n * ldo;
+            if (n >= Nv) continue;
+            float *yc = grp.moe_off ? item.y + (int64_t)grp.moe_perm[col0 + n] * item.ldy : yout + (int64_t)n * ldo;
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) {
                 const int m = m0 + wm * 64 + i * 32 + 8 * v4 + 4 * (lane >> 5);
@@ -430,9 +463,9 @@ hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, c
         using XT = decltype(tag);
         const XT *xp = static_cast<const XT *>(x);
         if (vec)
-            x_to_f16_perm<true, XT><<<(unsigned)N, 256, 0, s>>>(xp, ldx, K, x16, xe);
+            x_to_f16_perm<true, XT><<<(unsigned)N, 256, 0, s>>>(xp, ldx, K, x16, xe, XGather{nullptr, 1, 1});
         else
-            x_to_f16_perm<false, XT><<<(unsigned)N, 256, 0, s>>>(xp, ldx, K, x16, xe);
+            x_to_f16_perm<false, XT><<<(unsigned)N, 256, 0, s>>>(xp, ldx, K, x16, xe, XGather{nullptr, 1, 1});
         return hipGetLastError();
     });
     if (e != hipSuccess) return e;
@@ -444,6 +477,7 @@ hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, c
         GemmGroup grp;
         grp.n = 0;
         grp.tm_base = (int)tm_next;
+        grp.moe_off = nullptr;
         int64_t rows = 0;
         for (int64_t i = i0; i < n_items && i < i0 + kGemmMaxGroup; ++i) {
             const int64_t M = mats[i].M;
@@ -480,6 +514,50 @@ hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, c
         }
     }
     return hipSuccess;
+}
+
+// Expert product on the fp16 GEMM: x is gathered into expert order and converted once
+// (scratch: x16 then the column exponents), then one launch runs every (expert, column
+// tile) entry of the routing's tile list against all row tiles; entries past the
+// list's length exit at once.  No K split, so every result is written once, in a
+// fixed order.
+size_t gemm_f16_moe_scratch_bytes(int64_t K, int64_t n_pairs) {
+    return align256((size_t)n_pairs * K * 2) + align256((size_t)n_pairs * 4);
+}
+
+hipError_t launch_gemm_f16_moe(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx,
+                               const MoeRoute &r, float *y, int64_t ldy, void *scratch, hipStream_t s) {
+    const int K = nb * kBlockWeights;
+    uint8_t *ws = static_cast<uint8_t *>(scratch);
+    _Float16 *x16 = reinterpret_cast<_Float16 *>(ws);
+    int *xe = reinterpret_cast<int *>(ws + align256((size_t)r.n_pairs * K * 2));
+    const bool vec = ((uintptr_t)x % (4 * act_bytes(xt)) == 0) && (ldx % 4 == 0);
+    const XGather gather{r.perm, r.n_used, r.x_slots};
+    hipError_t e = with_act(xt, [&](auto tag) -> hipError_t {
+        using XT = decltype(tag);
+        const XT *xp = static_cast<const XT *>(x);
+        if (vec)
+            x_to_f16_perm<true, XT><<<(unsigned)r.n_pairs, 256, 0, s>>>(xp, ldx, K, x16, xe, gather);
+        else
+            x_to_f16_perm<false, XT><<<(unsigned)r.n_pairs, 256, 0, s>>>(xp, ldx, K, x16, xe, gather);
+        return hipGetLastError();
+    });
+    if (e != hipSuccess) return e;
+    const int tiles_m = (int)((M + GM - 1) / GM);
+    GemmGroup grp;
+    grp.n = 1;
+    grp.tm_base = 0;
+    grp.p[0] = GemmItem{w, y, ldy, nullptr, (int)M, 0};
+    for (int k = 0; k < kGemmMaxGroup; ++k) grp.tm0[k] = k ? INT_MAX : 0;
+    grp.moe_off = r.off;
+    grp.moe_perm = r.perm;
+    grp.moe_tiles = r.tiles;
+    grp.moe_ntiles = r.ntiles;
+    grp.moe_expert_bytes = M * (int64_t)nb * kBlockBytes;
+    grp.moe_tiles_m = tiles_m;
+    const int64_t grid = (int64_t)tiles_m * moe_max_tiles(r.n_expert, r.n_pairs, GN);
+    gemm_f16_mfma<<<(unsigned)grid, 256, 0, s>>>(grp, nb, x16, xe, r.n_pairs, 1, 0, 1);
+    return hipGetLastError();
 }
 
 }  // namespace q2_0

@@ -1,0 +1,122 @@
+// Expert ("mixture of experts") product: y[t][u] = W_{ids[t][u]} x[t][u mod x_slots].
+//
+// bisque.today "WebGPU: add Q2_0 support" leaves the expert mat-mul out for Q2_0 (the
+// paragraph on what the change does not cover); this is that product on the same
+// block decode.  The routing runs on the GPU, so the call needs no host copy of ids:
+//
+//  1. moe_route (one workgroup): counts the (token, slot) pairs of every expert, an
+//     exclusive scan gives each expert's run of sorted positions, and a stable
+//     placement writes the pairs into their runs in pair order (ids outside
+//     [0, n_expert) go to one extra run).  Deterministic: no order depends on timing.
+//  2. the product: per expert, its columns only, on the fp16 GEMM (x gathered and
+//     converted once) or the fp32 GEMM (columns read through the pair index); the
+//     results go straight to their y columns.
+//  3. the columns of out-of-range ids are filled with NaN.
+#include "q2_0_internal.h"
+
+namespace q2_0 {
+
+namespace {
+
+constexpr int kRouteThreads = 1024;
+
+// off[0..n_expert+1]: run starts (off[n_expert] .. off[n_expert+1] holds the bad ids);
+// perm[pos] = pair; tiles: (expert, column tile) for every tile_w-column tile of every
+// expert's run, *ntiles of them.  LDS: one counter per run, then the current chunk.
+__global__ __launch_bounds__(kRouteThreads) void moe_route(const int32_t *__restrict__ ids, int n_pairs,
+                                                          int n_expert, int tile_w, int *__restrict__ off,
+                                                          int *__restrict__ perm, int *__restrict__ tiles,
+                                                          int *__restrict__ ntiles) {
+    extern __shared__ int lds[];
+    int *cnt = lds;                              // n_expert + 1 counters, then cursors
+    int *chunk = lds + n_expert + 1;             // the current chunk's runs
+    const int tid = threadIdx.x;
+    const int runs = n_expert + 1;
+    auto run_of = [&](int p) {
+        const int e = ids[p];
+        return (e >= 0 && e < n_expert) ? e : n_expert;
+    };
+    for (int b = tid; b < runs; b += kRouteThreads) cnt[b] = 0;
+    __syncthreads();
+    for (int p = tid; p < n_pairs; p += kRouteThreads) atomicAdd(&cnt[run_of(p)], 1);
+    __syncthreads();
+    // exclusive scan and tile list by one thread (runs is small: at most a few thousand)
+    if (tid == 0) {
+        int acc = 0, nt = 0;
+        for (int b = 0; b < runs; ++b) {
+            const int c = cnt[b];
+            off[b] = acc;
+            cnt[b] = acc;   // now the run's cursor
+            acc += c;
+            if (b < n_expert)
+                for (int t = 0; t * tile_w < c; ++t, ++nt) {
+                    tiles[2 * nt] = b;
+                    tiles[2 * nt + 1] = t;
+                }
+        }
+        off[runs] = acc;
+        *ntiles = nt;
+    }
+    __syncthreads();
+    // stable placement, one chunk of pairs at a time: a pair's position is its run's
+    // cursor plus the number of earlier pairs of the chunk in the same run
+    for (int c0 = 0; c0 < n_pairs; c0 += kRouteThreads) {
+        const int p = c0 + tid;
+        const int b = p < n_pairs ? run_of(p) : -1;
+        chunk[tid] = b;
+        __syncthreads();
+        if (b >= 0) {
+            int rank = 0;
+            for (int q = 0; q < tid; ++q) rank += (chunk[q] == b);
+            perm[cnt[b] + rank] = p;
+        }
+        __syncthreads();
+        if (b >= 0) atomicAdd(&cnt[b], 1);
+        __syncthreads();
+    }
+}
+
+// y columns of pairs with out-of-range ids: quiet NaN.
+__global__ __launch_bounds__(256) void moe_fill_bad(const int *__restrict__ off, const int *__restrict__ perm,
+                                                    int n_expert, int64_t M, float *__restrict__ y, int64_t ldy) {
+    const int64_t m = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (m >= M) return;
+    for (int j = off[n_expert]; j < off[n_expert + 1]; ++j)
+        y[(int64_t)perm[j] * ldy + m] = __builtin_nanf("");
+}
+
+}  // namespace
+
+namespace {
+size_t a256(size_t v) { return (v + 255) & ~(size_t)255; }
+}  // namespace
+
+// Routing tables, each 256-byte aligned: off (n_expert + 2), perm (n_pairs), ntiles (1),
+// tiles (2 per possible entry).
+size_t moe_route_bytes(int64_t n_expert, int64_t n_pairs, int tile_w) {
+    return a256((size_t)(n_expert + 2) * 4) + a256((size_t)n_pairs * 4) + 256 +
+           a256((size_t)moe_max_tiles(n_expert, n_pairs, tile_w) * 8);
+}
+
+hipError_t launch_moe_route(const int32_t *ids, int n_pairs, int n_expert, int n_used, int x_slots, int tile_w,
+                            void *ws, MoeRoute *r, hipStream_t s) {
+    uint8_t *p = static_cast<uint8_t *>(ws);
+    int *off = reinterpret_cast<int *>(p);
+    p += a256((size_t)(n_expert + 2) * 4);
+    int *perm = reinterpret_cast<int *>(p);
+    p += a256((size_t)n_pairs * 4);
+    int *ntiles = reinterpret_cast<int *>(p);
+    p += 256;
+    int *tiles = reinterpret_cast<int *>(p);
+    *r = MoeRoute{off, perm, tiles, ntiles, n_expert, n_pairs, n_used, x_slots, tile_w};
+    const size_t lds = (size_t)(n_expert + 1 + kRouteThreads) * 4;
+    moe_route<<<1, kRouteThreads, lds, s>>>(ids, n_pairs, n_expert, tile_w, off, perm, tiles, ntiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_moe_fill_bad(const MoeRoute &r, int64_t M, float *y, int64_t ldy, hipStream_t s) {
+    moe_fill_bad<<<(unsigned)((M + 255) / 256), 256, 0, s>>>(r.off, r.perm, r.n_expert, M, y, ldy);
+    return hipGetLastError();
+}
+
+}  // namespace q2_0

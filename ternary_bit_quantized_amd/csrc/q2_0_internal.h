@@ -112,12 +112,53 @@ struct GemmGroup {
     int tm0[kGemmMaxGroup];   // p[i].tm0 contiguously; INT_MAX past n
     int n;
     int tm_base;              // first row tile of this launch
+    // Expert routing (mul_mat_id), when moe_off is set: workgroup b takes row tile
+    // b % moe_tiles_m of the (expert, column tile) entry b / moe_tiles_m of moe_tiles
+    // (device; *moe_ntiles entries, the rest exit); expert e is the matrix at
+    // p[0].w + e * moe_expert_bytes, its columns are x16 columns moe_off[e] ..
+    // moe_off[e+1]-1, and result column j goes to y column moe_perm[j] of p[0].
+    const int *moe_off;
+    const int *moe_perm;
+    const int *moe_tiles;     // pairs (expert, column tile)
+    const int *moe_ntiles;
+    int64_t moe_expert_bytes;
+    int moe_tiles_m;
 };
 size_t gemm_f16_workspace_bytes(const int64_t *Ms, int64_t n_items, int64_t K, int64_t N);
 hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, const void *x, Act xt,
                                  int64_t ldx, int64_t N, void *workspace, hipStream_t s);
 hipError_t launch_gemm_f32(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx,
                            int64_t N, float *y, int64_t ldy, hipStream_t s);
+
+// ---- expert product (mul_mat_id).  Routing tables in device memory: off[e] .. off[e+1]
+// are the sorted positions of expert e's (token, slot) pairs (e = n_expert: ids out of
+// range), perm[j] the pair at sorted position j (pair p = t * n_used + u).
+// tiles: (expert, column tile of tile_w columns) for every tile an expert has, in expert
+// order, *ntiles of them (at most moe_max_tiles()).
+struct MoeRoute {
+    const int *off;       // n_expert + 2 entries
+    const int *perm;      // n_pairs entries
+    const int *tiles;     // 2 * moe_max_tiles() entries
+    const int *ntiles;
+    int n_expert;
+    int n_pairs;
+    int n_used;
+    int x_slots;          // 1: every slot of a token uses x column t; n_used: column t*n_used + u
+    int tile_w;
+};
+inline int64_t moe_max_tiles(int64_t n_expert, int64_t n_pairs, int tile_w) {
+    return (n_expert < n_pairs ? n_expert : n_pairs) + (n_pairs + tile_w - 1) / tile_w;
+}
+size_t moe_route_bytes(int64_t n_expert, int64_t n_pairs, int tile_w);
+// Lays out the routing tables in ws (moe_route_bytes bytes) and enqueues the routing.
+hipError_t launch_moe_route(const int32_t *ids, int n_pairs, int n_expert, int n_used, int x_slots, int tile_w,
+                            void *ws, MoeRoute *r, hipStream_t s);
+hipError_t launch_gemm_f16_moe(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx,
+                               const MoeRoute &r, float *y, int64_t ldy, void *scratch, hipStream_t s);
+size_t gemm_f16_moe_scratch_bytes(int64_t K, int64_t n_pairs);
+hipError_t launch_moe_fill_bad(const MoeRoute &r, int64_t M, float *y, int64_t ldy, hipStream_t s);
+hipError_t launch_gemm_f32_moe(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx,
+                               const MoeRoute &r, float *y, int64_t ldy, hipStream_t s);
 
 hipError_t launch_quantize(const float *src, int64_t M, int nb, int64_t ld, uint8_t *w, hipStream_t s);
 hipError_t launch_repack_g128(const uint8_t *w128, int64_t M, int64_t K, uint8_t *w, hipStream_t s);

@@ -34,7 +34,7 @@ MAT_VEC_MAX_N = 8
 EXPORTS = ("q2_0_get_rows", "q2_0_mul_mat_vec", "q2_0_mul_mat_vec_group", "q2_0_mul_mat",
            "q2_0_mul_mat_workspace_bytes", "q2_0_mul_mat_group", "q2_0_mul_mat_group_workspace_bytes",
            "q2_0_mul_mat_vec_act", "q2_0_mul_mat_vec_group_act", "q2_0_mul_mat_act", "q2_0_mul_mat_group_act",
-           "q2_0_quantize", "q2_0_repack_g128",
+           "q2_0_quantize", "q2_0_repack_g128", "q2_0_mul_mat_id", "q2_0_mul_mat_id_workspace_bytes",
            "q2_0_status_string", "q2_0_last_hip_error", "q2_0_version")
 
 
@@ -91,9 +91,13 @@ def lib() -> ctypes.CDLL:
         L.q2_0_mul_mat_act.argtypes = [P, I64, I64, P, C, I64, I64, P, I64, C, P, ctypes.c_size_t, P]
         L.q2_0_mul_mat_group_act.argtypes = [P, I64, I64, P, C, I64, I64, C, P, ctypes.c_size_t, P]
         L.q2_0_quantize.argtypes = [P, I64, I64, I64, P, P]
+        L.q2_0_mul_mat_id.argtypes = [P, I64, I64, I64, P, C, I64, I64, P, I64, I64, P, I64, C, P,
+                                      ctypes.c_size_t, P]
+        L.q2_0_mul_mat_id_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, C]
+        L.q2_0_mul_mat_id_workspace_bytes.restype = ctypes.c_size_t
         L.q2_0_repack_g128.argtypes = [P, I64, I64, P, P]
         for f in (L.q2_0_mul_mat_vec_act, L.q2_0_mul_mat_vec_group_act, L.q2_0_mul_mat_act,
-                  L.q2_0_mul_mat_group_act, L.q2_0_quantize, L.q2_0_repack_g128):
+                  L.q2_0_mul_mat_group_act, L.q2_0_quantize, L.q2_0_repack_g128, L.q2_0_mul_mat_id):
             f.restype = ctypes.c_int
         L.q2_0_status_string.argtypes = [ctypes.c_int]
         L.q2_0_status_string.restype = ctypes.c_char_p
@@ -173,6 +177,17 @@ def mul_mat_group_act_raw(items, n_items: int, K: int, x: int, x_type: int, ldx:
                                         workspace, ws_bytes, stream)
 
 
+def mul_mat_id_raw(w: int, n_expert: int, M: int, K: int, x: int, x_type: int, ldx: int, x_slots: int,
+                   ids: int, n_used: int, n_tokens: int, y: int, ldy: int, precision: int, workspace: int,
+                   ws_bytes: int, stream: int = 0) -> int:
+    return lib().q2_0_mul_mat_id(w, n_expert, M, K, x, x_type, ldx, x_slots, ids, n_used, n_tokens, y, ldy,
+                                 precision, workspace, ws_bytes, stream)
+
+
+def mul_mat_id_workspace_bytes(n_expert: int, M: int, K: int, n_used: int, n_tokens: int, precision: int) -> int:
+    return int(lib().q2_0_mul_mat_id_workspace_bytes(n_expert, M, K, n_used, n_tokens, precision))
+
+
 def quantize_raw(src: int, M: int, K: int, ld_src: int, w: int, stream: int = 0) -> int:
     return lib().q2_0_quantize(src, M, K, ld_src, w, stream)
 
@@ -216,6 +231,31 @@ def _xcols(t, K, name):
         raise ValueError("%s must have at least %d columns" % (name, K))
     ld = t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
     return t.data_ptr(), t.shape[0], ld, types[t.dtype]
+
+
+def q2_0_mul_mat_id(w, n_expert: int, M: int, K: int, x, ids, precision: int = Q2_0_PREC_F16_MFMA, y=None,
+                    workspace=None, stream=None):
+    """Expert product: w holds n_expert (M, K) Q2_0 matrices back to back; ids (n_tokens, n_used)
+    int32 on the device; x (n_tokens * x_slots, K) with x_slots 1 or n_used.  Returns
+    y (n_tokens * n_used, M) float32, row t * n_used + u = W_{ids[t, u]} x[t * x_slots + u % x_slots]."""
+    import torch
+    if ids.dtype != torch.int32 or not ids.is_contiguous() or ids.dim() != 2:
+        raise ValueError("ids must be a contiguous 2-D int32 tensor")
+    n_tokens, n_used = ids.shape
+    xp, rows, ldx, xt = _xcols(x, K, "x")
+    if rows != n_tokens and rows != n_tokens * n_used:
+        raise ValueError("x must have n_tokens or n_tokens * n_used rows")
+    x_slots = 1 if rows == n_tokens else n_used
+    if y is None:
+        y = torch.empty((n_tokens * n_used, M), dtype=torch.float32, device=x.device)
+    yp, _, ldy = _cols(y, M, "y")
+    need = mul_mat_id_workspace_bytes(n_expert, M, K, n_used, n_tokens, precision)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    wsb = workspace.numel() * workspace.element_size()
+    _check(mul_mat_id_raw(w.data_ptr(), n_expert, M, K, xp, xt, ldx, x_slots, ids.data_ptr(), n_used, n_tokens,
+                          yp, ldy, precision, workspace.data_ptr(), wsb, _stream(stream)), "q2_0_mul_mat_id")
+    return y
 
 
 def q2_0_quantize(src, w=None, stream=None):

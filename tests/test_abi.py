@@ -194,3 +194,34 @@ def test_quantize_and_repack_validation():
     assert B.repack_g128_raw(0, 0, 128, 0) == B.Q2_0_OK
     assert B.repack_g128_raw(P16, 10, 128, 0) == B.Q2_0_ERR_NULL
     assert B.repack_g128_raw(P16 + 1, 10, 128, P16) == B.Q2_0_ERR_ALIGN
+
+
+def test_mul_mat_id_validation():
+    F16, F32 = B.Q2_0_PREC_F16_MFMA, B.Q2_0_PREC_F32
+    ws = 1 << 24
+
+    def call(w=P16, ne=4, M=10, K=64, x=P16, xt=B.Q2_0_ACT_F32, ldx=64, xs=1, ids=P16, nu=2, nt=3, y=P16, ldy=10,
+             prec=F16, wsp=P16, wsb=ws):
+        return B.mul_mat_id_raw(w, ne, M, K, x, xt, ldx, xs, ids, nu, nt, y, ldy, prec, wsp, wsb)
+
+    assert call(K=100) == B.Q2_0_ERR_SHAPE
+    assert call(ne=0) == B.Q2_0_ERR_SHAPE
+    assert call(ne=8193) == B.Q2_0_ERR_SHAPE
+    assert call(nu=1 << 11, nt=1 << 10) == B.Q2_0_ERR_SHAPE            # more than 2^20 pairs
+    assert call(xs=3) == B.Q2_0_ERR_SHAPE                              # x_slots neither 1 nor n_used
+    assert call(M=0, w=0, x=0, ids=0, y=0) == B.Q2_0_OK
+    assert call(nt=0, w=0, x=0, ids=0, y=0) == B.Q2_0_OK
+    assert call(ids=0) == B.Q2_0_ERR_NULL
+    assert call(x=0) == B.Q2_0_ERR_NULL
+    assert call(ldx=63) == B.Q2_0_ERR_LAYOUT
+    assert call(ldy=9) == B.Q2_0_ERR_LAYOUT
+    assert call(xt=5) == B.Q2_0_ERR_UNSUPPORTED
+    assert call(ids=P16 + 2) == B.Q2_0_ERR_ALIGN
+    assert call(x=P16 + 2) == B.Q2_0_ERR_ALIGN
+    assert call(prec=2) == B.Q2_0_ERR_UNSUPPORTED
+    need = B.mul_mat_id_workspace_bytes(4, 10, 64, 2, 3, F16)
+    assert need >= 6 * 64 * 2 and B.mul_mat_id_workspace_bytes(4, 10, 64, 2, 3, F32) > 0
+    assert call(wsb=need - 1) == B.Q2_0_ERR_WORKSPACE
+    assert call(wsp=0) == B.Q2_0_ERR_WORKSPACE
+    assert call(wsp=P16 + 8) == B.Q2_0_ERR_WORKSPACE
+    assert B.mul_mat_id_workspace_bytes(0, 10, 64, 2, 3, F16) == 0

@@ -423,3 +423,30 @@ def test_g128_repack_preserves_every_weight():
     v = w64.reshape(M, K // 64, 18)
     l = w128.reshape(M, K // 128, 34)
     assert np.array_equal(v[:, 0::2, :2], l[:, :, :2]) and np.array_equal(v[:, 1::2, :2], l[:, :, :2])
+
+
+# --------------------------------------------------------------- expert product
+
+def test_oracle_mul_mat_id_by_brute_force():
+    """Every pair's product equals the dense product of its own expert (dequantized, numpy
+    matmul), for both activation layouts; bad ids give NaN."""
+    rng = np.random.default_rng(11)
+    ne, M, K, nt, nu = 5, 7, 128, 6, 3
+    ws = [synth.weight(60, e, 0, M, K, "quad", synth.ScaleDist("uniform", 0.01, 0.1)) for e in range(ne)]
+    wall = np.concatenate([w.reshape(-1) for w in ws])
+    ids = rng.integers(0, ne, size=(nt, nu)).astype(np.int32)
+    ids[2, 1] = ne      # out of range
+    ids[4, 0] = -1
+    dense = [oracle.dequant(w, M, K) for w in ws]
+    for slots in (1, nu):
+        x = synth.activations(60, slots, 0, nt * slots, K)
+        y, bound = oracle.mul_mat_id(wall, ne, M, K, x, ids)
+        for t in range(nt):
+            for u in range(nu):
+                p, e = t * nu + u, ids[t, u]
+                xc = x[t * slots + (u % slots)].astype(np.float64)
+                if 0 <= e < ne:
+                    assert np.allclose(y[p], dense[e] @ xc, rtol=1e-12, atol=1e-12)
+                    assert np.allclose(bound[p], np.abs(dense[e]) @ np.abs(xc), rtol=1e-12)
+                else:
+                    assert np.all(np.isnan(y[p])) and np.all(bound[p] == 0)
