@@ -236,7 +236,58 @@ def main():
                                 yPn[key[1]].data_ptr(), M, B.Q2_0_PREC_F16_MFMA, ws.data_ptr(), ws_bytes, st),
                   "mul_mat")
 
-    # ---- capture the four parts as graphs
+    # ---- the widened rows, measured beside the step (not part of it): 16-bit activations,
+    # the quantizer and the legacy group-128 reader, an expert layer
+    x1h = {K: v.to(torch.float16) for K, v in x1.items()}
+    xPb = {K: v.to(torch.bfloat16) for K, v in xP.items()}
+
+    def run_decode_f16_activations():
+        st = s()
+        for items, n, K in act_groups:
+            check(B.mul_mat_vec_group_act_raw(items, n, K, x1h[K].data_ptr(), B.Q2_0_ACT_F16, K, 1, st),
+                  "mat_vec_group_act")
+        check(B.mul_mat_vec_act_raw(emb.data_ptr(), VM, VK, x1h[VK].data_ptr(), B.Q2_0_ACT_F16, VK, 1,
+                                    y1[VM].data_ptr(), VM, st), "lm_head_act")
+
+    def run_prefill_bf16_activations():
+        st = s()
+        for items, n, K in prefill_groups:
+            check(B.mul_mat_group_act_raw(items, n, K, xPb[K].data_ptr(), B.Q2_0_ACT_BF16, K, PREFILL_N,
+                                          B.Q2_0_PREC_F16_MFMA, ws.data_ptr(), ws_bytes, st), "mul_mat_group_act")
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    qsrc = torch.randn((VM, VK), generator=gen, device=dev) * 0.02      # the vocabulary tensor's shape in f32
+    qdst = torch.empty_like(emb)
+    g128_src = emb.view(-1)[:VM * (VK // 128) * 34]                     # any bytes: a legacy-layout stand-in
+
+    def run_quantize():
+        check(B.quantize_raw(qsrc.data_ptr(), VM, VK, VK, qdst.data_ptr(), s()), "quantize")
+
+    def run_repack_g128():
+        check(B.repack_g128_raw(g128_src.data_ptr(), VM, VK, qdst.data_ptr(), s()), "repack_g128")
+
+    # an expert layer: 128 experts of 768 x 2048 (random blocks with finite scales), 8 of
+    # them per token; prefill 512 tokens on the fp16 GEMM, decode one token on the fp32 path
+    MOE_E, MOE_M, MOE_K, MOE_USED = 128, 768, 2048, 8
+    moe_w = torch.randint(0, 256, (MOE_E * MOE_M, MOE_K // 64, 18), dtype=torch.uint8, device=dev, generator=gen)
+    moe_w[:, :, 1] &= 0x3B
+    moe_ids_p = torch.stack([torch.randperm(MOE_E, device=dev, generator=gen)[:MOE_USED]
+                             for _ in range(PREFILL_N)]).to(torch.int32)
+    moe_ids_d = moe_ids_p[:1].contiguous()
+    moe_x = torch.randn((PREFILL_N, MOE_K), generator=gen, device=dev)
+    moe_y = torch.empty((PREFILL_N * MOE_USED, MOE_M), dtype=torch.float32, device=dev)
+    moe_ws_bytes = max(B.mul_mat_id_workspace_bytes(MOE_E, MOE_M, MOE_K, MOE_USED, PREFILL_N, p_)
+                       for p_ in (B.Q2_0_PREC_F16_MFMA, B.Q2_0_PREC_F32))
+    moe_ws = torch.empty(moe_ws_bytes, dtype=torch.uint8, device=dev)
+
+    def run_moe(ids, precision):
+        nt = ids.shape[0]
+        check(B.mul_mat_id_raw(moe_w.data_ptr(), MOE_E, MOE_M, MOE_K, moe_x.data_ptr(), B.Q2_0_ACT_F32, MOE_K, 1,
+                               ids.data_ptr(), MOE_USED, nt, moe_y.data_ptr(), MOE_M, precision,
+                               moe_ws.data_ptr(), moe_ws_bytes, s()), "mul_mat_id")
+
+    # ---- capture the parts as graphs
     parts = {
         "prefill_get_rows": lambda: run_get_rows(ids_p, emb_out_p),
         "prefill_gemm": run_prefill_gemms,
@@ -246,6 +297,12 @@ def main():
         "decode_mat_vec_per_matrix": run_decode_per_matrix,
         "prefill_gemm_per_matrix": run_prefill_per_matrix,
         "prefill_gemm_f32_layer0": lambda: run_prefill_gemms(B.Q2_0_PREC_F32, groups=prefill_groups[:4]),
+        "decode_mat_vec_f16_activations": run_decode_f16_activations,
+        "prefill_gemm_bf16_activations": run_prefill_bf16_activations,
+        "quantize_vocab_f32": run_quantize,
+        "repack_g128_vocab": run_repack_g128,
+        "expert_layer_prefill": lambda: run_moe(moe_ids_p, B.Q2_0_PREC_F16_MFMA),
+        "expert_layer_decode": lambda: run_moe(moe_ids_d, B.Q2_0_PREC_F32),
     }
     if args.parts:
         keep = args.parts.split(",")
@@ -282,7 +339,10 @@ def main():
     step_parts = [p for p in ("prefill_get_rows", "prefill_gemm", "decode_get_rows", "decode_mat_vec")
                   if p in graphs]
     compare_parts = [p for p in ("decode_mat_vec_per_layer", "decode_mat_vec_per_matrix",
-                                 "prefill_gemm_per_matrix", "prefill_gemm_f32_layer0") if p in graphs]
+                                 "prefill_gemm_per_matrix", "prefill_gemm_f32_layer0",
+                                 "decode_mat_vec_f16_activations", "prefill_gemm_bf16_activations",
+                                 "quantize_vocab_f32", "repack_g128_vocab", "expert_layer_prefill",
+                                 "expert_layer_decode") if p in graphs]
     ev = {n: [] for n in parts}
 
     def replay(names, record):
@@ -316,6 +376,19 @@ def main():
     for _ in range(args.steps):
         replay(compare_parts, True)
     torch.cuda.synchronize()
+    # the step's decode replayed back to back, as a run of decode tokens would be (in the
+    # step it follows 11 ms of prefill GEMM on the same GPU)
+    b2b = None
+    if "decode_mat_vec" in graphs:
+        graphs["decode_mat_vec"].replay()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(4 * args.steps):
+            graphs["decode_mat_vec"].replay()
+        b.record()
+        torch.cuda.synchronize()
+        b2b = a.elapsed_time(b) / (4 * args.steps)
 
     ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in parts if ev[n]}
     if set(step_parts) != {"prefill_get_rows", "prefill_gemm", "decode_get_rows", "decode_mat_vec"}:
@@ -360,6 +433,7 @@ def main():
         "ms": {k: round(v, 4) for k, v in ms.items()},
         "decode_schedules_GBps": {
             "by_activation (%d launches, the step)" % n_dec_launches: round(matvec_gbs, 1),
+            "by_activation, decode tokens back to back": round(dec_bytes / (b2b * 1e-3) / 1e9, 1) if b2b else None,
             "per_layer_groups (%d launches)" % (len(layer_groups) + 1):
                 round(dec_bytes / (ms["decode_mat_vec_per_layer"] * 1e-3) / 1e9, 1),
             "per_matrix (%d launches)" % (len(order) + 1):
@@ -387,6 +461,7 @@ def main():
             "unit": "TFLOP/s", "frac": round(gemm_tflops / F16_MFMA_PEAK_TFLOPS, 4),
             "traffic": traffic.get("gemm_f16_mfma"), "algorithmic_bytes": int(pre_bytes),
         },
+        "next_rows": next_rows(ms, wl, order, VM, VK, pre_flops, MOE_E, MOE_M, MOE_K, MOE_USED),
         "cpu_baseline": None,
     }
 
@@ -394,6 +469,32 @@ def main():
         result["cpu_baseline"] = cpu_baseline(host_w, order, wl, args)
 
     print(json.dumps(result), flush=True)
+
+
+def next_rows(ms, wl, order, VM, VK, pre_flops, ne, mm, mk, nu):
+    """Rates of the widened rows, timed beside the step (HIP events around their graphs)."""
+    out = {}
+
+    def rate(name, work, scale):
+        if name in ms and ms[name] > 0:
+            return round(work / (ms[name] * 1e-3) / scale, 1)
+        return None
+
+    dec16 = sum(M * (K // 64) * 18 + 2 * K + 4 * M for (_, n) in order for (M, K) in [wl.shapes[n]])
+    dec16 += VM * (VK // 64) * 18 + 2 * VK + 4 * VM
+    out["decode_mat_vec_f16_activations_GBps"] = rate("decode_mat_vec_f16_activations", dec16, 1e9)
+    out["prefill_gemm_bf16_activations_TFLOPs"] = rate("prefill_gemm_bf16_activations", pre_flops, 1e12)
+    out["quantize_151936x4096_f32_GBps"] = rate("quantize_vocab_f32", VM * VK * 4 + VM * (VK // 64) * 18, 1e9)
+    out["repack_g128_151936x4096_GBps"] = rate("repack_g128_vocab", VM * (VK // 128) * 34 + VM * (VK // 64) * 18,
+                                              1e9)
+    out["expert_layer_prefill_TFLOPs"] = rate("expert_layer_prefill", 2.0 * mm * mk * PREFILL_N * nu, 1e12)
+    out["expert_layer_decode_GBps"] = rate("expert_layer_decode", nu * (mm * (mk // 64) * 18 + 4 * mk + 4 * mm), 1e9)
+    out["expert_layer"] = "%d experts of %dx%d, %d per token; prefill %d tokens (fp16 MFMA), decode 1 token (fp32)" % (
+        ne, mm, mk, nu, PREFILL_N)
+    out["ms"] = {k: round(ms[k], 4) for k in ("decode_mat_vec_f16_activations", "prefill_gemm_bf16_activations",
+                                              "quantize_vocab_f32", "repack_g128_vocab", "expert_layer_prefill",
+                                              "expert_layer_decode") if k in ms}
+    return out
 
 
 def cpu_baseline(host_w, order, wl, args):

@@ -222,7 +222,9 @@ int q2_0_mul_mat_group_act(const q2_0_mat_vec_item *items, int64_t n_items, int6
  *             outside [0, n_expert) makes its y column quiet NaN and reads nothing.
  *   y       : f32 column (t, u) at y + (t*n_used + u)*ldy, ldy >= M.
  *   precision: as for q2_0_mul_mat: Q2_0_PREC_F16_MFMA (x rounded to fp16 as there,
- *             2e-3 bound) or Q2_0_PREC_F32 (fp32-grade, 1e-5 bound).
+ *             2e-3 bound) or Q2_0_PREC_F32 (fp32-grade, 1e-5 bound).  As there, few
+ *             tokens (n_tokens <= 8) take the fp32-grade mat-vec, one per pair, for
+ *             either precision.
  *   workspace / ws_bytes: at least q2_0_mul_mat_id_workspace_bytes() bytes, 16-byte
  *             aligned: the routing tables (the pairs sorted by expert, stably) and,
  *             for Q2_0_PREC_F16_MFMA, x as fp16 in expert order.  Overwritten.

@@ -42,10 +42,28 @@ constexpr int kTile = kMvTile;
 
 // NC: activation columns; KS: K slices per workgroup (RG = 4 / KS row tiles);
 // SB: blocks per stage.
+// route.ids set (expert product, NC = 1): blockIdx.y is a (token, slot) pair p; its
+// expert e = ids[p] selects the matrix at w + e * expert_bytes, its activation column is
+// t (x_slots == 1) or p, and its result column p.  Pairs with an id outside
+// [0, n_expert) are left to the caller (nothing is read or written for them).
+struct PairRoute {
+    const int32_t *ids;
+    int n_expert, n_used, x_slots;
+    int64_t expert_bytes;
+};
+
 template <int NC, int KS, int SB, typename XT>
 __global__ __launch_bounds__(256) void mat_vec_mfma(const uint8_t *__restrict__ w, int M, int nb,
                                                     const XT *__restrict__ x, int64_t ldx,
-                                                    float *__restrict__ y, int64_t ldy) {
+                                                    float *__restrict__ y, int64_t ldy, PairRoute route) {
+    if (route.ids) {
+        const int p = blockIdx.y;
+        const int e = route.ids[p];
+        if (e < 0 || e >= route.n_expert) return;   // the whole workgroup
+        w += e * route.expert_bytes;
+        x += (int64_t)(route.x_slots == 1 ? p / route.n_used : p) * ldx;
+        y += (int64_t)p * ldy;
+    }
     constexpr int RG = 4 / KS;
     constexpr int NR = 2 * NC;                      // A rows that carry data
     constexpr int RSB = SB * kBlockBytes + 16;       // LDS bytes per row per stage (16-B multiple)
@@ -176,23 +194,23 @@ __global__ __launch_bounds__(256) void mat_vec_mfma(const uint8_t *__restrict__ 
 // while the grid still has at least two workgroups per CU.
 template <int NC, typename XT>
 static hipError_t launch_nc(const uint8_t *w, int M, int nb, const XT *x, int64_t ldx, float *y,
-                            int64_t ldy, hipStream_t s) {
+                            int64_t ldy, hipStream_t s, const PairRoute &route = PairRoute{}, int pairs = 1) {
     const int tiles = (M + kTile - 1) / kTile;
     int ks = 1;
-    const int want = 512;
+    const int want = 512 / pairs > 0 ? 512 / pairs : 1;
     const int maxks = (NC <= 4) ? 4 : 2;
     while (ks < maxks && (tiles + (4 / ks) - 1) / (4 / ks) < want && nb % (8 * ks * 2) == 0) ks *= 2;
     const int rg = 4 / ks;
-    dim3 grid((unsigned)((tiles + rg - 1) / rg));
+    dim3 grid((unsigned)((tiles + rg - 1) / rg), (unsigned)pairs);
     constexpr int SB1 = (NC <= 4) ? 32 : 16;
     constexpr int SB2 = (NC <= 2) ? 32 : 16;
     constexpr int SB4 = (NC <= 1) ? 32 : ((NC <= 2) ? 16 : 8);
     if (ks == 1)
-        mat_vec_mfma<NC, 1, SB1, XT><<<grid, 256, 0, s>>>(w, M, nb, x, ldx, y, ldy);
+        mat_vec_mfma<NC, 1, SB1, XT><<<grid, 256, 0, s>>>(w, M, nb, x, ldx, y, ldy, route);
     else if (ks == 2)
-        mat_vec_mfma<NC, 2, SB2, XT><<<grid, 256, 0, s>>>(w, M, nb, x, ldx, y, ldy);
+        mat_vec_mfma<NC, 2, SB2, XT><<<grid, 256, 0, s>>>(w, M, nb, x, ldx, y, ldy, route);
     else if constexpr (NC <= 4)
-        mat_vec_mfma<NC, 4, SB4, XT><<<grid, 256, 0, s>>>(w, M, nb, x, ldx, y, ldy);
+        mat_vec_mfma<NC, 4, SB4, XT><<<grid, 256, 0, s>>>(w, M, nb, x, ldx, y, ldy, route);
     return hipGetLastError();
 }
 
@@ -220,6 +238,18 @@ hipError_t launch_mat_vec_mfma(const uint8_t *w, int64_t M, int nb, const void *
             case 8: return launch_nc<8>(w, m, nb, x, ldx, y, ldy, s);
             default: return hipErrorInvalidValue;
         }
+    });
+}
+
+// Expert product with few tokens: one mat-vec (N = 1) per (token, slot) pair, the
+// expert looked up on the GPU (fp32-grade, as q2_0_mul_mat gives for N <= 8).
+hipError_t launch_mat_vec_mfma_pairs(const uint8_t *w, int64_t M, int nb, const void *xv, Act xt, int64_t ldx,
+                                     const int32_t *ids, int n_expert, int n_used, int x_slots, int n_pairs,
+                                     float *y, int64_t ldy, hipStream_t s) {
+    const PairRoute route{ids, n_expert, n_used, x_slots, M * (int64_t)nb * kBlockBytes};
+    return with_act(xt, [&](auto tag) -> hipError_t {
+        using XT = decltype(tag);
+        return launch_nc<1>(w, (int)M, nb, static_cast<const XT *>(xv), ldx, y, ldy, s, route, n_pairs);
     });
 }
 

@@ -59,12 +59,19 @@ def check(y, y_ref, bound, rel, what):
         what, r["n_bad"], r["n"], rel, r["max_err_over_bound"], r["first_bad"])
 
 
-ROUTINGS = ["decode", "prefill", "one_expert", "bad_ids"]
+# few tokens (<= 8) take one mat-vec per pair, more tokens the expert-tiled GEMM
+ROUTINGS = ["decode", "decode_bad_ids", "few_one_expert", "prefill", "one_expert", "bad_ids"]
 
 
 def make_ids(kind, rng, ne):
     if kind == "decode":
         return rng.permutation(ne)[:8][None, :].astype(np.int32)          # 1 token, 8 distinct experts
+    if kind == "decode_bad_ids":
+        ids = rng.integers(0, ne, size=(4, 8)).astype(np.int32)
+        ids[0, 2], ids[3, 7] = -5, ne
+        return ids
+    if kind == "few_one_expert":
+        return np.full((8, 2), 5, dtype=np.int32)
     if kind == "prefill":
         return rng.integers(0, ne, size=(100, 8)).astype(np.int32)
     if kind == "one_expert":
