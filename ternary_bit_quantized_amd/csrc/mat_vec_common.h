@@ -27,6 +27,7 @@ constexpr int kMvStreamSB = 16;    // blocks per stage in the streaming kernel
 constexpr int kMvMaxGroup = 64;    // matrices per grouped launch (kernel argument size)
 constexpr size_t kMvStreamStaticLds = 1024;  // static LDS bound of the streaming kernel
 constexpr int kMvStreamMaxWaves = 16;        // largest streaming workgroup (waves)
+constexpr int kMvBcastRows = 16;             // rows per tile of the broadcast kernel
 
 struct MvProblem {
     const uint8_t *w;
@@ -54,6 +55,58 @@ __device__ __forceinline__ int find_problem(const MvGroup &grp, int tile) {
     for (int step = kMvMaxGroup / 2; step >= 1; step >>= 1)
         if (grp.tile0[idx + step] <= tile) idx += step;
     return idx;
+}
+
+// The wave's current matrix and tile, all wave-uniform.
+struct TileRef {
+    const uint8_t *w;
+    float *y;
+    int64_t ldy;
+    int M;
+    int m0;
+};
+
+template <int TILE>
+__device__ __forceinline__ TileRef tile_ref(const MvGroup &grp, int tile) {
+    const MvProblem &p = grp.p[find_problem(grp, tile)];
+    return TileRef{p.w, p.y, p.ldy, p.M, (tile - p.tile0) * TILE};
+}
+
+// A wave's tiles only move forward, so it follows them with a cursor: the current
+// matrix's fields and tile range stay in SGPRs, and the kernel arguments are read again
+// only when a tile passes the end of that matrix.
+struct TileCursor {
+    TileRef r;   // r.m0 is that of the matrix's first tile (0)
+    int idx, t0, t1;
+};
+
+__device__ __forceinline__ void cursor_load(const MvGroup &grp, TileCursor &c) {
+    const MvProblem &p = grp.p[c.idx];
+    c.r = TileRef{p.w, p.y, p.ldy, p.M, 0};
+    c.t0 = grp.tile0[c.idx];
+    c.t1 = grp.tile0[c.idx + 1];
+}
+
+__device__ __forceinline__ void cursor_init(const MvGroup &grp, TileCursor &c, int tile) {
+    c.idx = find_problem(grp, tile);
+    cursor_load(grp, c);
+}
+
+// The tile's matrix and rows (TILE rows per tile); tile >= every tile the cursor
+// was moved to before.
+template <int TILE>
+__device__ __forceinline__ TileRef cursor_tile(const MvGroup &grp, TileCursor &c, int tile) {
+    if (tile >= c.t1) {
+        do ++c.idx; while (grp.tile0[c.idx + 1] <= tile);
+        cursor_load(grp, c);
+        // wait for the argument loads here, on the rare path: a wait left to the join
+        // would also wait, on every tile, for the LDS stores just issued (one counter
+        // covers both).  lgkmcnt(0), vmcnt and expcnt untouched.
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+    }
+    TileRef t = c.r;
+    t.m0 = (tile - c.t0) * TILE;
+    return t;
 }
 
 __device__ __forceinline__ half8_t as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -254,5 +307,10 @@ size_t mat_vec_stream_lds(int N, int nb, int waves);
 int mat_vec_stream_waves(int N, int nb, int *resident);
 hipError_t launch_mat_vec_stream(const MvGroup &grp, int nb, const void *x, Act xt, int64_t ldx, int N,
                                  hipStream_t s);
+// N = 1, 2; grp counts tiles of kMvBcastRows rows
+size_t mat_vec_bcast_lds(int N, int nb, int waves);
+int mat_vec_bcast_waves(int N, int nb, int *resident);
+hipError_t launch_mat_vec_bcast(const MvGroup &grp, int nb, const void *x, Act xt, int64_t ldx, int N,
+                                hipStream_t s);
 
 }  // namespace q2_0

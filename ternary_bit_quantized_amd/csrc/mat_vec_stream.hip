@@ -35,55 +35,6 @@ namespace q2_0 {
 
 namespace {
 
-// The wave's current matrix and tile, all wave-uniform.
-struct TileRef {
-    const uint8_t *w;
-    float *y;
-    int64_t ldy;
-    int M;
-    int m0;
-};
-
-__device__ __forceinline__ TileRef tile_ref(const MvGroup &grp, int tile) {
-    const MvProblem &p = grp.p[find_problem(grp, tile)];
-    return TileRef{p.w, p.y, p.ldy, p.M, (tile - p.tile0) * kMvTile};
-}
-
-// A wave's tiles only move forward, so it follows them with a cursor: the current
-// matrix's fields and tile range stay in SGPRs, and the kernel arguments are read again
-// only when a tile passes the end of that matrix.
-struct TileCursor {
-    TileRef r;   // r.m0 is that of the matrix's first tile (0)
-    int idx, t0, t1;
-};
-
-__device__ __forceinline__ void cursor_load(const MvGroup &grp, TileCursor &c) {
-    const MvProblem &p = grp.p[c.idx];
-    c.r = TileRef{p.w, p.y, p.ldy, p.M, 0};
-    c.t0 = grp.tile0[c.idx];
-    c.t1 = grp.tile0[c.idx + 1];
-}
-
-__device__ __forceinline__ void cursor_init(const MvGroup &grp, TileCursor &c, int tile) {
-    c.idx = find_problem(grp, tile);
-    cursor_load(grp, c);
-}
-
-// The tile's matrix and rows; tile >= every tile the cursor was moved to before.
-__device__ __forceinline__ TileRef cursor_tile(const MvGroup &grp, TileCursor &c, int tile) {
-    if (tile >= c.t1) {
-        do ++c.idx; while (grp.tile0[c.idx + 1] <= tile);
-        cursor_load(grp, c);
-        // wait for the argument loads here, on the rare path: a wait left to the join
-        // would also wait, on every tile, for the LDS stores just issued (one counter
-        // covers both).  lgkmcnt(0), vmcnt and expcnt untouched.
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-    }
-    TileRef t = c.r;
-    t.m0 = (tile - c.t0) * kMvTile;
-    return t;
-}
-
 struct Item {
     int tile, st;
 };
@@ -159,7 +110,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_stream(MvGroup grp, int nb,
     cursor_init(grp, ld_cur, first.tile);
 #define Q2_0_SET_LOAD_TILE(TILE)                                                                   \
     {                                                                                              \
-        const TileRef tr_ = cursor_tile(grp, ld_cur, (TILE));                                      \
+        const TileRef tr_ = cursor_tile<kMvTile>(grp, ld_cur, (TILE));                             \
         ld_base = tr_.w + (int64_t)tr_.m0 * rowbytes;                                              \
         const int rows_ = min(tr_.M - tr_.m0, kMvTile);                                            \
         if (rows_ != ld_rows) {   /* only a matrix's last tile clamps */                           \
@@ -226,7 +177,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_stream(MvGroup grp, int nb,
 
     TileCursor out_cur;
     cursor_init(grp, out_cur, first.tile);
-    TileRef tr_out = cursor_tile(grp, out_cur, first.tile);   // matrix and rows of the tile being computed
+    TileRef tr_out = cursor_tile<kMvTile>(grp, out_cur, first.tile);   // matrix and rows of the tile being computed
     auto compute_and_store = [&](Item it) {
         const int sb = min(SB, nb - it.st * SB);
         const half8_t *ax = lds_x + (it.st * SB * 2 * 4) * NR + arow;
@@ -267,7 +218,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_stream(MvGroup grp, int nb,
         Q2_0_ISSUE(load, reg)
         compute_and_store(cur);
         __builtin_amdgcn_wave_barrier();
-        if (k + 1 < n_items && nxt.tile != cur.tile) tr_out = cursor_tile(grp, out_cur, nxt.tile);
+        if (k + 1 < n_items && nxt.tile != cur.tile) tr_out = cursor_tile<kMvTile>(grp, out_cur, nxt.tile);
         cur = nxt;
         nxt = next_item(nxt);
     }
@@ -290,7 +241,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_stream(MvGroup grp, int nb,
                 r1 += p.y;
             }
         }
-        store_tile(tile_ref(grp, first.tile), r0 + pend.x, r1 + pend.y);
+        store_tile(tile_ref<kMvTile>(grp, first.tile), r0 + pend.x, r1 + pend.y);
     }
 }
 

@@ -77,28 +77,40 @@ static void launch_generic_nc(const uint8_t *w, int64_t M, int nb, const XT *x, 
 }
 
 // Fast-path choice.  Rows 16-byte aligned and x 16-byte aligned: the MFMA kernels.
-// Matrices with at least kStreamTiles 16-row tiles stream with whole-K waves; smaller
-// ones split K over the waves of a workgroup to fill the chip.  Anything else takes
-// the generic kernel.
-constexpr int64_t kStreamTiles = 1024;
+// Matrices of at least kStreamRows rows, and every group launch, stream with whole-K
+// waves: one weight row per lane for N <= 2 (mat_vec_bcast.hip), 16-row tiles
+// otherwise (mat_vec_stream.hip).  Smaller single matrices split K over the waves of a
+// workgroup to fill the chip.  Anything else takes the generic kernel.
+constexpr int64_t kStreamRows = 16384;
 
-// The streaming kernel needs the whole activation staged per workgroup; where that
+static int stream_tile_rows(int N) { return N <= 2 ? kMvBcastRows : kMvTile; }
+
+// The streaming kernels need the whole activation staged per workgroup; where that
 // leaves fewer than 8 resident waves per CU the K-split kernel is used instead.
 static bool stream_fits(int N, int nb) {
     int resident = 0;
-    return mat_vec_stream_waves(N, nb, &resident) > 0 && resident >= 8;
+    const int waves = N <= 2 ? mat_vec_bcast_waves(N, nb, &resident) : mat_vec_stream_waves(N, nb, &resident);
+    return waves > 0 && resident >= 8;
+}
+
+// grp counts tiles of stream_tile_rows(N) rows
+static hipError_t launch_streaming(const MvGroup &grp, int nb, const void *x, Act xt, int64_t ldx, int N,
+                                   hipStream_t s) {
+    return N <= 2 ? launch_mat_vec_bcast(grp, nb, x, xt, ldx, N, s)
+                  : launch_mat_vec_stream(grp, nb, x, xt, ldx, N, s);
 }
 
 hipError_t launch_mat_vec(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx, int N,
                           float *y, int64_t ldy, hipStream_t s) {
     if (mat_vec_mfma_eligible(w, M, nb, x, xt, ldx)) {
-        if ((M + kMvTile - 1) / kMvTile >= kStreamTiles && stream_fits(N, nb)) {
+        if (M >= kStreamRows && stream_fits(N, nb)) {
+            const int tr = stream_tile_rows(N);
             MvGroup grp;
             grp.n = 1;
             grp.p[0] = MvProblem{w, y, ldy, (int)M, 0};
             for (int i = 0; i <= kMvMaxGroup; ++i) grp.tile0[i] = i ? INT_MAX : 0;
-            grp.total_tiles = (int)((M + kMvTile - 1) / kMvTile);
-            return launch_mat_vec_stream(grp, nb, x, xt, ldx, N, s);
+            grp.total_tiles = (int)((M + tr - 1) / tr);
+            return launch_streaming(grp, nb, x, xt, ldx, N, s);
         }
         return launch_mat_vec_mfma(w, M, nb, x, xt, ldx, N, y, ldy, s);
     }
@@ -123,6 +135,7 @@ hipError_t launch_mat_vec(const uint8_t *w, int64_t M, int nb, const void *x, Ac
 
 hipError_t launch_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items, int nb,
                                 const void *x, Act xt, int64_t ldx, int N, hipStream_t s) {
+    const int tr = stream_tile_rows(N);
     int64_t i = 0;
     while (i < n_items) {
         // Gather up to kMvMaxGroup consecutive stream-eligible matrices into one launch.
@@ -134,7 +147,7 @@ hipError_t launch_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items,
             const uint8_t *w = static_cast<const uint8_t *>(it.w);
             if (it.M == 0) { ++i; continue; }
             const bool ok = mat_vec_mfma_eligible(w, it.M, nb, x, xt, ldx) && stream_fits(N, nb) &&
-                            tiles + (it.M + kMvTile - 1) / kMvTile < 0x7fffffff;
+                            tiles + (it.M + tr - 1) / tr < 0x7fffffff;
             if (!ok) {
                 if (grp.n) break;   // launch what is gathered first
                 hipError_t e = launch_mat_vec(w, it.M, nb, x, xt, ldx, N, it.y, it.ldy, s);
@@ -144,13 +157,13 @@ hipError_t launch_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items,
             }
             grp.tile0[grp.n] = tiles;
             grp.p[grp.n++] = MvProblem{w, it.y, it.ldy, (int)it.M, tiles};
-            tiles += (int)((it.M + kMvTile - 1) / kMvTile);
+            tiles += (int)((it.M + tr - 1) / tr);
             ++i;
         }
         if (grp.n) {
             for (int k = grp.n; k <= kMvMaxGroup; ++k) grp.tile0[k] = INT_MAX;
             grp.total_tiles = tiles;
-            hipError_t e = launch_mat_vec_stream(grp, nb, x, xt, ldx, N, s);
+            hipError_t e = launch_streaming(grp, nb, x, xt, ldx, N, s);
             if (e != hipSuccess) return e;
         }
     }

@@ -62,6 +62,27 @@ __device__ __forceinline__ float4_t load_act4<bf16_t>(const bf16_t *p) {
                     __builtin_bit_cast(float, v.y << 16), __builtin_bit_cast(float, v.y & 0xffff0000u)};
 }
 
+// Two consecutive activations as f32; p is aligned to two elements.
+template <typename XT>
+__device__ __forceinline__ float2_t load_act2(const XT *p);
+
+template <>
+__device__ __forceinline__ float2_t load_act2<float>(const float *p) {
+    return *reinterpret_cast<const float2_t *>(p);
+}
+
+template <>
+__device__ __forceinline__ float2_t load_act2<_Float16>(const _Float16 *p) {
+    const half2_t v = *reinterpret_cast<const half2_t *>(p);
+    return float2_t{(float)v.x, (float)v.y};
+}
+
+template <>
+__device__ __forceinline__ float2_t load_act2<bf16_t>(const bf16_t *p) {
+    const uint32_t v = *reinterpret_cast<const uint32_t *>(p);
+    return float2_t{__builtin_bit_cast(float, v << 16), __builtin_bit_cast(float, v & 0xffff0000u)};
+}
+
 // Runs f(XT{}) with XT the element type of a (host side).
 template <typename F>
 inline hipError_t with_act(Act a, F &&f) {
