@@ -18,6 +18,8 @@
 // weight.
 #pragma once
 
+#include <cstddef>
+
 #include "q2_0_internal.h"
 
 namespace q2_0 {
@@ -48,13 +50,19 @@ struct MvGroup {
     int total_tiles;
 };
 
-__device__ __forceinline__ int find_problem(const MvGroup &grp, int tile) {
-    // binary search: the last i with tile0[i] <= tile (tile0 ascends, INT_MAX past n)
-    int idx = 0;
-#pragma unroll
-    for (int step = kMvMaxGroup / 2; step >= 1; step >>= 1)
-        if (grp.tile0[idx + step] <= tile) idx += step;
-    return idx;
+// The launch's tile table, one entry per lane: lane i holds grp.tile0[i] (i < 64;
+// entries from n on are INT_MAX).  Loaded once per wave with one vector load from the
+// kernel arguments, it turns every later matrix lookup into a ballot.
+__device__ __forceinline__ int load_tile_table(const MvGroup &grp) {
+    static_assert(kMvMaxGroup == 64, "one table entry per lane");
+    // (a C cast: the kernel-argument address space converts to a generic pointer)
+    const int *t = (const int *)((const uint8_t *)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(MvGroup, tile0));
+    return t[__lane_id()];
+}
+
+// The last i with tile0[i] <= tile (tile0 ascends, so those i are a prefix); uniform.
+__device__ __forceinline__ int find_problem(int t0v, int tile) {
+    return (int)__popcll(__ballot(t0v <= tile)) - 1;
 }
 
 // The wave's current matrix and tile, all wave-uniform.
@@ -67,9 +75,10 @@ struct TileRef {
 };
 
 template <int TILE>
-__device__ __forceinline__ TileRef tile_ref(const MvGroup &grp, int tile) {
-    const MvProblem &p = grp.p[find_problem(grp, tile)];
-    return TileRef{p.w, p.y, p.ldy, p.M, (tile - p.tile0) * TILE};
+__device__ __forceinline__ TileRef tile_ref(const MvGroup &grp, int t0v, int tile) {
+    const int idx = find_problem(t0v, tile);
+    const MvProblem &p = grp.p[idx];
+    return TileRef{p.w, p.y, p.ldy, p.M, (tile - __builtin_amdgcn_readlane(t0v, idx)) * TILE};
 }
 
 // A wave's tiles only move forward, so it follows them with a cursor: the current
@@ -80,25 +89,25 @@ struct TileCursor {
     int idx, t0, t1;
 };
 
-__device__ __forceinline__ void cursor_load(const MvGroup &grp, TileCursor &c) {
+__device__ __forceinline__ void cursor_load(const MvGroup &grp, int t0v, TileCursor &c) {
     const MvProblem &p = grp.p[c.idx];
     c.r = TileRef{p.w, p.y, p.ldy, p.M, 0};
-    c.t0 = grp.tile0[c.idx];
-    c.t1 = grp.tile0[c.idx + 1];
+    c.t0 = __builtin_amdgcn_readlane(t0v, c.idx);
+    c.t1 = c.idx + 1 < kMvMaxGroup ? __builtin_amdgcn_readlane(t0v, c.idx + 1) : 0x7fffffff;
 }
 
-__device__ __forceinline__ void cursor_init(const MvGroup &grp, TileCursor &c, int tile) {
-    c.idx = find_problem(grp, tile);
-    cursor_load(grp, c);
+__device__ __forceinline__ void cursor_init(const MvGroup &grp, int t0v, TileCursor &c, int tile) {
+    c.idx = find_problem(t0v, tile);
+    cursor_load(grp, t0v, c);
 }
 
 // The tile's matrix and rows (TILE rows per tile); tile >= every tile the cursor
 // was moved to before.
 template <int TILE>
-__device__ __forceinline__ TileRef cursor_tile(const MvGroup &grp, TileCursor &c, int tile) {
+__device__ __forceinline__ TileRef cursor_tile(const MvGroup &grp, int t0v, TileCursor &c, int tile) {
     if (tile >= c.t1) {
-        do ++c.idx; while (grp.tile0[c.idx + 1] <= tile);
-        cursor_load(grp, c);
+        c.idx = find_problem(t0v, tile);
+        cursor_load(grp, t0v, c);
         // wait for the argument loads here, on the rare path: a wait left to the join
         // would also wait, on every tile, for the LDS stores just issued (one counter
         // covers both).  lgkmcnt(0), vmcnt and expcnt untouched.
@@ -108,6 +117,18 @@ __device__ __forceinline__ TileRef cursor_tile(const MvGroup &grp, TileCursor &c
     t.m0 = (tile - c.t0) * TILE;
     return t;
 }
+
+// floor(a * b / c) for 0 <= a, b and 0 < c with a * b < 2^53, without a 64-bit integer
+// division: the double quotient, corrected by at most one either way.
+__device__ __forceinline__ int64_t mul_div(int64_t a, int64_t b, int64_t c) {
+    const int64_t p = a * b;
+    int64_t q = (int64_t)((double)p / (double)c);
+    if (q * c > p) --q;
+    else if ((q + 1) * c <= p) ++q;
+    return q;
+}
+
+__device__ __forceinline__ int64_t div_floor(int64_t a, int64_t c) { return mul_div(a, 1, c); }
 
 __device__ __forceinline__ half8_t as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
     typedef uint32_t u4 __attribute__((ext_vector_type(4)));
@@ -308,8 +329,9 @@ int mat_vec_stream_waves(int N, int nb, int *resident);
 hipError_t launch_mat_vec_stream(const MvGroup &grp, int nb, const void *x, Act xt, int64_t ldx, int N,
                                  hipStream_t s);
 // N = 1, 2; grp counts tiles of kMvBcastRows rows
-size_t mat_vec_bcast_lds(int N, int nb, int waves);
-int mat_vec_bcast_waves(int N, int nb, int *resident);
+size_t mat_vec_bcast_lds(int N, int nb, int waves, bool exact);
+int mat_vec_bcast_waves(int N, int nb, bool exact, int *resident);
+int mat_vec_bcast_waves(int N, int nb, int *resident);   // for the mode the launch picks
 hipError_t launch_mat_vec_bcast(const MvGroup &grp, int nb, const void *x, Act xt, int64_t ldx, int N,
                                 hipStream_t s);
 

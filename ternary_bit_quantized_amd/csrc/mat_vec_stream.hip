@@ -70,17 +70,21 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_stream(MvGroup grp, int nb,
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 15, g = lane >> 4;
     const int total = grp.total_tiles;
+    const int t0v = load_tile_table(grp);   // the tile table, one entry per lane
     const int ns = (nb + SB - 1) / SB;
     const uint32_t rowbytes = (uint32_t)nb * kBlockBytes;
     const bool ragged = (nb % SB) != 0;   // the last stage of a row holds SB/2 blocks
 
     // This workgroup's tiles [tb0, tb1) and this wave's items [i0, i1) among them.
-    const int tb0 = (int)((int64_t)total * blockIdx.x / gridDim.x);
-    const int tb1 = (int)((int64_t)total * (blockIdx.x + 1) / gridDim.x);
+    // (products and quotients without 64-bit integer divisions, which would cost
+    // hundreds of instructions before the first load)
+    const int tb0 = (int)mul_div(total, blockIdx.x, gridDim.x);
+    const int tb1 = (int)mul_div(total, blockIdx.x + 1, gridDim.x);
     const int64_t n_wg = (int64_t)(tb1 - tb0) * ns;
-    const int64_t i0 = n_wg * wave / WAVES, i1 = n_wg * (wave + 1) / WAVES;
+    const int64_t i0 = mul_div(n_wg, wave, WAVES), i1 = mul_div(n_wg, wave + 1, WAVES);
     const int n_items = (int)(i1 - i0);
-    const Item first{tb0 + (int)(i0 / ns), (int)(i0 % ns)};
+    const int64_t i0_tile = div_floor(i0, ns);
+    const Item first{tb0 + (int)i0_tile, (int)(i0 - i0_tile * ns)};
 
     // Per-lane chunk geometry of a stage: chunk q*64 + lane -> tile row cr, 16-byte column
     // cc, parked at lds_off.  In a half stage (SB/2 blocks) the chunks past its end load a
@@ -107,10 +111,10 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_stream(MvGroup grp, int nb,
     const uint8_t *ld_base = nullptr;   // first byte of the tile being loaded (uniform)
     int ld_tile = -1, ld_rows = -1;
     TileCursor ld_cur;
-    cursor_init(grp, ld_cur, first.tile);
+    cursor_init(grp, t0v, ld_cur, first.tile);
 #define Q2_0_SET_LOAD_TILE(TILE)                                                                   \
     {                                                                                              \
-        const TileRef tr_ = cursor_tile<kMvTile>(grp, ld_cur, (TILE));                             \
+        const TileRef tr_ = cursor_tile<kMvTile>(grp, t0v, ld_cur, (TILE));                             \
         ld_base = tr_.w + (int64_t)tr_.m0 * rowbytes;                                              \
         const int rows_ = min(tr_.M - tr_.m0, kMvTile);                                            \
         if (rows_ != ld_rows) {   /* only a matrix's last tile clamps */                           \
@@ -176,8 +180,8 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_stream(MvGroup grp, int nb,
     };
 
     TileCursor out_cur;
-    cursor_init(grp, out_cur, first.tile);
-    TileRef tr_out = cursor_tile<kMvTile>(grp, out_cur, first.tile);   // matrix and rows of the tile being computed
+    cursor_init(grp, t0v, out_cur, first.tile);
+    TileRef tr_out = cursor_tile<kMvTile>(grp, t0v, out_cur, first.tile);   // matrix and rows of the tile being computed
     auto compute_and_store = [&](Item it) {
         const int sb = min(SB, nb - it.st * SB);
         const half8_t *ax = lds_x + (it.st * SB * 2 * 4) * NR + arow;
@@ -218,7 +222,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_stream(MvGroup grp, int nb,
         Q2_0_ISSUE(load, reg)
         compute_and_store(cur);
         __builtin_amdgcn_wave_barrier();
-        if (k + 1 < n_items && nxt.tile != cur.tile) tr_out = cursor_tile<kMvTile>(grp, out_cur, nxt.tile);
+        if (k + 1 < n_items && nxt.tile != cur.tile) tr_out = cursor_tile<kMvTile>(grp, t0v, out_cur, nxt.tile);
         cur = nxt;
         nxt = next_item(nxt);
     }
@@ -228,9 +232,10 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_stream(MvGroup grp, int nb,
 
     // An unfinished last tile leaves its partial sums for the wave that holds the
     // tile's last stage; that wave adds the earlier waves' partials in order.
-    const bool open_end = n_items > 0 && ((int)((i1 - 1) % ns) != ns - 1);
+    const int64_t last_tile = div_floor(i1 - 1, ns);
+    const bool open_end = n_items > 0 && (i1 - 1 - last_tile * ns != ns - 1);
     if (open_end) lds_part[wave * 64 + lane] = float2_t{acc0[0] + acc1[0], acc0[1] + acc1[1]};
-    if (lane == 0) lds_part_tile[wave] = open_end ? (tb0 + (int)((i1 - 1) / ns)) : -1;
+    if (lane == 0) lds_part_tile[wave] = open_end ? (tb0 + (int)last_tile) : -1;
     __syncthreads();
     if (has_pend) {
         float r0 = 0.f, r1 = 0.f;
@@ -241,7 +246,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_stream(MvGroup grp, int nb,
                 r1 += p.y;
             }
         }
-        store_tile(tile_ref<kMvTile>(grp, first.tile), r0 + pend.x, r1 + pend.y);
+        store_tile(tile_ref<kMvTile>(grp, t0v, first.tile), r0 + pend.x, r1 + pend.y);
     }
 }
 
