@@ -480,6 +480,40 @@ def test_mat_vec_stream_across_k(K, N):
     assert_products(y, w, M, K, x, REL_F32, what="stream K=%d N=%d" % (K, N))
 
 
+@pytest.mark.parametrize("K,N", [(4096, 1), (12288, 1), (4096, 2)])
+def test_mat_vec_stream_nonfinite_activation(K, N):
+    """An inf or NaN activation makes every output of its column non-finite, as in the
+    oracle (a zero weight times inf is NaN); the other column stays within tolerance."""
+    M = 16384 + 5
+    w = synth.weight(26, K // 64, N, M, K, "tern_c3", synth.ScaleDist("uniform", 0.005, 0.05))
+    x = synth.activations(26, K // 64, N, N, K)
+    x[0, 100] = np.inf
+    if N == 2:
+        x[0, 7] = np.nan
+    y = run_mat_vec(dev(w), M, K, x, ldy=M + 3)
+    rows = np.arange(0, M, 7)
+    y_ref, bound = oracle.mul_mat(w, M, K, x, rows=rows)
+    assert not np.isfinite(y_ref[0]).any()
+    assert not np.isfinite(y[0]).any(), "column with an inf activation gave finite outputs"
+    if N == 2:
+        assert np.isfinite(y[1]).all()
+        r = oracle.check_products(y[1:, rows], y_ref[1:], bound[1:], REL_F32)
+        assert r["ok"], r
+
+
+@pytest.mark.parametrize("K", [4096, 12288])
+def test_mat_vec_stream_blocks_of_far_apart_magnitudes(K):
+    """Each 64-weight block of the activation scaled by its own power of ten, 1e-30 .. 1e30:
+    the per-block (N = 1, K <= 8192) and per-column staging both meet the bound."""
+    M, N = 16384 + 5, 1
+    w = synth.weight(27, K // 64, N, M, K, "quad", synth.ScaleDist("uniform", 0.005, 0.05))
+    x = synth.activations(27, K // 64, N, N, K)
+    rng = np.random.default_rng(27)
+    x *= (10.0 ** rng.integers(-30, 31, K // 64)).repeat(64).astype(np.float32)[None, :]
+    y = run_mat_vec(dev(w), M, K, x)
+    assert_products(y, w, M, K, x, REL_F32, rows=np.arange(0, M, 3), what="far-apart blocks K=%d" % K)
+
+
 def test_mat_vec_group_ragged_members_long_rows():
     """Group members whose row counts leave partial tiles, at K = 12288 (12 stages a row)."""
     K, N = 12288, 1
