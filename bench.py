@@ -54,7 +54,7 @@ F16_MFMA_PEAK_TFLOPS = 2500.0
 PREFILL_N = 512
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "mat_vec_stream_gemm_f16_hbm_traffic.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "mat_vec_bcast_gemm_f16_hbm_traffic.md")
 
 
 def kernel_sources_sha256() -> str:
@@ -448,9 +448,10 @@ def main():
                 round(pre_flops / (ms["prefill_gemm_per_matrix"] * 1e-3) / 1e12, 1),
         },
         "roofline": {
-            "kernel": "mat_vec_stream (N=1; %d grouped launches per decode token)" % n_dec_launches,
+            "kernel": "mat_vec_bcast (N=1; %d grouped launches per decode token: exact mode where K <= 8192, "
+                      "hi/lo mode at K = 12288)" % n_dec_launches,
             "bound": "hbm", "achieved": round(matvec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(matvec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic.get("mat_vec_stream"),
+            "frac": round(matvec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic.get("mat_vec_bcast"),
             "bytes_per_launch_avg": int(dec_bytes / n_dec_launches),
             "avg_launch_us": round(ms["decode_mat_vec"] * 1e3 / n_dec_launches, 3),
         },
