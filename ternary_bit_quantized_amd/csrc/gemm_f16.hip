@@ -37,7 +37,7 @@ namespace q2_0 {
 
 namespace {
 
-constexpr int GM = 128, GN = 128, GK = 64;
+constexpr int GM = 128, GN = 128, GK = 64;   // GM: row tile of the expert path
 constexpr int GLD = GK + 8;   // fp16 row stride in LDS (144 B): 8 consecutive rows hit distinct banks
 
 // x (N columns of K floats) -> fp16, k permuted inside each 16-group, one workgroup
@@ -138,28 +138,40 @@ __global__ __launch_bounds__(256) void x_to_f16_perm(const XT *__restrict__ x, i
     }
 }
 
-// 16 weights of one code word as fp16 d*(q-1), in pair order (code s of the low
-// half, code s of the high half), s = 0..7.
-__device__ __forceinline__ void dequant_word_f16(uint32_t word, uint32_t d2, const PairMasks &pm,
-                                                 uint32_t out[8]) {
-    const uint32_t hi = word >> 10;
-    out[0] = pair_qm1<0>(word, pm); out[1] = pair_qm1<1>(word, pm);
-    out[2] = pair_qm1<2>(word, pm); out[3] = pair_qm1<3>(word, pm);
-    out[4] = pair_qm1<4>(word, pm); out[5] = pair_qm1<0>(hi, pm);
-    out[6] = pair_qm1<1>(hi, pm);   out[7] = pair_qm1<2>(hi, pm);
-    const half2_t dd = __builtin_bit_cast(half2_t, d2);
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-        out[s] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, out[s]) * dd);
-}
+// ---- W staging.  Each wave owns 32*RF rows of the tile (RF = 1 or 2 row fragments) and
+// decodes them itself, straight into its MFMA A operands; no fp16 copy of W passes
+// through LDS.  Per group of four blocks (72 bytes of a row) lane (rr, hf) of the wave
+// loads block pair hf of its rows rr + 32i (36 bytes each, three 12-byte loads: 128 rows
+// x 72 bytes take 3 coalesced loads per thread where one 2-byte load per scale and
+// half-word took 24), regroups them, and writes them to
+// the wave's raw area: per row 80 bytes, the four blocks' 4 code words each (an even
+// block's words straddle dwords and are realigned with one v_perm), then the four
+// scales, each as a half pair (d, d).  The area is private to the wave, so LDS program
+// order alone orders its writes and reads (no barrier).
+constexpr int kWRowDw = 20;                   // raw-area dwords per row (80 bytes)
 
-// A step's code words and scales as loaded.  Nothing is computed from them until the
-// step is stored, two steps later: an ALU op on a fresh load would make the wave wait
-// for it right away.
-struct WRegs {
-    uint32_t d[2];      // half scale (low 16 bits)
-    uint32_t word[2];
-};
+// Raw bytes of one block pair (9 dwords) at byte off of a row of rowbytes bytes.
+// kAligned (rows of an even number of blocks from a 4-byte-aligned matrix): three
+// 12-byte loads, the pair's offset clamped to the row's last 36 bytes.  Otherwise 2-byte
+// loads, each clamped to the row's last two bytes.  Either way the loads stay inside
+// the row; data past the split's blocks is never used.
+template <bool kAligned>
+__device__ __forceinline__ void load_pair(const uint8_t *row, int off, int rowbytes, uint32_t r[9]) {
+    if constexpr (kAligned) {
+        const uint8_t *p = row + min(off, rowbytes - 36);
+        const u32x3_t a = *reinterpret_cast<const u32x3_t *>(p);
+        const u32x3_t b = *reinterpret_cast<const u32x3_t *>(p + 12);
+        const u32x3_t c = *reinterpret_cast<const u32x3_t *>(p + 24);
+        r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = b.x; r[4] = b.y; r[5] = b.z; r[6] = c.x; r[7] = c.y; r[8] = c.z;
+    } else {
+        const uint16_t *h = reinterpret_cast<const uint16_t *>(row);
+        const int lim = (rowbytes >> 1) - 1;
+        const int o = off >> 1;
+#pragma unroll
+        for (int i = 0; i < 9; ++i)
+            r[i] = (uint32_t)h[min(o + 2 * i, lim)] | ((uint32_t)h[min(o + 2 * i + 1, lim)] << 16);
+    }
+}
 
 }  // namespace
 
@@ -177,15 +189,22 @@ __device__ __forceinline__ int find_gemm_item(const GemmGroup &grp, int tmg) {
 // splits > 1: workgroup (tile, split) covers blocks [split*nbs, (split+1)*nbs) and writes
 // its partial tile to the item's part + split*N*M (column n at n*M); gemm_split_reduce
 // then adds the partials in split order.
-__global__ __launch_bounds__(256, 2) void gemm_f16_mfma(GemmGroup grp, int nb, const _Float16 *__restrict__ x16,
-                                                        const int *__restrict__ xe, int N, int tiles_n,
-                                                        int xcd_map, int splits) {
-    __shared__ __attribute__((aligned(16))) _Float16 As[2][GM * GLD];
+// Steps run in groups of four blocks; a split's last group is padded past its end with
+// steps whose A and B operands are zero.  NSETS register sets carry the x tiles in
+// flight (each loaded NSETS steps before it is stored to LDS).  The workgroup tile is
+// (128 RF) x 128: four waves of (32 RF) x 128.
+template <int RF, int NSETS, bool kAligned, int OCC>
+__global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb, const _Float16 *__restrict__ x16,
+                                                          const int *__restrict__ xe, int N, int tiles_n,
+                                                          int xcd_map, int splits) {
+    static_assert(NSETS == 1 || NSETS == 2 || NSETS == 4, "one, two or four register sets");
+    static_assert(RF == 1 || RF == 2, "one or two row fragments per wave");
+    constexpr int TM = 128 * RF, kWRows = 32 * RF, kWAreaDw = kWRows * kWRowDw;
     __shared__ __attribute__((aligned(16))) _Float16 Bs[2][GN * GLD];
+    __shared__ __attribute__((aligned(16))) uint32_t Wraw[4 * kWAreaDw];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave & 1, wn = wave >> 1;   // 64 x 64 sub-tile of this wave
 
     // ---- tile of this workgroup (row tile tmg counted across the call).  xcd_map: XCD
     // j = blockIdx % 8 handles column tile j % tiles_n and every (8 / tiles_n)-th row tile.
@@ -213,7 +232,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_mfma(GemmGroup grp, int nb, c
         itp = &grp.p[find_gemm_item(grp, tmg)];
         w = itp->w;
         M = itp->M;
-        m0 = (tmg - itp->tm0) * GM;
+        m0 = (tmg - itp->tm0) * TM;
         n0 = tn * GN;
     } else {
         const int t = blockIdx.x / grp.moe_tiles_m;
@@ -222,27 +241,57 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_mfma(GemmGroup grp, int nb, c
         itp = &grp.p[0];
         w = itp->w + e * grp.moe_expert_bytes;
         M = itp->M;
-        m0 = (blockIdx.x % grp.moe_tiles_m) * GM;
+        m0 = (blockIdx.x % grp.moe_tiles_m) * TM;
         n0 = grp.moe_tiles[2 * t + 1] * GN;
         col0 = grp.moe_off[e];
         Nv = grp.moe_off[e + 1] - col0;
     }
     const GemmItem &item = *itp;
     const int K = nb * kBlockWeights;
-    const int64_t rowbytes = (int64_t)nb * kBlockBytes;
+    const int rowbytes = nb * kBlockBytes;
     const int nbs = nb / splits;                 // blocks of this split
     const int kb0 = split * nbs;
+    const int ngroups = (nbs + 3) >> 2;
 
-    // ---- loader roles: two code words (rows r0, r0 + 64; word g) and four 16-byte x chunks.
-    // Rows past M and columns past N read row / column 0 instead: they only feed
-    // outputs that are never stored, so the loads need no guard (and no branch).
-    const int g = tid & 3, r0 = tid >> 2;
-    const uint8_t *wrow[2];
+    // ---- W loader: lane (rr, hf) = block pair hf of rows rr + 32i of this wave's rows.  Rows
+    // past M read row M-1 (they feed outputs that are never stored); byte offsets are
+    // clamped to the row's last 36 bytes, so a padded group stays inside the matrix.
+    const int wrow0 = m0 + kWRows * wave;
+    const int rbase = min(wrow0, M - 1);
+    const uint8_t *const wbase = w + (int64_t)rbase * rowbytes;
+    const int rr = lane >> 1, hf = lane & 1;
+    uint32_t roff[RF];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int row = m0 + r0 + 64 * i;
-        wrow[i] = w + (int64_t)(row < M ? row : 0) * rowbytes + (int64_t)kb0 * kBlockBytes;
-    }
+    for (int i = 0; i < RF; ++i) roff[i] = (uint32_t)(min(wrow0 + rr + 32 * i, M - 1) - rbase) * (uint32_t)rowbytes;
+    auto load_raw = [&](int grp4, uint32_t (&r)[RF][9]) {
+#pragma unroll
+        for (int i = 0; i < RF; ++i)
+            load_pair<kAligned>(wbase + roff[i], (kb0 + 4 * grp4 + 2 * hf) * kBlockBytes, rowbytes, r[i]);
+    };
+    uint32_t *const warea = Wraw + wave * kWAreaDw;
+    auto write_raw = [&](int grp4, const uint32_t (&rs)[RF][9]) {
+        const int blk = 4 * grp4 + 2 * hf;       // even block of this pair, within the split
+#pragma unroll
+        for (int i = 0; i < RF; ++i) {
+            const uint32_t *r = rs[i];
+            u32x4_t ev, od;
+            ev.x = __builtin_amdgcn_perm(r[1], r[0], 0x05040302u);
+            ev.y = __builtin_amdgcn_perm(r[2], r[1], 0x05040302u);
+            ev.z = __builtin_amdgcn_perm(r[3], r[2], 0x05040302u);
+            ev.w = __builtin_amdgcn_perm(r[4], r[3], 0x05040302u);
+            od = u32x4_t{r[5], r[6], r[7], r[8]};
+            const uint32_t de = blk < nbs ? __builtin_amdgcn_perm(r[0], r[0], 0x01000100u) : 0u;
+            const uint32_t dod = blk + 1 < nbs ? __builtin_amdgcn_perm(r[4], r[4], 0x03020302u) : 0u;
+            uint32_t *row = warea + (rr + 32 * i) * kWRowDw;
+            *reinterpret_cast<u32x4_t *>(row + 8 * hf) = ev;
+            *reinterpret_cast<u32x4_t *>(row + 8 * hf + 4) = od;
+            *reinterpret_cast<u32x2_t *>(row + 16 + 2 * hf) = u32x2_t{de, dod};
+        }
+    };
+
+    // ---- x loader: four 16-byte chunks per thread (column c >> 3, k chunk c & 7).
+    // Columns past N read column 0 (outputs never stored); blocks past the split are
+    // clamped to its last block and stored to LDS as zeros.
     const _Float16 *xcol[4];
     int xn[4], xpart[4];
 #pragma unroll
@@ -253,109 +302,108 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_mfma(GemmGroup grp, int nb, c
         const int n = n0 + xn[q];
         xcol[q] = x16 + (int64_t)(col0 + (n < Nv ? n : 0)) * K + (int64_t)kb0 * GK + 8 * xpart[q];
     }
-
-    // Loads of a step past the last are clamped to the last block (harmless reloads),
-    // so every step issues the same loads and the wait counts stay exact.
-    auto load_w = [&](int blk, WRegs &r) {
-        blk = min(blk, nbs - 1);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const uint16_t *b16 = reinterpret_cast<const uint16_t *>(wrow[i] + (int64_t)blk * kBlockBytes);
-            r.d[i] = b16[0];
-            r.word[i] = (uint32_t)b16[1 + 2 * g] | ((uint32_t)b16[2 + 2 * g] << 16);
-        }
-    };
     auto load_x = [&](int blk, u32x4_t (&r)[4]) {
         blk = min(blk, nbs - 1);
 #pragma unroll
         for (int q = 0; q < 4; ++q) r[q] = *reinterpret_cast<const u32x4_t *>(xcol[q] + (int64_t)blk * GK);
     };
-    const PairMasks pm;
-    auto store_stage = [&](int buf, const WRegs &wr, const u32x4_t (&xr)[4]) {
+    auto store_x = [&](int buf, int blk, const u32x4_t (&xr)[4]) {
+        if (blk < nbs) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            uint32_t o[8];
-            dequant_word_f16(wr.word[i], wr.d[i] | (wr.d[i] << 16), pm, o);
-            u32x4_t *dst = reinterpret_cast<u32x4_t *>(&As[buf][(r0 + 64 * i) * GLD + 16 * g]);
-            dst[0] = u32x4_t{o[0], o[1], o[2], o[3]};
-            dst[1] = u32x4_t{o[4], o[5], o[6], o[7]};
+            for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4_t *>(&Bs[buf][xn[q] * GLD + 8 * xpart[q]]) = xr[q];
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4_t *>(&Bs[buf][xn[q] * GLD + 8 * xpart[q]]) = u32x4_t{};
         }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<u32x4_t *>(&Bs[buf][xn[q] * GLD + 8 * xpart[q]]) = xr[q];
     };
 
-    float16_t acc[2][2];
+    float16_t acc[RF][4];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int i = 0; i < RF; ++i)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = float16_t{};
+        for (int j = 0; j < 4; ++j) acc[i][j] = float16_t{};
 
-    // A lane l: row l%32 of a 32-row sub-tile, k-slot (l/32)*8; B lane: column l%32.
+    // A lane l: row l%32 of a row fragment, k-slot (l/32)*8 of each 16-k step: word kk of
+    // the block, code pairs 4h..4h+3 (h = l/32; the word is shifted down 8h bits so that
+    // they sit at pairs 0..3).  In the permuted k order of x16 these are exactly the 8 k
+    // that B lane (column, h) holds.  B lane: column l%32 of a 32-column sub-tile.
     const int frow = lane & 31, fk = (lane >> 5) * 8;
-    auto mma_stage = [&](int buf) {
+    const uint32_t sh = (uint32_t)(lane >> 5) * 8u;
+    const PairMasks pm;
+    const uint32_t *const wmy = warea + frow * kWRowDw;
+    auto step = [&](int buf, int b) {
+        u32x4_t wd[RF];
+        half2_t dd[RF];
 #pragma unroll
-        for (int kk = 0; kk < GK / 16; ++kk) {
-            half8_t a[2], bv[2];
+        for (int i = 0; i < RF; ++i) {
+            wd[i] = *reinterpret_cast<const u32x4_t *>(wmy + 32 * i * kWRowDw + 4 * b);
+            dd[i] = __builtin_bit_cast(half2_t, wmy[32 * i * kWRowDw + 16 + b]);
+        }
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                a[i] = *reinterpret_cast<const half8_t *>(&As[buf][(wm * 64 + i * 32 + frow) * GLD + kk * 16 + fk]);
+        for (int kk = 0; kk < 4; ++kk) {
+            half8_t a[RF];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                bv[i] = *reinterpret_cast<const half8_t *>(&Bs[buf][(wn * 64 + i * 32 + frow) * GLD + kk * 16 + fk]);
+            for (int i = 0; i < RF; ++i) {
+                const uint32_t c = wd[i][kk] >> sh;
+                const half2_t d2 = dd[i];
+                a[i] = as_half8(__builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, pair_qm1<0>(c, pm)) * d2),
+                                __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, pair_qm1<1>(c, pm)) * d2),
+                                __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, pair_qm1<2>(c, pm)) * d2),
+                                __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, pair_qm1<3>(c, pm)) * d2));
+            }
+            half8_t bv[4];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int j = 0; j < 4; ++j)
+                bv[j] = *reinterpret_cast<const half8_t *>(&Bs[buf][(j * 32 + frow) * GLD + kk * 16 + fk]);
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj)
-                    acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], bv[jj], acc[i][jj], 0, 0, 0);
+            for (int i = 0; i < RF; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], bv[j], acc[i][j], 0, 0, 0);
         }
     };
 
-    // ---- pipeline: registers hold step s+1 while step s computes; loads run two steps ahead
-    WRegs wA, wB;
-    u32x4_t xA[4], xB[4];
-    load_w(0, wA);
-    load_x(0, xA);
-    load_w(1, wB);
-    load_x(1, xB);
-    store_stage(0, wA, xA);
-    load_w(2, wA);
-    load_x(2, xA);
+    // ---- pipeline: x tiles double buffered in LDS (one barrier per step), NSETS x
+    // register sets in flight; W raw groups loaded one group ahead into registers and
+    // written to the wave's area after the group's last step has read it.
+    uint32_t wr[RF][9];
+    u32x4_t xr[NSETS][4];
+    load_raw(0, wr);
+#pragma unroll
+    for (int i = 0; i < NSETS; ++i) load_x(i, xr[i]);
+    write_raw(0, wr);
+    load_raw(1, wr);
+    store_x(0, 0, xr[0]);
+    load_x(NSETS, xr[0]);
     __syncthreads();
 
-    // Two steps per iteration so that the register sets alternate statically.  The loop
-    // has no exit in the middle (an exit there makes the compiler keep the
-    // accumulators in two register sets and copy between them every iteration); an
-    // odd last step runs after it.
-    int s = 0;
-    for (; s + 1 < nbs; s += 2) {
-        __builtin_amdgcn_iglp_opt(0);    // let the scheduler interleave MFMA with the step's other work
-        mma_stage(0);
-        store_stage(1, wB, xB);          // step s+1
-        load_w(s + 3, wB);
-        load_x(s + 3, xB);
-        __syncthreads();
-        __builtin_amdgcn_iglp_opt(0);
-        mma_stage(1);
-        store_stage(0, wA, xA);          // step s+2 (a clamped duplicate past the end)
-        load_w(s + 4, wA);
-        load_x(s + 4, xA);
-        __syncthreads();
+    for (int g = 0; g < ngroups; ++g) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int t = 4 * g + u;
+            step(u & 1, u);
+            if (u == 3) {
+                write_raw(g + 1, wr);    // read from the next step on
+                load_raw(g + 2, wr);
+            }
+            store_x((u + 1) & 1, t + 1, xr[(u + 1) % NSETS]);
+            load_x(t + 1 + NSETS, xr[(u + 1) % NSETS]);
+            __syncthreads();
+        }
     }
-    if (s < nbs) mma_stage(0);
 
     // ---- epilogue: D lane l, register v -> row 8*(v/4) + 4*(l/32) + v%4, column l%32
     // Results are scaled back by the column's 2^-e first (exact), so partials and y
     // hold the same numbers.
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 4; ++j) {
+        const int n = n0 + j * 32 + (lane & 31);
+        const int ye = -xe[col0 + (n < Nv ? n : 0)];
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int n = n0 + wn * 64 + jj * 32 + (lane & 31);
-            const int ye = -xe[col0 + (n < Nv ? n : 0)];
+        for (int i = 0; i < RF; ++i)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][jj][v] = __builtin_amdgcn_ldexpf(acc[i][jj][v], ye);
-        }
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_amdgcn_ldexpf(acc[i][j][v], ye);
+    }
     // Stores of a 4-row run of column n at row m: float4 when in range and aligned.
     auto store4 = [&](float *col, int m, const float4_t &val) {
         if (m + 3 < M && ((((uintptr_t)(col + m)) & 15) == 0)) {
@@ -370,19 +418,19 @@ __global__ __launch_bounds__(256, 2) void gemm_f16_mfma(GemmGroup grp, int nb, c
     float *const yout = (splits > 1) ? item.part + (int64_t)split * N * M : item.y;
     const int64_t ldo = (splits > 1) ? M : item.ldy;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 4; ++j) {
+        const int n = n0 + j * 32 + (lane & 31);
+        if (n >= Nv) continue;
+        float *yc = grp.moe_off ? item.y + (int64_t)grp.moe_perm[col0 + n] * item.ldy : yout + (int64_t)n * ldo;
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int n = n0 + wn * 64 + jj * 32 + (lane & 31);
-            if (n >= Nv) continue;
-            float *yc = grp.moe_off ? item.y + (int64_t)grp.moe_perm[col0 + n] * item.ldy : yout + (int64_t)n * ldo;
+        for (int i = 0; i < RF; ++i)
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) {
-                const int m = m0 + wm * 64 + i * 32 + 8 * v4 + 4 * (lane >> 5);
-                store4(yc, m, float4_t{acc[i][jj][4 * v4], acc[i][jj][4 * v4 + 1], acc[i][jj][4 * v4 + 2],
-                                       acc[i][jj][4 * v4 + 3]});
+                const int m = wrow0 + 32 * i + 8 * v4 + 4 * (lane >> 5);
+                store4(yc, m, float4_t{acc[i][j][4 * v4], acc[i][j][4 * v4 + 1], acc[i][j][4 * v4 + 2],
+                                       acc[i][j][4 * v4 + 3]});
             }
-        }
+    }
 }
 
 // y_i[n][m] = sum over splits of part_i[split][n][m], in split order.  Grid: x over
@@ -419,28 +467,63 @@ size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 }  // namespace
 
+// The GEMM kernel for rf row fragments per wave, with 4-byte code loads where every
+// matrix row is 4-byte aligned.
+static void launch_gemm_kernel(unsigned grid, hipStream_t s, const GemmGroup &grp, int nb, const _Float16 *x16,
+                               const int *xe, int N, int tiles_n, int xcd_map, int splits, int rf, bool aligned) {
+    if (rf == 2) {
+        if (aligned)
+            gemm_f16_mfma<2, 2, true, 2><<<grid, 256, 0, s>>>(grp, nb, x16, xe, N, tiles_n, xcd_map, splits);
+        else
+            gemm_f16_mfma<2, 2, false, 2><<<grid, 256, 0, s>>>(grp, nb, x16, xe, N, tiles_n, xcd_map, splits);
+    } else {
+        if (aligned)
+            gemm_f16_mfma<1, 2, true, 2><<<grid, 256, 0, s>>>(grp, nb, x16, xe, N, tiles_n, xcd_map, splits);
+        else
+            gemm_f16_mfma<1, 2, false, 2><<<grid, 256, 0, s>>>(grp, nb, x16, xe, N, tiles_n, xcd_map, splits);
+    }
+}
+
+// Tile shape and K split of a call.  256-row tiles (two row fragments per wave: half
+// the LDS reads per MFMA and half the x traffic of 128-row tiles) where they alone give
+// at least kRf2MinTiles workgroups and the block count is even (4-byte code loads);
+// otherwise 128-row tiles, and K split (at most 8
+// ways, at least 8 blocks a split) until there are 512 workgroups.
+constexpr int kRf2MinTiles = 256;
+struct GemmPlan {
+    int rf, splits;
+};
+static GemmPlan gemm_plan(const int64_t *Ms, int64_t n_items, int nb, int64_t N) {
+    int64_t t1 = 0, t2 = 0;
+    for (int64_t i = 0; i < n_items; ++i) {
+        t1 += (Ms[i] + 127) / 128;
+        t2 += (Ms[i] + 255) / 256;
+    }
+    const int64_t tiles_n = (N + GN - 1) / GN;
+    if (nb % 2 == 0 && t2 * tiles_n >= kRf2MinTiles) return {2, 1};
+    int sp = 1;
+    while (t1 * tiles_n * sp < 512 && sp < 8 && nb % (2 * sp) == 0 && nb / (2 * sp) >= 8) sp *= 2;
+    return {1, sp};
+}
+
 // Workspace of a call: fp16 x (N*K halves), the column exponents (N ints), and with
 // a K split each matrix's partials (splits * N * M floats).
-static size_t gemm_layout(const int64_t *Ms, int64_t n_items, int nb, int64_t N, int *splits_out,
+static size_t gemm_layout(const int64_t *Ms, int64_t n_items, int nb, int64_t N, GemmPlan *plan,
                           size_t *parts_off) {
-    int64_t tiles_m = 0;
-    for (int64_t i = 0; i < n_items; ++i) tiles_m += (Ms[i] + GM - 1) / GM;
+    const GemmPlan pl = gemm_plan(Ms, n_items, nb, N);
     const int64_t K = (int64_t)nb * kBlockWeights;
-    const int tiles_n = (int)((N + GN - 1) / GN);
-    int sp = 1;
-    while (tiles_m * tiles_n * sp < 512 && sp < 8 && nb % (2 * sp) == 0 && nb / (2 * sp) >= 8) sp *= 2;
     size_t off = align256((size_t)N * K * 2) + align256((size_t)N * 4);
     *parts_off = off;
-    if (sp > 1)
-        for (int64_t i = 0; i < n_items; ++i) off += align256((size_t)sp * N * Ms[i] * 4);
-    *splits_out = sp;
+    if (pl.splits > 1)
+        for (int64_t i = 0; i < n_items; ++i) off += align256((size_t)pl.splits * N * Ms[i] * 4);
+    *plan = pl;
     return off;
 }
 
 size_t gemm_f16_workspace_bytes(const int64_t *Ms, int64_t n_items, int64_t K, int64_t N) {
-    int sp;
+    GemmPlan pl;
     size_t po;
-    return gemm_layout(Ms, n_items, (int)(K / kBlockWeights), N, &sp, &po);
+    return gemm_layout(Ms, n_items, (int)(K / kBlockWeights), N, &pl, &po);
 }
 
 hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, const void *x, Act xt,
@@ -449,10 +532,11 @@ hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, c
     int64_t Ms_local[64];
     int64_t *Ms = n_items <= 64 ? Ms_local : new int64_t[n_items];
     for (int64_t i = 0; i < n_items; ++i) Ms[i] = mats[i].M;
-    int splits;
+    GemmPlan plan;
     size_t parts_off;
-    gemm_layout(Ms, n_items, nb, N, &splits, &parts_off);
+    gemm_layout(Ms, n_items, nb, N, &plan, &parts_off);
     if (Ms != Ms_local) delete[] Ms;
+    const int splits = plan.splits, TM = 128 * plan.rf;
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     _Float16 *x16 = reinterpret_cast<_Float16 *>(ws);
     int *xe = reinterpret_cast<int *>(ws + align256((size_t)N * K * 2));
@@ -478,7 +562,6 @@ hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, c
         grp.n = 0;
         grp.tm_base = (int)tm_next;
         grp.moe_off = nullptr;
-        int64_t rows = 0;
         for (int64_t i = i0; i < n_items && i < i0 + kGemmMaxGroup; ++i) {
             const int64_t M = mats[i].M;
             if (M == 0) continue;
@@ -491,8 +574,7 @@ hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, c
             it.tm0 = (int)tm_next;
             grp.tm0[grp.n] = it.tm0;
             ++grp.n;
-            tm_next += (M + GM - 1) / GM;
-            rows += M;
+            tm_next += (M + TM - 1) / TM;
             if (splits > 1) part += align256((size_t)splits * N * M * 4) / 4;
         }
         if (grp.n == 0) continue;
@@ -500,8 +582,10 @@ hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, c
         const int tiles_m = (int)tm_next - grp.tm_base;
         const int per = (tiles_n <= 8 && 8 % tiles_n == 0) ? 8 / tiles_n : 0;
         const int xcd_map = (splits == 1 && per != 0 && tiles_m % per == 0) ? 1 : 0;
-        gemm_f16_mfma<<<tiles_m * tiles_n * splits, 256, 0, s>>>(grp, nb, x16, xe, (int)N, tiles_n, xcd_map,
-                                                                  splits);
+        bool aligned = nb % 2 == 0;
+        for (int k = 0; k < grp.n; ++k) aligned = aligned && ((uintptr_t)grp.p[k].w % 4 == 0);
+        launch_gemm_kernel((unsigned)(tiles_m * tiles_n * splits), s, grp, nb, x16, xe, (int)N, tiles_n, xcd_map,
+                           splits, plan.rf, aligned);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (splits > 1) {
@@ -556,7 +640,8 @@ hipError_t launch_gemm_f16_moe(const uint8_t *w, int64_t M, int nb, const void *
     grp.moe_expert_bytes = M * (int64_t)nb * kBlockBytes;
     grp.moe_tiles_m = tiles_m;
     const int64_t grid = (int64_t)tiles_m * moe_max_tiles(r.n_expert, r.n_pairs, GN);
-    gemm_f16_mfma<<<(unsigned)grid, 256, 0, s>>>(grp, nb, x16, xe, r.n_pairs, 1, 0, 1);
+    launch_gemm_kernel((unsigned)grid, s, grp, nb, x16, xe, (int)r.n_pairs, 1, 0, 1, 1,
+                       nb % 2 == 0 && (uintptr_t)w % 4 == 0);
     return hipGetLastError();
 }
 

@@ -17,6 +17,8 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // IEEE half bits -> f32 (v_cvt_f32_f16: exact for every half, subnormals included).
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
@@ -56,7 +58,6 @@ __device__ __forceinline__ float4_t load_act4<_Float16>(const _Float16 *p) {
 
 template <>
 __device__ __forceinline__ float4_t load_act4<bf16_t>(const bf16_t *p) {
-    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
     const u32x2_t v = *reinterpret_cast<const u32x2_t *>(p);
     return float4_t{__builtin_bit_cast(float, v.x << 16), __builtin_bit_cast(float, v.x & 0xffff0000u),
                     __builtin_bit_cast(float, v.y << 16), __builtin_bit_cast(float, v.y & 0xffff0000u)};

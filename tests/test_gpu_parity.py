@@ -577,6 +577,33 @@ def test_mul_mat_group_matches_oracle(precision, rel, Ms, K, N):
             assert_products(y, w, M, K, x, rel, what="group item M=%d K=%d N=%d" % (M, K, N))
 
 
+def test_mul_mat_group_gate_up_8b_256_row_tiles():
+    """The 8B stack's gate/up pair at N = 512 (192 row tiles of 256 rows x 4 column tiles:
+    the two-row-fragment kernel, no K split); sampled rows of both, run to run bit-equal."""
+    wl = synth.STACK_8B
+    names = ["gate", "up"]
+    K = wl.shapes["gate"][1]
+    mats = [(ws(wl, n, layer=0), wl.shapes[n][0]) for n in names]
+    x = synth.activations(wl.seed, 0, synth.stack_x_matrix_index(K) + 11, 512, K)
+    a = run_gemm_group(mats, K, x, B.Q2_0_PREC_F16_MFMA)
+    b = run_gemm_group(mats, K, x, B.Q2_0_PREC_F16_MFMA)
+    for (w, M), ya, yb, n in zip(mats, a, b, names):
+        assert np.array_equal(ya.view(np.uint32), yb.view(np.uint32)), "run-to-run difference in " + n
+        rows = np.unique(np.concatenate([np.arange(0, M, 61), np.arange(M - 40, M)]))
+        assert_products(ya, w, M, K, x, REL_F16, rows=rows, what="gate/up " + n)
+
+
+def test_mul_mat_256_row_tiles_ragged():
+    """256-row tiles with a partial last row tile (M = 96 * 256 + 77), partial column
+    tile (N = 300) and a padded last step group (K / 64 = 10 blocks)."""
+    M, K, N = 96 * 256 + 77, 640, 300
+    w = synth.weight(29, M, N, M, K, "quad", synth.ScaleDist("loguniform", 1e-3, 1e-1, 0.02))
+    x = synth.activations(29, M, N, N, K)
+    y = run_mul_mat(dev(w), M, K, x, B.Q2_0_PREC_F16_MFMA, ldy=M + 3)
+    rows = np.unique(np.concatenate([np.arange(0, M, 13), np.arange(M - 300, M)]))
+    assert_products(y, w, M, K, x, REL_F16, rows=rows, what="256-row tiles M=%d K=%d N=%d" % (M, K, N))
+
+
 def test_mul_mat_group_prefill_qkv_deterministic():
     wl = synth.PREFILL_1P7B
     names = ["q", "k", "v"]
