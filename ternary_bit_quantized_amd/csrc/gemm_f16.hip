@@ -150,26 +150,36 @@ __global__ __launch_bounds__(256) void x_to_f16_perm(const XT *__restrict__ x, i
 // order alone orders its writes and reads (no barrier).
 constexpr int kWRowDw = 20;                   // raw-area dwords per row (80 bytes)
 
-// Raw bytes of one block pair (9 dwords) at byte off of a row of rowbytes bytes.
-// kAligned (rows of an even number of blocks from a 4-byte-aligned matrix): three
-// 12-byte loads, the pair's offset clamped to the row's last 36 bytes.  Otherwise 2-byte
-// loads, each clamped to the row's last two bytes.  Either way the loads stay inside
-// the row; data past the split's blocks is never used.
+// Raw bytes of one block pair (9 dwords: two 16-byte pieces and a last dword, the form
+// the loads take, so that loop-carried copies stay in the load's register tuples) at
+// byte off of a row of rowbytes bytes.  kAligned (rows of an even number of blocks from
+// a 4-byte-aligned matrix): three loads, the pair's offset clamped to the row's last 36
+// bytes.  Otherwise 2-byte loads, each clamped to the row's last two bytes.  Either way
+// the loads stay inside the row; data past the split's blocks is never used.  (Three
+// loads per pair at least: the kernel's wait counts rely on that lower bound.)
+struct RawPair {
+    u32x4_t a, b;   // dwords 0..3, 4..7
+    uint32_t c;     // dword 8
+};
 template <bool kAligned>
-__device__ __forceinline__ void load_pair(const uint8_t *row, int off, int rowbytes, uint32_t r[9]) {
+__device__ __forceinline__ void load_pair(const uint8_t *row, int off, int rowbytes, RawPair &r) {
     if constexpr (kAligned) {
+        typedef uint32_t u32x4a4_t __attribute__((ext_vector_type(4), aligned(4)));
         const uint8_t *p = row + min(off, rowbytes - 36);
-        const u32x3_t a = *reinterpret_cast<const u32x3_t *>(p);
-        const u32x3_t b = *reinterpret_cast<const u32x3_t *>(p + 12);
-        const u32x3_t c = *reinterpret_cast<const u32x3_t *>(p + 24);
-        r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = b.x; r[4] = b.y; r[5] = b.z; r[6] = c.x; r[7] = c.y; r[8] = c.z;
+        r.a = *reinterpret_cast<const u32x4a4_t *>(p);
+        r.b = *reinterpret_cast<const u32x4a4_t *>(p + 16);
+        r.c = *reinterpret_cast<const uint32_t *>(p + 32);
     } else {
         const uint16_t *h = reinterpret_cast<const uint16_t *>(row);
         const int lim = (rowbytes >> 1) - 1;
         const int o = off >> 1;
+        uint32_t t[9];
 #pragma unroll
         for (int i = 0; i < 9; ++i)
-            r[i] = (uint32_t)h[min(o + 2 * i, lim)] | ((uint32_t)h[min(o + 2 * i + 1, lim)] << 16);
+            t[i] = (uint32_t)h[min(o + 2 * i, lim)] | ((uint32_t)h[min(o + 2 * i + 1, lim)] << 16);
+        r.a = u32x4_t{t[0], t[1], t[2], t[3]};
+        r.b = u32x4_t{t[4], t[5], t[6], t[7]};
+        r.c = t[8];
     }
 }
 
@@ -189,18 +199,40 @@ __device__ __forceinline__ int find_gemm_item(const GemmGroup &grp, int tmg) {
 // splits > 1: workgroup (tile, split) covers blocks [split*nbs, (split+1)*nbs) and writes
 // its partial tile to the item's part + split*N*M (column n at n*M); gemm_split_reduce
 // then adds the partials in split order.
-// Steps run in groups of four blocks; a split's last group is padded past its end with
-// steps whose A and B operands are zero.  NSETS register sets carry the x tiles in
-// flight (each loaded NSETS steps before it is stored to LDS).  The workgroup tile is
-// (128 RF) x 128: four waves of (32 RF) x 128.
-template <int RF, int NSETS, bool kAligned, int OCC>
+// Steps run in groups of four blocks; the steps of a split's last group past its end
+// load (clamped) like the others but skip the decode and the MFMAs.  The workgroup tile
+// is (128 RF) x 128: four waves of (32 RF) x 128.
+//
+// x tiles go global -> LDS directly (16-byte LDS-DMA loads: lane i of a wave's load
+// lands at the destination + 16 i), NXB LDS buffers, each step's tile loaded NXB - 1
+// steps ahead.  A column's 64 k (128 bytes, 8 chunks of 16) sit unpadded, chunk ch of column c
+// at position ch ^ (c & 7), so that the MFMA operand reads (8 consecutive columns, one
+// chunk each) hit distinct banks; a load lane picks the global chunk that belongs at its
+// LDS position.
+// One 16-byte LDS-DMA load per lane: lane i's 16 bytes at src land at LDS byte address
+// lds + 16 i.  Issued as inline assembly so that the compiler does not track it: its
+// own wait insertion would otherwise make every later LDS read wait for all of these
+// loads (it cannot tell that they fill a different buffer).  The caller orders them
+// with wait_vmcnt before the barrier that publishes the tile.
+__device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+}
+
+// s_waitcnt with only the vector-memory count set (expcnt and lgkmcnt at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int RF, int NXB, bool kAligned, int OCC>
 __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb, const _Float16 *__restrict__ x16,
                                                           const int *__restrict__ xe, int N, int tiles_n,
                                                           int xcd_map, int splits) {
-    static_assert(NSETS == 1 || NSETS == 2 || NSETS == 4, "one, two or four register sets");
     static_assert(RF == 1 || RF == 2, "one or two row fragments per wave");
+    static_assert(NXB == 2 || NXB == 3, "two or three x buffers");
     constexpr int TM = 128 * RF, kWRows = 32 * RF, kWAreaDw = kWRows * kWRowDw;
-    __shared__ __attribute__((aligned(16))) _Float16 Bs[2][GN * GLD];
+    __shared__ __attribute__((aligned(16))) _Float16 Bs[NXB][GN * GK];
     __shared__ __attribute__((aligned(16))) uint32_t Wraw[4 * kWAreaDw];
 
     const int tid = threadIdx.x;
@@ -263,25 +295,25 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
     uint32_t roff[RF];
 #pragma unroll
     for (int i = 0; i < RF; ++i) roff[i] = (uint32_t)(min(wrow0 + rr + 32 * i, M - 1) - rbase) * (uint32_t)rowbytes;
-    auto load_raw = [&](int grp4, uint32_t (&r)[RF][9]) {
+    auto load_raw = [&](int grp4, RawPair (&r)[RF]) {
 #pragma unroll
         for (int i = 0; i < RF; ++i)
             load_pair<kAligned>(wbase + roff[i], (kb0 + 4 * grp4 + 2 * hf) * kBlockBytes, rowbytes, r[i]);
     };
     uint32_t *const warea = Wraw + wave * kWAreaDw;
-    auto write_raw = [&](int grp4, const uint32_t (&rs)[RF][9]) {
+    auto write_raw = [&](int grp4, const RawPair (&rs)[RF]) {
         const int blk = 4 * grp4 + 2 * hf;       // even block of this pair, within the split
 #pragma unroll
         for (int i = 0; i < RF; ++i) {
-            const uint32_t *r = rs[i];
+            const RawPair &r = rs[i];
             u32x4_t ev, od;
-            ev.x = __builtin_amdgcn_perm(r[1], r[0], 0x05040302u);
-            ev.y = __builtin_amdgcn_perm(r[2], r[1], 0x05040302u);
-            ev.z = __builtin_amdgcn_perm(r[3], r[2], 0x05040302u);
-            ev.w = __builtin_amdgcn_perm(r[4], r[3], 0x05040302u);
-            od = u32x4_t{r[5], r[6], r[7], r[8]};
-            const uint32_t de = blk < nbs ? __builtin_amdgcn_perm(r[0], r[0], 0x01000100u) : 0u;
-            const uint32_t dod = blk + 1 < nbs ? __builtin_amdgcn_perm(r[4], r[4], 0x03020302u) : 0u;
+            ev.x = __builtin_amdgcn_perm(r.a.y, r.a.x, 0x05040302u);
+            ev.y = __builtin_amdgcn_perm(r.a.z, r.a.y, 0x05040302u);
+            ev.z = __builtin_amdgcn_perm(r.a.w, r.a.z, 0x05040302u);
+            ev.w = __builtin_amdgcn_perm(r.b.x, r.a.w, 0x05040302u);
+            od = u32x4_t{r.b.y, r.b.z, r.b.w, r.c};
+            const uint32_t de = blk < nbs ? __builtin_amdgcn_perm(r.a.x, r.a.x, 0x01000100u) : 0u;
+            const uint32_t dod = blk + 1 < nbs ? __builtin_amdgcn_perm(r.b.x, r.b.x, 0x03020302u) : 0u;
             uint32_t *row = warea + (rr + 32 * i) * kWRowDw;
             *reinterpret_cast<u32x4_t *>(row + 8 * hf) = ev;
             *reinterpret_cast<u32x4_t *>(row + 8 * hf + 4) = od;
@@ -289,32 +321,25 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
         }
     };
 
-    // ---- x loader: four 16-byte chunks per thread (column c >> 3, k chunk c & 7).
-    // Columns past N read column 0 (outputs never stored); blocks past the split are
-    // clamped to its last block and stored to LDS as zeros.
-    const _Float16 *xcol[4];
-    int xn[4], xpart[4];
+    // ---- x loader: wave w fills columns 32w .. 32w+31 of a tile, four LDS-DMA loads of
+    // 8 columns; lane i: column 8q + i/8 of them, LDS chunk position i%8, global chunk
+    // (i%8) ^ (i/8).  Columns past N read column 0 (outputs never stored); blocks past
+    // the split are clamped to its last block (loaded but never multiplied).
+    const _Float16 *xsrc[4];
+    {
+        const int cq = lane >> 3, ch = (lane & 7) ^ cq;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int c = tid + 256 * q;
-        xn[q] = c >> 3;
-        xpart[q] = c & 7;
-        const int n = n0 + xn[q];
-        xcol[q] = x16 + (int64_t)(col0 + (n < Nv ? n : 0)) * K + (int64_t)kb0 * GK + 8 * xpart[q];
-    }
-    auto load_x = [&](int blk, u32x4_t (&r)[4]) {
-        blk = min(blk, nbs - 1);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) r[q] = *reinterpret_cast<const u32x4_t *>(xcol[q] + (int64_t)blk * GK);
-    };
-    auto store_x = [&](int buf, int blk, const u32x4_t (&xr)[4]) {
-        if (blk < nbs) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4_t *>(&Bs[buf][xn[q] * GLD + 8 * xpart[q]]) = xr[q];
-        } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4_t *>(&Bs[buf][xn[q] * GLD + 8 * xpart[q]]) = u32x4_t{};
+        for (int q = 0; q < 4; ++q) {
+            const int n = n0 + 32 * wave + 8 * q + cq;
+            xsrc[q] = x16 + (int64_t)(col0 + (n < Nv ? n : 0)) * K + (int64_t)kb0 * GK + 8 * ch;
         }
+    }
+    const uint32_t bs_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)&Bs[0][0];
+    auto load_x = [&](int buf, int blk) {
+        blk = min(blk, nbs - 1);
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(bs_lds + (uint32_t)(buf * GN * GK + 32 * wave * GK) * 2u);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) lds_dma16(xsrc[q] + (int64_t)blk * GK, dst + (uint32_t)(8 * q * GK * 2));
     };
 
     float16_t acc[RF][4];
@@ -327,18 +352,29 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
     // the block, code pairs 4h..4h+3 (h = l/32; the word is shifted down 8h bits so that
     // they sit at pairs 0..3).  In the permuted k order of x16 these are exactly the 8 k
     // that B lane (column, h) holds.  B lane: column l%32 of a 32-column sub-tile.
-    const int frow = lane & 31, fk = (lane >> 5) * 8;
+    const int frow = lane & 31;
     const uint32_t sh = (uint32_t)(lane >> 5) * 8u;
+    int bsw[4];   // swizzled position (halves) of chunk 2kk + h of this lane's columns
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) bsw[kk] = 8 * ((2 * kk + (lane >> 5)) ^ (frow & 7));
     const PairMasks pm;
     const uint32_t *const wmy = warea + frow * kWRowDw;
-    auto step = [&](int buf, int b) {
-        u32x4_t wd[RF];
-        half2_t dd[RF];
+    struct WStep {
+        u32x4_t wd[RF];   // the block's 4 code words, per row fragment
+        half2_t dd[RF];   // its scale pair
+    };
+    auto read_w = [&](int b) {
+        WStep r;
 #pragma unroll
         for (int i = 0; i < RF; ++i) {
-            wd[i] = *reinterpret_cast<const u32x4_t *>(wmy + 32 * i * kWRowDw + 4 * b);
-            dd[i] = __builtin_bit_cast(half2_t, wmy[32 * i * kWRowDw + 16 + b]);
+            r.wd[i] = *reinterpret_cast<const u32x4_t *>(wmy + 32 * i * kWRowDw + 4 * b);
+            r.dd[i] = __builtin_bit_cast(half2_t, wmy[32 * i * kWRowDw + 16 + b]);
         }
+        return r;
+    };
+    auto step = [&](int buf, const WStep &ws) {
+        const u32x4_t *wd = ws.wd;
+        const half2_t *dd = ws.dd;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             half8_t a[RF];
@@ -354,7 +390,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
             half8_t bv[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                bv[j] = *reinterpret_cast<const half8_t *>(&Bs[buf][(j * 32 + frow) * GLD + kk * 16 + fk]);
+                bv[j] = *reinterpret_cast<const half8_t *>(&Bs[buf][(j * 32 + frow) * GK + bsw[kk]]);
 #pragma unroll
             for (int i = 0; i < RF; ++i)
 #pragma unroll
@@ -363,32 +399,48 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
         }
     };
 
-    // ---- pipeline: x tiles double buffered in LDS (one barrier per step), NSETS x
-    // register sets in flight; W raw groups loaded one group ahead into registers and
-    // written to the wave's area after the group's last step has read it.
-    uint32_t wr[RF][9];
-    u32x4_t xr[NSETS][4];
+    // ---- pipeline.  Step t multiplies x buffer t % NXB while the tile of step t+NXB-1
+    // loads into buffer (t+NXB-1) % NXB (last read at step t-1, before the barrier that
+    // ended it).  W raw groups are loaded one group ahead into registers; a group's last
+    // step reads its own words first, then writes the next group to the wave's area and
+    // issues the loads of the one after, then the x load and the MFMAs.  Before the
+    // barrier that ends step t each wave waits for its own loads of tile t+1; younger are
+    // (NXB = 3) tile t+2's four and, in a group's last step, the raw loads, (NXB = 2)
+    // none.  Raw loads are counted per row fragment as three 12-byte loads (at least that
+    // many are issued); the 2-byte path counts none (its waits then also cover them).
+    constexpr int kRaw = kAligned ? 3 * RF : 0;
+    RawPair wr[RF];
     load_raw(0, wr);
 #pragma unroll
-    for (int i = 0; i < NSETS; ++i) load_x(i, xr[i]);
+    for (int i = 0; i + 1 < NXB; ++i) load_x(i, i);
     write_raw(0, wr);
     load_raw(1, wr);
-    store_x(0, 0, xr[0]);
-    load_x(NSETS, xr[0]);
+    wait_vmcnt<kRaw>();          // x tiles 0 .. NXB-2 (younger: raw group 1)
     __syncthreads();
 
+    int buf = 0;                 // t % NXB
     for (int g = 0; g < ngroups; ++g) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int t = 4 * g + u;
-            step(u & 1, u);
+            const int bufn = NXB == 3 ? (buf == 0 ? 2 : buf - 1) : (buf ^ 1);   // (t + NXB - 1) % NXB
+            const WStep ws = read_w(u);
             if (u == 3) {
-                write_raw(g + 1, wr);    // read from the next step on
+                write_raw(g + 1, wr);    // after this step's read of the area
                 load_raw(g + 2, wr);
             }
-            store_x((u + 1) & 1, t + 1, xr[(u + 1) % NSETS]);
-            load_x(t + 1 + NSETS, xr[(u + 1) % NSETS]);
+            load_x(bufn, t + NXB - 1);
+            if (t < nbs) step(buf, ws);
+            if constexpr (NXB == 3) {
+                if (u == 3)
+                    wait_vmcnt<4 + kRaw>();   // tile t+1 (younger: raw group g+2, tile t+2)
+                else
+                    wait_vmcnt<4>();          // tile t+1 (younger: tile t+2)
+            } else {
+                wait_vmcnt<0>();              // tile t+1 (issued last)
+            }
             __syncthreads();
+            buf = NXB == 3 ? (buf == 2 ? 0 : buf + 1) : (buf ^ 1);
         }
     }
 
@@ -468,42 +520,70 @@ size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 }  // namespace
 
 // The GEMM kernel for rf row fragments per wave, with 4-byte code loads where every
-// matrix row is 4-byte aligned.
+// matrix row is 4-byte aligned.  One row fragment: two x buffers (42 KiB of LDS, 120
+// VGPRs), three workgroups per CU; two: three x buffers, two workgroups per CU.
 static void launch_gemm_kernel(unsigned grid, hipStream_t s, const GemmGroup &grp, int nb, const _Float16 *x16,
                                const int *xe, int N, int tiles_n, int xcd_map, int splits, int rf, bool aligned) {
     if (rf == 2) {
         if (aligned)
-            gemm_f16_mfma<2, 2, true, 2><<<grid, 256, 0, s>>>(grp, nb, x16, xe, N, tiles_n, xcd_map, splits);
+            gemm_f16_mfma<2, 3, true, 2><<<grid, 256, 0, s>>>(grp, nb, x16, xe, N, tiles_n, xcd_map, splits);
         else
-            gemm_f16_mfma<2, 2, false, 2><<<grid, 256, 0, s>>>(grp, nb, x16, xe, N, tiles_n, xcd_map, splits);
+            gemm_f16_mfma<2, 3, false, 2><<<grid, 256, 0, s>>>(grp, nb, x16, xe, N, tiles_n, xcd_map, splits);
     } else {
         if (aligned)
-            gemm_f16_mfma<1, 2, true, 2><<<grid, 256, 0, s>>>(grp, nb, x16, xe, N, tiles_n, xcd_map, splits);
+            gemm_f16_mfma<1, 2, true, 3><<<grid, 256, 0, s>>>(grp, nb, x16, xe, N, tiles_n, xcd_map, splits);
         else
-            gemm_f16_mfma<1, 2, false, 2><<<grid, 256, 0, s>>>(grp, nb, x16, xe, N, tiles_n, xcd_map, splits);
+            gemm_f16_mfma<1, 2, false, 3><<<grid, 256, 0, s>>>(grp, nb, x16, xe, N, tiles_n, xcd_map, splits);
     }
 }
 
-// Tile shape and K split of a call.  256-row tiles (two row fragments per wave: half
-// the LDS reads per MFMA and half the x traffic of 128-row tiles) where they alone give
-// at least kRf2MinTiles workgroups and the block count is even (4-byte code loads);
-// otherwise 128-row tiles, and K split (at most 8
-// ways, at least 8 blocks a split) until there are 512 workgroups.
-constexpr int kRf2MinTiles = 256;
+// Tile shape and K split of a call, from a model of the busiest CU's time.  Workgroups
+// go out in rounds of (workgroups per CU) x 256; a round in which a CU holds w of them
+// takes (blocks per split) x step time(w), the step times measured on MI355X at N = 512
+// (the CU's throughput saturates: 2 and 3 concurrent 128-row workgroups take about the
+// same time per workgroup-step).  A K split s adds its partials, written and read back
+// (s N M floats each way at ~4 TB/s), and the reduction launch.  Candidates: 128-row
+// tiles (one row fragment per wave, three workgroups per CU) with s in {1, 2, 3, 4, 6, 8}
+// (s dividing the blocks, at least 8 per split and, for even block counts, an even
+// number), and 256-row tiles (two row fragments: half the LDS reads per MFMA and half
+// the x traffic; two workgroups per CU; even block counts only) without a split.  Ties
+// keep the earlier candidate (smaller split, 128-row tiles).
 struct GemmPlan {
     int rf, splits;
 };
+constexpr double kStepUsRf1[4] = {0.0, 1.1, 1.3, 1.76};   // by concurrent workgroups per CU
+constexpr double kStepUsRf2[3] = {0.0, 1.2, 1.94};
+constexpr double kPartBytesPerUs = 4.0e6, kReduceLaunchUs = 4.0;
+
+static double rounds_us(int64_t wgs, int per_cu, const double *step_us, int steps) {
+    const int64_t slots = 256 * (int64_t)per_cu;
+    const int64_t full = (wgs - 1) / slots;                  // rounds before the last
+    const int64_t last = wgs - full * slots;                 // workgroups in the last round
+    const int w_last = (int)((last + 255) / 256);
+    return ((double)full * step_us[per_cu] + step_us[w_last]) * steps;
+}
+
 static GemmPlan gemm_plan(const int64_t *Ms, int64_t n_items, int nb, int64_t N) {
-    int64_t t1 = 0, t2 = 0;
+    int64_t t1 = 0, t2 = 0, rows = 0;
     for (int64_t i = 0; i < n_items; ++i) {
         t1 += (Ms[i] + 127) / 128;
         t2 += (Ms[i] + 255) / 256;
+        rows += Ms[i];
     }
     const int64_t tiles_n = (N + GN - 1) / GN;
-    if (nb % 2 == 0 && t2 * tiles_n >= kRf2MinTiles) return {2, 1};
-    int sp = 1;
-    while (t1 * tiles_n * sp < 512 && sp < 8 && nb % (2 * sp) == 0 && nb / (2 * sp) >= 8) sp *= 2;
-    return {1, sp};
+    GemmPlan best{1, 1};
+    double best_us = 1e300;
+    for (int sp : {1, 2, 3, 4, 6, 8}) {
+        if (sp > 1 && (nb % sp != 0 || nb / sp < 8 || (nb % 2 == 0 && (nb / sp) % 2 != 0))) continue;
+        double us = rounds_us(t1 * tiles_n * sp, 3, kStepUsRf1, nb / sp);
+        if (sp > 1) us += 8.0 * sp * (double)N * (double)rows / kPartBytesPerUs + kReduceLaunchUs;
+        if (us < best_us) {
+            best_us = us;
+            best = {1, sp};
+        }
+    }
+    if (nb % 2 == 0 && rounds_us(t2 * tiles_n, 2, kStepUsRf2, nb) < best_us) best = {2, 1};
+    return best;
 }
 
 // Workspace of a call: fp16 x (N*K halves), the column exponents (N ints), and with

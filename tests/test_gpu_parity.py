@@ -577,9 +577,9 @@ def test_mul_mat_group_matches_oracle(precision, rel, Ms, K, N):
             assert_products(y, w, M, K, x, rel, what="group item M=%d K=%d N=%d" % (M, K, N))
 
 
-def test_mul_mat_group_gate_up_8b_256_row_tiles():
-    """The 8B stack's gate/up pair at N = 512 (192 row tiles of 256 rows x 4 column tiles:
-    the two-row-fragment kernel, no K split); sampled rows of both, run to run bit-equal."""
+def test_mul_mat_group_gate_up_8b_full_size():
+    """The 8B stack's gate/up pair at N = 512 (768 tiles of 128 x 128, no K split: one
+    round at three workgroups per CU); sampled rows of both, run to run bit-equal."""
     wl = synth.STACK_8B
     names = ["gate", "up"]
     K = wl.shapes["gate"][1]
@@ -594,13 +594,14 @@ def test_mul_mat_group_gate_up_8b_256_row_tiles():
 
 
 def test_mul_mat_256_row_tiles_ragged():
-    """256-row tiles with a partial last row tile (M = 96 * 256 + 77), partial column
-    tile (N = 300) and a padded last step group (K / 64 = 10 blocks)."""
-    M, K, N = 96 * 256 + 77, 640, 300
+    """256-row tiles (chosen for 1024 of them in two full rounds) with a partial last row
+    tile (M = 65357), a partial column tile (N = 500) and a padded last step group
+    (K / 64 = 10 blocks)."""
+    M, K, N = 65357, 640, 500
     w = synth.weight(29, M, N, M, K, "quad", synth.ScaleDist("loguniform", 1e-3, 1e-1, 0.02))
     x = synth.activations(29, M, N, N, K)
     y = run_mul_mat(dev(w), M, K, x, B.Q2_0_PREC_F16_MFMA, ldy=M + 3)
-    rows = np.unique(np.concatenate([np.arange(0, M, 13), np.arange(M - 300, M)]))
+    rows = np.unique(np.concatenate([np.arange(0, M, 29), np.arange(M - 300, M)]))
     assert_products(y, w, M, K, x, REL_F16, rows=rows, what="256-row tiles M=%d K=%d N=%d" % (M, K, N))
 
 
