@@ -2,31 +2,32 @@
 // Q2_0, x rounded to fp16, f32 accumulation.
 //
 // bisque.today "WebGPU: add Q2_0 support": the tiled matrix multiply unpacks 16
-// codes per thread into shared memory as half precision.  Here each thread unpacks
-// one 32-bit code word (16 weights) of one row per 64-k step straight into the LDS
-// tile as fp16 d*(q-1) -- exact, because d is a half and |q-1| <= 2 -- using the
+// codes per thread into shared memory as half precision.  Here no fp16 copy of W is
+// made: every wave owns whole rows of the tile and unpacks them straight into its MFMA
+// A operands as fp16 d*(q-1) -- exact, because d is a half and |q-1| <= 2 -- using the
 // fp16-pair decode of the mat-vec (OR the code under a magic exponent, one packed
-// subtract) and one packed multiply by d.
+// subtract) and one packed multiply by d.  Only the raw code bytes pass through LDS
+// (a wave-private area), and only x is shared between the waves.
 //
 //  * x is converted once per call into the caller's workspace as fp16, each column
 //    scaled by a power of two that keeps it inside fp16's normal range (undone on
 //    the results), and within every group of 16 k its order is permuted to (0, 8,
 //    1, 9, ..., 7, 15): the order in which the pair decode emits a word's 16
 //    weights.  A and B then share the k order without any shuffling.
-//  * Workgroup tile 128 (m) x 128 (n), four waves of 64 x 64, each a 2 x 2 grid of
-//    v_mfma_f32_32x32x16_f16; one Q2_0 block (64 k) per step.
-//  * LDS is double buffered (one barrier per step); the next step's code words and
-//    x tile are loaded into registers two steps ahead.
-//  * Tiles are ordered so that all workgroups on one XCD (dispatch is round-robin
-//    over the 8 XCDs) share one 128-column slice of x, which then stays in that
-//    XCD's L2.
+//  * Workgroup tile (128 RF) (m) x 128 (n), four waves of (32 RF) x 128, each an RF x 4
+//    grid of v_mfma_f32_32x32x16_f16; one Q2_0 block (64 k) per step.
+//  * x tiles go straight from global memory to LDS (LDS-DMA), loaded one or two steps
+//    ahead; one barrier per step.
+//  * Without a K split, tiles are ordered so that all workgroups on one XCD (dispatch
+//    is round-robin over the 8 XCDs) share one 128-column slice of x, which then stays
+//    in that XCD's L2.
 //  * A launch may cover several matrices that share K and x (q/k/v, gate/up): their
 //    row tiles are numbered across the group and x is converted once for all.
-//  * When the tile grid is too small to fill the chip, K is split (at most 8 ways);
-//    every split writes its partial tile to the workspace and a reduction kernel adds
-//    them in split order (deterministic).  Finishing the tile in the last split to
-//    arrive would save that launch, but the partials cross XCDs whose L2 caches are
-//    not coherent: device-scope stores bypass the write-back L2 and L2 flushes stall
+//  * The tile height and the K split (at most 8 ways) come from a model of the busiest
+//    CU's time; every split writes its partial tile to the workspace and a reduction
+//    kernel adds them in split order (deterministic).  Finishing the tile in the last
+//    split to arrive would save that launch, but the partials cross XCDs whose L2 caches
+//    are not coherent: device-scope stores bypass the write-back L2 and L2 flushes stall
 //    every workgroup, and both measured several times slower than the extra launch.
 #include <climits>
 
