@@ -58,15 +58,19 @@ TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "mat_vec_bcast_gemm_f16_hbm_tra
 
 
 def kernel_sources_sha256() -> str:
-    """sha256 over the HIP sources of libq2_0.so (sorted by name), to tell whether the
-    recorded counter readings still describe the kernels being timed."""
+    """sha256 over the code of the HIP sources of libq2_0.so (sorted by name; comments and
+    blank lines removed, so that a comment edit keeps it), to tell whether the recorded
+    counter readings still describe the kernels being timed."""
     import hashlib
+    import re
     h = hashlib.sha256()
     src = os.path.join(ROOT, "ternary_bit_quantized_amd", "csrc")
     for name in sorted(os.listdir(src)):
         if name.endswith((".hip", ".h")):
-            with open(os.path.join(src, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+            with open(os.path.join(src, name), encoding="utf-8") as f:
+                text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+            code = "\n".join(ln.rstrip() for ln in (re.sub(r"//.*", "", l) for l in text.splitlines()) if ln.strip())
+            h.update(name.encode() + b"\0" + code.encode())
     return h.hexdigest()
 
 
