@@ -19,60 +19,119 @@ namespace q2_0 {
 namespace {
 
 constexpr int kRouteThreads = 1024;
+constexpr int kRouteWaves = kRouteThreads / 64;
+constexpr int kFastRuns = 512;   // runs (experts + 1) up to which the per-wave counts fit in LDS
 
 // off[0..n_expert+1]: run starts (off[n_expert] .. off[n_expert+1] holds the bad ids);
 // perm[pos] = pair; tiles: (expert, column tile) for every tile_w-column tile of every
-// expert's run, *ntiles of them.  LDS: one counter per run, then the current chunk.
+// expert's run, *ntiles of them.
+//  * counts: one LDS counter per run;
+//  * scan: one wave, each lane over a contiguous range of runs, then a lane scan, gives
+//    the run starts and the tile list;
+//  * stable placement, one chunk of kRouteThreads pairs at a time: a pair goes to its
+//    run's cursor + the pairs of its run in earlier waves of the chunk + those in earlier
+//    lanes of its own wave.  kFast: the per-wave counts of every run sit in LDS and a
+//    pair's rank in its wave comes from 64 lane reads; otherwise (many runs) each pair
+//    counts the earlier pairs of its run in the chunk one by one.
+template <bool kFast>
 __global__ __launch_bounds__(kRouteThreads) void moe_route(const int32_t *__restrict__ ids, int n_pairs,
                                                           int n_expert, int tile_w, int *__restrict__ off,
                                                           int *__restrict__ perm, int *__restrict__ tiles,
                                                           int *__restrict__ ntiles) {
     extern __shared__ int lds[];
-    int *cnt = lds;                              // n_expert + 1 counters, then cursors
-    int *chunk = lds + n_expert + 1;             // the current chunk's runs
-    const int tid = threadIdx.x;
     const int runs = n_expert + 1;
+    int *cnt = lds;                                       // runs: counts, then cursors
+    int *wh = lds + runs;                                 // kFast: kRouteWaves x runs
+    int *tot = wh + kRouteWaves * runs;                   // kFast: runs (a chunk's counts)
+    int *chunk = lds + runs;                              // !kFast: the chunk's runs
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     auto run_of = [&](int p) {
         const int e = ids[p];
         return (e >= 0 && e < n_expert) ? e : n_expert;
     };
     for (int b = tid; b < runs; b += kRouteThreads) cnt[b] = 0;
+    if (kFast)
+        for (int i = tid; i < kRouteWaves * runs; i += kRouteThreads) wh[i] = 0;
     __syncthreads();
     for (int p = tid; p < n_pairs; p += kRouteThreads) atomicAdd(&cnt[run_of(p)], 1);
     __syncthreads();
-    // exclusive scan and tile list by one thread (runs is small: at most a few thousand)
-    if (tid == 0) {
-        int acc = 0, nt = 0;
-        for (int b = 0; b < runs; ++b) {
-            const int c = cnt[b];
-            off[b] = acc;
-            cnt[b] = acc;   // now the run's cursor
-            acc += c;
-            if (b < n_expert)
-                for (int t = 0; t * tile_w < c; ++t, ++nt) {
-                    tiles[2 * nt] = b;
-                    tiles[2 * nt + 1] = t;
-                }
+    if (tid < 64) {
+        const int L = (runs + 63) / 64, b0 = lane * L;
+        int sum = 0, tsum = 0;
+        for (int i = 0; i < L; ++i) {
+            const int b = b0 + i;
+            if (b < runs) {
+                const int c = cnt[b];
+                sum += c;
+                if (b < n_expert) tsum += (c + tile_w - 1) / tile_w;
+            }
         }
-        off[runs] = acc;
-        *ntiles = nt;
+        int inc = sum, tinc = tsum;
+        for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(inc, d), tv = __shfl_up(tinc, d);
+            if (lane >= d) {
+                inc += v;
+                tinc += tv;
+            }
+        }
+        int acc = inc - sum, tacc = tinc - tsum;
+        for (int i = 0; i < L; ++i) {
+            const int b = b0 + i;
+            if (b < runs) {
+                const int c = cnt[b];
+                off[b] = acc;
+                cnt[b] = acc;   // now the run's cursor
+                if (b < n_expert)
+                    for (int t = 0; t * tile_w < c; ++t, ++tacc) {
+                        tiles[2 * tacc] = b;
+                        tiles[2 * tacc + 1] = t;
+                    }
+                acc += c;
+            }
+        }
+        if (lane == 63) {
+            off[runs] = acc;
+            *ntiles = tacc;
+        }
     }
     __syncthreads();
-    // stable placement, one chunk of pairs at a time: a pair's position is its run's
-    // cursor plus the number of earlier pairs of the chunk in the same run
     for (int c0 = 0; c0 < n_pairs; c0 += kRouteThreads) {
         const int p = c0 + tid;
         const int b = p < n_pairs ? run_of(p) : -1;
-        chunk[tid] = b;
-        __syncthreads();
-        if (b >= 0) {
+        if constexpr (kFast) {
             int rank = 0;
-            for (int q = 0; q < tid; ++q) rank += (chunk[q] == b);
-            perm[cnt[b] + rank] = p;
+            for (int j = 0; j < 64; ++j) rank += (j < lane) & (__shfl(b, j) == b);
+            if (b >= 0) atomicAdd(&wh[wv * runs + b], 1);
+            __syncthreads();
+            for (int r = tid; r < runs; r += kRouteThreads) {
+                int sum = 0;
+                for (int v = 0; v < kRouteWaves; ++v) {
+                    const int c = wh[v * runs + r];
+                    wh[v * runs + r] = sum;
+                    sum += c;
+                }
+                tot[r] = sum;
+            }
+            __syncthreads();
+            if (b >= 0) perm[cnt[b] + wh[wv * runs + b] + rank] = p;
+            __syncthreads();
+            for (int r = tid; r < runs; r += kRouteThreads) {
+                cnt[r] += tot[r];
+                for (int v = 0; v < kRouteWaves; ++v) wh[v * runs + r] = 0;
+            }
+            __syncthreads();
+        } else {
+            chunk[tid] = b;
+            __syncthreads();
+            if (b >= 0) {
+                int rank = 0;
+                for (int q = 0; q < tid; ++q) rank += (chunk[q] == b);
+                perm[cnt[b] + rank] = p;
+            }
+            __syncthreads();
+            if (b >= 0) atomicAdd(&cnt[b], 1);
+            __syncthreads();
         }
-        __syncthreads();
-        if (b >= 0) atomicAdd(&cnt[b], 1);
-        __syncthreads();
     }
 }
 
@@ -124,8 +183,13 @@ hipError_t launch_moe_route(const int32_t *ids, int n_pairs, int n_expert, int n
     p += 256;
     int *tiles = reinterpret_cast<int *>(p);
     *r = MoeRoute{off, perm, tiles, ntiles, n_expert, n_pairs, n_used, x_slots, tile_w};
-    const size_t lds = (size_t)(n_expert + 1 + kRouteThreads) * 4;
-    moe_route<<<1, kRouteThreads, lds, s>>>(ids, n_pairs, n_expert, tile_w, off, perm, tiles, ntiles);
+    const int runs = n_expert + 1;
+    if (runs <= kFastRuns)
+        moe_route<true><<<1, kRouteThreads, (size_t)runs * (2 + kRouteWaves) * 4, s>>>(ids, n_pairs, n_expert, tile_w,
+                                                                                    off, perm, tiles, ntiles);
+    else
+        moe_route<false><<<1, kRouteThreads, (size_t)(runs + kRouteThreads) * 4, s>>>(ids, n_pairs, n_expert, tile_w,
+                                                                                    off, perm, tiles, ntiles);
     return hipGetLastError();
 }
 

@@ -97,6 +97,23 @@ def test_mul_mat_id_matches_oracle(precision, kind, slots):
     check(y, y_ref, bound, REL[precision], "%s/%s/p%d" % (kind, slots, precision))
 
 
+@pytest.mark.parametrize("precision", [B.Q2_0_PREC_F16_MFMA, B.Q2_0_PREC_F32])
+@pytest.mark.parametrize("ne", [511, 512, 600])
+def test_mul_mat_id_many_experts(precision, ne):
+    """Routing with 511 experts (the last count whose per-wave run counts fit in LDS), 512
+    and 600 (the pair-by-pair placement): 300 tokens x 4 slots (two placement chunks),
+    some ids out of range, every output checked."""
+    rng = np.random.default_rng(ne + 10 * precision)
+    M, K = 64, 128
+    wall = experts(65, ne, M, K)
+    ids = rng.integers(0, ne, size=(300, 4)).astype(np.int32)
+    ids[5, 0], ids[77, 3], ids[299, 1] = -1, ne, ne + 1000
+    x = synth.activations(65, 300, 0, 300, K)
+    y = run_id(wall, ne, M, K, x, B.Q2_0_ACT_F32, ids, precision)
+    y_ref, bound = oracle.mul_mat_id(wall, ne, M, K, x, ids)
+    check(y, y_ref, bound, REL[precision], "ne=%d p%d" % (ne, precision))
+
+
 def test_mul_mat_id_f32_equals_per_expert_mul_mat_bitwise():
     """On the fp32 path each result column depends only on its expert and activation, so it
     equals, bit for bit, q2_0_mul_mat of that expert on the gathered columns."""
