@@ -226,14 +226,15 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int RF, int NXB, bool kAligned, int OCC>
+template <int RF, int NJ, int NXB, bool kAligned, int OCC>
 __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb, const _Float16 *__restrict__ x16,
                                                           const int *__restrict__ xe, int N, int tiles_n,
                                                           int xcd_map, int splits) {
     static_assert(RF == 1 || RF == 2, "one or two row fragments per wave");
+    static_assert(NJ == 2 || NJ == 4, "two or four column fragments per wave");
     static_assert(NXB == 2 || NXB == 3, "two or three x buffers");
-    constexpr int TM = 128 * RF, kWRows = 32 * RF, kWAreaDw = kWRows * kWRowDw;
-    __shared__ __attribute__((aligned(16))) _Float16 Bs[NXB][GN * GK];
+    constexpr int TM = 128 * RF, TN = 32 * NJ, kWRows = 32 * RF, kWAreaDw = kWRows * kWRowDw;
+    __shared__ __attribute__((aligned(16))) _Float16 Bs[NXB][TN * GK];
     __shared__ __attribute__((aligned(16))) uint32_t Wraw[4 * kWAreaDw];
 
     const int tid = threadIdx.x;
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
         w = itp->w;
         M = itp->M;
         m0 = (tmg - itp->tm0) * TM;
-        n0 = tn * GN;
+        n0 = tn * TN;
     } else {
         const int t = blockIdx.x / grp.moe_tiles_m;
         if (t >= *grp.moe_ntiles) return;   // the whole workgroup: no tile here
@@ -275,7 +276,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
         w = itp->w + e * grp.moe_expert_bytes;
         M = itp->M;
         m0 = (blockIdx.x % grp.moe_tiles_m) * TM;
-        n0 = grp.moe_tiles[2 * t + 1] * GN;
+        n0 = grp.moe_tiles[2 * t + 1] * TN;
         col0 = grp.moe_off[e];
         Nv = grp.moe_off[e + 1] - col0;
     }
@@ -322,32 +323,32 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
         }
     };
 
-    // ---- x loader: wave w fills columns 32w .. 32w+31 of a tile, four LDS-DMA loads of
-    // 8 columns; lane i: column 8q + i/8 of them, LDS chunk position i%8, global chunk
+    // ---- x loader: wave w fills columns 8NJ w .. 8NJ (w+1) - 1 of a tile, NJ LDS-DMA loads
+    // of 8 columns; lane i: column 8q + i/8 of them, LDS chunk position i%8, global chunk
     // (i%8) ^ (i/8).  Columns past N read column 0 (outputs never stored); blocks past
     // the split are clamped to its last block (loaded but never multiplied).
-    const _Float16 *xsrc[4];
+    const _Float16 *xsrc[NJ];
     {
         const int cq = lane >> 3, ch = (lane & 7) ^ cq;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int n = n0 + 32 * wave + 8 * q + cq;
+        for (int q = 0; q < NJ; ++q) {
+            const int n = n0 + 8 * NJ * wave + 8 * q + cq;
             xsrc[q] = x16 + (int64_t)(col0 + (n < Nv ? n : 0)) * K + (int64_t)kb0 * GK + 8 * ch;
         }
     }
     const uint32_t bs_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)&Bs[0][0];
     auto load_x = [&](int buf, int blk) {
         blk = min(blk, nbs - 1);
-        const uint32_t dst = __builtin_amdgcn_readfirstlane(bs_lds + (uint32_t)(buf * GN * GK + 32 * wave * GK) * 2u);
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(bs_lds + (uint32_t)(buf * TN * GK + 8 * NJ * wave * GK) * 2u);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) lds_dma16(xsrc[q] + (int64_t)blk * GK, dst + (uint32_t)(8 * q * GK * 2));
+        for (int q = 0; q < NJ; ++q) lds_dma16(xsrc[q] + (int64_t)blk * GK, dst + (uint32_t)(8 * q * GK * 2));
     };
 
-    float16_t acc[RF][4];
+    float16_t acc[RF][NJ];
 #pragma unroll
     for (int i = 0; i < RF; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = float16_t{};
+        for (int j = 0; j < NJ; ++j) acc[i][j] = float16_t{};
 
     // A lane l: row l%32 of a row fragment, k-slot (l/32)*8 of each 16-k step: word kk of
     // the block, code pairs 4h..4h+3 (h = l/32; the word is shifted down 8h bits so that
@@ -388,14 +389,14 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
                                 __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, pair_qm1<2>(c, pm)) * d2),
                                 __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, pair_qm1<3>(c, pm)) * d2));
             }
-            half8_t bv[4];
+            half8_t bv[NJ];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < NJ; ++j)
                 bv[j] = *reinterpret_cast<const half8_t *>(&Bs[buf][(j * 32 + frow) * GK + bsw[kk]]);
 #pragma unroll
             for (int i = 0; i < RF; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < NJ; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], bv[j], acc[i][j], 0, 0, 0);
         }
     };
@@ -434,9 +435,9 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
             if (t < nbs) step(buf, ws);
             if constexpr (NXB == 3) {
                 if (u == 3)
-                    wait_vmcnt<4 + kRaw>();   // tile t+1 (younger: raw group g+2, tile t+2)
+                    wait_vmcnt<NJ + kRaw>();   // tile t+1 (younger: raw group g+2, tile t+2)
                 else
-                    wait_vmcnt<4>();          // tile t+1 (younger: tile t+2)
+                    wait_vmcnt<NJ>();          // tile t+1 (younger: tile t+2)
             } else {
                 wait_vmcnt<0>();              // tile t+1 (issued last)
             }
@@ -449,7 +450,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
     // Results are scaled back by the column's 2^-e first (exact), so partials and y
     // hold the same numbers.
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
         const int n = n0 + j * 32 + (lane & 31);
         const int ye = -xe[col0 + (n < Nv ? n : 0)];
 #pragma unroll
@@ -471,7 +472,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
     float *const yout = (splits > 1) ? item.part + (int64_t)split * N * M : item.y;
     const int64_t ldo = (splits > 1) ? M : item.ldy;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
         const int n = n0 + j * 32 + (lane & 31);
         if (n >= Nv) continue;
         float *yc = grp.moe_off ? item.y + (int64_t)grp.moe_perm[col0 + n] * item.ldy : yout + (int64_t)n * ldo;
@@ -520,40 +521,52 @@ size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 }  // namespace
 
-// The GEMM kernel for rf row fragments per wave, with 4-byte code loads where every
-// matrix row is 4-byte aligned.  One row fragment: two x buffers (42 KiB of LDS, 120
-// VGPRs), three workgroups per CU; two: three x buffers, two workgroups per CU.
+// GEMM kernel configurations (workgroup tile rows x columns, per wave RF x NJ MFMA tiles):
+//   A: 128 x 128, RF 1 x NJ 4, two x buffers, three workgroups per CU;
+//   B: 256 x 128, RF 2 x NJ 4, three x buffers, two workgroups per CU.
+// (256 x 64 tiles, RF 2 x NJ 2 at three workgroups per CU -- half the LDS operand reads
+// per MFMA of A, twice the decode per MFMA -- measured ~10 % slower than A at N = 512.)
+enum GemmCfg { kCfgA = 0, kCfgB = 1 };
+constexpr int cfg_rows(int cfg) { return cfg == kCfgA ? 128 : 256; }
+constexpr int cfg_cols(int) { return 128; }
+
+// The GEMM kernel of a configuration, with 4-byte code loads where every matrix row is
+// 4-byte aligned.
 static void launch_gemm_kernel(unsigned grid, hipStream_t s, const GemmGroup &grp, int nb, const _Float16 *x16,
-                               const int *xe, int N, int tiles_n, int xcd_map, int splits, int rf, bool aligned) {
-    if (rf == 2) {
-        if (aligned)
-            gemm_f16_mfma<2, 3, true, 2><<<grid, 256, 0, s>>>(grp, nb, x16, xe, N, tiles_n, xcd_map, splits);
-        else
-            gemm_f16_mfma<2, 3, false, 2><<<grid, 256, 0, s>>>(grp, nb, x16, xe, N, tiles_n, xcd_map, splits);
-    } else {
-        if (aligned)
-            gemm_f16_mfma<1, 2, true, 3><<<grid, 256, 0, s>>>(grp, nb, x16, xe, N, tiles_n, xcd_map, splits);
-        else
-            gemm_f16_mfma<1, 2, false, 3><<<grid, 256, 0, s>>>(grp, nb, x16, xe, N, tiles_n, xcd_map, splits);
-    }
+                               const int *xe, int N, int tiles_n, int xcd_map, int splits, int cfg, bool aligned) {
+#define Q2_0_GEMM_LAUNCH(RF, NJ, NXB, OCC)                                                                      \
+    do {                                                                                                        \
+        if (aligned)                                                                                            \
+            gemm_f16_mfma<RF, NJ, NXB, true, OCC><<<grid, 256, 0, s>>>(grp, nb, x16, xe, N, tiles_n,      \
+                                                                             xcd_map, splits);                 \
+        else                                                                                                    \
+            gemm_f16_mfma<RF, NJ, NXB, false, OCC><<<grid, 256, 0, s>>>(grp, nb, x16, xe, N, tiles_n,     \
+                                                                              xcd_map, splits);                \
+    } while (0)
+    if (cfg == kCfgB)
+        Q2_0_GEMM_LAUNCH(2, 4, 3, 2);
+    else
+        Q2_0_GEMM_LAUNCH(1, 4, 2, 3);
+#undef Q2_0_GEMM_LAUNCH
 }
 
-// Tile shape and K split of a call, from a model of the busiest CU's time.  Workgroups
-// go out in rounds of (workgroups per CU) x 256; a round in which a CU holds w of them
-// takes (blocks per split) x step time(w), the step times measured on MI355X at N = 512
-// (the CU's throughput saturates: 2 and 3 concurrent 128-row workgroups take about the
-// same time per workgroup-step).  A K split s adds its partials, written and read back
-// (s N M floats each way at ~4 TB/s), and the reduction launch.  Candidates: 128-row
-// tiles (one row fragment per wave, three workgroups per CU) with s in {1, 2, 3, 4, 6, 8}
-// (s dividing the blocks, at least 8 per split and, for even block counts, an even
-// number), and 256-row tiles (two row fragments: half the LDS reads per MFMA and half
-// the x traffic; two workgroups per CU; even block counts only) without a split.  Ties
-// keep the earlier candidate (smaller split, 128-row tiles).
+// Configuration and K split of a call, from a model of the busiest CU's time.
+// Workgroups go out in rounds of (workgroups per CU) x 256; a round in which a CU holds
+// w of them takes (blocks per split) x step time(w), the step times measured on MI355X
+// at N = 512 (the CU's throughput saturates: 2 and 3 concurrent workgroups take about
+// the same time per workgroup-step).  A K split s adds its partials, written and read
+// back (s N M floats each way at ~4 TB/s), and the reduction launch.  Candidates: A with
+// s in {1, 2, 3, 4, 6, 8} (s dividing the blocks, at least 8 per split and, for even
+// block counts, an even number), B without a split and only for an even block count.
+// Ties keep the earlier candidate.
 struct GemmPlan {
-    int rf, splits;
+    int cfg, splits;
 };
-constexpr double kStepUsRf1[4] = {0.0, 1.1, 1.3, 1.76};   // by concurrent workgroups per CU
-constexpr double kStepUsRf2[3] = {0.0, 1.2, 1.94};
+constexpr double kStepUs[2][4] = {
+    {0.0, 1.1, 1.3, 1.76},   // A, by concurrent workgroups per CU
+    {0.0, 1.2, 1.94, 0.0},   // B
+};
+constexpr int kPerCu[2] = {3, 2};
 constexpr double kPartBytesPerUs = 4.0e6, kReduceLaunchUs = 4.0;
 
 static double rounds_us(int64_t wgs, int per_cu, const double *step_us, int steps) {
@@ -565,25 +578,28 @@ static double rounds_us(int64_t wgs, int per_cu, const double *step_us, int step
 }
 
 static GemmPlan gemm_plan(const int64_t *Ms, int64_t n_items, int nb, int64_t N) {
-    int64_t t1 = 0, t2 = 0, rows = 0;
+    int64_t rows = 0, tiles[2] = {0, 0};
     for (int64_t i = 0; i < n_items; ++i) {
-        t1 += (Ms[i] + 127) / 128;
-        t2 += (Ms[i] + 255) / 256;
+        tiles[0] += (Ms[i] + 127) / 128;
+        tiles[1] += (Ms[i] + 255) / 256;
         rows += Ms[i];
     }
-    const int64_t tiles_n = (N + GN - 1) / GN;
-    GemmPlan best{1, 1};
+    GemmPlan best{kCfgA, 1};
     double best_us = 1e300;
-    for (int sp : {1, 2, 3, 4, 6, 8}) {
-        if (sp > 1 && (nb % sp != 0 || nb / sp < 8 || (nb % 2 == 0 && (nb / sp) % 2 != 0))) continue;
-        double us = rounds_us(t1 * tiles_n * sp, 3, kStepUsRf1, nb / sp);
-        if (sp > 1) us += 8.0 * sp * (double)N * (double)rows / kPartBytesPerUs + kReduceLaunchUs;
-        if (us < best_us) {
-            best_us = us;
-            best = {1, sp};
+    for (int cfg : {kCfgA, kCfgB}) {
+        if (cfg != kCfgA && nb % 2 != 0) continue;
+        const int64_t t = tiles[cfg == kCfgA ? 0 : 1] * ((N + cfg_cols(cfg) - 1) / cfg_cols(cfg));
+        for (int sp : {1, 2, 3, 4, 6, 8}) {
+            if (sp > 1 && (cfg == kCfgB || nb % sp != 0 || nb / sp < 8 || (nb % 2 == 0 && (nb / sp) % 2 != 0)))
+                continue;
+            double us = rounds_us(t * sp, kPerCu[cfg], kStepUs[cfg], nb / sp);
+            if (sp > 1) us += 8.0 * sp * (double)N * (double)rows / kPartBytesPerUs + kReduceLaunchUs;
+            if (us < best_us) {
+                best_us = us;
+                best = {cfg, sp};
+            }
         }
     }
-    if (nb % 2 == 0 && rounds_us(t2 * tiles_n, 2, kStepUsRf2, nb) < best_us) best = {2, 1};
     return best;
 }
 
@@ -617,11 +633,11 @@ hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, c
     size_t parts_off;
     gemm_layout(Ms, n_items, nb, N, &plan, &parts_off);
     if (Ms != Ms_local) delete[] Ms;
-    const int splits = plan.splits, TM = 128 * plan.rf;
+    const int splits = plan.splits, TM = cfg_rows(plan.cfg), TN = cfg_cols(plan.cfg);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     _Float16 *x16 = reinterpret_cast<_Float16 *>(ws);
     int *xe = reinterpret_cast<int *>(ws + align256((size_t)N * K * 2));
-    const int tiles_n = (int)((N + GN - 1) / GN);
+    const int tiles_n = (int)((N + TN - 1) / TN);
 
     const bool vec = ((uintptr_t)x % (4 * act_bytes(xt)) == 0) && (ldx % 4 == 0);
     hipError_t e = with_act(xt, [&](auto tag) -> hipError_t {
@@ -666,7 +682,7 @@ hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, c
         bool aligned = nb % 2 == 0;
         for (int k = 0; k < grp.n; ++k) aligned = aligned && ((uintptr_t)grp.p[k].w % 4 == 0);
         launch_gemm_kernel((unsigned)(tiles_m * tiles_n * splits), s, grp, nb, x16, xe, (int)N, tiles_n, xcd_map,
-                           splits, plan.rf, aligned);
+                           splits, plan.cfg, aligned);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (splits > 1) {
@@ -721,7 +737,7 @@ hipError_t launch_gemm_f16_moe(const uint8_t *w, int64_t M, int nb, const void *
     grp.moe_expert_bytes = M * (int64_t)nb * kBlockBytes;
     grp.moe_tiles_m = tiles_m;
     const int64_t grid = (int64_t)tiles_m * moe_max_tiles(r.n_expert, r.n_pairs, GN);
-    launch_gemm_kernel((unsigned)grid, s, grp, nb, x16, xe, (int)r.n_pairs, 1, 0, 1, 1,
+    launch_gemm_kernel((unsigned)grid, s, grp, nb, x16, xe, (int)r.n_pairs, 1, 0, 1, kCfgA,
                        nb % 2 == 0 && (uintptr_t)w % 4 == 0);
     return hipGetLastError();
 }
