@@ -39,7 +39,6 @@ namespace q2_0 {
 namespace {
 
 constexpr int GM = 128, GN = 128, GK = 64;   // GM: row tile of the expert path
-constexpr int GLD = GK + 8;   // fp16 row stride in LDS (144 B): 8 consecutive rows hit distinct banks
 
 // x (N columns of K floats) -> fp16, k permuted inside each 16-group, one workgroup
 // per column.  The column is scaled by 2^e (e = xe[n]) so that its max |x| lands in
@@ -215,8 +214,18 @@ __device__ __forceinline__ int find_gemm_item(const GemmGroup &grp, int tmg) {
 // own wait insertion would otherwise make every later LDS read wait for all of these
 // loads (it cannot tell that they fill a different buffer).  The caller orders them
 // with wait_vmcnt before the barrier that publishes the tile.
+// M0 (the LDS address) is saved and restored around the load, so the compiler's view of
+// it does not change.
 __device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(lds)
+        : "memory");
 }
 
 // s_waitcnt with only the vector-memory count set (expcnt and lgkmcnt at their maxima).
