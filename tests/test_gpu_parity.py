@@ -311,7 +311,9 @@ def test_mat_vec_group_activation_range():
 @pytest.mark.parametrize("precision,rel", [(B.Q2_0_PREC_F16_MFMA, REL_F16), (B.Q2_0_PREC_F32, REL_F32)])
 @pytest.mark.parametrize("M,K,N,ldx,ldy", [
     (64, 64, 64, 64, 64), (1, 64, 9, 64, 1), (65, 192, 63, 200, 70), (200, 512, 130, 512, 203),
-    (127, 2048, 65, 2050, 127), (33, 576, 100, 576, 33)])
+    (127, 2048, 65, 2050, 127), (33, 576, 100, 576, 33),
+    # one tile: K split 3 ways (24 blocks) and 6 ways (48 blocks), ragged rows and columns
+    (120, 1536, 60, 1536, 121), (127, 3072, 63, 3080, 127)])
 def test_mul_mat_ragged(precision, rel, M, K, N, ldx, ldy):
     w = synth.weight(12, M, N, M, K, "quad", synth.ScaleDist("loguniform", 1e-3, 1e-1, 0.02))
     x = synth.activations(12, M, N, N, K)
@@ -342,6 +344,35 @@ def test_mul_mat_stack_8b_workload(precision, rel):
         y = run_mul_mat(dev(w), M, K, x, precision)
         rows = np.unique(np.concatenate([rng.integers(0, M, 48), [0, M - 1]]))
         assert_products(y, w, M, K, x, rel, rows=rows, what=name)
+
+
+def test_weights_at_two_byte_offset():
+    """W at an address 2 mod 4 (the API's minimum alignment for 18-byte blocks): the GEMM
+    then reads its codes with 2-byte loads, in both tile configurations (200 x 512 at
+    N = 130: 128-row tiles; 65357 x 640 at N = 500: 256-row tiles).  The results are bit
+    for bit those of the same W at an aligned address, and within the fp16 bound of the
+    oracle; get_rows and the mat-vec are checked on the offset W too."""
+    torch = _torch()
+    for M, K, N in [(200, 512, 130), (65357, 640, 500)]:
+        w = synth.weight(31, M, N, M, K, "quad", synth.ScaleDist("loguniform", 1e-3, 1e-1, 0.02))
+        flat = np.ascontiguousarray(w).reshape(-1)
+        buf = torch.zeros(flat.size + 16, dtype=torch.uint8, device="cuda")
+        buf[2:2 + flat.size].copy_(torch.from_numpy(flat).cuda())
+        w_off = buf[2:]
+        assert w_off.data_ptr() % 4 == 2
+        x = synth.activations(31, M, N, N, K)
+        y_al = run_mul_mat(dev(w), M, K, x, B.Q2_0_PREC_F16_MFMA)
+        y_off = run_mul_mat(w_off, M, K, x, B.Q2_0_PREC_F16_MFMA)
+        assert np.array_equal(y_al.view(np.uint32), y_off.view(np.uint32)), "M=%d: offset W changed the GEMM" % M
+        rows = np.unique(np.concatenate([np.arange(0, M, max(1, M // 200)), [M - 1]]))
+        assert_products(y_off, w, M, K, x, REL_F16, rows=rows, what="offset W M=%d" % M)
+        x1 = x[:1]
+        y1 = run_mat_vec(w_off, M, K, x1)
+        assert_products(y1, w, M, K, x1, REL_F32, rows=rows, what="offset W mat-vec M=%d" % M)
+        ids = np.array([0, M - 1, M // 2, 7 % M], dtype=np.int32)
+        out = run_get_rows(w_off, M, K, ids)
+        ok, nbad = same_bits(out, oracle.get_rows(w, M, K, ids))
+        assert ok, "offset W get_rows M=%d: %d values differ" % (M, nbad)
 
 
 def test_mul_mat_small_n_routes_to_mat_vec():
