@@ -490,10 +490,60 @@ def main():
         "cpu_baseline": None,
     }
 
+    result["ceilings"] = measured_ceilings(dev, wl, matvec_gbs, gemm_tflops)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(host_w, order, wl, args)
 
     print(json.dumps(result), flush=True)
+
+
+def measured_ceilings(dev, wl, matvec_gbs, gemm_tflops):
+    """Context for the roofline fractions, measured on this GPU outside the timed region with
+    torch's own kernels (not this library): a 2 GiB device copy (HBM read + write rate), a
+    dense fp16 GEMM of 8192^3 (hipBLASLt), and the stack's per-layer prefill shapes as dense
+    fp16 GEMMs (the weights as fp16, 7.1x the bytes of Q2_0) at N = 512.  Random operands."""
+    import torch
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3
+    out = {}
+    n = (2 << 30) // 4
+    src = torch.randn(n, device=dev)
+    dst = torch.empty_like(src)
+    t = timed(lambda: dst.copy_(src), 5)
+    out["hbm_copy_GBps"] = round(2 * 4 * n / t / 1e9, 1)
+    del src, dst
+    a16 = torch.randn((8192, 8192), device=dev, dtype=torch.float16)
+    b16 = torch.randn((8192, 8192), device=dev, dtype=torch.float16)
+    t = timed(lambda: torch.matmul(a16, b16), 5)
+    out["f16_gemm_8192_TFLOPs"] = round(2 * 8192 ** 3 / t / 1e12, 1)
+    del a16, b16
+    shapes = [(wl.shapes["q"][0] + 2 * wl.shapes["k"][0], wl.shapes["q"][1]), wl.shapes["o"],
+              (2 * wl.shapes["gate"][0], wl.shapes["gate"][1]), wl.shapes["down"]]
+    ops = []
+    for M, K in shapes:
+        x16 = torch.randn((PREFILL_N, K), device=dev, dtype=torch.float16)
+        wt = torch.randn((K, M), device=dev, dtype=torch.float16) * 0.01
+        ops.append((x16, wt))
+    t = timed(lambda: [torch.matmul(x16, wt) for x16, wt in ops], 10)
+    flops = sum(2.0 * PREFILL_N * M * K for M, K in shapes)
+    out["f16_dense_prefill_layer_TFLOPs"] = round(flops / t / 1e12, 1)
+    del ops
+    out["decode_frac_of_copy_rate"] = round(matvec_gbs / out["hbm_copy_GBps"], 4)
+    out["prefill_frac_of_f16_gemm_8192"] = round(gemm_tflops / out["f16_gemm_8192_TFLOPs"], 4)
+    out["note"] = ("torch's own kernels on this GPU, outside the timed region: an elementwise copy, hipBLASLt "
+                   "fp16 GEMMs (8192^3, and the stack's q/k/v, o, gate/up, down shapes at N = 512 with fp16 "
+                   "weights)")
+    return out
 
 
 def next_rows(ms, wl, order, VM, VK, pre_flops, ne, mm, mk, nu):
