@@ -21,6 +21,7 @@ namespace {
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kFastRuns = 512;   // runs (experts + 1) up to which the per-wave counts fit in LDS
+constexpr int kRouteKeep = 4;    // chunks whose runs stay in registers between counting and placement
 
 // off[0..n_expert+1]: run starts (off[n_expert] .. off[n_expert+1] holds the bad ids);
 // perm[pos] = pair; tiles: (expert, column tile) for every tile_w-column tile of every
@@ -53,7 +54,15 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route(const int32_t *__rest
     if (kFast)
         for (int i = tid; i < kRouteWaves * runs; i += kRouteThreads) wh[i] = 0;
     __syncthreads();
-    for (int p = tid; p < n_pairs; p += kRouteThreads) atomicAdd(&cnt[run_of(p)], 1);
+    // The first kRouteKeep chunks' runs stay in registers for the placement.
+    int keep[kRouteKeep];
+#pragma unroll
+    for (int c = 0; c < kRouteKeep; ++c) {
+        const int p = c * kRouteThreads + tid;
+        keep[c] = p < n_pairs ? run_of(p) : -1;
+        if (keep[c] >= 0) atomicAdd(&cnt[keep[c]], 1);
+    }
+    for (int p = kRouteKeep * kRouteThreads + tid; p < n_pairs; p += kRouteThreads) atomicAdd(&cnt[run_of(p)], 1);
     __syncthreads();
     if (tid < 64) {
         const int L = (runs + 63) / 64, b0 = lane * L;
@@ -95,20 +104,26 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route(const int32_t *__rest
         }
     }
     __syncthreads();
-    for (int c0 = 0; c0 < n_pairs; c0 += kRouteThreads) {
+    for (int c0 = 0, ci = 0; c0 < n_pairs; c0 += kRouteThreads, ++ci) {
         const int p = c0 + tid;
-        const int b = p < n_pairs ? run_of(p) : -1;
+        int b = -1;
+#pragma unroll
+        for (int c = 0; c < kRouteKeep; ++c) b = ci == c ? keep[c] : b;
+        if (ci >= kRouteKeep) b = p < n_pairs ? run_of(p) : -1;
         if constexpr (kFast) {
             int rank = 0;
             for (int j = 0; j < 64; ++j) rank += (j < lane) & (__shfl(b, j) == b);
             if (b >= 0) atomicAdd(&wh[wv * runs + b], 1);
             __syncthreads();
             for (int r = tid; r < runs; r += kRouteThreads) {
+                int c[kRouteWaves];   // all loads first: the stores below would serialize them
+#pragma unroll
+                for (int v = 0; v < kRouteWaves; ++v) c[v] = wh[v * runs + r];
                 int sum = 0;
+#pragma unroll
                 for (int v = 0; v < kRouteWaves; ++v) {
-                    const int c = wh[v * runs + r];
                     wh[v * runs + r] = sum;
-                    sum += c;
+                    sum += c[v];
                 }
                 tot[r] = sum;
             }
