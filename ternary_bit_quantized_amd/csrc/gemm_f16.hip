@@ -561,22 +561,24 @@ static void launch_gemm_kernel(unsigned grid, hipStream_t s, const GemmGroup &gr
 
 // Configuration and K split of a call, from a model of the busiest CU's time.
 // Workgroups go out in rounds of (workgroups per CU) x 256; a round in which a CU holds
-// w of them takes (blocks per split) x step time(w), the step times measured on MI355X
-// at N = 512 (the CU's throughput saturates: 2 and 3 concurrent workgroups take about
-// the same time per workgroup-step).  A K split s adds its partials, written and read
-// back (s N M floats each way at ~4 TB/s), and the reduction launch.  Candidates: A with
-// s in {1, 2, 3, 4, 6, 8} (s dividing the blocks, at least 8 per split and, for even
-// block counts, an even number), B without a split and only for an even block count.
-// Ties keep the earlier candidate.
+// w of them takes (blocks per split) x step time(w).  A K split s adds its partials,
+// written by the GEMM (s N M floats at ~5 TB/s) and read back with the result written
+// by the reduction ((s + 1) N M floats at ~4.5 TB/s, plus its launch).  The constants
+// are fitted to the stack's shapes at N = 512 on MI355X, measured for every split: a
+// CU's throughput saturates from two workgroups on (0.62, 0.53 and 0.51 us per
+// 128-row workgroup-step with 1, 2 and 3 of them).  Candidates: A with s in
+// {1, 2, 3, 4, 6, 8} (s dividing the blocks, at least 8 per split and, for even block
+// counts, an even number), B without a split and only for an even block count.  Ties
+// keep the earlier candidate (smaller split, A).
 struct GemmPlan {
     int cfg, splits;
 };
 constexpr double kStepUs[2][4] = {
-    {0.0, 1.1, 1.3, 1.76},   // A, by concurrent workgroups per CU
-    {0.0, 1.2, 1.94, 0.0},   // B
+    {0.0, 0.62, 1.05, 1.54},   // A, by concurrent workgroups per CU
+    {0.0, 0.96, 1.71, 0.0},    // B
 };
 constexpr int kPerCu[2] = {3, 2};
-constexpr double kPartBytesPerUs = 4.0e6, kReduceLaunchUs = 4.0;
+constexpr double kPartWriteBytesPerUs = 5.0e6, kReduceBytesPerUs = 4.5e6, kReduceLaunchUs = 2.0;
 
 static double rounds_us(int64_t wgs, int per_cu, const double *step_us, int steps) {
     const int64_t slots = 256 * (int64_t)per_cu;
@@ -593,6 +595,7 @@ static GemmPlan gemm_plan(const int64_t *Ms, int64_t n_items, int nb, int64_t N)
         tiles[1] += (Ms[i] + 255) / 256;
         rows += Ms[i];
     }
+    const double nm_bytes = 4.0 * (double)N * (double)rows;   // one f32 copy of all outputs
     GemmPlan best{kCfgA, 1};
     double best_us = 1e300;
     for (int cfg : {kCfgA, kCfgB}) {
@@ -602,7 +605,8 @@ static GemmPlan gemm_plan(const int64_t *Ms, int64_t n_items, int nb, int64_t N)
             if (sp > 1 && (cfg == kCfgB || nb % sp != 0 || nb / sp < 8 || (nb % 2 == 0 && (nb / sp) % 2 != 0)))
                 continue;
             double us = rounds_us(t * sp, kPerCu[cfg], kStepUs[cfg], nb / sp);
-            if (sp > 1) us += 8.0 * sp * (double)N * (double)rows / kPartBytesPerUs + kReduceLaunchUs;
+            if (sp > 1)
+                us += sp * nm_bytes / kPartWriteBytesPerUs + (sp + 1) * nm_bytes / kReduceBytesPerUs + kReduceLaunchUs;
             if (us < best_us) {
                 best_us = us;
                 best = {cfg, sp};
