@@ -183,11 +183,11 @@ int check_moe_shape(int64_t n_expert, int64_t M, int64_t K, int64_t n_used, int6
     const int64_t n_pairs = n_used * n_tokens;
     // launch grids: the fp32 path has one workgroup row per tile-list entry (grid.y)
     if (precision == Q2_0_PREC_F32 && q2_0::moe_max_tiles(n_expert, n_pairs, 64) > 65535) return Q2_0_ERR_SHAPE;
-    if ((M + 127) / 128 * q2_0::moe_max_tiles(n_expert, n_pairs, 128) > kMaxRows) return Q2_0_ERR_SHAPE;
+    if ((M + 127) / 128 * q2_0::moe_max_tiles(n_expert, n_pairs, 64) > kMaxRows) return Q2_0_ERR_SHAPE;
     return Q2_0_OK;
 }
 
-int moe_tile_w(int precision) { return precision == Q2_0_PREC_F32 ? 64 : 128; }
+int moe_tile_w(int) { return 64; }   // column tile of both expert GEMMs
 
 }  // namespace
 

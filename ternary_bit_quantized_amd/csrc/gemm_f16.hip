@@ -38,7 +38,7 @@ namespace q2_0 {
 
 namespace {
 
-constexpr int GM = 128, GN = 128, GK = 64;   // GM: row tile of the expert path
+constexpr int GM = 128, GK = 64;   // GM: row tile of the expert path
 
 // x (N columns of K floats) -> fp16, k permuted inside each 16-group, one workgroup
 // per column.  The column is scaled by 2^e (e = xe[n]) so that its max |x| lands in
@@ -533,11 +533,14 @@ size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 // GEMM kernel configurations (workgroup tile rows x columns, per wave RF x NJ MFMA tiles):
 //   A: 128 x 128, RF 1 x NJ 4, two x buffers, three workgroups per CU;
 //   B: 256 x 128, RF 2 x NJ 4, three x buffers, two workgroups per CU.
+//   C: 128 x 64, RF 1 x NJ 2, two x buffers, four workgroups per CU: the expert product,
+//      whose experts hold a few dozen columns each (half the MFMAs and x loads of A per
+//      tile there, for the same weight decode).
 // (256 x 64 tiles, RF 2 x NJ 2 at three workgroups per CU -- half the LDS operand reads
 // per MFMA of A, twice the decode per MFMA -- measured ~10 % slower than A at N = 512.)
-enum GemmCfg { kCfgA = 0, kCfgB = 1 };
-constexpr int cfg_rows(int cfg) { return cfg == kCfgA ? 128 : 256; }
-constexpr int cfg_cols(int) { return 128; }
+enum GemmCfg { kCfgA = 0, kCfgB = 1, kCfgC = 2 };
+constexpr int cfg_rows(int cfg) { return cfg == kCfgB ? 256 : 128; }
+constexpr int cfg_cols(int cfg) { return cfg == kCfgC ? 64 : 128; }
 
 // The GEMM kernel of a configuration, with 4-byte code loads where every matrix row is
 // 4-byte aligned.
@@ -554,6 +557,8 @@ static void launch_gemm_kernel(unsigned grid, hipStream_t s, const GemmGroup &gr
     } while (0)
     if (cfg == kCfgB)
         Q2_0_GEMM_LAUNCH(2, 4, 3, 2);
+    else if (cfg == kCfgC)
+        Q2_0_GEMM_LAUNCH(1, 2, 2, 4);
     else
         Q2_0_GEMM_LAUNCH(1, 4, 2, 3);
 #undef Q2_0_GEMM_LAUNCH
@@ -749,8 +754,9 @@ hipError_t launch_gemm_f16_moe(const uint8_t *w, int64_t M, int nb, const void *
     grp.moe_ntiles = r.ntiles;
     grp.moe_expert_bytes = M * (int64_t)nb * kBlockBytes;
     grp.moe_tiles_m = tiles_m;
-    const int64_t grid = (int64_t)tiles_m * moe_max_tiles(r.n_expert, r.n_pairs, GN);
-    launch_gemm_kernel((unsigned)grid, s, grp, nb, x16, xe, (int)r.n_pairs, 1, 0, 1, kCfgA,
+    if (r.tile_w != cfg_cols(kCfgC)) return hipErrorInvalidValue;
+    const int64_t grid = (int64_t)tiles_m * moe_max_tiles(r.n_expert, r.n_pairs, cfg_cols(kCfgC));
+    launch_gemm_kernel((unsigned)grid, s, grp, nb, x16, xe, (int)r.n_pairs, 1, 0, 1, kCfgC,
                        nb % 2 == 0 && (uintptr_t)w % 4 == 0);
     return hipGetLastError();
 }
