@@ -290,6 +290,11 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
         Nv = grp.moe_off[e + 1] - col0;
     }
     const GemmItem &item = *itp;
+    // x16 row of column n of the tile (columns past Nv use the tile's first column)
+    auto xrow = [&](int n) {
+        const int c = col0 + (n < Nv ? n : 0);
+        return grp.moe_off ? grp.moe_perm[c] / grp.moe_xdiv : c;
+    };
     const int K = nb * kBlockWeights;
     const int rowbytes = nb * kBlockBytes;
     const int nbs = nb / splits;                 // blocks of this split
@@ -342,7 +347,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
 #pragma unroll
         for (int q = 0; q < NJ; ++q) {
             const int n = n0 + 8 * NJ * wave + 8 * q + cq;
-            xsrc[q] = x16 + (int64_t)(col0 + (n < Nv ? n : 0)) * K + (int64_t)kb0 * GK + 8 * ch;
+            xsrc[q] = x16 + (int64_t)xrow(n) * K + (int64_t)kb0 * GK + 8 * ch;
         }
     }
     const uint32_t bs_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)&Bs[0][0];
@@ -461,7 +466,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int n = n0 + j * 32 + (lane & 31);
-        const int ye = -xe[col0 + (n < Nv ? n : 0)];
+        const int ye = -xe[xrow(n)];
 #pragma unroll
         for (int i = 0; i < RF; ++i)
 #pragma unroll
@@ -715,10 +720,11 @@ hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, c
     return hipSuccess;
 }
 
-// Expert product on the fp16 GEMM: x is gathered into expert order and converted once
-// (scratch: x16 then the column exponents), then one launch runs every (expert, column
-// tile) entry of the routing's tile list against all row tiles; entries past the
-// list's length exit at once.  No K split, so every result is written once, in a
+// Expert product on the fp16 GEMM: x is converted once, one row per token (one per pair
+// when every slot has its own x column; scratch: x16 then the row exponents), then one
+// launch runs every (expert, column tile) entry of the routing's tile list against all
+// row tiles, each column's x row read through the routing's pair index; entries past
+// the list's length exit at once.  No K split, so every result is written once, in a
 // fixed order.
 size_t gemm_f16_moe_scratch_bytes(int64_t K, int64_t n_pairs) {
     return align256((size_t)n_pairs * K * 2) + align256((size_t)n_pairs * 4);
@@ -731,14 +737,15 @@ hipError_t launch_gemm_f16_moe(const uint8_t *w, int64_t M, int nb, const void *
     _Float16 *x16 = reinterpret_cast<_Float16 *>(ws);
     int *xe = reinterpret_cast<int *>(ws + align256((size_t)r.n_pairs * K * 2));
     const bool vec = ((uintptr_t)x % (4 * act_bytes(xt)) == 0) && (ldx % 4 == 0);
-    const XGather gather{r.perm, r.n_used, r.x_slots};
+    const XGather ident{nullptr, r.n_used, r.x_slots};
+    const int nx = r.x_slots == 1 ? r.n_pairs / r.n_used : r.n_pairs;   // x rows
     hipError_t e = with_act(xt, [&](auto tag) -> hipError_t {
         using XT = decltype(tag);
         const XT *xp = static_cast<const XT *>(x);
         if (vec)
-            x_to_f16_perm<true, XT><<<(unsigned)r.n_pairs, 256, 0, s>>>(xp, ldx, K, x16, xe, gather);
+            x_to_f16_perm<true, XT><<<(unsigned)nx, 256, 0, s>>>(xp, ldx, K, x16, xe, ident);
         else
-            x_to_f16_perm<false, XT><<<(unsigned)r.n_pairs, 256, 0, s>>>(xp, ldx, K, x16, xe, gather);
+            x_to_f16_perm<false, XT><<<(unsigned)nx, 256, 0, s>>>(xp, ldx, K, x16, xe, ident);
         return hipGetLastError();
     });
     if (e != hipSuccess) return e;
@@ -754,6 +761,7 @@ hipError_t launch_gemm_f16_moe(const uint8_t *w, int64_t M, int nb, const void *
     grp.moe_ntiles = r.ntiles;
     grp.moe_expert_bytes = M * (int64_t)nb * kBlockBytes;
     grp.moe_tiles_m = tiles_m;
+    grp.moe_xdiv = r.x_slots == 1 ? r.n_used : 1;
     if (r.tile_w != cfg_cols(kCfgC)) return hipErrorInvalidValue;
     const int64_t grid = (int64_t)tiles_m * moe_max_tiles(r.n_expert, r.n_pairs, cfg_cols(kCfgC));
     launch_gemm_kernel((unsigned)grid, s, grp, nb, x16, xe, (int)r.n_pairs, 1, 0, 1, kCfgC,

@@ -21,6 +21,7 @@ namespace {
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kFastRuns = 512;   // runs (experts + 1) up to which the per-wave counts fit in LDS
+static_assert(kFastRuns <= 1023, "kFast run indexes and the idle value fit in 10 bits");
 constexpr int kRouteKeep = 4;    // chunks whose runs stay in registers between counting and placement
 
 // off[0..n_expert+1]: run starts (off[n_expert] .. off[n_expert+1] holds the bad ids);
@@ -32,7 +33,8 @@ constexpr int kRouteKeep = 4;    // chunks whose runs stay in registers between 
 //  * stable placement, one chunk of kRouteThreads pairs at a time: a pair goes to its
 //    run's cursor + the pairs of its run in earlier waves of the chunk + those in earlier
 //    lanes of its own wave.  kFast: the per-wave counts of every run sit in LDS and a
-//    pair's rank in its wave comes from 64 lane reads; otherwise (many runs) each pair
+//    pair's rank in its wave is the count of earlier lanes whose run
+//    index matches in every bit (one ballot per bit); otherwise (many runs) each pair
 //    counts the earlier pairs of its run in the chunk one by one.
 template <bool kFast>
 __global__ __launch_bounds__(kRouteThreads) void moe_route(const int32_t *__restrict__ ids, int n_pairs,
@@ -111,8 +113,17 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route(const int32_t *__rest
         for (int c = 0; c < kRouteKeep; ++c) b = ci == c ? keep[c] : b;
         if (ci >= kRouteKeep) b = p < n_pairs ? run_of(p) : -1;
         if constexpr (kFast) {
-            int rank = 0;
-            for (int j = 0; j < 64; ++j) rank += (j < lane) & (__shfl(b, j) == b);
+            // lanes of the wave with the same run: equal in every bit of the run index
+            // (b < 512; the idle value -1 reads as 1023)
+            const unsigned ub = (unsigned)b & 1023u;
+            uint64_t same = ~0ull;
+#pragma unroll
+            for (int i = 0; i < 10; ++i) {
+                const uint64_t m = __ballot((ub >> i) & 1u);
+                same &= ((ub >> i) & 1u) ? m : ~m;
+            }
+            const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(same >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)same, 0u));
             if (b >= 0) atomicAdd(&wh[wv * runs + b], 1);
             __syncthreads();
             for (int r = tid; r < runs; r += kRouteThreads) {

@@ -138,13 +138,16 @@ struct GemmGroup {
     // b % moe_tiles_m of the (expert, column tile) entry b / moe_tiles_m of moe_tiles
     // (device; *moe_ntiles entries, the rest exit); expert e is the matrix at
     // p[0].w + e * moe_expert_bytes, its columns are x16 columns moe_off[e] ..
-    // moe_off[e+1]-1, and result column j goes to y column moe_perm[j] of p[0].
+    // moe_off[e+1]-1, and result column j goes to y column moe_perm[j] of p[0]; it
+    // multiplies x16 row moe_perm[j] / moe_xdiv (the token's x row, shared by its slots
+    // when moe_xdiv is the slots per token).
     const int *moe_off;
     const int *moe_perm;
     const int *moe_tiles;     // pairs (expert, column tile)
     const int *moe_ntiles;
     int64_t moe_expert_bytes;
     int moe_tiles_m;
+    int moe_xdiv;
 };
 size_t gemm_f16_workspace_bytes(const int64_t *Ms, int64_t n_items, int64_t K, int64_t N);
 hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, const void *x, Act xt,
