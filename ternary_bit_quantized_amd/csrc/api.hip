@@ -235,11 +235,13 @@ int q2_0_mul_mat_id(const void *w, int64_t n_expert, int64_t M, int64_t K, const
                                            moe_tile_w(precision), workspace, &r, s));
     if (st) return st;
     if (precision == Q2_0_PREC_F16_MFMA) {
-        void *scratch = static_cast<uint8_t *>(workspace) + q2_0::moe_route_bytes(n_expert, n_pairs, 128);
-        st = hip_status(q2_0::launch_gemm_f16_moe(wb, M, nb, x, xt, ldx, r, y, ldy, scratch, s));
-    } else {
-        st = hip_status(q2_0::launch_gemm_f32_moe(wb, M, nb, x, xt, ldx, r, y, ldy, s));
+        // the fp16 GEMM's scratch follows the routing tables; its launch also fills the
+        // out-of-range pairs' columns
+        void *scratch =
+            static_cast<uint8_t *>(workspace) + q2_0::moe_route_bytes(n_expert, n_pairs, moe_tile_w(precision));
+        return hip_status(q2_0::launch_gemm_f16_moe(wb, M, nb, x, xt, ldx, r, y, ldy, scratch, s));
     }
+    st = hip_status(q2_0::launch_gemm_f32_moe(wb, M, nb, x, xt, ldx, r, y, ldy, s));
     if (st) return st;
     return hip_status(q2_0::launch_moe_fill_bad(r, M, y, ldy, s));
 }

@@ -279,6 +279,15 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
         n0 = tn * TN;
     } else {
         const int t = blockIdx.x / grp.moe_tiles_m;
+        if (t >= grp.moe_max_tiles) {       // NaN into the out-of-range pairs' columns
+            const GemmItem &it = grp.p[0];
+            const int m = (blockIdx.x % grp.moe_tiles_m) * TM + (tid % TM);
+            const int j1 = grp.moe_off[grp.moe_n_expert + 1];
+            if (m < it.M)
+                for (int j = grp.moe_off[grp.moe_n_expert] + tid / TM; j < j1; j += 256 / TM)
+                    it.y[(int64_t)grp.moe_perm[j] * it.ldy + m] = __builtin_nanf("");
+            return;
+        }
         if (t >= *grp.moe_ntiles) return;   // the whole workgroup: no tile here
         const int e = grp.moe_tiles[2 * t];
         itp = &grp.p[0];
@@ -763,7 +772,9 @@ hipError_t launch_gemm_f16_moe(const uint8_t *w, int64_t M, int nb, const void *
     grp.moe_tiles_m = tiles_m;
     grp.moe_xdiv = r.x_slots == 1 ? r.n_used : 1;
     if (r.tile_w != cfg_cols(kCfgC)) return hipErrorInvalidValue;
-    const int64_t grid = (int64_t)tiles_m * moe_max_tiles(r.n_expert, r.n_pairs, cfg_cols(kCfgC));
+    grp.moe_max_tiles = (int)moe_max_tiles(r.n_expert, r.n_pairs, cfg_cols(kCfgC));
+    grp.moe_n_expert = r.n_expert;
+    const int64_t grid = (int64_t)tiles_m * (grp.moe_max_tiles + 1);   // + the NaN fill
     launch_gemm_kernel((unsigned)grid, s, grp, nb, x16, xe, (int)r.n_pairs, 1, 0, 1, kCfgC,
                        nb % 2 == 0 && (uintptr_t)w % 4 == 0);
     return hipGetLastError();

@@ -148,6 +148,10 @@ struct GemmGroup {
     int64_t moe_expert_bytes;
     int moe_tiles_m;
     int moe_xdiv;
+    // the tile list's bound: workgroups past moe_max_tiles * moe_tiles_m fill the y
+    // columns of the out-of-range run (moe_off[moe_n_expert] ..) with NaN, one row tile each
+    int moe_max_tiles;
+    int moe_n_expert;
 };
 size_t gemm_f16_workspace_bytes(const int64_t *Ms, int64_t n_items, int64_t K, int64_t N);
 hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, const void *x, Act xt,

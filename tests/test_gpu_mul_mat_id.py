@@ -114,6 +114,24 @@ def test_mul_mat_id_many_experts(precision, ne):
     check(y, y_ref, bound, REL[precision], "ne=%d p%d" % (ne, precision))
 
 
+@pytest.mark.parametrize("precision", [B.Q2_0_PREC_F16_MFMA, B.Q2_0_PREC_F32])
+def test_mul_mat_id_two_column_tiles_per_expert(precision):
+    """256 experts with 65 pairs each: every expert's run spans two 64-column tiles, so the
+    tile list is as long as it gets for this pair count and the fp16 path's scratch, laid
+    out after it, must not overlap it; three ids out of range (NaN columns)."""
+    rng = np.random.default_rng(257 + precision)
+    ne, M, K, nu = 256, 96, 256, 5
+    flat = rng.permutation(np.repeat(np.arange(ne, dtype=np.int32), 65))
+    ids = flat.reshape(-1, nu).copy()
+    ids[0, 0], ids[100, 4], ids[-1, 2] = -3, ne, ne + 7
+    nt = ids.shape[0]
+    wall = experts(67, ne, M, K)
+    x = synth.activations(67, nt, 0, nt, K)
+    y = run_id(wall, ne, M, K, x, B.Q2_0_ACT_F32, ids, precision)
+    y_ref, bound = oracle.mul_mat_id(wall, ne, M, K, x, ids)
+    check(y, y_ref, bound, REL[precision], "two tiles p%d" % precision)
+
+
 def test_mul_mat_id_f32_equals_per_expert_mul_mat_bitwise():
     """On the fp32 path each result column depends only on its expert and activation, so it
     equals, bit for bit, q2_0_mul_mat of that expert on the gathered columns."""
