@@ -225,10 +225,9 @@ int q2_0_mul_mat_id(const void *w, int64_t n_expert, int64_t M, int64_t K, const
     // few tokens (as q2_0_mul_mat with N <= 8): one fp32-grade mat-vec per pair
     if (n_tokens <= Q2_0_MAT_VEC_MAX_N && n_pairs <= 65535 &&
         q2_0::mat_vec_mfma_eligible(wb, M, nb, x, xt, ldx)) {
-        st = hip_status(q2_0::launch_mat_vec_mfma_pairs(wb, M, nb, x, xt, ldx, ids, (int)n_expert, (int)n_used,
-                                                        (int)x_slots, (int)n_pairs, y, ldy, s));
-        if (st) return st;
-        return hip_status(q2_0::launch_moe_fill_bad_ids(ids, (int)n_pairs, (int)n_expert, M, y, ldy, s));
+        // (out-of-range ids: NaN columns, written by the same launch)
+        return hip_status(q2_0::launch_mat_vec_mfma_pairs(wb, M, nb, x, xt, ldx, ids, (int)n_expert, (int)n_used,
+                                                          (int)x_slots, (int)n_pairs, y, ldy, s));
     }
     q2_0::MoeRoute r;
     st = hip_status(q2_0::launch_moe_route(ids, (int)n_pairs, (int)n_expert, (int)n_used, (int)x_slots,

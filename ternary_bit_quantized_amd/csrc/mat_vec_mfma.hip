@@ -44,8 +44,8 @@ constexpr int kTile = kMvTile;
 // SB: blocks per stage.
 // route.ids set (expert product, NC = 1): blockIdx.y is a (token, slot) pair p; its
 // expert e = ids[p] selects the matrix at w + e * expert_bytes, its activation column is
-// t (x_slots == 1) or p, and its result column p.  Pairs with an id outside
-// [0, n_expert) are left to the caller (nothing is read or written for them).
+// t (x_slots == 1) or p, and its result column p.  A pair with an id outside
+// [0, n_expert) reads nothing: its workgroups write NaN into their rows of column p.
 struct PairRoute {
     const int32_t *ids;
     int n_expert, n_used, x_slots;
@@ -59,7 +59,13 @@ __global__ __launch_bounds__(256) void mat_vec_mfma(const uint8_t *__restrict__ 
     if (route.ids) {
         const int p = blockIdx.y;
         const int e = route.ids[p];
-        if (e < 0 || e >= route.n_expert) return;   // the whole workgroup
+        if (e < 0 || e >= route.n_expert) {          // the whole workgroup
+            constexpr int kRows = (4 / KS) * kTile;  // rows of this workgroup
+            const int r1 = min(M, (int)blockIdx.x * kRows + kRows);
+            for (int r = (int)blockIdx.x * kRows + (int)threadIdx.x; r < r1; r += 256)
+                y[(int64_t)p * ldy + r] = __builtin_nanf("");
+            return;
+        }
         w += e * route.expert_bytes;
         x += (int64_t)(route.x_slots == 1 ? p / route.n_used : p) * ldx;
         y += (int64_t)p * ldy;

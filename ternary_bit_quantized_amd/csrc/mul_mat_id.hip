@@ -170,24 +170,6 @@ __global__ __launch_bounds__(256) void moe_fill_bad(const int *__restrict__ off,
         y[(int64_t)perm[j] * ldy + m] = __builtin_nanf("");
 }
 
-// y columns of pairs whose id is out of range, read from ids directly: quiet NaN.
-__global__ __launch_bounds__(256) void moe_fill_bad_ids(const int32_t *__restrict__ ids, int n_expert, int64_t M,
-                                                        float *__restrict__ y, int64_t ldy) {
-    const int p = blockIdx.y;
-    const int e = ids[p];
-    const int64_t m = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if ((e < 0 || e >= n_expert) && m < M) y[(int64_t)p * ldy + m] = __builtin_nanf("");
-}
-
-}  // namespace
-
-hipError_t launch_moe_fill_bad_ids(const int32_t *ids, int n_pairs, int n_expert, int64_t M, float *y, int64_t ldy,
-                                   hipStream_t s) {
-    moe_fill_bad_ids<<<dim3((unsigned)((M + 255) / 256), (unsigned)n_pairs), 256, 0, s>>>(ids, n_expert, M, y, ldy);
-    return hipGetLastError();
-}
-
-namespace {
 size_t a256(size_t v) { return (v + 255) & ~(size_t)255; }
 }  // namespace
 

@@ -187,12 +187,10 @@ hipError_t launch_gemm_f16_moe(const uint8_t *w, int64_t M, int nb, const void *
 size_t gemm_f16_moe_scratch_bytes(int64_t K, int64_t n_pairs);
 hipError_t launch_moe_fill_bad(const MoeRoute &r, int64_t M, float *y, int64_t ldy, hipStream_t s);
 // few tokens: one K-split mat-vec per pair, expert read from ids on the GPU; pairs with
-// ids out of range are skipped (launch_moe_fill_bad_ids writes them)
+// ids out of range get NaN columns from the same launch
 hipError_t launch_mat_vec_mfma_pairs(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx,
                                      const int32_t *ids, int n_expert, int n_used, int x_slots, int n_pairs,
                                      float *y, int64_t ldy, hipStream_t s);
-hipError_t launch_moe_fill_bad_ids(const int32_t *ids, int n_pairs, int n_expert, int64_t M, float *y, int64_t ldy,
-                                   hipStream_t s);
 hipError_t launch_gemm_f32_moe(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx,
                                const MoeRoute &r, float *y, int64_t ldy, hipStream_t s);
 
