@@ -325,7 +325,7 @@ def main():
         "quantize_vocab_f32": run_quantize,
         "repack_g128_vocab": run_repack_g128,
         "expert_layer_prefill": lambda: run_moe(moe_ids_p, B.Q2_0_PREC_F16_MFMA),
-        "expert_layer_decode": lambda: run_moe(moe_ids_d, B.Q2_0_PREC_F32),
+        "expert_layer_decode": lambda: run_moe(moe_ids_d, B.Q2_0_PREC_F16_MFMA),
     }
     if args.parts:
         keep = args.parts.split(",")

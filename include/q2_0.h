@@ -19,8 +19,10 @@
  *
  * Conventions shared by all calls:
  *   - Every pointer is a DEVICE pointer owned by the caller.  The library never
- *     allocates device memory, keeps no reference after the call returns and has
- *     no global state besides a thread-local copy of the last HIP error.
+ *     allocates device memory on a call and keeps no reference after the call
+ *     returns.  Its only global state is a thread-local copy of the last HIP error
+ *     and a per-device flag, set once with an atomic store, that records that the
+ *     kernels' shared-memory limit was raised.  Calls may come from any thread.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
  *     work; the caller keeps buffers alive until the stream has passed them.
  *   - Arguments are validated on the host before anything is launched; on any
@@ -54,8 +56,8 @@ typedef enum {
 } q2_0_status;
 
 typedef enum {
-    Q2_0_PREC_F16_MFMA = 0,   /* W tiles as fp16 d*(q-1) (exact), x rounded to fp16, MFMA, f32 accumulate */
-    Q2_0_PREC_F32 = 1         /* W as f32 (q-1) and d, x in f32, f32 FMA with fp64 across blocks */
+    Q2_0_PREC_F16_MFMA = 0,   /* fast: W as fp16 d*(q-1) (exact), x rounded to fp16, MFMA, f32 accumulate */
+    Q2_0_PREC_F32 = 1         /* accuracy fallback: W as f32 (q-1) and d, x in f32, f32 FMA, no range condition */
 } q2_0_precision;
 
 /* Largest activation-column count of q2_0_mul_mat_vec. */
@@ -98,12 +100,20 @@ int q2_0_get_rows(const void *w, int64_t M, int64_t K, const int32_t *ids, int64
  *   x : N columns of K floats at x + n*ldx, ldx >= K, 4-byte aligned.
  *   y : N columns of M floats at y + n*ldy, ldy >= M, 4-byte aligned; y[n][m] is
  *       overwritten.  x and y must not overlap.
- * Accuracy: |y - y_exact| <= 1e-5 * sum_k |W[m][k] * x[n][k]|, and exactly 0 when
- * that sum is 0, for finite inputs with |x| < 2^100.  x is carried as an fp16
- * hi/lo pair after an exact power-of-two scaling per column: every element within
- * 2^18 of its column's largest |x| keeps 2^-22 relative accuracy and smaller ones
- * err by at most 2^-40 of that largest value, so the bound can fail only where
- * sum|W x| is carried by elements that far below a zero-weighted neighbour.
+ * Accuracy.  With A = sum_k |W[m][k] * x[n][k]|: y is exactly 0 where A is 0, and
+ *     |y - y_exact| <= 1e-5 * A
+ * for finite inputs with |x| < 2^100 and K <= 16384 whenever
+ *     max_k |x[n][k]| * sum_k |W[m][k]| <= 2^21 * A          (range condition).
+ * Why the condition: products are exact and sums f32, but x enters the matrix cores
+ * in a form whose absolute error is tied to the largest activation near it.  For
+ * N = 1 each 64-element block is scaled by a power of two and split into four 11-bit
+ * fixed-point limbs (elements within 2^20 of the block's largest |x| are exact, the
+ * others err by at most 2^-44 of it); otherwise each column is scaled by a power of
+ * two and carried as an fp16 hi/lo pair (2^-22 relative error for elements within
+ * 2^17 of the column's largest |x|, at most 2^-39 of that largest |x| below).  The
+ * bound can therefore fail only where A is carried by activations some 2^21 below a
+ * larger one that meets zero weights.  q2_0_mul_mat with Q2_0_PREC_F32 has no range
+ * condition.
  * N > 8 returns Q2_0_ERR_UNSUPPORTED (use q2_0_mul_mat).
  */
 int q2_0_mul_mat_vec(const void *w, int64_t M, int64_t K, const float *x, int64_t ldx, int64_t N,
@@ -137,14 +147,22 @@ int q2_0_mul_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items, int6
  * (bisque.today "WebGPU: add Q2_0 support": the tiled matrix multiply unpacks 16
  * codes per thread into shared memory as half precision.)
  *   Layouts and alignment as for q2_0_mul_mat_vec; precision is a q2_0_precision.
- *   N <= 8 is routed to the mat-vec for either precision (fp32-grade result).
- *   Otherwise Q2_0_PREC_F16_MFMA stages each weight tile in LDS as fp16 d*(q-1),
- *   which is exact for |d| <= 32752, rounds x to fp16 (nearest-even) after
- *   scaling each column by a power of two that puts its max |x| in [2^14, 2^15)
- *   (undone exactly on the results), and accumulates in f32 on the matrix cores:
- *   |y - y_exact| <= 2e-3 * sum|W x| for finite x with |x| < 2^100 and
- *   |d| <= 32752.  Q2_0_PREC_F32 is the fp32-grade fallback (same bound as the
- *   mat-vec).
+ *   Q2_0_PREC_F16_MFMA (fast):
+ *     N <= 8 runs the mat-vec: its fp32-grade bound under its range condition.
+ *     N > 8 forms the weights as fp16 d*(q-1), which is exact for |d| <= 32752,
+ *     rounds x to fp16 (nearest-even) after scaling each column by a power of two
+ *     that puts its max |x| in [2^14, 2^15) (undone exactly on the results), and
+ *     accumulates in f32 on the matrix cores.  An element then errs by at most
+ *     2^-11 of itself (within 2^28 of the column's largest |x|) or 2^-39 of that
+ *     largest |x| (below), so with A = sum_k |W[m][k] x[n][k]|:
+ *         |y - y_exact| <= 2e-3 * A
+ *     for finite x with |x| < 2^100, |d| <= 32752 and K <= 16384 whenever
+ *         max_k |x[n][k]| * sum_k |W[m][k]| <= 2^28 * A     (range condition).
+ *   Q2_0_PREC_F32 (the accuracy fallback), any N: W as f32 (q-1) with d apart, x in
+ *     f32, f32 fused multiply-adds of at most 64 terms per block sum (fp64 across
+ *     blocks for N > 8): |y - y_exact| <= 1e-5 * A for all finite inputs whose
+ *     products stay finite in f32, with no range condition (a weight of zero
+ *     contributes exactly nothing); y is exactly 0 where A is 0.
  *   workspace / ws_bytes: device scratch the caller provides, 16-byte aligned, at
  *   least q2_0_mul_mat_workspace_bytes(M, K, N, precision) bytes: for
  *   Q2_0_PREC_F16_MFMA with N > 8, x as fp16 (N*K*2) and N column exponents, plus,
@@ -159,6 +177,7 @@ int q2_0_mul_mat(const void *w, int64_t M, int64_t K, const float *x, int64_t ld
 
 /* Workspace bytes q2_0_mul_mat needs for these sizes (0 when none, and for invalid sizes). */
 size_t q2_0_mul_mat_workspace_bytes(int64_t M, int64_t K, int64_t N, int precision);
+
 
 /*
  * mul_mat_group: several q2_0_mul_mat products that share K and the activation x,
@@ -222,9 +241,10 @@ int q2_0_mul_mat_group_act(const q2_0_mat_vec_item *items, int64_t n_items, int6
  *             outside [0, n_expert) makes its y column quiet NaN and reads nothing.
  *   y       : f32 column (t, u) at y + (t*n_used + u)*ldy, ldy >= M.
  *   precision: as for q2_0_mul_mat: Q2_0_PREC_F16_MFMA (x rounded to fp16 as there,
- *             2e-3 bound) or Q2_0_PREC_F32 (fp32-grade, 1e-5 bound).  As there, few
- *             tokens (n_tokens <= 8) take the fp32-grade mat-vec, one per pair, for
- *             either precision.
+ *             2e-3 bound under its range condition; few tokens, n_tokens <= 8, take
+ *             the fp32-grade mat-vec, one per pair, with the mat-vec's bound and range
+ *             condition) or Q2_0_PREC_F32 (the fp32 GEMM, 1e-5 bound, no range
+ *             condition).
  *   workspace / ws_bytes: at least q2_0_mul_mat_id_workspace_bytes() bytes, 16-byte
  *             aligned: the routing tables (the pairs sorted by expert, stably) and,
  *             for Q2_0_PREC_F16_MFMA, x as fp16 in expert order.  Overwritten.

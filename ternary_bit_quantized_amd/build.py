@@ -2,7 +2,9 @@
 
 Usage: python -m ternary_bit_quantized_amd.build
 Every source in csrc/ is compiled for gfx950 only; object files go to _build/ at the
-repository root and the shared library next to this file.
+repository root and the shared library next to this file.  The measurement kernels in
+ceilings/ (HBM read stream, MFMA loop, empty launch) become libq2_0_ceilings.so, which
+only the benchmark loads.
 """
 
 from __future__ import annotations
@@ -19,6 +21,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libq2_0.so")
+CEIL_SRC = os.path.join(PKG, "ceilings", "ceilings.hip")
+CEIL_LIB = os.path.join(PKG, "libq2_0_ceilings.so")
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 COMPILE_TIMEOUT_S = 600
@@ -44,19 +48,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib):
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=COMPILE_TIMEOUT_S)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs) + 1)) as ex:
+        objs = list(ex.map(_compile, srcs + [CEIL_SRC]))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], CEIL_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", CEIL_LIB)
     return LIB
 
 

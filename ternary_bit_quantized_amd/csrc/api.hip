@@ -126,7 +126,8 @@ int q2_0_mul_mat_vec_group_act(const q2_0_mat_vec_item *items, int64_t n_items, 
 size_t q2_0_mul_mat_workspace_bytes(int64_t M, int64_t K, int64_t N, int precision) {
     if (check_shape(M, K, N) || N > kMaxGemmN) return 0;
     if (precision != Q2_0_PREC_F16_MFMA || N <= Q2_0_MAT_VEC_MAX_N) return 0;
-    return q2_0::gemm_f16_workspace_bytes(&M, 1, K, N);   // x as fp16 (+ split-K state)
+    const q2_0_mat_vec_item item{nullptr, M, nullptr, M};
+    return q2_0::gemm_f16_workspace_bytes(&item, 1, K, N);   // x as fp16 (+ split-K state)
 }
 
 int q2_0_mul_mat(const void *w, int64_t M, int64_t K, const float *x, int64_t ldx, int64_t N,
@@ -144,16 +145,9 @@ size_t q2_0_mul_mat_group_workspace_bytes(const q2_0_mat_vec_item *items, int64_
                                           int64_t N, int precision) {
     if (check_shape(0, K, N) || N > kMaxGemmN || n_items < 0 || (n_items > 0 && !items)) return 0;
     if (precision != Q2_0_PREC_F16_MFMA || N <= Q2_0_MAT_VEC_MAX_N || n_items == 0) return 0;
-    int64_t local[64];
-    int64_t *Ms = n_items <= 64 ? local : new int64_t[n_items];
-    bool ok = true;
-    for (int64_t i = 0; i < n_items; ++i) {
-        if (check_shape(items[i].M, K, N)) ok = false;
-        Ms[i] = items[i].M;
-    }
-    const size_t r = ok ? q2_0::gemm_f16_workspace_bytes(Ms, n_items, K, N) : 0;
-    if (Ms != local) delete[] Ms;
-    return r;
+    for (int64_t i = 0; i < n_items; ++i)
+        if (check_shape(items[i].M, K, N)) return 0;
+    return q2_0::gemm_f16_workspace_bytes(items, n_items, K, N);
 }
 
 int q2_0_mul_mat_group(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, const float *x,
@@ -222,8 +216,9 @@ int q2_0_mul_mat_id(const void *w, int64_t n_expert, int64_t M, int64_t K, const
     const uint8_t *wb = static_cast<const uint8_t *>(w);
     const int nb = (int)(K / Q2_0_BLOCK_WEIGHTS);
     const q2_0::Act xt = (q2_0::Act)x_type;
-    // few tokens (as q2_0_mul_mat with N <= 8): one fp32-grade mat-vec per pair
-    if (n_tokens <= Q2_0_MAT_VEC_MAX_N && n_pairs <= 65535 &&
+    // few tokens with the fast precision (as q2_0_mul_mat with N <= 8): one fp32-grade
+    // mat-vec per pair
+    if (precision == Q2_0_PREC_F16_MFMA && n_tokens <= Q2_0_MAT_VEC_MAX_N && n_pairs <= 65535 &&
         q2_0::mat_vec_mfma_eligible(wb, M, nb, x, xt, ldx)) {
         // (out-of-range ids: NaN columns, written by the same launch)
         return hip_status(q2_0::launch_mat_vec_mfma_pairs(wb, M, nb, x, xt, ldx, ids, (int)n_expert, (int)n_used,
@@ -289,29 +284,54 @@ const char *q2_0_version(void) { return "q2_0 0.1.0 gfx950"; }
 
 namespace {
 
-int mul_mat_impl(const void *w, int64_t M, int64_t K, const void *x, int x_type, int64_t ldx, int64_t N,
-                 float *y, int64_t ldy, int precision, void *workspace, size_t ws_bytes, void *stream) {
+}  // namespace
+
+namespace q2_0 {
+
+int record_hip_error(hipError_t e) { return hip_status(e); }
+
+// Every check of q2_0_mul_mat but the workspace one; *noop is set for the empty no-op.
+int check_mul_mat(const void *w, int64_t M, int64_t K, const void *x, int x_type, int64_t ldx, int64_t N,
+                  const float *y, int64_t ldy, int precision, bool *noop) {
+    *noop = false;
     int st = check_shape(M, K, N);
     if (st) return st;
     if (N > kMaxGemmN) return Q2_0_ERR_SHAPE;
     if (((M + 127) / 128) * ((N + 127) / 128) * 8 > kMaxRows) return Q2_0_ERR_SHAPE;   // launch grid
-    if (M == 0 || N == 0) return Q2_0_OK;
+    if (M == 0 || N == 0) {
+        *noop = true;
+        return Q2_0_OK;
+    }
     st = check_product(w, M, K, x, x_type, ldx, y, ldy);
     if (st) return st;
     if (precision != Q2_0_PREC_F16_MFMA && precision != Q2_0_PREC_F32) return Q2_0_ERR_UNSUPPORTED;
+    return Q2_0_OK;
+}
+
+}  // namespace q2_0
+
+namespace {
+
+int mul_mat_impl(const void *w, int64_t M, int64_t K, const void *x, int x_type, int64_t ldx, int64_t N,
+                 float *y, int64_t ldy, int precision, void *workspace, size_t ws_bytes, void *stream) {
+    bool noop;
+    const int st = q2_0::check_mul_mat(w, M, K, x, x_type, ldx, N, y, ldy, precision, &noop);
+    if (st || noop) return st;
     const size_t need = q2_0_mul_mat_workspace_bytes(M, K, N, precision);
     if (ws_bytes < need || (need && (!workspace || !aligned(workspace, 16)))) return Q2_0_ERR_WORKSPACE;
     const uint8_t *wb = static_cast<const uint8_t *>(w);
     const int nb = (int)(K / Q2_0_BLOCK_WEIGHTS);
     const q2_0::Act xt = (q2_0::Act)x_type;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (precision == Q2_0_PREC_F32) {
+        // the accuracy fallback: f32 arithmetic, no condition on the activations' range
+        if (N <= Q2_0_MAT_VEC_MAX_N) return hip_status(q2_0::launch_mat_vec_f32(wb, M, nb, x, xt, ldx, (int)N, y, ldy, s));
+        return hip_status(q2_0::launch_gemm_f32(wb, M, nb, x, xt, ldx, N, y, ldy, s));
+    }
     if (N <= Q2_0_MAT_VEC_MAX_N)
         return hip_status(q2_0::launch_mat_vec(wb, M, nb, x, xt, ldx, (int)N, y, ldy, s));
-    if (precision == Q2_0_PREC_F16_MFMA) {
-        const q2_0::GemmMat m{wb, M, y, ldy};
-        return hip_status(q2_0::launch_gemm_f16_group(&m, 1, nb, x, xt, ldx, N, workspace, s));
-    }
-    return hip_status(q2_0::launch_gemm_f32(wb, M, nb, x, xt, ldx, N, y, ldy, s));
+    const q2_0_mat_vec_item m{w, M, y, ldy};
+    return hip_status(q2_0::launch_gemm_f16_group(&m, 1, nb, x, xt, ldx, N, workspace, s));
 }
 
 int mul_mat_group_impl(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, const void *x, int x_type,
@@ -342,24 +362,22 @@ int mul_mat_group_impl(const q2_0_mat_vec_item *items, int64_t n_items, int64_t 
     const int nb = (int)(K / Q2_0_BLOCK_WEIGHTS);
     const q2_0::Act xt = (q2_0::Act)x_type;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (N <= Q2_0_MAT_VEC_MAX_N)
-        return hip_status(q2_0::launch_mat_vec_group(items, n_items, nb, x, xt, ldx, (int)N, s));
     if (precision == Q2_0_PREC_F32) {
         for (int64_t i = 0; i < n_items; ++i) {
             if (items[i].M == 0) continue;
-            st = hip_status(q2_0::launch_gemm_f32(static_cast<const uint8_t *>(items[i].w), items[i].M, nb, x, xt,
-                                                  ldx, N, items[i].y, items[i].ldy, s));
+            const uint8_t *wi = static_cast<const uint8_t *>(items[i].w);
+            st = hip_status(N <= Q2_0_MAT_VEC_MAX_N
+                                ? q2_0::launch_mat_vec_f32(wi, items[i].M, nb, x, xt, ldx, (int)N, items[i].y,
+                                                           items[i].ldy, s)
+                                : q2_0::launch_gemm_f32(wi, items[i].M, nb, x, xt, ldx, N, items[i].y, items[i].ldy,
+                                                        s));
             if (st) return st;
         }
         return Q2_0_OK;
     }
-    q2_0::GemmMat local[64];
-    q2_0::GemmMat *mats = n_items <= 64 ? local : new q2_0::GemmMat[n_items];
-    for (int64_t i = 0; i < n_items; ++i)
-        mats[i] = q2_0::GemmMat{static_cast<const uint8_t *>(items[i].w), items[i].M, items[i].y, items[i].ldy};
-    st = hip_status(q2_0::launch_gemm_f16_group(mats, n_items, nb, x, xt, ldx, N, workspace, s));
-    if (mats != local) delete[] mats;
-    return st;
+    if (N <= Q2_0_MAT_VEC_MAX_N)
+        return hip_status(q2_0::launch_mat_vec_group(items, n_items, nb, x, xt, ldx, (int)N, s));
+    return hip_status(q2_0::launch_gemm_f16_group(items, n_items, nb, x, xt, ldx, N, workspace, s));
 }
 
 }  // namespace

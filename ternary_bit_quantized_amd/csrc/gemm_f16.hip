@@ -607,12 +607,12 @@ static double rounds_us(int64_t wgs, int per_cu, const double *step_us, int step
     return ((double)full * step_us[per_cu] + step_us[w_last]) * steps;
 }
 
-static GemmPlan gemm_plan(const int64_t *Ms, int64_t n_items, int nb, int64_t N) {
+static GemmPlan gemm_plan(const q2_0_mat_vec_item *items, int64_t n_items, int nb, int64_t N) {
     int64_t rows = 0, tiles[2] = {0, 0};
     for (int64_t i = 0; i < n_items; ++i) {
-        tiles[0] += (Ms[i] + 127) / 128;
-        tiles[1] += (Ms[i] + 255) / 256;
-        rows += Ms[i];
+        tiles[0] += (items[i].M + 127) / 128;
+        tiles[1] += (items[i].M + 255) / 256;
+        rows += items[i].M;
     }
     const double nm_bytes = 4.0 * (double)N * (double)rows;   // one f32 copy of all outputs
     GemmPlan best{kCfgA, 1};
@@ -637,34 +637,34 @@ static GemmPlan gemm_plan(const int64_t *Ms, int64_t n_items, int nb, int64_t N)
 
 // Workspace of a call: fp16 x (N*K halves), the column exponents (N ints), and with
 // a K split each matrix's partials (splits * N * M floats).
-static size_t gemm_layout(const int64_t *Ms, int64_t n_items, int nb, int64_t N, GemmPlan *plan,
+static size_t gemm_layout(const q2_0_mat_vec_item *items, int64_t n_items, int nb, int64_t N, GemmPlan *plan,
                           size_t *parts_off) {
-    const GemmPlan pl = gemm_plan(Ms, n_items, nb, N);
+    const GemmPlan pl = gemm_plan(items, n_items, nb, N);
     const int64_t K = (int64_t)nb * kBlockWeights;
     size_t off = align256((size_t)N * K * 2) + align256((size_t)N * 4);
     *parts_off = off;
     if (pl.splits > 1)
-        for (int64_t i = 0; i < n_items; ++i) off += align256((size_t)pl.splits * N * Ms[i] * 4);
+        for (int64_t i = 0; i < n_items; ++i) off += align256((size_t)pl.splits * N * items[i].M * 4);
     *plan = pl;
     return off;
 }
 
-size_t gemm_f16_workspace_bytes(const int64_t *Ms, int64_t n_items, int64_t K, int64_t N) {
+size_t gemm_f16_workspace_bytes(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, int64_t N) {
     GemmPlan pl;
     size_t po;
-    return gemm_layout(Ms, n_items, (int)(K / kBlockWeights), N, &pl, &po);
+    return gemm_layout(items, n_items, (int)(K / kBlockWeights), N, &pl, &po);
 }
 
-hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, const void *x, Act xt,
+int gemm_f16_splits(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, int64_t N) {
+    return gemm_plan(items, n_items, (int)(K / kBlockWeights), N).splits;
+}
+
+hipError_t launch_gemm_f16_group(const q2_0_mat_vec_item *mats, int64_t n_items, int nb, const void *x, Act xt,
                                  int64_t ldx, int64_t N, void *workspace, hipStream_t s) {
     const int K = nb * kBlockWeights;
-    int64_t Ms_local[64];
-    int64_t *Ms = n_items <= 64 ? Ms_local : new int64_t[n_items];
-    for (int64_t i = 0; i < n_items; ++i) Ms[i] = mats[i].M;
     GemmPlan plan;
     size_t parts_off;
-    gemm_layout(Ms, n_items, nb, N, &plan, &parts_off);
-    if (Ms != Ms_local) delete[] Ms;
+    gemm_layout(mats, n_items, nb, N, &plan, &parts_off);
     const int splits = plan.splits, TM = cfg_rows(plan.cfg), TN = cfg_cols(plan.cfg);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     _Float16 *x16 = reinterpret_cast<_Float16 *>(ws);
@@ -695,7 +695,7 @@ hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, c
             const int64_t M = mats[i].M;
             if (M == 0) continue;
             GemmItem &it = grp.p[grp.n];
-            it.w = mats[i].w;
+            it.w = static_cast<const uint8_t *>(mats[i].w);
             it.y = mats[i].y;
             it.ldy = mats[i].ldy;
             it.part = part;

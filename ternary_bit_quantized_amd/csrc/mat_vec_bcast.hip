@@ -30,6 +30,8 @@
 // reads its quarter with five 16-byte reads.  A tile whose stages are split between
 // waves is finished after one barrier at the end, in stage order, so results are
 // deterministic.
+#include <atomic>
+
 #include "q2_0_internal.h"
 #include "mat_vec_common.h"
 
@@ -586,19 +588,20 @@ static hipError_t launch_bcast_nc(const MvGroup &grp, int nb, const XT *x, int64
                                   int waves) {
     const size_t lds = mat_vec_bcast_lds(NC, nb, waves, EXACT);
     auto kern = mat_vec_bcast<NC, XT, EXACT>;
-    // Raise the dynamic-LDS cap once per device (idempotent, so a race is harmless).
-    static bool configured[64] = {};
+    // Raise the dynamic-LDS cap once per device.  Setting it is idempotent, so threads
+    // that race past the flag set the same value; the flag itself is atomic.
+    static std::atomic<bool> configured[64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64 || !configured[dev]) {
+    if (dev < 0 || dev >= 64 || !configured[dev].load(std::memory_order_acquire)) {
         hipFuncAttributes fa;
         e = hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(kern));
         if (e != hipSuccess) return e;
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)(160 * 1024 - fa.sharedSizeBytes));
         if (e != hipSuccess) return e;
-        if (dev >= 0 && dev < 64) configured[dev] = true;
+        if (dev >= 0 && dev < 64) configured[dev].store(true, std::memory_order_release);
     }
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * waves), lds, s, grp, nb, x, ldx);
     return hipGetLastError();

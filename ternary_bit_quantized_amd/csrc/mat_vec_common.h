@@ -189,8 +189,8 @@ __device__ __forceinline__ int half_hi(int g, int odd) { return odd ? 2 * g + 1 
 // subnormal spacing (2^-24).  Each column n is therefore staged as x * 2^e_n, with
 // the power of two chosen so that the column's max |x| lands in [2^14, 2^15), and
 // its results are multiplied by 2^-e_n on the way out (v_ldexp_f32 both times, exact
-// barring f32 under/overflow).  Elements within 2^18 of the column maximum keep
-// 2^-22 relative accuracy; smaller ones err by at most 2^-40 of the maximum.
+// barring f32 under/overflow).  Elements within 2^17 of the column maximum keep
+// 2^-22 relative accuracy; smaller ones err by at most 2^-39 of the maximum.
 // An all-zero (or non-finite) maximum keeps e = 0.
 // TOP: the staged maximum lies in [2^(TOP-1), 2^TOP).
 template <int TOP = 15>

@@ -29,7 +29,7 @@
 //    slice partials are added in LDS in a fixed order (deterministic).
 //
 // Accuracy: each column is staged scaled by a power of two that takes its max |x|
-// to [2^14, 2^15); the hi/lo split then errs <= 2^-22 |x| (at most 2^-40 of the
+// to [2^14, 2^15); the hi/lo split then errs <= 2^-22 |x| (at most 2^-39 of the
 // column maximum for elements far below it), MFMA products are exact, and the f32
 // chain is the MFMA sum plus K/128/KS block partials per accumulator (two
 // accumulators alternate over blocks) -- inside the 1e-5 * sum|W x| bound.

@@ -28,6 +28,8 @@
 //  * One launch may cover several matrices that share K and the activation (for
 //    example the q, k, v projections, or gate and up): tiles are numbered across
 //    the group and a wave looks its matrix up once per tile.
+#include <atomic>
+
 #include "q2_0_internal.h"
 #include "mat_vec_common.h"
 
@@ -285,12 +287,13 @@ static hipError_t launch_stream_nc(const MvGroup &grp, int nb, const XT *x, int6
     constexpr int SB = kMvStreamSB;
     const size_t lds = mat_vec_stream_lds(NC, nb, waves);
     auto kern = mat_vec_stream<NC, SB, XT>;
-    // Raise the dynamic-LDS cap once per device (idempotent, so a race is harmless).
-    static bool configured[64] = {};
+    // Raise the dynamic-LDS cap once per device.  Setting it is idempotent, so threads
+    // that race past the flag set the same value; the flag itself is atomic.
+    static std::atomic<bool> configured[64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64 || !configured[dev]) {
+    if (dev < 0 || dev >= 64 || !configured[dev].load(std::memory_order_acquire)) {
         // the cap on dynamic LDS is what the kernel's static LDS leaves of 160 KiB
         hipFuncAttributes fa;
         e = hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(kern));
@@ -298,7 +301,7 @@ static hipError_t launch_stream_nc(const MvGroup &grp, int nb, const XT *x, int6
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)(160 * 1024 - fa.sharedSizeBytes));
         if (e != hipSuccess) return e;
-        if (dev >= 0 && dev < 64) configured[dev] = true;
+        if (dev >= 0 && dev < 64) configured[dev].store(true, std::memory_order_release);
     }
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * waves), lds, s, grp, nb, x, ldx);
     return hipGetLastError();

@@ -114,6 +114,14 @@ hipError_t launch_mat_vec(const uint8_t *w, int64_t M, int nb, const void *x, Ac
         }
         return launch_mat_vec_mfma(w, M, nb, x, xt, ldx, N, y, ldy, s);
     }
+    return launch_mat_vec_f32(w, M, nb, x, xt, ldx, N, y, ldy, s);
+}
+
+// The generic kernel: f32 arithmetic throughout, so a weight of zero contributes
+// exactly nothing and the bound holds whatever the activations' range (the fp32
+// precision of q2_0_mul_mat for N <= 8, and any input the fast kernels cannot take).
+hipError_t launch_mat_vec_f32(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx, int N,
+                              float *y, int64_t ldy, hipStream_t s) {
     const bool vec = ((uintptr_t)x % (4 * act_bytes(xt)) == 0) && (ldx % 4 == 0);
     return with_act(xt, [&](auto tag) -> hipError_t {
         using XT = decltype(tag);

@@ -102,24 +102,28 @@ __device__ __forceinline__ uint32_t load_word_u16x2(const uint16_t *blk16, int w
     return (uint32_t)blk16[1 + 2 * w] | ((uint32_t)blk16[2 + 2 * w] << 16);
 }
 
+// Argument checks of q2_0_mul_mat other than the workspace (api.hip); *noop is set
+// for the empty no-op.  record_hip_error stores e as the calling thread's last HIP error
+// and returns the status for it.
+int check_mul_mat(const void *w, int64_t M, int64_t K, const void *x, int x_type, int64_t ldx, int64_t N,
+                  const float *y, int64_t ldy, int precision, bool *noop);
+int record_hip_error(hipError_t e);
+
 // Launchers (return the HIP error of the launch).
 hipError_t launch_get_rows(const uint8_t *w, int64_t M, int nb, const int32_t *ids, int64_t n_ids,
                            float *out, int64_t ld_out, hipStream_t s);
 // x points at activations of element type xt; ldx counts elements.
 hipError_t launch_mat_vec(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx, int N,
                           float *y, int64_t ldy, hipStream_t s);
+// the generic f32 kernel only (no condition on the activations' range)
+hipError_t launch_mat_vec_f32(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx, int N,
+                              float *y, int64_t ldy, hipStream_t s);
 hipError_t launch_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items, int nb,
                                 const void *x, Act xt, int64_t ldx, int N, hipStream_t s);
 bool mat_vec_mfma_eligible(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx);
 hipError_t launch_mat_vec_mfma(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx,
                                int N, float *y, int64_t ldy, hipStream_t s);
-// fp16-MFMA GEMM over one or more matrices that share K and x.
-struct GemmMat {
-    const uint8_t *w;
-    int64_t M;
-    float *y;
-    int64_t ldy;
-};
+// fp16-MFMA GEMM over one or more matrices that share K and x (items: w, M, y, ldy).
 constexpr int kGemmMaxGroup = 16;   // matrices per GEMM launch (kernel argument size)
 struct GemmItem {
     const uint8_t *w;
@@ -153,8 +157,10 @@ struct GemmGroup {
     int moe_max_tiles;
     int moe_n_expert;
 };
-size_t gemm_f16_workspace_bytes(const int64_t *Ms, int64_t n_items, int64_t K, int64_t N);
-hipError_t launch_gemm_f16_group(const GemmMat *mats, int64_t n_items, int nb, const void *x, Act xt,
+size_t gemm_f16_workspace_bytes(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, int64_t N);
+// the K split the call's plan picks (1: none)
+int gemm_f16_splits(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, int64_t N);
+hipError_t launch_gemm_f16_group(const q2_0_mat_vec_item *items, int64_t n_items, int nb, const void *x, Act xt,
                                  int64_t ldx, int64_t N, void *workspace, hipStream_t s);
 hipError_t launch_gemm_f32(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx,
                            int64_t N, float *y, int64_t ldy, hipStream_t s);

@@ -225,3 +225,4 @@ def test_mul_mat_id_validation():
     assert call(wsp=0) == B.Q2_0_ERR_WORKSPACE
     assert call(wsp=P16 + 8) == B.Q2_0_ERR_WORKSPACE
     assert B.mul_mat_id_workspace_bytes(0, 10, 64, 2, 3, F16) == 0
+

@@ -376,14 +376,16 @@ def test_weights_at_two_byte_offset():
 
 
 def test_mul_mat_small_n_routes_to_mat_vec():
+    """The fast precision with N <= 8 is the mat-vec, bit for bit; the fp32 precision is
+    the f32 generic kernel (bitwise checks of that in test_gpu_accuracy.py)."""
     M, K = 300, 1024
     w = synth.weight(13, 0, 0, M, K, "quad", synth.ScaleDist("uniform", 0.01, 0.1))
     wd = dev(w)
     for N in (1, 5, 8):
         x = synth.activations(13, 0, N, N, K)
         a = run_mat_vec(wd, M, K, x)
-        for p in (B.Q2_0_PREC_F16_MFMA, B.Q2_0_PREC_F32):
-            assert np.array_equal(run_mul_mat(wd, M, K, x, p), a)
+        assert np.array_equal(run_mul_mat(wd, M, K, x, B.Q2_0_PREC_F16_MFMA), a)
+        assert_products(run_mul_mat(wd, M, K, x, B.Q2_0_PREC_F32), w, M, K, x, REL_F32, what="PREC_F32 N=%d" % N)
 
 
 @pytest.mark.parametrize("precision,rel", [(B.Q2_0_PREC_F16_MFMA, REL_F16), (B.Q2_0_PREC_F32, REL_F32)])
