@@ -52,7 +52,8 @@ typedef enum {
     Q2_0_ERR_ALIGN = 4,       /* w not 2-byte aligned, or x / y / out / ids not aligned to their element size */
     Q2_0_ERR_UNSUPPORTED = 5, /* N > 8 for the mat-vec, or an unknown precision or activation type */
     Q2_0_ERR_WORKSPACE = 6,   /* workspace smaller than q2_0_mul_mat_workspace_bytes(), or not 16-byte aligned */
-    Q2_0_ERR_HIP = 7          /* a HIP launch failed; see q2_0_last_hip_error() */
+    Q2_0_ERR_HIP = 7,         /* a HIP launch failed; see q2_0_last_hip_error() */
+    Q2_0_ERR_TOO_LARGE = 8    /* q2_0_mul_mat_noalloc: the call needs more than Q2_0_NOALLOC_SCRATCH_BYTES */
 } q2_0_status;
 
 typedef enum {
@@ -178,6 +179,21 @@ int q2_0_mul_mat(const void *w, int64_t M, int64_t K, const float *x, int64_t ld
 /* Workspace bytes q2_0_mul_mat needs for these sizes (0 when none, and for invalid sizes). */
 size_t q2_0_mul_mat_workspace_bytes(int64_t M, int64_t K, int64_t N, int precision);
 
+/*
+ * mul_mat_noalloc: q2_0_mul_mat for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation).  No
+ * workspace argument and no allocation of any kind: the fp16 GEMM's scratch is a
+ * static device array of Q2_0_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds on
+ * every GPU it runs on until the process ends.  Arguments, arithmetic, results and errors
+ * are those of q2_0_mul_mat, plus Q2_0_ERR_TOO_LARGE (checked last, nothing launched)
+ * when q2_0_mul_mat_workspace_bytes(M, K, N, precision) exceeds that size -- e.g. the
+ * 4096 x 12288 down projection at N = 512 needs 46 MB.  Every call on one GPU uses the
+ * same scratch: calls that overlap in time on one GPU (two streams, two threads) race
+ * and must be serialized by the caller.
+ */
+#define Q2_0_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int q2_0_mul_mat_noalloc(const void *w, int64_t M, int64_t K, const float *x, int64_t ldx, int64_t N,
+                         float *y, int64_t ldy, int precision, void *stream);
 
 /*
  * mul_mat_group: several q2_0_mul_mat products that share K and the activation x,

@@ -272,6 +272,8 @@ const char *q2_0_status_string(int status) {
         case Q2_0_ERR_UNSUPPORTED: return "Q2_0_ERR_UNSUPPORTED: N > 8 for mat-vec, or unknown precision or activation type";
         case Q2_0_ERR_WORKSPACE: return "Q2_0_ERR_WORKSPACE: workspace missing, too small or not 16-byte aligned";
         case Q2_0_ERR_HIP: return "Q2_0_ERR_HIP: a HIP launch failed";
+        case Q2_0_ERR_TOO_LARGE:
+            return "Q2_0_ERR_TOO_LARGE: the call needs more scratch than Q2_0_NOALLOC_SCRATCH_BYTES";
         default: return "unknown q2_0 status";
     }
 }

@@ -22,6 +22,7 @@ Q2_0_ERR_ALIGN = 4
 Q2_0_ERR_UNSUPPORTED = 5
 Q2_0_ERR_WORKSPACE = 6
 Q2_0_ERR_HIP = 7
+Q2_0_ERR_TOO_LARGE = 8
 Q2_0_PREC_F16_MFMA = 0
 Q2_0_PREC_F32 = 1
 Q2_0_ACT_F32 = 0
@@ -30,12 +31,13 @@ Q2_0_ACT_BF16 = 2
 BLOCK_WEIGHTS = 64
 BLOCK_BYTES = 18
 MAT_VEC_MAX_N = 8
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = ("q2_0_get_rows", "q2_0_mul_mat_vec", "q2_0_mul_mat_vec_group", "q2_0_mul_mat",
            "q2_0_mul_mat_workspace_bytes", "q2_0_mul_mat_group", "q2_0_mul_mat_group_workspace_bytes",
            "q2_0_mul_mat_vec_act", "q2_0_mul_mat_vec_group_act", "q2_0_mul_mat_act", "q2_0_mul_mat_group_act",
            "q2_0_quantize", "q2_0_repack_g128", "q2_0_mul_mat_id", "q2_0_mul_mat_id_workspace_bytes",
-           "q2_0_status_string", "q2_0_last_hip_error", "q2_0_version")
+           "q2_0_mul_mat_noalloc", "q2_0_status_string", "q2_0_last_hip_error", "q2_0_version")
 
 
 class MatVecItem(ctypes.Structure):
@@ -96,6 +98,8 @@ def lib() -> ctypes.CDLL:
         L.q2_0_mul_mat_id_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, C]
         L.q2_0_mul_mat_id_workspace_bytes.restype = ctypes.c_size_t
         L.q2_0_repack_g128.argtypes = [P, I64, I64, P, P]
+        L.q2_0_mul_mat_noalloc.argtypes = [P, I64, I64, P, I64, I64, P, I64, ctypes.c_int, P]
+        L.q2_0_mul_mat_noalloc.restype = ctypes.c_int
         for f in (L.q2_0_mul_mat_vec_act, L.q2_0_mul_mat_vec_group_act, L.q2_0_mul_mat_act,
                   L.q2_0_mul_mat_group_act, L.q2_0_quantize, L.q2_0_repack_g128, L.q2_0_mul_mat_id):
             f.restype = ctypes.c_int
@@ -135,6 +139,11 @@ def mul_mat_vec_group_raw(items, n_items: int, K: int, x: int, ldx: int, N: int,
 def mul_mat_raw(w: int, M: int, K: int, x: int, ldx: int, N: int, y: int, ldy: int, precision: int,
                 workspace: int, ws_bytes: int, stream: int = 0) -> int:
     return lib().q2_0_mul_mat(w, M, K, x, ldx, N, y, ldy, precision, workspace, ws_bytes, stream)
+
+
+def mul_mat_noalloc_raw(w: int, M: int, K: int, x: int, ldx: int, N: int, y: int, ldy: int, precision: int,
+                        stream: int = 0) -> int:
+    return lib().q2_0_mul_mat_noalloc(w, M, K, x, ldx, N, y, ldy, precision, stream)
 
 
 def mul_mat_workspace_bytes(M: int, K: int, N: int, precision: int) -> int:

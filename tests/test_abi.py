@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert "gfx950" in B.version()
-    for s in range(8):
+    for s in range(9):
         assert B.lib().q2_0_status_string(s).decode().startswith("Q2_0_")
     assert B.lib().q2_0_status_string(99) == b"unknown q2_0 status"
     assert B.lib().q2_0_last_hip_error() == 0
@@ -226,3 +226,19 @@ def test_mul_mat_id_validation():
     assert call(wsp=P16 + 8) == B.Q2_0_ERR_WORKSPACE
     assert B.mul_mat_id_workspace_bytes(0, 10, 64, 2, 3, F16) == 0
 
+
+def test_mul_mat_noalloc_validation():
+    """The allocation-free variant checks its arguments as q2_0_mul_mat does, then rejects
+    calls whose scratch would exceed its static array -- all before any HIP call."""
+    nr = B.mul_mat_noalloc_raw
+    assert nr(P16, 10, 100, P16, 100, 16, P16, 10, 0) == B.Q2_0_ERR_SHAPE
+    assert nr(0, 0, 64, 0, 64, 16, 0, 0, 0) == B.Q2_0_OK          # empty no-op
+    assert nr(P16, 10, 64, 0, 64, 16, P16, 10, 0) == B.Q2_0_ERR_NULL
+    assert nr(P16, 10, 64, P16, 63, 16, P16, 10, 0) == B.Q2_0_ERR_LAYOUT
+    assert nr(P16 + 1, 10, 64, P16, 64, 16, P16, 10, 0) == B.Q2_0_ERR_ALIGN
+    assert nr(P16, 10, 64, P16, 64, 16, P16, 10, 7) == B.Q2_0_ERR_UNSUPPORTED
+    # 4096 x 12288 at N = 512 fits (46 MB, with its K split); at N = 4096 x alone is 100 MB
+    assert 0 < B.mul_mat_workspace_bytes(4096, 12288, 512, 0) <= B.NOALLOC_SCRATCH_BYTES
+    assert B.mul_mat_workspace_bytes(4096, 12288, 4096, 0) > B.NOALLOC_SCRATCH_BYTES
+    assert nr(P16, 4096, 12288, P16, 12288, 4096, P16, 4096, 0) == B.Q2_0_ERR_TOO_LARGE
+    assert B.lib().q2_0_status_string(B.Q2_0_ERR_TOO_LARGE).decode().startswith("Q2_0_ERR_TOO_LARGE")
