@@ -132,8 +132,8 @@ typedef struct {
  * mul_mat_vec_group: several mat-vecs that share K and the activation x, in as
  * few launches as possible: y_i = W_i x for i < n_items (for example the q, k and
  * v projections of one layer, or gate and up).  Same arithmetic, accuracy and
- * layouts as q2_0_mul_mat_vec; each y_i meets the same bound and does not
- * depend on the other items or on how they are grouped.
+ * layouts as q2_0_mul_mat_vec; each y_i meets the same bound, and is deterministic
+ * run to run (its last bits may depend on how items are grouped).
  *   items  : HOST array of n_items descriptors; read during the call only.
  *   x, ldx, N, stream: as for q2_0_mul_mat_vec (1 <= N <= 8).
  * The y_i must not overlap each other or x.  Errors are those of
@@ -142,6 +142,34 @@ typedef struct {
  */
 int q2_0_mul_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K,
                            const float *x, int64_t ldx, int64_t N, void *stream);
+
+/* One product of a batched mat-vec (see q2_0_mul_mat_vec_batch). */
+typedef struct {
+    const void *w;   /* M x K Q2_0 matrix (device), 2-byte aligned */
+    int64_t M;       /* rows; 0 is allowed and writes nothing */
+    int64_t K;       /* a positive multiple of 64 */
+    const void *x;   /* device activations of the call's x_type: N columns of K at x + n*ldx */
+    int64_t ldx;     /* >= K, in elements */
+    float *y;        /* device: N columns of M floats at y + n*ldy, 4-byte aligned */
+    int64_t ldy;     /* >= M */
+} q2_0_mat_vec_batch_item;
+
+/*
+ * mul_mat_vec_batch: y_i = W_i x_i for i < n_items, each item with its own K and
+ * activation, in as few launches as possible -- for example every matrix a decode step
+ * streams, whatever activation each reads.  Same arithmetic, accuracy and layouts as
+ * q2_0_mul_mat_vec for every item.  Consecutive items with the same x, ldx and K share
+ * one staging of x; one launch takes up to 64 items in up to 8 such runs (N <= 2; one run
+ * for N > 2).  Results are deterministic run to run; their last bits may depend on how
+ * items are grouped (the split of the work changes the order of f32 additions).
+ *   items  : HOST array of n_items descriptors; read during the call only.
+ *   x_type : a q2_0_act_type, for every item; 1 <= N <= 8 columns for every item.
+ * The y_i must not overlap each other or any x_j.  Errors are those of
+ * q2_0_mul_mat_vec_act, checked for every item before anything is launched (NULL also
+ * for items == NULL with n_items > 0; n_items < 0 is SHAPE).
+ */
+int q2_0_mul_mat_vec_batch(const q2_0_mat_vec_batch_item *items, int64_t n_items, int x_type, int64_t N,
+                           void *stream);
 
 /*
  * mul_mat: y = W x for any N (batched prefill GEMM).

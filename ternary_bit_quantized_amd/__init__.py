@@ -9,6 +9,6 @@ loudly if it has not been built.
 
 from .q2_0 import (  # noqa: F401
     Q2_0_ACT_BF16, Q2_0_ACT_F16, Q2_0_ACT_F32, Q2_0_PREC_F16_MFMA, Q2_0_PREC_F32, Q2_0Error, q2_0_get_rows,
-    q2_0_mul_mat, q2_0_mul_mat_group, q2_0_mul_mat_id, q2_0_mul_mat_vec, q2_0_mul_mat_vec_group,
+    q2_0_mul_mat, q2_0_mul_mat_group, q2_0_mul_mat_id, q2_0_mul_mat_vec, q2_0_mul_mat_vec_batch, q2_0_mul_mat_vec_group,
     q2_0_quantize, q2_0_repack_g128,
 )

@@ -80,6 +80,28 @@ int mul_mat_vec_group_impl(const q2_0_mat_vec_item *items, int64_t n_items, int6
                                                  static_cast<hipStream_t>(stream)));
 }
 
+int mul_mat_vec_batch_impl(const q2_0_mat_vec_batch_item *items, int64_t n_items, int x_type, int64_t N,
+                           void *stream) {
+    if (n_items < 0 || N < 0) return Q2_0_ERR_SHAPE;
+    if (n_items > 0 && !items) return Q2_0_ERR_NULL;
+    for (int64_t i = 0; i < n_items; ++i) {
+        const int st = check_shape(items[i].M, items[i].K, N);
+        if (st) return st;
+    }
+    bool any = false;
+    for (int64_t i = 0; i < n_items && N > 0; ++i) {
+        if (items[i].M == 0) continue;
+        any = true;
+        const int st = check_product(items[i].w, items[i].M, items[i].K, items[i].x, x_type, items[i].ldx,
+                                     items[i].y, items[i].ldy);
+        if (st) return st;
+    }
+    if (!any) return Q2_0_OK;
+    if (N > Q2_0_MAT_VEC_MAX_N) return Q2_0_ERR_UNSUPPORTED;
+    return hip_status(q2_0::launch_mat_vec_batch(items, n_items, (q2_0::Act)x_type, (int)N,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 int mul_mat_impl(const void *w, int64_t M, int64_t K, const void *x, int x_type, int64_t ldx, int64_t N,
                  float *y, int64_t ldy, int precision, void *workspace, size_t ws_bytes, void *stream);
 int mul_mat_group_impl(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, const void *x, int x_type,
@@ -121,6 +143,11 @@ int q2_0_mul_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items, int6
 int q2_0_mul_mat_vec_group_act(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, const void *x,
                                int x_type, int64_t ldx, int64_t N, void *stream) {
     return mul_mat_vec_group_impl(items, n_items, K, x, x_type, ldx, N, stream);
+}
+
+int q2_0_mul_mat_vec_batch(const q2_0_mat_vec_batch_item *items, int64_t n_items, int x_type, int64_t N,
+                           void *stream) {
+    return mul_mat_vec_batch_impl(items, n_items, x_type, N, stream);
 }
 
 size_t q2_0_mul_mat_workspace_bytes(int64_t M, int64_t K, int64_t N, int precision) {

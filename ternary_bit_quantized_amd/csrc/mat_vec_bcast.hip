@@ -30,6 +30,7 @@
 // reads its quarter with five 16-byte reads.  A tile whose stages are split between
 // waves is finished after one barrier at the end, in stage order, so results are
 // deterministic.
+#include <algorithm>
 #include <atomic>
 
 #include "q2_0_internal.h"
@@ -286,21 +287,37 @@ __device__ __forceinline__ void stage_x_limbs(const XT *__restrict__ x, int nb, 
 
 }  // namespace
 
+// The launch: a group of matrices (their 16-row tiles numbered across the group) in
+// segments that each share one activation (MvSegs in mat_vec_common.h).  Each workgroup
+// belongs to one segment and takes a contiguous range of its tiles.  The activation is
+// staged in LDS one window of ws stages (16 ws blocks) at a time: phase p multiplies
+// stages [p ws, (p + 1) ws) of every tile of the workgroup, and a tile's sum over the
+// phases is kept in LDS (lds_tacc) between them, added in phase order.  Within a phase
+// the (tile, stage) items are split evenly over the waves in tile-major order; a tile
+// whose stages fall to two waves is finished after the phase's barrier by the wave that
+// holds its last stage, adding the earlier waves' partials in wave order.  Every order of
+// addition is fixed by the launch's geometry, so a call's results do not change from run
+// to run.
+struct BcIt {
+    int tile, st;   // a (tile, stage) item
+};
+
 template <int NC, typename XT, bool EXACT>
 __global__ __launch_bounds__(kMvStreamMaxWaves * 64)
-__attribute__((amdgpu_waves_per_eu(4))) void mat_vec_bcast(MvGroup grp, int nb, const XT *__restrict__ x,
-                                                     int64_t ldx) {
+__attribute__((amdgpu_waves_per_eu(4))) void mat_vec_bcast(MvGroup grp, MvSegs segs) {
     static_assert(NC == 1 || NC == 2, "one or two activation columns");
     static_assert(!EXACT || NC == 1, "exact mode: one column");
     constexpr int NR = EXACT ? 4 : 2 * NC;   // A rows: 4 limbs, or hi and lo per column
     const int WAVES = __builtin_amdgcn_readfirstlane((int)(blockDim.x >> 6));   // 4..16, chosen by the host
 
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int xcap = segs.xcap;
     uint8_t *lds_w = smem;                                                          // WAVES x kBcWaveLds
     float2_t *lds_part = reinterpret_cast<float2_t *>(smem + WAVES * kBcWaveLds);   // WAVES x 64
-    half4_t *lds_x = reinterpret_cast<half4_t *>(lds_part + WAVES * 64);            // nb x 16 x NR
-    float4_t *lds_bs = reinterpret_cast<float4_t *>(lds_x + nb * 16 * NR);          // exact mode: nb
-    float *lds_bsc = reinterpret_cast<float *>(lds_bs + nb);                        // exact mode: nb
+    half4_t *lds_x = reinterpret_cast<half4_t *>(lds_part + WAVES * 64);            // xcap x 16 x NR
+    float4_t *lds_bs = reinterpret_cast<float4_t *>(lds_x + xcap * 16 * NR);        // exact mode: xcap
+    float *lds_bsc = reinterpret_cast<float *>(lds_bs + (EXACT ? xcap : 0));        // exact mode: xcap
+    float *lds_tacc = lds_bsc + (EXACT ? xcap : 0);                                 // tacc x 16 x NC
     __shared__ int lds_e[NC];
     __shared__ float lds_tmp[kMvStreamMaxWaves * NC];
     __shared__ int lds_part_tile[kMvStreamMaxWaves];   // lds_part: a wave's unfinished last tile
@@ -310,38 +327,46 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_bcast(MvGroup grp, int nb, 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, G = lane >> 4;   // this lane's row of the tile and quarter of the stage
-    const int total = grp.total_tiles;
     const int t0v = load_tile_table(grp);   // the tile table, one entry per lane
+
+    // ---- this workgroup's segment, activation, tiles [tb0, tb0 + nt) and phases
+    int sg = 0;
+    for (int i = 1; i < kMvMaxSegs; ++i)
+        if (i < segs.n && (int)blockIdx.x >= segs.s[i].wg0) sg = i;
+    const MvSeg &seg = segs.s[sg];
+    const XT *__restrict__ x = static_cast<const XT *>(seg.x);
+    const int64_t ldx = seg.ldx;
+    const int nb = seg.nb, W = seg.ws;
     const int ns = (nb + kBcSB - 1) / kBcSB;
+    const int P = (ns + W - 1) / W;
     const uint32_t rowbytes = (uint32_t)nb * kBlockBytes;
     const bool ragged = (nb % kBcSB) != 0;   // nb % 8 == 0: the last stage of a row then holds 8 blocks
-
-    // This workgroup's tiles [tb0, tb1) and this wave's items [i0, i1) among them.
-    // (products and quotients without 64-bit integer divisions, which would cost
-    // hundreds of instructions before the first load)
-    const int tb0 = (int)mul_div(total, blockIdx.x, gridDim.x);
-    const int tb1 = (int)mul_div(total, blockIdx.x + 1, gridDim.x);
-    const int64_t n_wg = (int64_t)(tb1 - tb0) * ns;
-    const int64_t i0 = mul_div(n_wg, wave, WAVES), i1 = mul_div(n_wg, wave + 1, WAVES);
-    const int n_items = (int)(i1 - i0);
-    const int64_t i0_tile = div_floor(i0, ns);
-    const BcItem first{tb0 + (int)i0_tile, (int)(i0 - i0_tile * ns)};
+    // (products and quotients without 64-bit integer divisions, which would cost hundreds
+    // of instructions before the first load)
+    const int ntile = seg.tile1 - seg.tile0;
+    const int bw = (int)blockIdx.x - seg.wg0;
+    const int tb0 = seg.tile0 + (int)mul_div(ntile, bw, seg.wgs);
+    const int nt = seg.tile0 + (int)mul_div(ntile, bw + 1, seg.wgs) - tb0;
 
     // Chunk q*64 + lane of a stage (chunks past the 288 repeat the last one): row
     // c / 18, bytes 16(c % 18) .. +15 of the row's 288.  Byte b of a row belongs to
     // quarter b / 72 and is parked at row * kBcRS + 80 (b / 72) + b % 72; a chunk's
     // two 8-byte halves are parked separately (at most one chunk per quarter boundary
-    // splits, and 72 is a multiple of 8).
-    int cr[kBcCH], cc[kBcCH];
+    // splits, and 72 is a multiple of 8).  (The chunk's row and column are recomputed
+    // where needed rather than kept in registers.)
+    auto chunk_rc = [&](int q, int &crow, int &ccol) {
+        const int c = min(q * 64 + lane, kBcNCH - 1);
+        crow = c / kBcCPR;
+        ccol = c - crow * kBcCPR;
+    };
     uint32_t pk0[kBcCH], pk1[kBcCH];   // LDS byte offsets of the chunk's two halves
 #pragma unroll
     for (int q = 0; q < kBcCH; ++q) {
-        const int c = min(q * 64 + lane, kBcNCH - 1);
-        cr[q] = c / kBcCPR;
-        cc[q] = c % kBcCPR;
-        const int b0 = 16 * cc[q], b1 = b0 + 8;
-        pk0[q] = (uint32_t)(wave * kBcWaveLds + cr[q] * kBcRS + b0 + 8 * (b0 / 72));
-        pk1[q] = (uint32_t)(wave * kBcWaveLds + cr[q] * kBcRS + b1 + 8 * (b1 / 72));
+        int crow, ccol;
+        chunk_rc(q, crow, ccol);
+        const int b0 = 16 * ccol, b1 = b0 + 8;
+        pk0[q] = (uint32_t)(wave * kBcWaveLds + crow * kBcRS + b0 + 8 * (b0 / 72));
+        pk1[q] = (uint32_t)(wave * kBcWaveLds + crow * kBcRS + b1 + 8 * (b1 / 72));
     }
 
     // Byte offsets of this lane's chunks from the first row of the tile being loaded;
@@ -351,29 +376,34 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_bcast(MvGroup grp, int nb, 
     const uint8_t *ld_base = nullptr;   // first byte of the tile being loaded (uniform)
     int ld_tile = -1, ld_rows = -1;
     TileCursor ld_cur;
-    cursor_init(grp, t0v, ld_cur, first.tile);
+    cursor_init(grp, t0v, ld_cur, tb0);
 #define Q2_0_SET_LOAD_TILE(TILE)                                                                   \
     {                                                                                              \
-        const TileRef tr_ = cursor_tile<kBcRows>(grp, t0v, ld_cur, (TILE));                             \
+        const TileRef tr_ = cursor_tile<kBcRows>(grp, t0v, ld_cur, (TILE));                        \
         ld_base = tr_.w + (int64_t)tr_.m0 * rowbytes;                                              \
         const int rows_ = min(tr_.M - tr_.m0, kBcRows);                                            \
         if (rows_ != ld_rows) {   /* only a matrix's last tile clamps */                           \
-            _Pragma("unroll") for (int q = 0; q < kBcCH; ++q)                                     \
-                off[q] = (uint32_t)min(cr[q], rows_ - 1) * rowbytes + 16u * (uint32_t)cc[q];       \
+            _Pragma("unroll") for (int q = 0; q < kBcCH; ++q) {                                   \
+                int crow_, ccol_;                                                                  \
+                chunk_rc(q, crow_, ccol_);                                                         \
+                off[q] = (uint32_t)min(crow_, rows_ - 1) * rowbytes + 16u * (uint32_t)ccol_;       \
+            }                                                                                      \
             ld_rows = rows_;                                                                       \
         }                                                                                          \
         ld_tile = (TILE);                                                                          \
     }
-    // Every call issues exactly kBcCH loads (items past the wave's range reload the
-    // current one), so the wait counts before each park stay exact.  In the half stage
-    // at the end of a ragged row, chunks past its 144 bytes load its last chunk again.
+    // Every call issues exactly kBcCH loads (items past the wave's range of the phase
+    // reload the last one), so the wait counts before each park stay exact.  In the half
+    // stage at the end of a ragged row, chunks past its 144 bytes load its last chunk again.
 #define Q2_0_ISSUE(IT, REG)                                                                    \
     {                                                                                          \
         if ((IT).tile != ld_tile) Q2_0_SET_LOAD_TILE((IT).tile)                               \
         const uint8_t *sbase = ld_base + (uint32_t)(IT).st * (uint32_t)(kBcSB * kBlockBytes);  \
         if (ragged && (IT).st == ns - 1) {                                                     \
             _Pragma("unroll") for (int q = 0; q < kBcCH; ++q) {                                \
-                const uint32_t o = off[q] - 16u * (uint32_t)max(cc[q] - (kBcCPR / 2 - 1), 0);  \
+                int crow_, ccol_;                                                              \
+                chunk_rc(q, crow_, ccol_);                                                     \
+                const uint32_t o = off[q] - 16u * (uint32_t)max(ccol_ - (kBcCPR / 2 - 1), 0);  \
                 REG[q] = *reinterpret_cast<const u32x4_t *>(sbase + o);                        \
             }                                                                                  \
         } else {                                                                               \
@@ -389,20 +419,69 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_bcast(MvGroup grp, int nb, 
         }                                                                                       \
     }
 
-    auto next_item = [&](BcItem it) {
-        BcItem n{it.tile, it.st + 1};
-        if (n.st == ns) { n.st = 0; n.tile += 1; }
-        return n;
+    // results leave as acc * 2^-e of their column (exact mode scales per block instead);
+    // hi/lo mode scales each column once, over all of K, so every phase uses one exponent
+    if (!EXACT) column_exponents<NC>(x, ldx, nb * kBlockWeights, lds_e, lds_tmp, tid, WAVES * 64);
+    const int ye0 = EXACT ? 0 : -lds_e[0], ye1 = EXACT ? 0 : -lds_e[NC - 1];
+    const uint8_t *lq = lds_w + wave * kBcWaveLds + r * kBcRS + G * kBcQuarter;   // this lane's quarter
+    // A operand of code dword u of block blk: entry (blk*16 + 4u + a)*NR + row, a and
+    // row from the lane's place in its 16-lane group
+    const half4_t *xl = lds_x + (4 * G * 16 + ((lane >> 2) & 3)) * NR + ((NR == 2) ? (lane & 1) : (lane & 3));
+    const PairMasks pm;
+    float acc_e[2] = {0.f, 0.f}, acc_o[2] = {0.f, 0.f};
+
+    // A finished tile of phase p: the row's four quarter sums are added (in a fixed order,
+    // so every lane of the row holds the same value); quarter 0's lanes add the earlier
+    // phases' sum and keep the total for the next phase, or, in the last phase, store it.
+    auto finish_tile = [&](int p, int tile, float *y, int64_t ldy, int M, int m0, float r0, float r1) {
+        r0 += __shfl_xor(r0, 16);
+        r0 += __shfl_xor(r0, 32);
+        if (NC > 1) {
+            r1 += __shfl_xor(r1, 16);
+            r1 += __shfl_xor(r1, 32);
+        }
+        if (G == 0) {
+            float *ta = lds_tacc + ((tile - tb0) * kBcRows + r) * NC;
+            if (p > 0) {
+                r0 = ta[0] + r0;
+                if (NC > 1) r1 = ta[1] + r1;
+            }
+            if (p + 1 < P) {
+                ta[0] = r0;
+                if (NC > 1) ta[1] = r1;
+            } else if (m0 + r < M) {
+                y[m0 + r] = __builtin_amdgcn_ldexpf(r0, ye0);
+                if (NC > 1) y[ldy + m0 + r] = __builtin_amdgcn_ldexpf(r1, ye1);
+            }
+        }
     };
 
     // Stages in flight per wave: two in exact mode (its registers allow a second set),
-    // one otherwise.  Q2_0_ISSUE_NEXT loads the wave's next item, or once all are issued
-    // the last one again, so that every call issues exactly kBcCH loads and the wait
-    // counts before each park stay exact.  The first stages are issued before x is
-    // staged, so their latency overlaps the staging.
+    // one otherwise.  Q2_0_ISSUE_NEXT loads the wave's next item of the phase, or once all
+    // are issued the last one again.
     constexpr int DEPTH = EXACT ? 2 : 1;
-    BcItem ld = first, last = first;
-    int n_left = n_items;   // items not issued yet
+    u32x4_t ra[kBcCH], rb[kBcCH];
+    for (int p = 0; p < P; ++p) {   // the same trip count in every wave: the barriers need it
+        const int sw0 = p * W;                               // first stage of the window
+        const int sp = min(W, ns - sw0);
+        const int blk0 = sw0 * kBcSB;
+        // this wave's items of the phase: (tile, stage) pairs i0 .. i1-1 of the workgroup's
+        // nt * sp, tile-major
+        const int64_t n_wg = (int64_t)nt * sp;
+        const int64_t i0 = mul_div(n_wg, wave, WAVES);
+        const int n = (int)(mul_div(n_wg, wave + 1, WAVES) - i0);
+        const int64_t i0t = div_floor(i0, sp);
+        const BcIt first{tb0 + (int)i0t, sw0 + (int)(i0 - i0t * sp)};
+        const bool pend_start = n > 0 && first.st != sw0;   // its first tile began in an earlier wave
+        auto next_item = [&](BcIt it) {
+            if (++it.st == sw0 + sp) {
+                it.st = sw0;
+                ++it.tile;
+            }
+            return it;
+        };
+        BcIt ld = first, last = first;
+        int n_left = n;   // items of the phase not issued yet
 #define Q2_0_ISSUE_NEXT(REG)                                                                   \
     {                                                                                          \
         if (n_left > 0) {                                                                      \
@@ -412,55 +491,30 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_bcast(MvGroup grp, int nb, 
         }                                                                                      \
         Q2_0_ISSUE(last, REG)                                                                  \
     }
-    u32x4_t ra[kBcCH], rb[kBcCH];
-    if (n_items > 0) {
-        Q2_0_ISSUE_NEXT(ra)
-        if (DEPTH == 2) Q2_0_ISSUE_NEXT(rb)
-    }
-
-    if (EXACT) {
-        stage_x_limbs(x, nb, lds_x, lds_bs, lds_bsc, tid, WAVES * 64);
-    } else {
-        column_exponents<NC>(x, ldx, nb * kBlockWeights, lds_e, lds_tmp, tid, WAVES * 64);
-        stage_x_bcast<NC>(x, ldx, nb, lds_e, lds_x, tid, WAVES * 64);
-    }
-    __syncthreads();
-
-    // results leave as acc * 2^-e of their column (exact mode scales per block instead)
-    const int ye0 = EXACT ? 0 : -lds_e[0], ye1 = EXACT ? 0 : -lds_e[NC - 1];
-    const uint8_t *lq = lds_w + wave * kBcWaveLds + r * kBcRS + G * kBcQuarter;   // this lane's quarter
-    // A operand of code dword u of block blk: entry (blk*16 + 4u + a)*NR + row, a and
-    // row from the lane's place in its 16-lane group
-    const half4_t *xl = lds_x + (4 * G * 16 + ((lane >> 2) & 3)) * NR + ((NR == 2) ? (lane & 1) : (lane & 3));
-    const PairMasks pm;
-    float acc_e[2] = {0.f, 0.f}, acc_o[2] = {0.f, 0.f};
-    float2_t pend = {0.f, 0.f};   // the first tile, when it started in an earlier wave
-    bool has_pend = false;
-
-    // The row's four quarter sums are added (in a fixed order, so every lane of the row
-    // holds the same value) and stored by the lanes of quarter 0.
-    auto store_tile = [&](const TileRef &tr, float r0, float r1) {
-        r0 += __shfl_xor(r0, 16);
-        r0 += __shfl_xor(r0, 32);
-        if (NC > 1) {
-            r1 += __shfl_xor(r1, 16);
-            r1 += __shfl_xor(r1, 32);
+        // the first stages are issued before the window is staged, so that their latency
+        // overlaps the staging
+        if (n > 0) {
+            Q2_0_ISSUE_NEXT(ra)
+            if (DEPTH == 2) Q2_0_ISSUE_NEXT(rb)
         }
-        const int row = tr.m0 + r;
-        if (G == 0 && row < tr.M) {
-            tr.y[row] = __builtin_amdgcn_ldexpf(r0, ye0);
-            if (NC > 1) tr.y[tr.ldy + row] = __builtin_amdgcn_ldexpf(r1, ye1);
-        }
-    };
+        if (EXACT)
+            stage_x_limbs(x + (int64_t)blk0 * kBlockWeights, min(sp * kBcSB, nb - blk0), lds_x, lds_bs, lds_bsc,
+                          tid, WAVES * 64);
+        else
+            stage_x_bcast<NC>(x + (int64_t)blk0 * kBlockWeights, ldx, min(sp * kBcSB, nb - blk0), lds_e, lds_x, tid,
+                              WAVES * 64);
+        __syncthreads();
 
-    TileCursor out_cur;
-    cursor_init(grp, t0v, out_cur, first.tile);
-    TileRef tr_out = cursor_tile<kBcRows>(grp, t0v, out_cur, first.tile);   // the tile being computed
+        float2_t pend = {0.f, 0.f};
+        bool has_pend = false;   // this wave holds the last stage of a tile begun in an earlier wave
+        BcIt cur = first;
+        TileCursor out_cur;
+        cursor_init(grp, t0v, out_cur, first.tile);
+        int out_m0 = (first.tile - out_cur.t0) * kBcRows;   // rows of the tile being computed
 
-    BcItem cur = first;
-
-    // Decode the parked stage `cur`, finish its tile after the row's last stage, and
-    // move on; MORE: another item follows.
+    // Decode the parked stage `cur`, finish its tile after the window's last stage, and
+    // move on within the phase; MORE: another item of the phase follows (on the last one
+    // cur stays put).
 #define Q2_0_COMPUTE(MORE)                                                                     \
     {                                                                                          \
         uint32_t R[4 * kBcCH];                                                                 \
@@ -469,124 +523,121 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_bcast(MvGroup grp, int nb, 
             R[4 * i] = v.x; R[4 * i + 1] = v.y; R[4 * i + 2] = v.z; R[4 * i + 3] = v.w;        \
         }                                                                                      \
         /* this lane's blocks are cur.st*16 + 4G .. +3; the empty quarters of a ragged     */ \
-        /* row's last stage read blocks 0..3 instead (their results are discarded)         */ \
+        /* row's last stage read the window's blocks 0..3 instead (results discarded)      */ \
         const bool valid = cur.st * kBcSB + 4 * G < nb;                                        \
-        const int xoff = valid ? cur.st * kBcSB * 16 * NR : -4 * G * 16 * NR;                  \
+        const int sl = cur.st - sw0;                                                           \
+        const int xoff = valid ? sl * kBcSB * 16 * NR : -4 * G * 16 * NR;                      \
         if (EXACT) {                                                                           \
-            const int boff = valid ? cur.st * kBcSB + 4 * G : 0;                               \
+            const int boff = valid ? sl * kBcSB + 4 * G : 0;                                   \
             bx_quarter(R, xl + xoff, lds_bs + boff, lds_bsc + boff, valid, acc_e, acc_o);      \
         } else {                                                                               \
             half4_t xa[16];                                                                    \
             _Pragma("unroll") for (int i = 0; i < 16; ++i) xa[i] = xl[xoff + 4 * i * NR];     \
             bc_quarter<NC>(R, xa, pm, valid, acc_e, acc_o);                                    \
         }                                                                                      \
-        if (cur.st == ns - 1) {                                                                \
+        if (cur.st == sw0 + sp - 1) {                                                          \
             const float r0 = acc_e[0] + acc_o[0], r1 = acc_e[1] + acc_o[1];                    \
-            if (cur.tile == first.tile && first.st != 0) {                                     \
+            if (cur.tile == first.tile && pend_start) {                                        \
                 pend = float2_t{r0, r1};                                                       \
                 has_pend = true;                                                               \
             } else {                                                                           \
-                store_tile(tr_out, r0, r1);                                                    \
+                finish_tile(p, cur.tile, out_cur.r.y, out_cur.r.ldy, out_cur.r.M, out_m0, r0, r1); \
             }                                                                                  \
             acc_e[0] = acc_e[1] = acc_o[0] = acc_o[1] = 0.f;                                   \
         }                                                                                      \
-        const BcItem nx_ = next_item(cur);                                                     \
-        if ((MORE) && nx_.tile != cur.tile) tr_out = cursor_tile<kBcRows>(grp, t0v, out_cur, nx_.tile); \
-        cur = nx_;                                                                             \
+        if (MORE) {                                                                            \
+            const BcIt nx_ = next_item(cur);                                                   \
+            if (nx_.tile != cur.tile) {                                                        \
+                cursor_tile<kBcRows>(grp, t0v, out_cur, nx_.tile);                             \
+                out_m0 = (nx_.tile - out_cur.t0) * kBcRows;                                    \
+            }                                                                                  \
+            cur = nx_;                                                                         \
+        }                                                                                      \
     }
 
-    // Each step parks the stage that arrived in one register set, reissues that set for
-    // the item DEPTH ahead and decodes the parked stage while the other loads are in
-    // flight.  No exit in the middle of a loop, which keeps the compiler's memory wait
-    // counts exact.
-    if (DEPTH == 1) {
-        for (int k = 0; k < n_items; ++k) {
-            Q2_0_PARK(ra)
-            __builtin_amdgcn_wave_barrier();
-            Q2_0_ISSUE_NEXT(ra)
-            Q2_0_COMPUTE(k + 1 < n_items)
-            __builtin_amdgcn_wave_barrier();
+        // Each step parks the stage that arrived in one register set, reissues that set
+        // for the item DEPTH ahead and decodes the parked stage while the other loads are
+        // in flight.  No exit in the middle of a loop, which keeps the compiler's memory
+        // wait counts exact.
+        if (DEPTH == 1) {
+            for (int k = 0; k < n; ++k) {
+                Q2_0_PARK(ra)
+                __builtin_amdgcn_wave_barrier();
+                Q2_0_ISSUE_NEXT(ra)
+                Q2_0_COMPUTE(k + 1 < n)
+                __builtin_amdgcn_wave_barrier();
+            }
+        } else {
+            for (int k = 0; k < n; k += 2) {
+                Q2_0_PARK(ra)
+                __builtin_amdgcn_wave_barrier();
+                Q2_0_ISSUE_NEXT(ra)
+                Q2_0_COMPUTE(k + 1 < n)
+                __builtin_amdgcn_wave_barrier();
+                Q2_0_PARK(rb)
+                __builtin_amdgcn_wave_barrier();
+                Q2_0_ISSUE_NEXT(rb)
+                if (k + 1 < n) Q2_0_COMPUTE(k + 2 < n)
+                __builtin_amdgcn_wave_barrier();
+            }
         }
-    } else {
-        for (int k = 0; k < n_items; k += 2) {
-            Q2_0_PARK(ra)
-            __builtin_amdgcn_wave_barrier();
-            Q2_0_ISSUE_NEXT(ra)
-            Q2_0_COMPUTE(k + 1 < n_items)
-            __builtin_amdgcn_wave_barrier();
-            Q2_0_PARK(rb)
-            __builtin_amdgcn_wave_barrier();
-            Q2_0_ISSUE_NEXT(rb)
-            if (k + 1 < n_items) Q2_0_COMPUTE(k + 2 < n_items)
-            __builtin_amdgcn_wave_barrier();
-        }
-    }
 #undef Q2_0_COMPUTE
 #undef Q2_0_ISSUE_NEXT
+
+        // An unfinished last tile (cur is the wave's last item) leaves its partial sums for
+        // the wave that holds the tile's last stage of the window; that wave adds the earlier
+        // waves' partials in order.
+        const bool open_end = n > 0 && cur.st != sw0 + sp - 1;
+        if (open_end) lds_part[wave * 64 + lane] = float2_t{acc_e[0] + acc_o[0], acc_e[1] + acc_o[1]};
+        if (lane == 0) lds_part_tile[wave] = open_end ? cur.tile : -1;
+        acc_e[0] = acc_e[1] = acc_o[0] = acc_o[1] = 0.f;
+        __syncthreads();
+        if (has_pend) {
+            float r0 = 0.f, r1 = 0.f;
+            for (int w = 0; w < wave; ++w) {
+                if (lds_part_tile[w] == first.tile) {
+                    const float2_t pp = lds_part[w * 64 + lane];
+                    r0 += pp.x;
+                    r1 += pp.y;
+                }
+            }
+            const TileRef tr = tile_ref<kBcRows>(grp, t0v, first.tile);
+            finish_tile(p, first.tile, tr.y, tr.ldy, tr.M, tr.m0, r0 + pend.x, r1 + pend.y);
+        }
+        __syncthreads();   // every wave is done with the window, lds_part and the accumulator
+    }
 #undef Q2_0_PARK
 #undef Q2_0_ISSUE
 #undef Q2_0_SET_LOAD_TILE
-
-    // An unfinished last tile leaves its partial sums for the wave that holds the
-    // tile's last stage; that wave adds the earlier waves' partials in order.
-    const int64_t last_tile = div_floor(i1 - 1, ns);
-    const bool open_end = n_items > 0 && (i1 - 1 - last_tile * ns != ns - 1);
-    if (open_end) lds_part[wave * 64 + lane] = float2_t{acc_e[0] + acc_o[0], acc_e[1] + acc_o[1]};
-    if (lane == 0) lds_part_tile[wave] = open_end ? (tb0 + (int)last_tile) : -1;
-    __syncthreads();
-    if (has_pend) {
-        float r0 = 0.f, r1 = 0.f;
-        for (int w = 0; w < wave; ++w) {
-            if (lds_part_tile[w] == first.tile) {
-                const float2_t p = lds_part[w * 64 + lane];
-                r0 += p.x;
-                r1 += p.y;
-            }
-        }
-        store_tile(tile_ref<kBcRows>(grp, t0v, first.tile), r0 + pend.x, r1 + pend.y);
-    }
 }
 
-// Dynamic LDS of one workgroup of `waves` waves: the wave tiles, the waves' partial
-// slots and the staged activation (16 chunks x 2N rows x 8 bytes per block).  The
+namespace {
+
+constexpr int kBcMaxWindowStages = 6;   // activation staged 96 blocks (6144 k) at a time
+
+size_t x_bytes_per_block(int N, bool exact) { return exact ? 16 * 4 * 8 + 16 + 4 : (size_t)16 * 2 * N * 8; }
+
+// Stages per window for a row of nb blocks: the fewest windows of at most
+// kBcMaxWindowStages stages, as even as possible.
+int window_stages(int nb) {
+    const int ns = (nb + kBcSB - 1) / kBcSB;
+    const int P = (ns + kBcMaxWindowStages - 1) / kBcMaxWindowStages;
+    return (ns + P - 1) / P;
+}
+
+}  // namespace
+
+// Dynamic LDS of one workgroup of `waves` waves: the wave tiles, the waves' partial slots,
+// the staged activation window (xcap blocks) and the tile accumulator (tacc tiles).  The
 // kernel's static LDS (under kMvStreamStaticLds bytes) comes on top.
-size_t mat_vec_bcast_lds(int N, int nb, int waves, bool exact) {
-    const size_t x_per_block = exact ? 16 * 4 * 8 + 16 + 4 : (size_t)16 * 2 * N * 8;
-    return (size_t)waves * (kBcWaveLds + 64 * 8) + (size_t)nb * x_per_block;
-}
-
-// Workgroup size: the wave count (4..16) that keeps the most waves resident per CU
-// given the LDS each workgroup needs and four waves per SIMD; ties go to fewer, larger
-// groups.  0 if even 4 waves do not fit; *resident (optional) receives the waves per CU.
-int mat_vec_bcast_waves(int N, int nb, bool exact, int *resident) {
-    const int per_simd = 4;
-    int best = 0, best_res = 0;
-    for (int w = kMvStreamMaxWaves; w >= 4; --w) {
-        const size_t lds = mat_vec_bcast_lds(N, nb, w, exact) + kMvStreamStaticLds;
-        if (lds > 160 * 1024) continue;
-        int wgs = (int)((160 * 1024) / lds);
-        while (wgs > 0 && wgs * w > 4 * per_simd) --wgs;
-        if (wgs * w > best_res) { best_res = wgs * w; best = w; }
-    }
-    if (resident) *resident = best_res;
-    return best;
-}
-
-// Exact mode for N = 1 wherever its larger activation staging still leaves 12 or more
-// resident waves per CU (K up to 8192); the hi/lo mode otherwise.
-static bool use_exact(int N, int nb) {
-    int resident = 0;
-    return N == 1 && mat_vec_bcast_waves(1, nb, true, &resident) > 0 && resident >= 12;
-}
-
-int mat_vec_bcast_waves(int N, int nb, int *resident) {
-    return mat_vec_bcast_waves(N, nb, use_exact(N, nb), resident);
+size_t mat_vec_bcast_lds(int N, int xcap, int tacc, int waves, bool exact) {
+    return (size_t)waves * (kBcWaveLds + 64 * 8) + (size_t)xcap * x_bytes_per_block(N, exact) +
+           (size_t)tacc * kBcRows * N * 4;
 }
 
 template <int NC, typename XT, bool EXACT>
-static hipError_t launch_bcast_nc(const MvGroup &grp, int nb, const XT *x, int64_t ldx, hipStream_t s, int grid,
-                                  int waves) {
-    const size_t lds = mat_vec_bcast_lds(NC, nb, waves, EXACT);
+static hipError_t launch_bcast_nc(const MvGroup &grp, const MvSegs &segs, hipStream_t s, int grid, int waves,
+                                  size_t lds) {
     auto kern = mat_vec_bcast<NC, XT, EXACT>;
     // Raise the dynamic-LDS cap once per device.  Setting it is idempotent, so threads
     // that race past the flag set the same value; the flag itself is atomic.
@@ -603,34 +654,67 @@ static hipError_t launch_bcast_nc(const MvGroup &grp, int nb, const XT *x, int64
         if (e != hipSuccess) return e;
         if (dev >= 0 && dev < 64) configured[dev].store(true, std::memory_order_release);
     }
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * waves), lds, s, grp, nb, x, ldx);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * waves), lds, s, grp, segs);
     return hipGetLastError();
 }
 
-// grp counts tiles of kMvBcastRows rows; N is 1 or 2; rows and x 16-byte aligned, nb % 8 == 0.
-hipError_t launch_mat_vec_bcast(const MvGroup &grp, int nb, const void *xv, Act xt, int64_t ldx, int N,
-                                hipStream_t s) {
-    if (N < 1 || N > 2 || nb % 8 != 0) return hipErrorInvalidValue;
-    const bool exact = use_exact(N, nb);
-    int waves = mat_vec_bcast_waves(N, nb, exact, nullptr);
-    if (waves == 0) return hipErrorInvalidValue;
-    // Small launches: fewer waves per workgroup until there is a workgroup per CU.
-    const int64_t ns = (nb + kBcSB - 1) / kBcSB;
-    const int64_t items = (int64_t)grp.total_tiles * ns;
+// grp counts tiles of kMvBcastRows rows; N is 1 or 2; every segment's rows and
+// activation 16-byte aligned and nb % 8 == 0.  Workgroups go to the segments in
+// proportion to their stages of work.
+hipError_t launch_mat_vec_bcast(const MvGroup &grp, const MvSegDesc *d, int nsegs, Act xt, int N, hipStream_t s) {
+    if (N < 1 || N > 2 || nsegs < 1 || nsegs > kMvMaxSegs) return hipErrorInvalidValue;
+    const bool exact = N == 1;
+    MvSegs segs;
+    segs.n = nsegs;
+    segs.xcap = 0;
+    int64_t items = 0;
+    bool phased = false;
+    for (int i = 0; i < nsegs; ++i) {
+        if (d[i].nb % 8 != 0 || d[i].tile1 <= d[i].tile0) return hipErrorInvalidValue;
+        MvSeg &g = segs.s[i];
+        g.x = d[i].x;
+        g.ldx = d[i].ldx;
+        g.nb = d[i].nb;
+        g.ws = window_stages(d[i].nb);
+        g.tile0 = d[i].tile0;
+        g.tile1 = d[i].tile1;
+        const int ns = (g.nb + kBcSB - 1) / kBcSB;
+        segs.xcap = std::max(segs.xcap, std::min(g.ws * kBcSB, g.nb));
+        phased = phased || g.ws < ns;
+        items += (int64_t)(g.tile1 - g.tile0) * ns;
+    }
+    for (int i = nsegs; i < kMvMaxSegs; ++i) segs.s[i] = MvSeg{nullptr, 0, 8, 1, 0, 0, 0x7fffffff, 0};
+    // Waves per workgroup: 16 (one workgroup per CU); small launches use fewer until
+    // there is a workgroup per CU.
+    int waves = kMvStreamMaxWaves;
     while (waves > 4 && (items + waves - 1) / waves < 256) waves = (waves + 1) / 2 < 4 ? 4 : (waves + 1) / 2;
-    const size_t lds = mat_vec_bcast_lds(N, nb, waves, exact) + kMvStreamStaticLds;
-    const int per_cu = (int)((160 * 1024) / lds);
-    const int max_grid = 256 * (per_cu < 1 ? 1 : per_cu);
-    // every wave gets at least about one stage; never more workgroups than tiles
-    int64_t need = (items + waves - 1) / waves;
-    if (need > grp.total_tiles) need = grp.total_tiles;
-    const int grid = (int)(need < max_grid ? need : max_grid);
+    const size_t fixed = mat_vec_bcast_lds(N, segs.xcap, 0, waves, exact) + kMvStreamStaticLds;
+    if (fixed > 160 * 1024) return hipErrorInvalidValue;
+    // the tile accumulator of phased segments takes what LDS is left
+    const int tacc_cap = phased ? (int)((160 * 1024 - fixed) / ((size_t)kBcRows * N * 4)) : 0;
+    if (phased && tacc_cap < 1) return hipErrorInvalidValue;
+    const int per_cu = std::max(1, (int)((160 * 1024) / fixed));
+    int64_t want = std::min<int64_t>((items + waves - 1) / waves, 256 * (int64_t)per_cu);
+    int wg = 0, tacc = 0;
+    for (int i = 0; i < nsegs; ++i) {
+        MvSeg &g = segs.s[i];
+        const int T = g.tile1 - g.tile0;
+        const int ns = (g.nb + kBcSB - 1) / kBcSB;
+        int64_t n = (want * T * ns + items / 2) / items;       // share of the workgroups
+        n = std::max<int64_t>(1, std::min<int64_t>(n, T));     // at least one tile each
+        if (g.ws < ns) n = std::max<int64_t>(n, (T + tacc_cap - 1) / tacc_cap);
+        if ((int64_t)wg + n > 0x7fffffff) return hipErrorInvalidValue;
+        g.wg0 = wg;
+        g.wgs = (int)n;
+        wg += (int)n;
+        if (g.ws < ns) tacc = std::max(tacc, (int)((T + n - 1) / n));
+    }
+    segs.tacc = tacc;
+    const size_t lds = mat_vec_bcast_lds(N, segs.xcap, tacc, waves, exact);
     return with_act(xt, [&](auto tag) -> hipError_t {
         using XT = decltype(tag);
-        const XT *x = static_cast<const XT *>(xv);
-        if (N == 2) return launch_bcast_nc<2, XT, false>(grp, nb, x, ldx, s, grid, waves);
-        return exact ? launch_bcast_nc<1, XT, true>(grp, nb, x, ldx, s, grid, waves)
-                     : launch_bcast_nc<1, XT, false>(grp, nb, x, ldx, s, grid, waves);
+        if (N == 2) return launch_bcast_nc<2, XT, false>(grp, segs, s, wg, waves, lds);
+        return launch_bcast_nc<1, XT, true>(grp, segs, s, wg, waves, lds);
     });
 }
 

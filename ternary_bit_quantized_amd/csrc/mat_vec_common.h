@@ -101,11 +101,12 @@ __device__ __forceinline__ void cursor_init(const MvGroup &grp, int t0v, TileCur
     cursor_load(grp, t0v, c);
 }
 
-// The tile's matrix and rows (TILE rows per tile); tile >= every tile the cursor
-// was moved to before.
+// The tile's matrix and rows (TILE rows per tile).  Tiles mostly move forward; a tile
+// outside the cursor's matrix (past it, or before it when a wave starts the next
+// window of its tiles) looks the matrix up again.
 template <int TILE>
 __device__ __forceinline__ TileRef cursor_tile(const MvGroup &grp, int t0v, TileCursor &c, int tile) {
-    if (tile >= c.t1) {
+    if (tile >= c.t1 || tile < c.t0) {
         c.idx = find_problem(t0v, tile);
         cursor_load(grp, t0v, c);
         // wait for the argument loads here, on the rare path: a wait left to the join
@@ -324,15 +325,39 @@ __device__ __forceinline__ void mv_block_pair(const uint8_t *lp, const half8_t *
     }
 }
 
+// ---- segments of a broadcast-kernel launch: runs of the group's tiles that share one
+// activation.  The host describes them (MvSegDesc); the launch adds its own layout
+// (MvSeg: the window of stages staged at a time, the segment's workgroups).
+constexpr int kMvMaxSegs = 8;
+struct MvSegDesc {
+    const void *x;    // activations of the launch's element type, column n at x + n*ldx
+    int64_t ldx;
+    int nb;           // blocks per row (K / 64)
+    int tile0, tile1; // the segment's tiles, numbered across the group
+};
+struct MvSeg {
+    const void *x;
+    int64_t ldx;
+    int nb;
+    int ws;           // stages per window: the activation is staged ws*16 blocks at a time
+    int tile0, tile1;
+    int wg0, wgs;     // the segment's workgroups
+};
+struct MvSegs {
+    MvSeg s[kMvMaxSegs];
+    int n;
+    int xcap;         // blocks of activation staged in LDS (the largest window)
+    int tacc;         // tiles per workgroup of the result accumulator (segments of several windows)
+};
+
 size_t mat_vec_stream_lds(int N, int nb, int waves);
 int mat_vec_stream_waves(int N, int nb, int *resident);
 hipError_t launch_mat_vec_stream(const MvGroup &grp, int nb, const void *x, Act xt, int64_t ldx, int N,
                                  hipStream_t s);
-// N = 1, 2; grp counts tiles of kMvBcastRows rows
-size_t mat_vec_bcast_lds(int N, int nb, int waves, bool exact);
-int mat_vec_bcast_waves(int N, int nb, bool exact, int *resident);
-int mat_vec_bcast_waves(int N, int nb, int *resident);   // for the mode the launch picks
-hipError_t launch_mat_vec_bcast(const MvGroup &grp, int nb, const void *x, Act xt, int64_t ldx, int N,
+// N = 1, 2; grp counts tiles of kMvBcastRows rows; nsegs <= kMvMaxSegs segments.  Any K
+// (the activation is staged in windows); rows and activations 16-byte aligned, nb % 8 == 0.
+size_t mat_vec_bcast_lds(int N, int xcap, int tacc, int waves, bool exact);
+hipError_t launch_mat_vec_bcast(const MvGroup &grp, const MvSegDesc *segs, int nsegs, Act xt, int N,
                                 hipStream_t s);
 
 }  // namespace q2_0

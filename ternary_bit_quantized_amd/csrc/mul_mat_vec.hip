@@ -85,19 +85,24 @@ constexpr int64_t kStreamRows = 16384;
 
 static int stream_tile_rows(int N) { return N <= 2 ? kMvBcastRows : kMvTile; }
 
-// The streaming kernels need the whole activation staged per workgroup; where that
-// leaves fewer than 8 resident waves per CU the K-split kernel is used instead.
+// The broadcast kernel (N <= 2) stages the activation in windows, so every K fits; the
+// 16-row-tile kernel (N >= 3) stages all of K and is used where that still leaves 8 or
+// more resident waves per CU (the K-split kernel otherwise).
 static bool stream_fits(int N, int nb) {
+    if (N <= 2) return true;
     int resident = 0;
-    const int waves = N <= 2 ? mat_vec_bcast_waves(N, nb, &resident) : mat_vec_stream_waves(N, nb, &resident);
+    const int waves = mat_vec_stream_waves(N, nb, &resident);
     return waves > 0 && resident >= 8;
 }
 
-// grp counts tiles of stream_tile_rows(N) rows
+// grp counts tiles of stream_tile_rows(N) rows; all its matrices share x
 static hipError_t launch_streaming(const MvGroup &grp, int nb, const void *x, Act xt, int64_t ldx, int N,
                                    hipStream_t s) {
-    return N <= 2 ? launch_mat_vec_bcast(grp, nb, x, xt, ldx, N, s)
-                  : launch_mat_vec_stream(grp, nb, x, xt, ldx, N, s);
+    if (N <= 2) {
+        const MvSegDesc d{x, ldx, nb, 0, grp.total_tiles};
+        return launch_mat_vec_bcast(grp, &d, 1, xt, N, s);
+    }
+    return launch_mat_vec_stream(grp, nb, x, xt, ldx, N, s);
 }
 
 hipError_t launch_mat_vec(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx, int N,
@@ -172,6 +177,57 @@ hipError_t launch_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items,
             for (int k = grp.n; k <= kMvMaxGroup; ++k) grp.tile0[k] = INT_MAX;
             grp.total_tiles = tiles;
             hipError_t e = launch_streaming(grp, nb, x, xt, ldx, N, s);
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
+}
+
+// Items with their own activation and K: consecutive streaming-eligible items that share
+// (x, ldx, K) form a segment; a launch takes up to kMvMaxGroup items in up to kMvMaxSegs
+// segments (N <= 2) or one segment (N >= 3, whose kernel stages one activation).  Other
+// items run alone.
+hipError_t launch_mat_vec_batch(const q2_0_mat_vec_batch_item *items, int64_t n_items, Act xt, int N,
+                                hipStream_t s) {
+    const int tr = stream_tile_rows(N);
+    int64_t i = 0;
+    while (i < n_items) {
+        MvGroup grp;
+        grp.n = 0;
+        int tiles = 0;
+        MvSegDesc segs[kMvMaxSegs];
+        int nsegs = 0;
+        while (i < n_items && grp.n < kMvMaxGroup) {
+            const q2_0_mat_vec_batch_item &it = items[i];
+            if (it.M == 0) { ++i; continue; }
+            const uint8_t *w = static_cast<const uint8_t *>(it.w);
+            const int nb = (int)(it.K / kBlockWeights);
+            const bool ok = mat_vec_mfma_eligible(w, it.M, nb, it.x, xt, it.ldx) && stream_fits(N, nb) &&
+                            tiles + (it.M + tr - 1) / tr < 0x7fffffff;
+            if (!ok) {
+                if (grp.n) break;   // launch what is gathered first
+                hipError_t e = launch_mat_vec(w, it.M, nb, it.x, xt, it.ldx, N, it.y, it.ldy, s);
+                if (e != hipSuccess) return e;
+                ++i;
+                continue;
+            }
+            const bool same = nsegs > 0 && segs[nsegs - 1].x == it.x && segs[nsegs - 1].ldx == it.ldx &&
+                              segs[nsegs - 1].nb == nb;
+            if (!same) {
+                if (nsegs == kMvMaxSegs || (N > 2 && nsegs == 1)) break;
+                segs[nsegs++] = MvSegDesc{it.x, it.ldx, nb, tiles, tiles};
+            }
+            grp.tile0[grp.n] = tiles;
+            grp.p[grp.n++] = MvProblem{w, it.y, it.ldy, (int)it.M, tiles};
+            tiles += (int)((it.M + tr - 1) / tr);
+            segs[nsegs - 1].tile1 = tiles;
+            ++i;
+        }
+        if (grp.n) {
+            for (int k = grp.n; k <= kMvMaxGroup; ++k) grp.tile0[k] = INT_MAX;
+            grp.total_tiles = tiles;
+            const hipError_t e = N <= 2 ? launch_mat_vec_bcast(grp, segs, nsegs, xt, N, s)
+                                        : launch_mat_vec_stream(grp, segs[0].nb, segs[0].x, xt, segs[0].ldx, N, s);
             if (e != hipSuccess) return e;
         }
     }

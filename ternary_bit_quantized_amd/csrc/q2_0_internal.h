@@ -120,6 +120,8 @@ hipError_t launch_mat_vec_f32(const uint8_t *w, int64_t M, int nb, const void *x
                               float *y, int64_t ldy, hipStream_t s);
 hipError_t launch_mat_vec_group(const q2_0_mat_vec_item *items, int64_t n_items, int nb,
                                 const void *x, Act xt, int64_t ldx, int N, hipStream_t s);
+hipError_t launch_mat_vec_batch(const q2_0_mat_vec_batch_item *items, int64_t n_items, Act xt, int N,
+                                hipStream_t s);
 bool mat_vec_mfma_eligible(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx);
 hipError_t launch_mat_vec_mfma(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx,
                                int N, float *y, int64_t ldy, hipStream_t s);

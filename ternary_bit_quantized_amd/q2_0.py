@@ -37,13 +37,27 @@ EXPORTS = ("q2_0_get_rows", "q2_0_mul_mat_vec", "q2_0_mul_mat_vec_group", "q2_0_
            "q2_0_mul_mat_workspace_bytes", "q2_0_mul_mat_group", "q2_0_mul_mat_group_workspace_bytes",
            "q2_0_mul_mat_vec_act", "q2_0_mul_mat_vec_group_act", "q2_0_mul_mat_act", "q2_0_mul_mat_group_act",
            "q2_0_quantize", "q2_0_repack_g128", "q2_0_mul_mat_id", "q2_0_mul_mat_id_workspace_bytes",
-           "q2_0_mul_mat_noalloc", "q2_0_status_string", "q2_0_last_hip_error", "q2_0_version")
+           "q2_0_mul_mat_noalloc", "q2_0_mul_mat_vec_batch", "q2_0_status_string", "q2_0_last_hip_error", "q2_0_version")
 
 
 class MatVecItem(ctypes.Structure):
     """q2_0_mat_vec_item: one matrix of a grouped mat-vec."""
     _fields_ = [("w", ctypes.c_void_p), ("M", ctypes.c_int64), ("y", ctypes.c_void_p),
                 ("ldy", ctypes.c_int64)]
+
+
+class MatVecBatchItem(ctypes.Structure):
+    """q2_0_mat_vec_batch_item: one product of a batched mat-vec (its own K and x)."""
+    _fields_ = [("w", ctypes.c_void_p), ("M", ctypes.c_int64), ("K", ctypes.c_int64), ("x", ctypes.c_void_p),
+                ("ldx", ctypes.c_int64), ("y", ctypes.c_void_p), ("ldy", ctypes.c_int64)]
+
+
+def make_batch_items(entries):
+    """[(w_ptr, M, K, x_ptr, ldx, y_ptr, ldy), ...] -> a ctypes array for mul_mat_vec_batch_raw."""
+    arr = (MatVecBatchItem * len(entries))()
+    for i, e in enumerate(entries):
+        arr[i] = MatVecBatchItem(*e)
+    return arr
 
 
 def make_items(entries):
@@ -98,6 +112,8 @@ def lib() -> ctypes.CDLL:
         L.q2_0_mul_mat_id_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, C]
         L.q2_0_mul_mat_id_workspace_bytes.restype = ctypes.c_size_t
         L.q2_0_repack_g128.argtypes = [P, I64, I64, P, P]
+        L.q2_0_mul_mat_vec_batch.argtypes = [P, I64, ctypes.c_int, I64, P]
+        L.q2_0_mul_mat_vec_batch.restype = ctypes.c_int
         L.q2_0_mul_mat_noalloc.argtypes = [P, I64, I64, P, I64, I64, P, I64, ctypes.c_int, P]
         L.q2_0_mul_mat_noalloc.restype = ctypes.c_int
         for f in (L.q2_0_mul_mat_vec_act, L.q2_0_mul_mat_vec_group_act, L.q2_0_mul_mat_act,
@@ -119,6 +135,10 @@ def _check(status: int, what: str) -> None:
 
 # ----------------------------------------------------------------------------- raw (pointers)
 
+def _items_ptr(items):
+    return ctypes.cast(items, ctypes.c_void_p) if items is not None else None
+
+
 def get_rows_raw(w: int, M: int, K: int, ids: int, n_ids: int, out: int, ld_out: int,
                  stream: int = 0) -> int:
     return lib().q2_0_get_rows(w, M, K, ids, n_ids, out, ld_out, stream)
@@ -136,6 +156,11 @@ def mul_mat_vec_group_raw(items, n_items: int, K: int, x: int, ldx: int, N: int,
                                         n_items, K, x, ldx, N, stream)
 
 
+def mul_mat_vec_batch_raw(items, n_items: int, x_type: int, N: int, stream: int = 0) -> int:
+    """items: a ctypes array from make_batch_items (or None with n_items == 0)."""
+    return lib().q2_0_mul_mat_vec_batch(_items_ptr(items), n_items, x_type, N, stream)
+
+
 def mul_mat_raw(w: int, M: int, K: int, x: int, ldx: int, N: int, y: int, ldy: int, precision: int,
                 workspace: int, ws_bytes: int, stream: int = 0) -> int:
     return lib().q2_0_mul_mat(w, M, K, x, ldx, N, y, ldy, precision, workspace, ws_bytes, stream)
@@ -148,10 +173,6 @@ def mul_mat_noalloc_raw(w: int, M: int, K: int, x: int, ldx: int, N: int, y: int
 
 def mul_mat_workspace_bytes(M: int, K: int, N: int, precision: int) -> int:
     return int(lib().q2_0_mul_mat_workspace_bytes(M, K, N, precision))
-
-
-def _items_ptr(items):
-    return ctypes.cast(items, ctypes.c_void_p) if items is not None else None
 
 
 def mul_mat_group_raw(items, n_items: int, K: int, x: int, ldx: int, N: int, precision: int,
@@ -328,6 +349,28 @@ def q2_0_mul_mat_vec_group(mats, K: int, x, ys=None, stream=None):
     _check(mul_mat_vec_group_act_raw(items, len(entries), K, xp, xt, ldx, N, _stream(stream)),
            "q2_0_mul_mat_vec_group_act")
     return ys
+
+
+def q2_0_mul_mat_vec_batch(products, x_type_tensor=None, ys=None, stream=None):
+    """products: [(w, M, K, x), ...] with x (N, >=K) device tensors of one dtype (float32,
+    float16 or bfloat16) and the same N; returns [y_i (N, M_i) float32] with y_i = W_i x_i."""
+    import torch
+    entries, out = [], []
+    xt0, N0 = None, None
+    for i, (w, M, K, x) in enumerate(products):
+        xp, N, ldx, xt = _xcols(x, K, "x")
+        if xt0 is None:
+            xt0, N0 = xt, N
+        elif xt != xt0 or N != N0:
+            raise ValueError("every x of a batch must have the same dtype and column count")
+        y = ys[i] if ys is not None else torch.empty((N, M), dtype=torch.float32, device=x.device)
+        yp, _, ldy = _cols(y, M, "y")
+        entries.append((w.data_ptr(), M, K, xp, ldx, yp, ldy))
+        out.append(y)
+    items = make_batch_items(entries)
+    _check(mul_mat_vec_batch_raw(items, len(entries), xt0 if xt0 is not None else Q2_0_ACT_F32, N0 or 0,
+                                 _stream(stream)), "q2_0_mul_mat_vec_batch")
+    return out
 
 
 def q2_0_mul_mat(w, M: int, K: int, x, precision: int = Q2_0_PREC_F16_MFMA, y=None, workspace=None,

@@ -242,3 +242,23 @@ def test_mul_mat_noalloc_validation():
     assert B.mul_mat_workspace_bytes(4096, 12288, 4096, 0) > B.NOALLOC_SCRATCH_BYTES
     assert nr(P16, 4096, 12288, P16, 12288, 4096, P16, 4096, 0) == B.Q2_0_ERR_TOO_LARGE
     assert B.lib().q2_0_status_string(B.Q2_0_ERR_TOO_LARGE).decode().startswith("Q2_0_ERR_TOO_LARGE")
+
+
+def test_mul_mat_vec_batch_validation():
+    """Every item is checked before anything is launched; the call launches nothing on
+    error or when it is empty."""
+    mk = B.make_batch_items
+    br = B.mul_mat_vec_batch_raw
+    good = (P16, 10, 128, P16, 128, P16, 10)
+    assert br(None, 0, 0, 1) == B.Q2_0_OK
+    assert br(None, 2, 0, 1) == B.Q2_0_ERR_NULL
+    assert br(mk([good]), -1, 0, 1) == B.Q2_0_ERR_SHAPE
+    assert br(mk([good, (P16, 10, 100, P16, 128, P16, 10)]), 2, 0, 1) == B.Q2_0_ERR_SHAPE   # K % 64
+    assert br(mk([good]), 1, 0, 0) == B.Q2_0_OK                                               # N = 0
+    assert br(mk([(0, 0, 64, 0, 64, 0, 0)]), 1, 0, 1) == B.Q2_0_OK                            # M = 0 only
+    assert br(mk([good, (P16, 10, 64, 0, 64, P16, 10)]), 2, 0, 1) == B.Q2_0_ERR_NULL
+    assert br(mk([good, (P16, 10, 64, P16, 63, P16, 10)]), 2, 0, 1) == B.Q2_0_ERR_LAYOUT
+    assert br(mk([good, (P16, 10, 64, P16, 64, P16, 9)]), 2, 0, 1) == B.Q2_0_ERR_LAYOUT
+    assert br(mk([good]), 1, 7, 1) == B.Q2_0_ERR_UNSUPPORTED                                 # x_type
+    assert br(mk([good, (P16 + 1, 10, 64, P16, 64, P16, 10)]), 2, 0, 1) == B.Q2_0_ERR_ALIGN
+    assert br(mk([good]), 1, 0, 9) == B.Q2_0_ERR_UNSUPPORTED                                 # N > 8
