@@ -138,24 +138,37 @@ template <int NC, typename XT>
 __device__ __forceinline__ void stage_x_bcast(const XT *__restrict__ x, int64_t ldx, int nb, const int *lds_e,
                                               half4_t *lds_x, int tid, int nthreads) {
     constexpr int NR = 2 * NC;
+    constexpr int U = 2;   // items per thread whose loads are issued before any is converted
     const int items = nb * 16 * NC;
-    for (int q = tid; q < items; q += nthreads) {
-        const int n = q % NC, c = (q / NC) % 16, blk = q / (16 * NC);
-        const int u = c >> 2, t = c & 3, odd = blk & 1;
-        const XT *xb = x + n * ldx + (int64_t)blk * kBlockWeights + 2 * t;
-        const float2_t a = load_act2(xb + 8 * half_lo(u, odd)), b = load_act2(xb + 8 * half_hi(u, odd));
-        const int xe = lds_e[n];
-        const float v[4] = {__builtin_amdgcn_ldexpf(a.x, xe), __builtin_amdgcn_ldexpf(b.x, xe),
-                            __builtin_amdgcn_ldexpf(a.y, xe), __builtin_amdgcn_ldexpf(b.y, xe)};
-        half4_t hi, lo;
+    for (int q0 = tid; q0 < items; q0 += U * nthreads) {
+        float2_t a[U], b[U];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            hi[e] = (_Float16)v[e];
-            lo[e] = (_Float16)(v[e] - (float)hi[e]);
+        for (int k = 0; k < U; ++k) {
+            const int q = min(q0 + k * nthreads, items - 1);
+            const int n = q % NC, c = (q / NC) % 16, blk = q / (16 * NC);
+            const int u = c >> 2, t = c & 3, odd = blk & 1;
+            const XT *xb = x + n * ldx + (int64_t)blk * kBlockWeights + 2 * t;
+            a[k] = load_act2(xb + 8 * half_lo(u, odd));
+            b[k] = load_act2(xb + 8 * half_hi(u, odd));
         }
-        half4_t *dst = lds_x + (blk * 16 + c) * NR + 2 * n;
-        dst[0] = hi;
-        dst[1] = lo;
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int q = q0 + k * nthreads;
+            if (q >= items) break;
+            const int n = q % NC, c = (q / NC) % 16, blk = q / (16 * NC);
+            const int xe = lds_e[n];
+            const float v[4] = {__builtin_amdgcn_ldexpf(a[k].x, xe), __builtin_amdgcn_ldexpf(b[k].x, xe),
+                                __builtin_amdgcn_ldexpf(a[k].y, xe), __builtin_amdgcn_ldexpf(b[k].y, xe)};
+            half4_t hi, lo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                hi[e] = (_Float16)v[e];
+                lo[e] = (_Float16)(v[e] - (float)hi[e]);
+            }
+            half4_t *dst = lds_x + (blk * 16 + c) * NR + 2 * n;
+            dst[0] = hi;
+            dst[1] = lo;
+        }
     }
 }
 
@@ -231,56 +244,70 @@ __device__ __forceinline__ void bx_quarter(const uint32_t (&R)[20], const half4_
 // Exact-mode staging of one activation column for blocks 0..nb-1: limb entries
 // (blk*16 + c)*4 + l (half4 of chunk c = 4u + t, limb l, in the weight order of
 // bx_dword, each element times bx_factor), and per block bs = -2^-20 sum L per limb
-// (NaN for limb 0 when the block holds a non-finite activation) and bsc = 2^(20-e).  One thread per chunk;
+// (NaN for limb 0 when the block holds a non-finite activation) and bsc = 2^(20-e).  One thread per chunk,
+// the loads of two passes issued before either is converted;
 // the 16 chunks of a block sit in 16 consecutive lanes, which reduce the block's
 // maximum and limb sums with lane exchanges.
 template <typename XT>
 __device__ __forceinline__ void stage_x_limbs(const XT *__restrict__ x, int nb, half4_t *lds_x, float4_t *lds_bs,
                                               float *lds_bsc, int tid, int nthreads) {
+    constexpr int U = 2;   // passes whose loads are issued before any is converted
     const int items = nb * 16;
-    for (int q0 = 0; q0 < items; q0 += nthreads) {   // the same trip count in every lane
-        const int q = min(q0 + tid, items - 1);
-        const bool act = q0 + tid < items;           // whole 16-lane groups are active or not
-        const int c = q % 16, blk = q / 16;
-        const int u = c >> 2, t = c & 3, odd = blk & 1;
-        const XT *xb = x + (int64_t)blk * kBlockWeights + 2 * t;
-        const float2_t a = load_act2(xb + 8 * half_lo(u, odd)), b = load_act2(xb + 8 * half_hi(u, odd));
-        const float v[4] = {a.x, b.x, a.y, b.y};
-        float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    for (int q0 = 0; q0 < items; q0 += U * nthreads) {   // the same trip count in every lane
+        float2_t a[U], b[U];
 #pragma unroll
-        for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
-        const bool finite = m <= 3.4028234663852886e38f;   // false for inf and NaN
-        const int e = (finite && m > 0.f) ? 11 - __builtin_amdgcn_frexp_expf(m) : 0;
-        float lim[4][4], sum[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            float w = finite ? __builtin_amdgcn_ldexpf(v[k], e) : 0.f;
-#pragma unroll
-            for (int l = 0; l < 4; ++l) {
-                const float L = __builtin_rintf(w);
-                w = (w - L) * 2048.f;   // exact: the remainder of a rounded f32 and a power of two
-                lim[l][k] = L;
-                sum[l] += L;
-            }
-        }
-        if (act) {
-#pragma unroll
-            for (int l = 0; l < 4; ++l) {
-                half4_t h;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) h[k] = (_Float16)(lim[l][k] * bx_factor(t, k));
-                lds_x[(blk * 16 + c) * 4 + l] = h;
-            }
+        for (int k = 0; k < U; ++k) {
+            const int q = min(q0 + k * nthreads + tid, items - 1);
+            const int c = q % 16, blk = q / 16;
+            const int u = c >> 2, t = c & 3, odd = blk & 1;
+            const XT *xb = x + (int64_t)blk * kBlockWeights + 2 * t;
+            a[k] = load_act2(xb + 8 * half_lo(u, odd));
+            b[k] = load_act2(xb + 8 * half_hi(u, odd));
         }
 #pragma unroll
-        for (int l = 0; l < 4; ++l)
+        for (int k = 0; k < U; ++k) {
+            if (q0 + k * nthreads >= items) break;      // uniform: whole passes are in or out
+            const int q = min(q0 + k * nthreads + tid, items - 1);
+            const bool act = q0 + k * nthreads + tid < items;   // whole 16-lane groups are active or not
+            const int c = q % 16, blk = q / 16;
+            const int t = c & 3;
+            const float v[4] = {a[k].x, b[k].x, a[k].y, b[k].y};
+            float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
 #pragma unroll
-            for (int off = 1; off < 16; off <<= 1) sum[l] += __shfl_xor(sum[l], off);
-        if (act && c == 0) {
-            const float nan = __builtin_nanf("");
-            lds_bs[blk] = float4_t{finite ? -sum[0] * 9.5367431640625e-7f : nan, -sum[1] * 9.5367431640625e-7f,
-                                   -sum[2] * 9.5367431640625e-7f, -sum[3] * 9.5367431640625e-7f};   // 2^-20
-            lds_bsc[blk] = __builtin_amdgcn_ldexpf(1.f, 20 - e);
+            for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+            const bool finite = m <= 3.4028234663852886e38f;   // false for inf and NaN
+            const int e = (finite && m > 0.f) ? 11 - __builtin_amdgcn_frexp_expf(m) : 0;
+            float lim[4][4], sum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                float w = finite ? __builtin_amdgcn_ldexpf(v[kk], e) : 0.f;
+#pragma unroll
+                for (int l = 0; l < 4; ++l) {
+                    const float L = __builtin_rintf(w);
+                    w = (w - L) * 2048.f;   // exact: the remainder of a rounded f32 and a power of two
+                    lim[l][kk] = L;
+                    sum[l] += L;
+                }
+            }
+            if (act) {
+#pragma unroll
+                for (int l = 0; l < 4; ++l) {
+                    half4_t h;
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) h[kk] = (_Float16)(lim[l][kk] * bx_factor(t, kk));
+                    lds_x[(blk * 16 + c) * 4 + l] = h;
+                }
+            }
+#pragma unroll
+            for (int l = 0; l < 4; ++l)
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) sum[l] += __shfl_xor(sum[l], off);
+            if (act && c == 0) {
+                const float nan = __builtin_nanf("");
+                lds_bs[blk] = float4_t{finite ? -sum[0] * 9.5367431640625e-7f : nan, -sum[1] * 9.5367431640625e-7f,
+                                       -sum[2] * 9.5367431640625e-7f, -sum[3] * 9.5367431640625e-7f};   // 2^-20
+                lds_bsc[blk] = __builtin_amdgcn_ldexpf(1.f, 20 - e);
+            }
         }
     }
 }
@@ -341,12 +368,13 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_bcast(MvGroup grp, MvSegs s
     const int P = (ns + W - 1) / W;
     const uint32_t rowbytes = (uint32_t)nb * kBlockBytes;
     const bool ragged = (nb % kBcSB) != 0;   // nb % 8 == 0: the last stage of a row then holds 8 blocks
-    // (products and quotients without 64-bit integer divisions, which would cost hundreds
-    // of instructions before the first load)
-    const int ntile = seg.tile1 - seg.tile0;
+    // (no divisions: the host splits the tiles, the waves are a power of two and the
+    // stages of a window divide by a multiply-high; a division costs hundreds of cycles
+    // on the path to the first load)
     const int bw = (int)blockIdx.x - seg.wg0;
-    const int tb0 = seg.tile0 + (int)mul_div(ntile, bw, seg.wgs);
-    const int nt = seg.tile0 + (int)mul_div(ntile, bw + 1, seg.wgs) - tb0;
+    const int tb0 = seg.tile0 + bw * seg.q + min(bw, seg.r);
+    const int nt = seg.q + (bw < seg.r ? 1 : 0);
+    const int lw = __builtin_ctz((unsigned)WAVES);
 
     // Chunk q*64 + lane of a stage (chunks past the 288 repeat the last one): row
     // c / 18, bytes 16(c % 18) .. +15 of the row's 288.  Byte b of a row belongs to
@@ -464,14 +492,15 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_bcast(MvGroup grp, MvSegs s
     for (int p = 0; p < P; ++p) {   // the same trip count in every wave: the barriers need it
         const int sw0 = p * W;                               // first stage of the window
         const int sp = min(W, ns - sw0);
+        const uint32_t mag = p + 1 < P ? seg.mag_w : seg.mag_last;   // divides by sp (below 2^29)
         const int blk0 = sw0 * kBcSB;
         // this wave's items of the phase: (tile, stage) pairs i0 .. i1-1 of the workgroup's
         // nt * sp, tile-major
-        const int64_t n_wg = (int64_t)nt * sp;
-        const int64_t i0 = mul_div(n_wg, wave, WAVES);
-        const int n = (int)(mul_div(n_wg, wave + 1, WAVES) - i0);
-        const int64_t i0t = div_floor(i0, sp);
-        const BcIt first{tb0 + (int)i0t, sw0 + (int)(i0 - i0t * sp)};
+        const uint64_t n_wg = (uint64_t)(uint32_t)nt * (uint32_t)sp;
+        const uint32_t i0 = (uint32_t)((n_wg * (uint32_t)wave) >> lw);
+        const int n = (int)((uint32_t)((n_wg * (uint32_t)(wave + 1)) >> lw) - i0);
+        const uint32_t i0t = sp == 1 ? i0 : __umulhi(i0, mag);   // (the magic of 1 would be 2^32)
+        const BcIt first{tb0 + (int)i0t, sw0 + (int)(i0 - i0t * (uint32_t)sp)};
         const bool pend_start = n > 0 && first.st != sw0;   // its first tile began in an earlier wave
         auto next_item = [&](BcIt it) {
             if (++it.st == sw0 + sp) {
@@ -614,6 +643,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_bcast(MvGroup grp, MvSegs s
 namespace {
 
 constexpr int kBcMaxWindowStages = 6;   // activation staged 96 blocks (6144 k) at a time
+static_assert(kBcMaxWindowStages <= 8, "the kernel's multiply-high division covers at most 8 stages");
 
 size_t x_bytes_per_block(int N, bool exact) { return exact ? 16 * 4 * 8 + 16 + 4 : (size_t)16 * 2 * N * 8; }
 
@@ -683,11 +713,11 @@ hipError_t launch_mat_vec_bcast(const MvGroup &grp, const MvSegDesc *d, int nseg
         phased = phased || g.ws < ns;
         items += (int64_t)(g.tile1 - g.tile0) * ns;
     }
-    for (int i = nsegs; i < kMvMaxSegs; ++i) segs.s[i] = MvSeg{nullptr, 0, 8, 1, 0, 0, 0x7fffffff, 0};
+    for (int i = nsegs; i < kMvMaxSegs; ++i) segs.s[i] = MvSeg{nullptr, 0, 8, 1, 0, 0, 0x7fffffff, 0, 0, 0, 1u, 1u};
     // Waves per workgroup: 16 (one workgroup per CU); small launches use fewer until
     // there is a workgroup per CU.
-    int waves = kMvStreamMaxWaves;
-    while (waves > 4 && (items + waves - 1) / waves < 256) waves = (waves + 1) / 2 < 4 ? 4 : (waves + 1) / 2;
+    int waves = kMvStreamMaxWaves;   // a power of two (the kernel splits work by shifts)
+    while (waves > 4 && (items + waves - 1) / waves < 256) waves /= 2;
     const size_t fixed = mat_vec_bcast_lds(N, segs.xcap, 0, waves, exact) + kMvStreamStaticLds;
     if (fixed > 160 * 1024) return hipErrorInvalidValue;
     // the tile accumulator of phased segments takes what LDS is left
@@ -706,8 +736,15 @@ hipError_t launch_mat_vec_bcast(const MvGroup &grp, const MvSegDesc *d, int nseg
         if ((int64_t)wg + n > 0x7fffffff) return hipErrorInvalidValue;
         g.wg0 = wg;
         g.wgs = (int)n;
+        g.q = (int)(T / n);
+        g.r = (int)(T % n);
         wg += (int)n;
         if (g.ws < ns) tacc = std::max(tacc, (int)((T + n - 1) / n));
+        // the kernel divides item counts below 2^29 by at most 8 stages with a multiply-high
+        if ((int64_t)(g.q + 1) * g.ws >= ((int64_t)1 << 29)) return hipErrorInvalidValue;
+        const int last = ns - (ns + g.ws - 1) / g.ws * g.ws + g.ws;   // stages of the last window
+        g.mag_w = (uint32_t)(0xffffffffu / (uint32_t)g.ws) + 1u;
+        g.mag_last = (uint32_t)(0xffffffffu / (uint32_t)last) + 1u;
     }
     segs.tacc = tacc;
     const size_t lds = mat_vec_bcast_lds(N, segs.xcap, tacc, waves, exact);

@@ -342,6 +342,8 @@ struct MvSeg {
     int ws;           // stages per window: the activation is staged ws*16 blocks at a time
     int tile0, tile1;
     int wg0, wgs;     // the segment's workgroups
+    int q, r;         // tiles per workgroup: q, and one more for the first r workgroups
+    uint32_t mag_w, mag_last;   // ceil(2^32 / d) for d = the stages of a window, of the last window
 };
 struct MvSegs {
     MvSeg s[kMvMaxSegs];
