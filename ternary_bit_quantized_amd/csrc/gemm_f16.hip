@@ -206,9 +206,12 @@ __device__ __forceinline__ int find_gemm_item(const GemmGroup &grp, int tmg) {
 // x tiles go global -> LDS directly (16-byte LDS-DMA loads: lane i of a wave's load
 // lands at the destination + 16 i), NXB LDS buffers, each step's tile loaded NXB - 1
 // steps ahead.  A column's 64 k (128 bytes, 8 chunks of 16) sit unpadded, chunk ch of column c
-// at position ch ^ (c & 7), so that the MFMA operand reads (8 consecutive columns, one
-// chunk each) hit distinct banks; a load lane picks the global chunk that belongs at its
-// LDS position.
+// at position ch ^ ((c >> 1) & 7): a 16-byte operand read is served 16 lanes at a time
+// across the 64 banks, and the 16 consecutive columns of such a group (one chunk each)
+// then fall on 16 distinct 16-byte bank groups (an even and an odd column share no
+// group, and the 8 even or odd ones differ in c >> 1); a load lane picks the global chunk
+// that belongs at its LDS position.  (With ch ^ (c & 7) the groups of 16 met in pairs:
+// ~7x the bank-conflict cycles, measured.)
 // One 16-byte LDS-DMA load per lane: lane i's 16 bytes at src land at LDS byte address
 // lds + 16 i.  Issued as inline assembly so that the compiler does not track it: its
 // own wait insertion would otherwise make every later LDS read wait for all of these
@@ -347,15 +350,17 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
     };
 
     // ---- x loader: wave w fills columns 8NJ w .. 8NJ (w+1) - 1 of a tile, NJ LDS-DMA loads
-    // of 8 columns; lane i: column 8q + i/8 of them, LDS chunk position i%8, global chunk
-    // (i%8) ^ (i/8).  Columns past N read column 0 (outputs never stored); blocks past
-    // the split are clamped to its last block (loaded but never multiplied).
+    // of 8 columns; lane i: column c = 8NJ w + 8q + i/8, LDS chunk position i%8, global
+    // chunk (i%8) ^ ((c >> 1) & 7) (= (i%8) ^ (i/16 + 4 (q & 1)), NJ being even).  Columns
+    // past N read column 0 (outputs never stored); blocks past the split are clamped to its
+    // last block (loaded but never multiplied).
     const _Float16 *xsrc[NJ];
     {
-        const int cq = lane >> 3, ch = (lane & 7) ^ cq;
+        const int cq = lane >> 3;
 #pragma unroll
         for (int q = 0; q < NJ; ++q) {
             const int n = n0 + 8 * NJ * wave + 8 * q + cq;
+            const int ch = (lane & 7) ^ ((cq >> 1) | ((q & 1) << 2));
             xsrc[q] = x16 + (int64_t)xrow(n) * K + (int64_t)kb0 * GK + 8 * ch;
         }
     }
@@ -381,7 +386,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
     const uint32_t sh = (uint32_t)(lane >> 5) * 8u;
     int bsw[4];   // swizzled position (halves) of chunk 2kk + h of this lane's columns
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) bsw[kk] = 8 * ((2 * kk + (lane >> 5)) ^ (frow & 7));
+    for (int kk = 0; kk < 4; ++kk) bsw[kk] = 8 * ((2 * kk + (lane >> 5)) ^ ((frow >> 1) & 7));
     const PairMasks pm;
     const uint32_t *const wmy = warea + frow * kWRowDw;
     struct WStep {
@@ -583,9 +588,9 @@ static void launch_gemm_kernel(unsigned grid, hipStream_t s, const GemmGroup &gr
 // w of them takes (blocks per split) x step time(w).  A K split s adds its partials,
 // written by the GEMM (s N M floats at ~5 TB/s) and read back with the result written
 // by the reduction ((s + 1) N M floats at ~4.5 TB/s, plus its launch).  The constants
-// are fitted to the stack's shapes at N = 512 on MI355X, measured for every split: a
-// CU's throughput saturates from two workgroups on (0.62, 0.53 and 0.51 us per
-// 128-row workgroup-step with 1, 2 and 3 of them).  Candidates: A with s in
+// are fitted to kernel traces of the stack's shapes at N = 512 on MI355X for every split
+// (0.74, 0.60 and 0.58 us per 128-row workgroup-step with 1, 2 and 3 of them on a CU,
+// the busiest CU's partial writes included).  Candidates: A with s in
 // {1, 2, 3, 4, 6, 8} (s dividing the blocks, at least 8 per split and, for even block
 // counts, an even number), B without a split and only for an even block count.  Ties
 // keep the earlier candidate (smaller split, A).
@@ -593,8 +598,8 @@ struct GemmPlan {
     int cfg, splits;
 };
 constexpr double kStepUs[2][4] = {
-    {0.0, 0.62, 1.05, 1.54},   // A, by concurrent workgroups per CU
-    {0.0, 0.96, 1.71, 0.0},    // B
+    {0.0, 0.74, 1.20, 1.75},   // A, by concurrent workgroups per CU
+    {0.0, 1.00, 1.87, 0.0},    // B
 };
 constexpr int kPerCu[2] = {3, 2};
 constexpr double kPartWriteBytesPerUs = 5.0e6, kReduceBytesPerUs = 4.5e6, kReduceLaunchUs = 2.0;
