@@ -1,10 +1,15 @@
 """Build libq2_0.so (HIP for gfx950) in-tree with hipcc.
 
-Usage: python -m ternary_bit_quantized_amd.build
+Usage: python -m ternary_bit_quantized_amd.build [--sanitize]
 Every source in csrc/ is compiled for gfx950 only; object files go to _build/ at the
 repository root and the shared library next to this file.  The measurement kernels in
 ceilings/ (HBM read stream, MFMA loop, empty launch) become libq2_0_ceilings.so, which
 only the benchmark loads.
+
+--sanitize builds a second copy, _build/sanitize/libq2_0.so, whose host code carries
+AddressSanitizer and UndefinedBehaviorSanitizer checks (device code as usual).  It is for
+the host-side ABI tests: load it with Q2_0_LIB=<path> and the clang ASan runtime
+preloaded (sanitized_env() gives that environment).
 """
 
 from __future__ import annotations
@@ -69,6 +74,66 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SAN_DIR = os.path.join(BUILD, "sanitize")
+# host code only: each sanitizer flag applies to the host pass alone
+SAN_FLAGS = ["-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def asan_runtime() -> str:
+    """The ASan runtime of hipcc's clang (it carries the UBSan handlers too)."""
+    llvm = os.path.dirname(os.path.dirname(os.path.realpath(HIPCC)))
+    hits = sorted(glob.glob(os.path.join(llvm, "llvm", "lib", "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")) +
+                  glob.glob(os.path.join(llvm, "lib", "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")))
+    if not hits:
+        raise RuntimeError("no libclang_rt.asan-x86_64.so next to " + HIPCC)
+    return hits[-1]
+
+
+def sanitized_env(base=None) -> dict:
+    """Environment for a process that loads the sanitized library: the library path, the
+    ASan runtime ahead of any preload already set, leaks off (the interpreter is not
+    instrumented), every report fatal."""
+    env = dict(os.environ if base is None else base)
+    env["Q2_0_LIB"] = os.path.join(SAN_DIR, "libq2_0.so")
+    pre = env.get("LD_PRELOAD", "")
+    env["LD_PRELOAD"] = asan_runtime() + (":" + pre if pre else "")
+    env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=1"
+    env["UBSAN_OPTIONS"] = "halt_on_error=1:print_stacktrace=1"
+    return env
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    os.makedirs(SAN_DIR, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+    def comp(src):
+        obj = os.path.join(SAN_DIR, os.path.basename(src) + ".o")
+        cmd = [HIPCC, *FLAGS, *SAN_FLAGS, *PER_FILE.get(os.path.basename(src), []), "-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=COMPILE_TIMEOUT_S)
+        if r.returncode != 0:
+            raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(comp, srcs))
+    lib = os.path.join(SAN_DIR, "libq2_0.so")
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp, "-shared-libasan", *SAN_FLAGS[1:]]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=COMPILE_TIMEOUT_S)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
+    os.replace(tmp, lib)
+    if verbose:
+        print("built", lib)
+    return lib
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--sanitize" in sys.argv[1:]:
+        build_sanitized(verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)

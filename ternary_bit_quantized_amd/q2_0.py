@@ -12,7 +12,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libq2_0.so")
+# Q2_0_LIB names another build of the library (the sanitized host-only build of
+# ternary_bit_quantized_amd.build --sanitize, for the ABI tests); default: the in-tree one.
+LIB_PATH = os.environ.get("Q2_0_LIB") or os.path.join(PKG, "libq2_0.so")
 
 Q2_0_OK = 0
 Q2_0_ERR_NULL = 1
