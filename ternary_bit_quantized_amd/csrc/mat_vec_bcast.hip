@@ -241,73 +241,98 @@ __device__ __forceinline__ void bx_quarter(const uint32_t (&R)[20], const half4_
     }
 }
 
+// Max and sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15), the result in every
+// lane of the row: four rotations within the row (row_ror 8, 4, 2, 1), each a VALU
+// operation, where lane exchanges through the LDS unit cost ~100 cycles apiece.
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x120 + N, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, row_ror<8>(v));
+    v = fmaxf(v, row_ror<4>(v));
+    v = fmaxf(v, row_ror<2>(v));
+    return fmaxf(v, row_ror<1>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += row_ror<8>(v);
+    v += row_ror<4>(v);
+    v += row_ror<2>(v);
+    return v + row_ror<1>(v);
+}
+
 // Exact-mode staging of one activation column for blocks 0..nb-1: limb entries
 // (blk*16 + c)*4 + l (half4 of chunk c = 4u + t, limb l, in the weight order of
 // bx_dword, each element times bx_factor), and per block bs = -2^-20 sum L per limb
-// (NaN for limb 0 when the block holds a non-finite activation) and bsc = 2^(20-e).  One thread per chunk,
-// the loads of two passes issued before either is converted;
-// the 16 chunks of a block sit in 16 consecutive lanes, which reduce the block's
-// maximum and limb sums with lane exchanges.
+// (NaN for limb 0 when the block holds a non-finite activation) and bsc = 2^(20-e).  One
+// thread per chunk, in passes of kLimbU * nthreads chunks whose loads are all issued
+// before any is converted (limbs_load, then limbs_convert; the kernel issues its first
+// weight loads between the two halves of the first pass).  The 16 chunks of a block sit
+// in the 16 lanes of a DPP row, which reduce the block's maximum and limb sums (exactly:
+// the limbs are integers below 2^12 and a block's sums stay below 2^18, so any order of
+// the additions gives the same sum).
+constexpr int kLimbU = 2;
+struct LimbLoads {
+    float2_t a[kLimbU], b[kLimbU];
+};
+
 template <typename XT>
-__device__ __forceinline__ void stage_x_limbs(const XT *__restrict__ x, int nb, half4_t *lds_x, float4_t *lds_bs,
-                                              float *lds_bsc, int tid, int nthreads) {
-    constexpr int U = 2;   // passes whose loads are issued before any is converted
+__device__ __forceinline__ void limbs_load(const XT *__restrict__ x, int nb, int q0, int tid, int nthreads,
+                                           LimbLoads &L) {
     const int items = nb * 16;
-    for (int q0 = 0; q0 < items; q0 += U * nthreads) {   // the same trip count in every lane
-        float2_t a[U], b[U];
 #pragma unroll
-        for (int k = 0; k < U; ++k) {
-            const int q = min(q0 + k * nthreads + tid, items - 1);
-            const int c = q % 16, blk = q / 16;
-            const int u = c >> 2, t = c & 3, odd = blk & 1;
-            const XT *xb = x + (int64_t)blk * kBlockWeights + 2 * t;
-            a[k] = load_act2(xb + 8 * half_lo(u, odd));
-            b[k] = load_act2(xb + 8 * half_hi(u, odd));
+    for (int k = 0; k < kLimbU; ++k) {
+        const int q = min(q0 + k * nthreads + tid, items - 1);
+        const int c = q % 16, blk = q / 16;
+        const int u = c >> 2, t = c & 3, odd = blk & 1;
+        const XT *xb = x + (int64_t)blk * kBlockWeights + 2 * t;
+        L.a[k] = load_act2(xb + 8 * half_lo(u, odd));
+        L.b[k] = load_act2(xb + 8 * half_hi(u, odd));
+    }
+}
+
+__device__ __forceinline__ void limbs_convert(int nb, int q0, int tid, int nthreads, const LimbLoads &L,
+                                              half4_t *lds_x, float4_t *lds_bs, float *lds_bsc) {
+    const int items = nb * 16;
+#pragma unroll
+    for (int k = 0; k < kLimbU; ++k) {
+        if (q0 + k * nthreads >= items) break;      // uniform: whole passes are in or out
+        const int q = min(q0 + k * nthreads + tid, items - 1);
+        const bool act = q0 + k * nthreads + tid < items;   // whole 16-lane groups are active or not
+        const int c = q % 16, blk = q / 16;
+        const int t = c & 3;
+        const float v[4] = {L.a[k].x, L.b[k].x, L.a[k].y, L.b[k].y};
+        const float m = row16_max(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+        const bool finite = m <= 3.4028234663852886e38f;   // false for inf and NaN
+        const int e = (finite && m > 0.f) ? 11 - __builtin_amdgcn_frexp_expf(m) : 0;
+        float lim[4][4], sum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            float w = finite ? __builtin_amdgcn_ldexpf(v[kk], e) : 0.f;
+#pragma unroll
+            for (int l = 0; l < 4; ++l) {
+                const float Lr = __builtin_rintf(w);
+                w = (w - Lr) * 2048.f;   // exact: the remainder of a rounded f32 and a power of two
+                lim[l][kk] = Lr;
+                sum[l] += Lr;
+            }
+        }
+        if (act) {
+#pragma unroll
+            for (int l = 0; l < 4; ++l) {
+                half4_t h;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) h[kk] = (_Float16)(lim[l][kk] * bx_factor(t, kk));
+                lds_x[(blk * 16 + c) * 4 + l] = h;
+            }
         }
 #pragma unroll
-        for (int k = 0; k < U; ++k) {
-            if (q0 + k * nthreads >= items) break;      // uniform: whole passes are in or out
-            const int q = min(q0 + k * nthreads + tid, items - 1);
-            const bool act = q0 + k * nthreads + tid < items;   // whole 16-lane groups are active or not
-            const int c = q % 16, blk = q / 16;
-            const int t = c & 3;
-            const float v[4] = {a[k].x, b[k].x, a[k].y, b[k].y};
-            float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
-            const bool finite = m <= 3.4028234663852886e38f;   // false for inf and NaN
-            const int e = (finite && m > 0.f) ? 11 - __builtin_amdgcn_frexp_expf(m) : 0;
-            float lim[4][4], sum[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                float w = finite ? __builtin_amdgcn_ldexpf(v[kk], e) : 0.f;
-#pragma unroll
-                for (int l = 0; l < 4; ++l) {
-                    const float L = __builtin_rintf(w);
-                    w = (w - L) * 2048.f;   // exact: the remainder of a rounded f32 and a power of two
-                    lim[l][kk] = L;
-                    sum[l] += L;
-                }
-            }
-            if (act) {
-#pragma unroll
-                for (int l = 0; l < 4; ++l) {
-                    half4_t h;
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) h[kk] = (_Float16)(lim[l][kk] * bx_factor(t, kk));
-                    lds_x[(blk * 16 + c) * 4 + l] = h;
-                }
-            }
-#pragma unroll
-            for (int l = 0; l < 4; ++l)
-#pragma unroll
-                for (int off = 1; off < 16; off <<= 1) sum[l] += __shfl_xor(sum[l], off);
-            if (act && c == 0) {
-                const float nan = __builtin_nanf("");
-                lds_bs[blk] = float4_t{finite ? -sum[0] * 9.5367431640625e-7f : nan, -sum[1] * 9.5367431640625e-7f,
-                                       -sum[2] * 9.5367431640625e-7f, -sum[3] * 9.5367431640625e-7f};   // 2^-20
-                lds_bsc[blk] = __builtin_amdgcn_ldexpf(1.f, 20 - e);
-            }
+        for (int l = 0; l < 4; ++l) sum[l] = row16_sum(sum[l]);
+        if (act && c == 0) {
+            const float nan = __builtin_nanf("");
+            lds_bs[blk] = float4_t{finite ? -sum[0] * 9.5367431640625e-7f : nan, -sum[1] * 9.5367431640625e-7f,
+                                   -sum[2] * 9.5367431640625e-7f, -sum[3] * 9.5367431640625e-7f};   // 2^-20
+            lds_bsc[blk] = __builtin_amdgcn_ldexpf(1.f, 20 - e);
         }
     }
 }
@@ -522,14 +547,23 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_bcast(MvGroup grp, MvSegs s
     }
         // the first stages are issued before the window is staged, so that their latency
         // overlaps the staging
+        // (exact mode: the window's first activation loads go out before them, so that the
+        // staging waits for those alone)
+        const XT *const xw = x + (int64_t)blk0 * kBlockWeights;
+        const int nbw = min(sp * kBcSB, nb - blk0);
+        LimbLoads xld;
+        if (EXACT) limbs_load(xw, nbw, 0, tid, WAVES * 64, xld);
         if (n > 0) {
             Q2_0_ISSUE_NEXT(ra)
             if (DEPTH == 2) Q2_0_ISSUE_NEXT(rb)
         }
-        if (EXACT)
-            stage_x_limbs(x + (int64_t)blk0 * kBlockWeights, min(sp * kBcSB, nb - blk0), lds_x, lds_bs, lds_bsc,
-                          tid, WAVES * 64);
-        else
+        if (EXACT) {
+            limbs_convert(nbw, 0, tid, WAVES * 64, xld, lds_x, lds_bs, lds_bsc);
+            for (int q0 = kLimbU * WAVES * 64; q0 < nbw * 16; q0 += kLimbU * WAVES * 64) {
+                limbs_load(xw, nbw, q0, tid, WAVES * 64, xld);
+                limbs_convert(nbw, q0, tid, WAVES * 64, xld, lds_x, lds_bs, lds_bsc);
+            }
+        } else
             stage_x_bcast<NC>(x + (int64_t)blk0 * kBlockWeights, ldx, min(sp * kBcSB, nb - blk0), lds_e, lds_x, tid,
                               WAVES * 64);
         __syncthreads();
