@@ -517,7 +517,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_bcast(MvGroup grp, MvSegs s
     for (int p = 0; p < P; ++p) {   // the same trip count in every wave: the barriers need it
         const int sw0 = p * W;                               // first stage of the window
         const int sp = min(W, ns - sw0);
-        const uint32_t mag = p + 1 < P ? seg.mag_w : seg.mag_last;   // divides by sp (below 2^29)
+        const uint32_t mag = p + 1 < P ? seg.mag_w : seg.mag_last;   // divides by sp (below 2^28)
         const int blk0 = sw0 * kBcSB;
         // this wave's items of the phase: (tile, stage) pairs i0 .. i1-1 of the workgroup's
         // nt * sp, tile-major
@@ -676,16 +676,21 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_bcast(MvGroup grp, MvSegs s
 
 namespace {
 
-constexpr int kBcMaxWindowStages = 6;   // activation staged 96 blocks (6144 k) at a time
-static_assert(kBcMaxWindowStages <= 8, "the kernel's multiply-high division covers at most 8 stages");
+// Window sizes: as many stages as the LDS left beside the wave tiles holds, up to 16 (the
+// kernel's multiply-high division by the window's stages is exact for item counts below
+// 2^28 up to 16 stages); where some row needs several windows, 16 KB stay free for the
+// tile accumulator.  (16 waves: 8 stages, 6 when phased; 8 waves: 13 stages, e.g. a
+// 12288-long row in one window; 4 waves: 16.)
+constexpr int kBcMaxWindowStages = 16;
+constexpr size_t kBcTaccReserve = 16 * 1024;
 
 size_t x_bytes_per_block(int N, bool exact) { return exact ? 16 * 4 * 8 + 16 + 4 : (size_t)16 * 2 * N * 8; }
 
-// Stages per window for a row of nb blocks: the fewest windows of at most
-// kBcMaxWindowStages stages, as even as possible.
-int window_stages(int nb) {
+// Stages per window for a row of nb blocks: the fewest windows of at most cap stages, as
+// even as possible.
+int window_stages(int nb, int cap) {
     const int ns = (nb + kBcSB - 1) / kBcSB;
-    const int P = (ns + kBcMaxWindowStages - 1) / kBcMaxWindowStages;
+    const int P = (ns + cap - 1) / cap;
     return (ns + P - 1) / P;
 }
 
@@ -732,26 +737,39 @@ hipError_t launch_mat_vec_bcast(const MvGroup &grp, const MvSegDesc *d, int nseg
     segs.n = nsegs;
     segs.xcap = 0;
     int64_t items = 0;
-    bool phased = false;
+    int ns_max = 0;
     for (int i = 0; i < nsegs; ++i) {
         if (d[i].nb % 8 != 0 || d[i].tile1 <= d[i].tile0) return hipErrorInvalidValue;
+        const int ns = (d[i].nb + kBcSB - 1) / kBcSB;
+        ns_max = std::max(ns_max, ns);
+        items += (int64_t)(d[i].tile1 - d[i].tile0) * ns;
+    }
+    // Waves per workgroup: 16 (one workgroup per CU); small launches use fewer until
+    // there is a workgroup per CU.
+    int waves = kMvStreamMaxWaves;   // a power of two (the kernel splits work by shifts)
+    while (waves > 4 && (items + waves - 1) / waves < 256) waves /= 2;
+    // windows: whole rows where the LDS left holds them all, else at most cap_phased stages
+    const int64_t per_stage = (int64_t)kBcSB * (int64_t)x_bytes_per_block(N, exact);
+    const int64_t avail = (int64_t)160 * 1024 - (int64_t)waves * (kBcWaveLds + 64 * 8) - (int64_t)kMvStreamStaticLds;
+    const int cap_full = (int)std::min<int64_t>(kBcMaxWindowStages, avail / per_stage);
+    const int cap_phased =
+        (int)std::min<int64_t>(kBcMaxWindowStages, (avail - (int64_t)kBcTaccReserve) / per_stage);
+    const int cap = ns_max <= cap_full ? cap_full : cap_phased;
+    if (cap < 1) return hipErrorInvalidValue;
+    bool phased = false;
+    for (int i = 0; i < nsegs; ++i) {
         MvSeg &g = segs.s[i];
         g.x = d[i].x;
         g.ldx = d[i].ldx;
         g.nb = d[i].nb;
-        g.ws = window_stages(d[i].nb);
+        g.ws = window_stages(d[i].nb, cap);
         g.tile0 = d[i].tile0;
         g.tile1 = d[i].tile1;
         const int ns = (g.nb + kBcSB - 1) / kBcSB;
         segs.xcap = std::max(segs.xcap, std::min(g.ws * kBcSB, g.nb));
         phased = phased || g.ws < ns;
-        items += (int64_t)(g.tile1 - g.tile0) * ns;
     }
     for (int i = nsegs; i < kMvMaxSegs; ++i) segs.s[i] = MvSeg{nullptr, 0, 8, 1, 0, 0, 0x7fffffff, 0, 0, 0, 1u, 1u};
-    // Waves per workgroup: 16 (one workgroup per CU); small launches use fewer until
-    // there is a workgroup per CU.
-    int waves = kMvStreamMaxWaves;   // a power of two (the kernel splits work by shifts)
-    while (waves > 4 && (items + waves - 1) / waves < 256) waves /= 2;
     const size_t fixed = mat_vec_bcast_lds(N, segs.xcap, 0, waves, exact) + kMvStreamStaticLds;
     if (fixed > 160 * 1024) return hipErrorInvalidValue;
     // the tile accumulator of phased segments takes what LDS is left
@@ -774,8 +792,8 @@ hipError_t launch_mat_vec_bcast(const MvGroup &grp, const MvSegDesc *d, int nseg
         g.r = (int)(T % n);
         wg += (int)n;
         if (g.ws < ns) tacc = std::max(tacc, (int)((T + n - 1) / n));
-        // the kernel divides item counts below 2^29 by at most 8 stages with a multiply-high
-        if ((int64_t)(g.q + 1) * g.ws >= ((int64_t)1 << 29)) return hipErrorInvalidValue;
+        // the kernel divides item counts below 2^28 by at most 16 stages with a multiply-high
+        if ((int64_t)(g.q + 1) * g.ws >= ((int64_t)1 << 28)) return hipErrorInvalidValue;
         const int last = ns - (ns + g.ws - 1) / g.ws * g.ws + g.ws;   // stages of the last window
         g.mag_w = (uint32_t)(0xffffffffu / (uint32_t)g.ws) + 1u;
         g.mag_last = (uint32_t)(0xffffffffu / (uint32_t)last) + 1u;

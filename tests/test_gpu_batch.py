@@ -3,7 +3,8 @@ batched entry point whose items each carry their own K and activation, against t
 oracle.
 
   * K from 7168 to 16384 at N = 1 and 2: two and three windows, a ragged half stage in the
-    last window (K / 64 = 136), 16-row tiles whose windows fall to different waves;
+    last window (K / 64 = 136), 16-row tiles whose windows fall to different waves, and
+    (fewer rows, smaller workgroups) whole rows in one window;
   * q2_0_mul_mat_vec_batch: a decode-step-like batch (K = 4096 and 12288 activations, a
     vocabulary-sized head), more than eight activations (several launches), more than 64
     items, items the fast kernels cannot take in the middle, and 16-bit activations;
@@ -32,8 +33,10 @@ def sample_rows(M, step=53):
 
 @pytest.mark.parametrize("K", [7168, 8704, 12288, 16384])
 @pytest.mark.parametrize("N", [1, 2])
-def test_windowed_mat_vec_long_rows(K, N):
-    M = 16400
+@pytest.mark.parametrize("M", [16400, 4100, 1000])
+def test_windowed_mat_vec_long_rows(K, N, M):
+    """M = 16400: 16-wave workgroups, rows in windows of at most 6 stages; 4100 and 1000:
+    8- and 4-wave workgroups, whose LDS holds a whole row of up to 13 and 16 stages."""
     w = tern(K % 97, M, K)
     x = synth.activations(81, K, N, N, K)
     y = run_mat_vec(dev(w), M, K, x)
