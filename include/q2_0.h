@@ -8,7 +8,7 @@
  *   - bytes 0-1: the scale d, IEEE half precision, little-endian;
  *   - bytes 2-17: four little-endian 32-bit words; code i of word w is bits
  *     2i..2i+1 and belongs to weight 16w+i;
- *   - a code q decodes to (q - 1) * d, i.e. -d, 0, d, 2d (code 3 is reserved by
+ *   - code q stands for the weight (q - 1) * d, i.e. -d, 0, d, 2d (code 3 is reserved by
  *     the model card but decodes to 2d and is accepted).
  *
  * Matrix layout used by every entry point:
@@ -80,8 +80,8 @@ typedef enum {
 
 /*
  * get_rows: gather rows of a Q2_0 matrix and dequantize them to f32
- * (bisque.today "WebGPU: add Q2_0 support": the get-rows shader copies rows out
- * of a Q2_0 tensor and writes 64 floats per block).
+ * (bisque.today "WebGPU: add Q2_0 support", the paragraph on its three shaders:
+ * the gather shader expands each selected row to f32, one block of 64 at a time).
  *   w      : M x K Q2_0 matrix (layout above), 2-byte aligned.
  *   ids    : n_ids int32 row indices, device memory, 4-byte aligned.
  *   out    : n_ids rows of K floats; row r starts at out + r*ld_out (ld_out >= K).
@@ -173,8 +173,9 @@ int q2_0_mul_mat_vec_batch(const q2_0_mat_vec_batch_item *items, int64_t n_items
 
 /*
  * mul_mat: y = W x for any N (batched prefill GEMM).
- * (bisque.today "WebGPU: add Q2_0 support": the tiled matrix multiply unpacks 16
- * codes per thread into shared memory as half precision.)
+ * (bisque.today "WebGPU: add Q2_0 support", the paragraph on its three shaders:
+ * its tiled GEMM expands the codes to fp16 weights in workgroup memory, sixteen
+ * per thread.)
  *   Layouts and alignment as for q2_0_mul_mat_vec; precision is a q2_0_precision.
  *   Q2_0_PREC_F16_MFMA (fast):
  *     N <= 8 runs the mat-vec: its fp32-grade bound under its range condition.

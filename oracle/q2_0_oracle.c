@@ -10,7 +10,7 @@
  *       the paragraph on the block format (64 weights in 18 bytes, a half
  *       precision scale d first, then four 32-bit words of sixteen 2-bit codes,
  *       code q decodes to (q - 1) * d) and the paragraph on the mat-vec kernel
- *       (code i of a word is shifted out two bits at a time; the scale is applied
+ *       (the codes of a word are taken two bits apiece, lowest first; the scale is applied
  *       once per block, after the sum of (q - 1) * x).
  *  [P3] aisvetem.cz, "Llama.cpp umi dvoubitovy Q2_0 i na kartach NVIDIA",
  *       section "Osmnact bajtu na ctyriasedesat vah" (18 bytes / 64 weights /

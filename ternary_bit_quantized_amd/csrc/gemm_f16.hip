@@ -1,8 +1,9 @@
 // Prefill GEMM on the gfx950 matrix cores: y[n][m] = sum_k W[m][k] x[n][k] with W in
 // Q2_0, x rounded to fp16, f32 accumulation.
 //
-// bisque.today "WebGPU: add Q2_0 support": the tiled matrix multiply unpacks 16
-// codes per thread into shared memory as half precision.  Here no fp16 copy of W is
+// bisque.today "WebGPU: add Q2_0 support", the paragraph on its three shaders: its
+// tiled GEMM expands the codes to fp16 weights in workgroup memory, sixteen per
+// thread, and multiplies from there.  Here no fp16 copy of W is
 // made: every wave owns whole rows of the tile and unpacks them straight into its MFMA
 // A operands as fp16 d*(q-1) -- exact, because d is a half and |q-1| <= 2 -- using the
 // fp16-pair decode of the mat-vec (OR the code under a magic exponent, one packed

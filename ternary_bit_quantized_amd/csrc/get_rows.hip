@@ -1,7 +1,8 @@
 // get_rows: gather Q2_0 rows and dequantize them to f32, bit-exact.
 //
-// bisque.today, "WebGPU: add Q2_0 support": the get-rows shader copies rows out of
-// a Q2_0 tensor and writes 64 floats per block; a code q decodes to (q - 1) * d.
+// bisque.today, "WebGPU: add Q2_0 support", the paragraph on its three shaders: the
+// gather shader expands selected rows to f32, 64 values per block, code q giving the
+// weight (q - 1) * d.
 //
 // One thread per 32-bit code word (16 weights): it reads the block's half scale and
 // its word, and writes 16 floats as 4 x 16-byte stores when the output row allows.

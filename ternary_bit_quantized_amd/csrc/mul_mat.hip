@@ -1,8 +1,9 @@
 // mul_mat fp32 fallback: batched Q2_0 x F32 GEMM, y[n][m] = sum_k W[m][k] x[n][k],
 // fp32-grade (the fp16-MFMA GEMM is gemm_f16.hip).
 //
-// bisque.today, "WebGPU: add Q2_0 support": the tiled matrix multiply unpacks 16
-// codes per thread into shared memory; here four threads per row each unpack one
+// bisque.today, "WebGPU: add Q2_0 support", the paragraph on its three shaders: its
+// tiled GEMM expands sixteen codes per thread into workgroup memory; here four
+// threads per row each unpack one
 // 32-bit word of the row's block into an LDS tile.
 //
 //  * gemm_f32: the accuracy fallback.  W is kept as f32 (q-1) with the block scale

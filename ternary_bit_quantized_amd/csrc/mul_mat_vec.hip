@@ -1,9 +1,9 @@
 // mul_mat_vec: y = W x for N = 1..8 activation columns, fp32-grade.
 //
-// bisque.today, "WebGPU: add Q2_0 support", the matrix-vector paragraph: a block's
-// 64 weights are split over four threads of 16 weights each; a thread loads the
-// block's scale and one 32-bit word, accumulates (q - 1) * x over its 16 codes and
-// multiplies that partial sum by the scale once.
+// bisque.today, "WebGPU: add Q2_0 support", the matrix-vector paragraph: there each
+// block goes to four threads, one 32-bit code word (16 weights) apiece; every thread
+// fetches the scale with its word, sums (q - 1) * x over its 16 codes and applies the
+// scale to that partial sum a single time.
 //
 // Generic kernel (any row alignment, any K): one wave per output row; lane l takes
 // code words l, l+64, ... of the row, forms the 16-term partial sum per column in
