@@ -354,8 +354,14 @@ struct MvSegs {
 
 size_t mat_vec_stream_lds(int N, int nb, int waves);
 int mat_vec_stream_waves(int N, int nb, int *resident);
+// rowstride: bytes between rows (0: nb * 18); accumulate: add to y instead of writing it
 hipError_t launch_mat_vec_stream(const MvGroup &grp, int nb, const void *x, Act xt, int64_t ldx, int N,
-                                 hipStream_t s);
+                                 hipStream_t s, uint32_t rowstride = 0, int accumulate = 0);
+// N >= 3, any K: one launch where the whole activation fits in LDS, else consecutive launches
+// over chunks of mat_vec_stream_chunk_blocks(N, nb) blocks (0: not even one stage fits)
+int mat_vec_stream_chunk_blocks(int N, int nb);
+hipError_t launch_mat_vec_stream_chunked(const MvGroup &grp, int nb, const void *x, Act xt, int64_t ldx, int N,
+                                         hipStream_t s);
 // N = 1, 2; grp counts tiles of kMvBcastRows rows; nsegs <= kMvMaxSegs segments.  Any K
 // (the activation is staged in windows); rows and activations 16-byte aligned, nb % 8 == 0.
 size_t mat_vec_bcast_lds(int N, int xcap, int tacc, int waves, bool exact);

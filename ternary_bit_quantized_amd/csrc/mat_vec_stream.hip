@@ -28,6 +28,10 @@
 //  * One launch may cover several matrices that share K and the activation (for
 //    example the q, k, v projections, or gate and up): tiles are numbered across
 //    the group and a wave looks its matrix up once per tile.
+//  * A K too long for its activation to fit in LDS is run as consecutive launches over
+//    chunks of whole stages: a launch reads nb blocks of each row (rows rowstride
+//    bytes apart), and every chunk after the first adds its results to y, in chunk
+//    order (deterministic; each chunk scales its activation by its own exponent).
 #include <atomic>
 
 #include "q2_0_internal.h"
@@ -46,7 +50,7 @@ struct Item {
 template <int NC, int SB, typename XT>
 __global__ __launch_bounds__(kMvStreamMaxWaves * 64)
 __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_stream(MvGroup grp, int nb, const XT *__restrict__ x,
-                                                      int64_t ldx) {
+                                                      int64_t ldx, uint32_t rowstride, int accumulate) {
     constexpr int NR = 2 * NC;
     constexpr int RSB = SB * kBlockBytes + 16;
     constexpr int CPR = SB * kBlockBytes / 16;        // 16-byte chunks per row of a full stage
@@ -74,7 +78,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_stream(MvGroup grp, int nb,
     const int total = grp.total_tiles;
     const int t0v = load_tile_table(grp);   // the tile table, one entry per lane
     const int ns = (nb + SB - 1) / SB;
-    const uint32_t rowbytes = (uint32_t)nb * kBlockBytes;
+    const uint32_t rowbytes = rowstride;   // bytes from one row to the next (nb blocks of each are read)
     const bool ragged = (nb % SB) != 0;   // the last stage of a row holds SB/2 blocks
 
     // This workgroup's tiles [tb0, tb1) and this wave's items [i0, i1) among them.
@@ -176,8 +180,10 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_stream(MvGroup grp, int nb,
     auto store_tile = [&](const TileRef &tr, float r0, float r1) {
         const int row = tr.m0 + j;
         if (row < tr.M) {
-            if (2 * g < NC) tr.y[(int64_t)(2 * g) * tr.ldy + row] = __builtin_amdgcn_ldexpf(r0, ye0);
-            if (2 * g + 1 < NC) tr.y[(int64_t)(2 * g + 1) * tr.ldy + row] = __builtin_amdgcn_ldexpf(r1, ye1);
+            float *const y0 = tr.y + (int64_t)(2 * g) * tr.ldy + row;
+            float *const y1 = tr.y + (int64_t)(2 * g + 1) * tr.ldy + row;
+            if (2 * g < NC) *y0 = (accumulate ? *y0 : 0.f) + __builtin_amdgcn_ldexpf(r0, ye0);
+            if (2 * g + 1 < NC) *y1 = (accumulate ? *y1 : 0.f) + __builtin_amdgcn_ldexpf(r1, ye1);
         }
     };
 
@@ -282,8 +288,8 @@ int mat_vec_stream_waves(int N, int nb, int *resident) {
 }
 
 template <int NC, typename XT>
-static hipError_t launch_stream_nc(const MvGroup &grp, int nb, const XT *x, int64_t ldx,
-                                   hipStream_t s, int grid, int waves) {
+static hipError_t launch_stream_nc(const MvGroup &grp, int nb, const XT *x, int64_t ldx, uint32_t rowstride,
+                                   int accumulate, hipStream_t s, int grid, int waves) {
     constexpr int SB = kMvStreamSB;
     const size_t lds = mat_vec_stream_lds(NC, nb, waves);
     auto kern = mat_vec_stream<NC, SB, XT>;
@@ -303,12 +309,13 @@ static hipError_t launch_stream_nc(const MvGroup &grp, int nb, const XT *x, int6
         if (e != hipSuccess) return e;
         if (dev >= 0 && dev < 64) configured[dev].store(true, std::memory_order_release);
     }
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * waves), lds, s, grp, nb, x, ldx);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * waves), lds, s, grp, nb, x, ldx, rowstride, accumulate);
     return hipGetLastError();
 }
 
 hipError_t launch_mat_vec_stream(const MvGroup &grp, int nb, const void *xv, Act xt, int64_t ldx, int N,
-                                 hipStream_t s) {
+                                 hipStream_t s, uint32_t rowstride, int accumulate) {
+    if (rowstride == 0) rowstride = (uint32_t)nb * kBlockBytes;
     int waves = mat_vec_stream_waves(N, nb, nullptr);
     if (waves == 0) return hipErrorInvalidValue;
     // Small launches: fewer waves per workgroup until there is a workgroup per CU.
@@ -326,17 +333,52 @@ hipError_t launch_mat_vec_stream(const MvGroup &grp, int nb, const void *xv, Act
         using XT = decltype(tag);
         const XT *x = static_cast<const XT *>(xv);
         switch (N) {
-            case 1: return launch_stream_nc<1>(grp, nb, x, ldx, s, grid, waves);
-            case 2: return launch_stream_nc<2>(grp, nb, x, ldx, s, grid, waves);
-            case 3: return launch_stream_nc<3>(grp, nb, x, ldx, s, grid, waves);
-            case 4: return launch_stream_nc<4>(grp, nb, x, ldx, s, grid, waves);
-            case 5: return launch_stream_nc<5>(grp, nb, x, ldx, s, grid, waves);
-            case 6: return launch_stream_nc<6>(grp, nb, x, ldx, s, grid, waves);
-            case 7: return launch_stream_nc<7>(grp, nb, x, ldx, s, grid, waves);
-            case 8: return launch_stream_nc<8>(grp, nb, x, ldx, s, grid, waves);
+            case 1: return launch_stream_nc<1>(grp, nb, x, ldx, rowstride, accumulate, s, grid, waves);
+            case 2: return launch_stream_nc<2>(grp, nb, x, ldx, rowstride, accumulate, s, grid, waves);
+            case 3: return launch_stream_nc<3>(grp, nb, x, ldx, rowstride, accumulate, s, grid, waves);
+            case 4: return launch_stream_nc<4>(grp, nb, x, ldx, rowstride, accumulate, s, grid, waves);
+            case 5: return launch_stream_nc<5>(grp, nb, x, ldx, rowstride, accumulate, s, grid, waves);
+            case 6: return launch_stream_nc<6>(grp, nb, x, ldx, rowstride, accumulate, s, grid, waves);
+            case 7: return launch_stream_nc<7>(grp, nb, x, ldx, rowstride, accumulate, s, grid, waves);
+            case 8: return launch_stream_nc<8>(grp, nb, x, ldx, rowstride, accumulate, s, grid, waves);
             default: return hipErrorInvalidValue;
         }
     });
+}
+
+// Blocks per chunk for a K whose activation does not fit: the largest multiple of 16
+// blocks that still leaves 8 or more waves resident per CU, evened out over the chunks
+// it takes; 0 if even one stage does not.  (Fewer, longer launches: at N = 8 and K =
+// 6144, two chunks of 48 blocks at 8 waves per CU took 84 us for 198 MB where three of
+// 32 at 16 waves took 92.)
+int mat_vec_stream_chunk_blocks(int N, int nb) {
+    int cb = nb / kMvStreamSB * kMvStreamSB;
+    for (; cb >= kMvStreamSB; cb -= kMvStreamSB) {
+        int resident = 0;
+        if (mat_vec_stream_waves(N, cb, &resident) > 0 && resident >= 8) break;
+    }
+    if (cb < kMvStreamSB) return 0;
+    const int chunks = (nb + cb - 1) / cb;
+    const int even = (nb + chunks - 1) / chunks;
+    return (even + kMvStreamSB - 1) / kMvStreamSB * kMvStreamSB;
+}
+
+hipError_t launch_mat_vec_stream_chunked(const MvGroup &grp, int nb, const void *xv, Act xt, int64_t ldx, int N,
+                                         hipStream_t s) {
+    int resident = 0;
+    if (mat_vec_stream_waves(N, nb, &resident) > 0 && resident >= 8)
+        return launch_mat_vec_stream(grp, nb, xv, xt, ldx, N, s, 0, 0);
+    const int cb = mat_vec_stream_chunk_blocks(N, nb);
+    if (cb == 0) return hipErrorInvalidValue;
+    const uint32_t rowstride = (uint32_t)nb * kBlockBytes;
+    for (int c0 = 0; c0 < nb; c0 += cb) {
+        MvGroup g = grp;
+        for (int i = 0; i < g.n; ++i) g.p[i].w += (size_t)c0 * kBlockBytes;
+        const void *xc = static_cast<const uint8_t *>(xv) + (size_t)c0 * kBlockWeights * act_bytes(xt);
+        const hipError_t e = launch_mat_vec_stream(g, std::min(cb, nb - c0), xc, xt, ldx, N, s, rowstride, c0 > 0);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace q2_0

@@ -86,14 +86,17 @@ constexpr int64_t kStreamRows = 16384;
 static int stream_tile_rows(int N) { return N <= 2 ? kMvBcastRows : kMvTile; }
 
 // The broadcast kernel (N <= 2) stages the activation in windows, so every K fits; the
-// 16-row-tile kernel (N >= 3) stages all of K and is used where that still leaves 8 or
-// more resident waves per CU (the K-split kernel otherwise).
+// 16-row-tile kernel (N >= 3) stages all of K where that still leaves 8 or more resident
+// waves per CU (groups and batches go through it only then), and a single matrix of at
+// least kStreamRows rows with a longer K runs it over chunks of whole stages.  Smaller
+// matrices with such a K take the K-split kernel, faster there than chunked launches.
 static bool stream_fits(int N, int nb) {
     if (N <= 2) return true;
     int resident = 0;
     const int waves = mat_vec_stream_waves(N, nb, &resident);
     return waves > 0 && resident >= 8;
 }
+static bool stream_fits_chunked(int N, int nb) { return stream_fits(N, nb) || mat_vec_stream_chunk_blocks(N, nb) > 0; }
 
 // grp counts tiles of stream_tile_rows(N) rows; all its matrices share x
 static hipError_t launch_streaming(const MvGroup &grp, int nb, const void *x, Act xt, int64_t ldx, int N,
@@ -102,13 +105,13 @@ static hipError_t launch_streaming(const MvGroup &grp, int nb, const void *x, Ac
         const MvSegDesc d{x, ldx, nb, 0, grp.total_tiles};
         return launch_mat_vec_bcast(grp, &d, 1, xt, N, s);
     }
-    return launch_mat_vec_stream(grp, nb, x, xt, ldx, N, s);
+    return launch_mat_vec_stream_chunked(grp, nb, x, xt, ldx, N, s);
 }
 
 hipError_t launch_mat_vec(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx, int N,
                           float *y, int64_t ldy, hipStream_t s) {
     if (mat_vec_mfma_eligible(w, M, nb, x, xt, ldx)) {
-        if (M >= kStreamRows && stream_fits(N, nb)) {
+        if (M >= kStreamRows && stream_fits_chunked(N, nb)) {
             const int tr = stream_tile_rows(N);
             MvGroup grp;
             grp.n = 1;
@@ -227,7 +230,7 @@ hipError_t launch_mat_vec_batch(const q2_0_mat_vec_batch_item *items, int64_t n_
             for (int k = grp.n; k <= kMvMaxGroup; ++k) grp.tile0[k] = INT_MAX;
             grp.total_tiles = tiles;
             const hipError_t e = N <= 2 ? launch_mat_vec_bcast(grp, segs, nsegs, xt, N, s)
-                                        : launch_mat_vec_stream(grp, segs[0].nb, segs[0].x, xt, segs[0].ldx, N, s);
+                                        : launch_mat_vec_stream_chunked(grp, segs[0].nb, segs[0].x, xt, segs[0].ldx, N, s);
             if (e != hipSuccess) return e;
         }
     }
