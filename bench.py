@@ -115,7 +115,7 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--layers", type=int, default=36, help="stack layers (36 = the full model)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -458,6 +458,10 @@ def main():
         launch_us = float(np.mean([evs[i].elapsed_time(evs[i + 1]) for i in range(1, 2 * args.steps)])) * 1e3
 
     ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in parts if ev[n]}
+    ms_stats = {n: {"min": round(float(np.min([a.elapsed_time(b) for a, b in ev[n]])), 4),
+                    "median": round(float(np.median([a.elapsed_time(b) for a, b in ev[n]])), 4),
+                    "samples": len(ev[n])}
+                for n in ("prefill_gemm", "decode_mat_vec", "decode_mat_vec_per_layer") if n in ev and ev[n]}
     if set(step_parts) != {"prefill_get_rows", "prefill_gemm", "decode_get_rows", "decode_mat_vec"}:
         print(json.dumps({"partial_run": True, "ms": ms}), flush=True)
         return
@@ -505,6 +509,7 @@ def main():
         "prefill_tokens_per_s": round(pre_tok_s, 1),
         "prefill_gemm_tflops": round(gemm_tflops, 2),
         "ms": {k: round(v, 4) for k, v in ms.items()},
+        "ms_min_median": ms_stats,
         "decode_schedules_GBps": {
             "one batched launch (the step)": round(matvec_gbs, 1),
             "one batched launch, decode tokens back to back": round(dec_bytes / (b2b * 1e-3) / 1e9, 1) if b2b else None,
@@ -544,6 +549,7 @@ def main():
     if not args.no_extra:
         result["other_workloads"] = other_workloads(torch, dev, B, synth, emb, VM, VK, check, s)
         result["ceilings"] = measured_ceilings(torch, dev, wl, matvec_gbs, gemm_tflops)
+    result["gpu_clocks_after_run"] = gpu_clocks()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(stk.host, order, wl, args)
 
@@ -764,6 +770,20 @@ def next_rows(ms, wl, order, VM, VK, pre_flops, ne, mm, mk, nu):
                                               "quantize_vocab_f32", "repack_g128_vocab", "expert_layer_prefill",
                                               "expert_layer_decode") if k in ms}
     return out
+
+
+def gpu_clocks() -> dict:
+    """The GPU's current and available sclk / mclk as rocm-smi reports them (read-only
+    query; None where the tool or a field is missing)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        d = json.loads(r.stdout)
+    except Exception:
+        return {"sclk": None, "mclk": None}
+    card = next(iter(d.values()), {}) if isinstance(d, dict) else {}
+    pick = lambda key: next((v for k, v in card.items() if key in k.lower()), None)
+    return {"sclk": pick("sclk"), "mclk": pick("mclk")}
 
 
 def cpu_model() -> str:
