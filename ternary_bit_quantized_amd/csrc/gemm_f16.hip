@@ -434,11 +434,14 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
     // loads into buffer (t+NXB-1) % NXB (last read at step t-1, before the barrier that
     // ended it).  W raw groups are loaded one group ahead into registers; a group's last
     // step reads its own words first, then writes the next group to the wave's area and
-    // issues the loads of the one after, then the x load and the MFMAs.  Before the
+    // issues the loads of the one after, and the x load, then the MFMAs.  Before the
     // barrier that ends step t each wave waits for its own loads of tile t+1; younger are
-    // (NXB = 3) tile t+2's four and, in a group's last step, the raw loads, (NXB = 2)
-    // none.  Raw loads are counted per row fragment as three 12-byte loads (at least that
-    // many are issued); the 2-byte path counts none (its waits then also cover them).
+    // (NXB = 3) tile t+2's four and, in a group's last step, the raw loads issued before
+    // them; (NXB = 2) in a group's last step the raw loads, issued after the tile so that
+    // they stay in flight into the next step (whose wait, for a younger tile, ends them),
+    // otherwise none.  Raw loads are counted per row fragment as three 12-byte loads (at
+    // least that many are issued); the 2-byte path counts none (its waits then also
+    // cover them).
     constexpr int kRaw = kAligned ? 3 * RF : 0;
     RawPair wr[RF];
     load_raw(0, wr);
@@ -456,11 +459,16 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
             const int t = 4 * g + u;
             const int bufn = NXB == 3 ? (buf == 0 ? 2 : buf - 1) : (buf ^ 1);   // (t + NXB - 1) % NXB
             const WStep ws = read_w(u);
-            if (u == 3) {
-                write_raw(g + 1, wr);    // after this step's read of the area
-                load_raw(g + 2, wr);
+            if (u == 3) write_raw(g + 1, wr);   // after this step's read of the area
+            if constexpr (NXB == 3) {
+                if (u == 3) load_raw(g + 2, wr);
+                load_x(bufn, t + NXB - 1);
+            } else {
+                // two x buffers: the raw loads go out after the x tile, so that the wait
+                // for the tile leaves them in flight until the next step's wait
+                load_x(bufn, t + NXB - 1);
+                if (u == 3) load_raw(g + 2, wr);
             }
-            load_x(bufn, t + NXB - 1);
             if (t < nbs) step(buf, ws);
             if constexpr (NXB == 3) {
                 if (u == 3)
@@ -468,7 +476,10 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
                 else
                     wait_vmcnt<NJ>();          // tile t+1 (younger: tile t+2)
             } else {
-                wait_vmcnt<0>();              // tile t+1 (issued last)
+                if (u == 3)
+                    wait_vmcnt<kRaw>();       // tile t+1 (younger: raw group g+2)
+                else
+                    wait_vmcnt<0>();          // tile t+1 (issued last; older raw loads with it)
             }
             __syncthreads();
             buf = NXB == 3 ? (buf == 2 ? 0 : buf + 1) : (buf ^ 1);
