@@ -15,8 +15,10 @@ One step is one pass of the whole hot path:
            N = 1 on the mat-vec, in one batched launch: the workload uses one
            activation per distinct K, so the launch has two activation segments (the
            K = 4096 matrices with the head, and the K = 12288 down projections).
-Each part is captured once in a HIP graph and replayed; inputs are resident in HBM
-before timing starts.
+The prefill parts are captured once in HIP graphs and replayed; the decode parts are
+single launches and go out directly, behind the prefill on the same stream (a graph
+replay of one launch would add its own ~20 us; that figure is reported beside).  Inputs
+are resident in HBM before timing starts.
 
 `value` is that decode launch's stream rate in GB/s (algorithmic bytes: Q2_0 weights +
 f32 activations + f32 outputs, over its time): a property of the kernel, which can
@@ -399,18 +401,23 @@ def main():
     compare_parts = [p for p in graphs if p not in step_parts]
     ev = {n: [] for n in parts}
 
+    # The step's decode parts are single launches: they go out directly, behind the
+    # prefill on the same stream (a graph replay of one launch adds ~20 us of its own);
+    # every other part replays its graph.
+    eager_in_step = {"decode_get_rows", "decode_mat_vec"}
+
     def replay(names, record):
         for name in names:
-            g = graphs[name]
+            go = parts[name] if name in eager_in_step else graphs[name].replay
             if record:
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
                 a.record()
-                g.replay()
+                go()
                 b.record()
                 ev[name].append((a, b))
             else:
-                g.replay()
+                go()
 
     for _ in range(args.warmup):
         replay(step_parts, False)
@@ -432,7 +439,7 @@ def main():
     torch.cuda.synchronize()
     # the step's decode replayed back to back, as a run of decode tokens would be (in the
     # step it follows the prefill GEMMs on the same GPU)
-    b2b = None
+    b2b = graph_one = None
     if "decode_mat_vec" in graphs:
         graphs["decode_mat_vec"].replay()
         a = torch.cuda.Event(enable_timing=True)
@@ -443,6 +450,17 @@ def main():
         b.record()
         torch.cuda.synchronize()
         b2b = a.elapsed_time(b) / (4 * args.steps)
+        # and one graph replay at a time, each bracketed by events (the graph's own launch)
+        gev = []
+        for _ in range(args.steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            graphs["decode_mat_vec"].replay()
+            b.record()
+            gev.append((a, b))
+        torch.cuda.synchronize()
+        graph_one = float(np.mean([a.elapsed_time(b) for a, b in gev]))
 
     # the decode kernel's own launch time: launches enqueued back to back, an event between
     # each two, so that the GPU finds the next launch queued (no graph launch, no gap)
@@ -512,7 +530,9 @@ def main():
         "ms_min_median": ms_stats,
         "decode_schedules_GBps": {
             "one batched launch (the step)": round(matvec_gbs, 1),
-            "one batched launch, decode tokens back to back": round(dec_bytes / (b2b * 1e-3) / 1e9, 1) if b2b else None,
+            "one batched launch, decode tokens back to back (graph replays)":
+                round(dec_bytes / (b2b * 1e-3) / 1e9, 1) if b2b else None,
+            "one batched launch as a graph replay": round(dec_bytes / (graph_one * 1e-3) / 1e9, 1) if graph_one else None,
             "per_layer_groups (%d launches)" % (len(layer_groups) + 1): round(per_layer_gbs, 1),
             "per_matrix (%d launches)" % (len(order) + 1):
                 round(dec_bytes / (ms["decode_mat_vec_per_matrix"] * 1e-3) / 1e9, 1),
@@ -531,8 +551,8 @@ def main():
             "traffic": int(traffic["mat_vec_bcast"]) if "mat_vec_bcast" in traffic else None,
             "bytes_per_launch": int(dec_bytes), "avg_launch_us": round(launch_us, 3),
             "note": "achieved = bytes_per_launch / avg_launch_us, the kernel's own launches back to back "
-                    "(HIP events between them on their stream); value = the step's decode graph replay "
-                    "(graph launch included)",
+                    "(HIP events between them on their stream); value = the step's decode launch, timed with "
+                    "HIP events around it behind the step's prefill",
         },
         "roofline_gemm": {
             "kernel": "gemm_f16_mfma (N=512; %d group calls per prefill, each an fp16 x conversion, one GEMM "
