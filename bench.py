@@ -285,8 +285,8 @@ def main():
 
     prefill_groups = [(prefill_items(l, names), len(names), wl.shapes[names[0]][1])
                       for l in range(L) for names in prefill_names]
-    ws_bytes = max(max(B.mul_mat_group_workspace_bytes(items, n, K, PREFILL_N, B.Q2_0_PREC_F16_MFMA)
-                       for (items, n, K) in prefill_groups),
+    ws_bytes = max(max(B.mul_mat_group_workspace_bytes(items, n, K, PREFILL_N, p_)
+                       for (items, n, K) in prefill_groups for p_ in (B.Q2_0_PREC_F16_MFMA, B.Q2_0_PREC_F32_MFMA)),
                    max(B.mul_mat_workspace_bytes(M, K, PREFILL_N, B.Q2_0_PREC_F16_MFMA)
                        for (M, K) in wl.shapes.values()))
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
@@ -357,6 +357,7 @@ def main():
         "decode_mat_vec_per_matrix": run_decode_per_matrix,
         "prefill_gemm_per_matrix": run_prefill_per_matrix,
         "prefill_gemm_f32_layer0": lambda: run_prefill_gemms(B.Q2_0_PREC_F32, groups=prefill_groups[:4]),
+        "prefill_gemm_f32_mfma": lambda: run_prefill_gemms(B.Q2_0_PREC_F32_MFMA),
         "decode_mat_vec_f16_activations": run_decode_f16_activations,
         "prefill_gemm_bf16_activations": lambda: run_prefill_gemms(xs=xPb, xt=B.Q2_0_ACT_BF16),
         "quantize_vocab_f32": run_quantize,
@@ -538,6 +539,10 @@ def main():
                 round(dec_bytes / (ms["decode_mat_vec_per_matrix"] * 1e-3) / 1e9, 1),
         },
         "f32_fallback_gemm_tflops_layer0": round(f32_flops / (ms["prefill_gemm_f32_layer0"] * 1e-3) / 1e12, 2),
+        "f32_mfma_gemm_tflops": (round(pre_flops / (ms["prefill_gemm_f32_mfma"] * 1e-3) / 1e12, 1)
+                                 if ms.get("prefill_gemm_f32_mfma") else None),
+        "f32_mfma_gemm_note": "Q2_0_PREC_F32_MFMA (x as fp16 hi/lo pairs, fp64 block sums, 1e-5 bound under the "
+                              "mat-vec's range condition) over the whole prefill (the same 144 group calls)",
         "prefill_schedules_TFLOPs": {
             "per_layer_groups (%d group calls, the step)" % len(prefill_groups): round(gemm_tflops, 1),
             "per_matrix (%d calls)" % len(order):

@@ -58,7 +58,9 @@ typedef enum {
 
 typedef enum {
     Q2_0_PREC_F16_MFMA = 0,   /* fast: W as fp16 d*(q-1) (exact), x rounded to fp16, MFMA, f32 accumulate */
-    Q2_0_PREC_F32 = 1         /* accuracy fallback: W as f32 (q-1) and d, x in f32, f32 FMA, no range condition */
+    Q2_0_PREC_F32 = 1,        /* accuracy fallback: W as f32 (q-1) and d, x in f32, f32 FMA, no range condition */
+    Q2_0_PREC_F32_MFMA = 2    /* fp32-grade on the matrix cores: x as an fp16 hi/lo pair, per-block f32 sums
+                                 added in fp64; the 1e-5 bound under the mat-vec's range condition */
 } q2_0_precision;
 
 /* Largest activation-column count of q2_0_mul_mat_vec. */
@@ -193,12 +195,26 @@ int q2_0_mul_mat_vec_batch(const q2_0_mat_vec_batch_item *items, int64_t n_items
  *     blocks for N > 8): |y - y_exact| <= 1e-5 * A for all finite inputs whose
  *     products stay finite in f32, with no range condition (a weight of zero
  *     contributes exactly nothing); y is exactly 0 where A is 0.
+ *   Q2_0_PREC_F32_MFMA (fp32-grade on the matrix cores):
+ *     N <= 8 runs the mat-vec, as Q2_0_PREC_F16_MFMA does.
+ *     N > 8 forms the weights as fp16 d*(q-1) (exact for |d| <= 32752), scales each
+ *     column of x by the power of two that puts its max |x| in [2^14, 2^15) and
+ *     carries every element as an fp16 pair hi = fp16(x), lo = fp16(x - hi) (2^-22
+ *     relative error within 2^17 of the column's largest |x|, at most 2^-39 of that
+ *     largest |x| below).  Both halves meet the weights on the matrix cores (products
+ *     exact); each 64-weight block is summed in an f32 accumulator of its own and the
+ *     block sums are added in fp64.  Then
+ *         |y - y_exact| <= 1e-5 * A
+ *     for finite x with |x| < 2^100, |d| <= 32752 and K <= 16384 whenever
+ *         max_k |x[n][k]| * sum_k |W[m][k]| <= 2^21 * A     (range condition),
+ *     the mat-vec's condition; y is exactly 0 where A is 0.
  *   workspace / ws_bytes: device scratch the caller provides, 16-byte aligned, at
  *   least q2_0_mul_mat_workspace_bytes(M, K, N, precision) bytes: for
  *   Q2_0_PREC_F16_MFMA with N > 8, x as fp16 (N*K*2) and N column exponents, plus,
  *   when the output tile grid is too small to fill the GPU, the f32 partial sums of a
- *   K split (splits*N*M*4, split count <= 8, added in a fixed order); otherwise 0
- *   (then workspace may be NULL).
+ *   K split (splits*N*M*4, split count <= 8, added in a fixed order); for
+ *   Q2_0_PREC_F32_MFMA with N > 8 the same with x as two fp16 halves (2*N*K*2);
+ *   otherwise 0 (then workspace may be NULL).
  *   Its contents are overwritten; it must not overlap w, x or y.
  */
 int q2_0_mul_mat(const void *w, int64_t M, int64_t K, const float *x, int64_t ldx, int64_t N,
@@ -228,7 +244,8 @@ int q2_0_mul_mat_noalloc(const void *w, int64_t M, int64_t K, const float *x, in
  * mul_mat_group: several q2_0_mul_mat products that share K and the activation x,
  * y_i = W_i x (a prefill layer's q, k and v projections, or gate and up).  Same
  * arithmetic, accuracy, layouts and routing as q2_0_mul_mat for each item; with
- * Q2_0_PREC_F16_MFMA and N > 8, x is converted to fp16 once for all items and their
+ * Q2_0_PREC_F16_MFMA or Q2_0_PREC_F32_MFMA and N > 8, x is converted to fp16 (its
+ * hi/lo pair) once for all items and their
  * tiles run in shared launches (up to 16 matrices each), so small matrices fill the
  * GPU together.  Each y_i does not depend on the other items or on the grouping.
  *   items  : HOST array of n_items descriptors {w, M, y, ldy} (q2_0_mat_vec_item);
@@ -289,7 +306,8 @@ int q2_0_mul_mat_group_act(const q2_0_mat_vec_item *items, int64_t n_items, int6
  *             2e-3 bound under its range condition; few tokens, n_tokens <= 8, take
  *             the fp32-grade mat-vec, one per pair, with the mat-vec's bound and range
  *             condition) or Q2_0_PREC_F32 (the fp32 GEMM, 1e-5 bound, no range
- *             condition).
+ *             condition); Q2_0_PREC_F32_MFMA runs as Q2_0_PREC_F32, whose guarantee
+ *             covers its own.
  *   workspace / ws_bytes: at least q2_0_mul_mat_id_workspace_bytes() bytes, 16-byte
  *             aligned: the routing tables (the pairs sorted by expert, stably) and,
  *             for Q2_0_PREC_F16_MFMA, x as fp16 in expert order.  Overwritten.

@@ -25,6 +25,8 @@ int hip_status(hipError_t e) {
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
+bool known_precision(int p) { return p == Q2_0_PREC_F16_MFMA || p == Q2_0_PREC_F32 || p == Q2_0_PREC_F32_MFMA; }
+
 int check_shape(int64_t M, int64_t K, int64_t N) {
     if (K <= 0 || K % Q2_0_BLOCK_WEIGHTS != 0 || K > kMaxK) return Q2_0_ERR_SHAPE;
     if (M < 0 || N < 0 || M > kMaxRows) return Q2_0_ERR_SHAPE;
@@ -152,9 +154,10 @@ int q2_0_mul_mat_vec_batch(const q2_0_mat_vec_batch_item *items, int64_t n_items
 
 size_t q2_0_mul_mat_workspace_bytes(int64_t M, int64_t K, int64_t N, int precision) {
     if (check_shape(M, K, N) || N > kMaxGemmN) return 0;
-    if (precision != Q2_0_PREC_F16_MFMA || N <= Q2_0_MAT_VEC_MAX_N) return 0;
+    if ((precision != Q2_0_PREC_F16_MFMA && precision != Q2_0_PREC_F32_MFMA) || N <= Q2_0_MAT_VEC_MAX_N) return 0;
     const q2_0_mat_vec_item item{nullptr, M, nullptr, M};
-    return q2_0::gemm_f16_workspace_bytes(&item, 1, K, N);   // x as fp16 (+ split-K state)
+    // x as fp16 (hi/lo pairs for the fp32-grade GEMM) (+ split-K state)
+    return q2_0::gemm_f16_workspace_bytes(&item, 1, K, N, precision == Q2_0_PREC_F32_MFMA);
 }
 
 int q2_0_mul_mat(const void *w, int64_t M, int64_t K, const float *x, int64_t ldx, int64_t N,
@@ -171,10 +174,12 @@ int q2_0_mul_mat_act(const void *w, int64_t M, int64_t K, const void *x, int x_t
 size_t q2_0_mul_mat_group_workspace_bytes(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K,
                                           int64_t N, int precision) {
     if (check_shape(0, K, N) || N > kMaxGemmN || n_items < 0 || (n_items > 0 && !items)) return 0;
-    if (precision != Q2_0_PREC_F16_MFMA || N <= Q2_0_MAT_VEC_MAX_N || n_items == 0) return 0;
+    if ((precision != Q2_0_PREC_F16_MFMA && precision != Q2_0_PREC_F32_MFMA) || N <= Q2_0_MAT_VEC_MAX_N ||
+        n_items == 0)
+        return 0;
     for (int64_t i = 0; i < n_items; ++i)
         if (check_shape(items[i].M, K, N)) return 0;
-    return q2_0::gemm_f16_workspace_bytes(items, n_items, K, N);
+    return q2_0::gemm_f16_workspace_bytes(items, n_items, K, N, precision == Q2_0_PREC_F32_MFMA);
 }
 
 int q2_0_mul_mat_group(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, const float *x,
@@ -216,6 +221,7 @@ extern "C" {
 
 size_t q2_0_mul_mat_id_workspace_bytes(int64_t n_expert, int64_t M, int64_t K, int64_t n_used, int64_t n_tokens,
                                        int precision) {
+    if (precision == Q2_0_PREC_F32_MFMA) precision = Q2_0_PREC_F32;   // the fp32 GEMM covers its guarantee
     if (check_moe_shape(n_expert, M, K, n_used, n_tokens, precision)) return 0;
     if (precision != Q2_0_PREC_F16_MFMA && precision != Q2_0_PREC_F32) return 0;
     const int64_t n_pairs = n_used * n_tokens;
@@ -227,6 +233,7 @@ size_t q2_0_mul_mat_id_workspace_bytes(int64_t n_expert, int64_t M, int64_t K, i
 int q2_0_mul_mat_id(const void *w, int64_t n_expert, int64_t M, int64_t K, const void *x, int x_type,
                     int64_t ldx, int64_t x_slots, const int32_t *ids, int64_t n_used, int64_t n_tokens,
                     float *y, int64_t ldy, int precision, void *workspace, size_t ws_bytes, void *stream) {
+    if (precision == Q2_0_PREC_F32_MFMA) precision = Q2_0_PREC_F32;   // the fp32 GEMM covers its guarantee
     int st = check_moe_shape(n_expert, M, K, n_used, n_tokens, precision);
     if (st) return st;
     if (x_slots != 1 && x_slots != n_used) return Q2_0_ERR_SHAPE;
@@ -333,7 +340,7 @@ int check_mul_mat(const void *w, int64_t M, int64_t K, const void *x, int x_type
     }
     st = check_product(w, M, K, x, x_type, ldx, y, ldy);
     if (st) return st;
-    if (precision != Q2_0_PREC_F16_MFMA && precision != Q2_0_PREC_F32) return Q2_0_ERR_UNSUPPORTED;
+    if (!known_precision(precision)) return Q2_0_ERR_UNSUPPORTED;
     return Q2_0_OK;
 }
 
@@ -360,7 +367,8 @@ int mul_mat_impl(const void *w, int64_t M, int64_t K, const void *x, int x_type,
     if (N <= Q2_0_MAT_VEC_MAX_N)
         return hip_status(q2_0::launch_mat_vec(wb, M, nb, x, xt, ldx, (int)N, y, ldy, s));
     const q2_0_mat_vec_item m{w, M, y, ldy};
-    return hip_status(q2_0::launch_gemm_f16_group(&m, 1, nb, x, xt, ldx, N, workspace, s));
+    return hip_status(
+        q2_0::launch_gemm_f16_group(&m, 1, nb, x, xt, ldx, N, workspace, s, precision == Q2_0_PREC_F32_MFMA));
 }
 
 int mul_mat_group_impl(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, const void *x, int x_type,
@@ -385,7 +393,7 @@ int mul_mat_group_impl(const q2_0_mat_vec_item *items, int64_t n_items, int64_t 
         if (st) return st;
     }
     if (!any) return Q2_0_OK;
-    if (precision != Q2_0_PREC_F16_MFMA && precision != Q2_0_PREC_F32) return Q2_0_ERR_UNSUPPORTED;
+    if (!known_precision(precision)) return Q2_0_ERR_UNSUPPORTED;
     const size_t need = q2_0_mul_mat_group_workspace_bytes(items, n_items, K, N, precision);
     if (ws_bytes < need || (need && (!workspace || !aligned(workspace, 16)))) return Q2_0_ERR_WORKSPACE;
     const int nb = (int)(K / Q2_0_BLOCK_WEIGHTS);
@@ -406,7 +414,8 @@ int mul_mat_group_impl(const q2_0_mat_vec_item *items, int64_t n_items, int64_t 
     }
     if (N <= Q2_0_MAT_VEC_MAX_N)
         return hip_status(q2_0::launch_mat_vec_group(items, n_items, nb, x, xt, ldx, (int)N, s));
-    return hip_status(q2_0::launch_gemm_f16_group(items, n_items, nb, x, xt, ldx, N, workspace, s));
+    return hip_status(
+        q2_0::launch_gemm_f16_group(items, n_items, nb, x, xt, ldx, N, workspace, s, precision == Q2_0_PREC_F32_MFMA));
 }
 
 }  // namespace

@@ -64,15 +64,26 @@ __device__ __forceinline__ void load16(const XT *src, bool vec, float v[16]) {
     }
 }
 
-__device__ __forceinline__ void store16_perm(const float v[16], int e, _Float16 *dst16) {
-    uint32_t o[8];
+// HL: also the low halves lo = fp16(v - hi) at dst16 + lo_off (v - hi is exact in f32:
+// hi is v rounded to 11 significant bits).
+template <bool HL>
+__device__ __forceinline__ void store16_perm(const float v[16], int e, _Float16 *dst16, int64_t lo_off) {
+    uint32_t o[8], l[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-        o[s] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)__builtin_amdgcn_ldexpf(v[s], e),
-                                                    (_Float16)__builtin_amdgcn_ldexpf(v[s + 8], e)});
+    for (int s = 0; s < 8; ++s) {
+        const float a = __builtin_amdgcn_ldexpf(v[s], e), b = __builtin_amdgcn_ldexpf(v[s + 8], e);
+        const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+        o[s] = __builtin_bit_cast(uint32_t, half2_t{ha, hb});
+        if (HL) l[s] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)(a - (float)ha), (_Float16)(b - (float)hb)});
+    }
     u32x4_t *dst = reinterpret_cast<u32x4_t *>(dst16);
     dst[0] = u32x4_t{o[0], o[1], o[2], o[3]};
     dst[1] = u32x4_t{o[4], o[5], o[6], o[7]};
+    if (HL) {
+        u32x4_t *dl = reinterpret_cast<u32x4_t *>(dst16 + lo_off);
+        dl[0] = u32x4_t{l[0], l[1], l[2], l[3]};
+        dl[1] = u32x4_t{l[4], l[5], l[6], l[7]};
+    }
 }
 
 // gather (expert routing): output column n converts x column of pair perm[n] (pair
@@ -83,10 +94,11 @@ struct XGather {
     int x_slots;
 };
 
-template <bool kVec, typename XT>
+// HL: the hi/lo pair of every element, the low halves lo_off halves after the high ones.
+template <bool kVec, typename XT, bool HL = false>
 __global__ __launch_bounds__(256) void x_to_f16_perm(const XT *__restrict__ x, int64_t ldx, int K,
                                                      _Float16 *__restrict__ x16, int *__restrict__ xe,
-                                                     XGather gather) {
+                                                     XGather gather, int64_t lo_off) {
     __shared__ float red[4];
     const int tid = threadIdx.x;
     const int64_t n = blockIdx.x;
@@ -128,13 +140,13 @@ __global__ __launch_bounds__(256) void x_to_f16_perm(const XT *__restrict__ x, i
 #pragma unroll
         for (int u = 0; u < kPreGroups; ++u) {
             const int gi = tid + 256 * u;
-            if (gi < groups) store16_perm(v[u], e, x16 + n * K + 16 * gi);
+            if (gi < groups) store16_perm<HL>(v[u], e, x16 + n * K + 16 * gi, lo_off);
         }
     } else {
         for (int gi = tid; gi < groups; gi += 256) {
             float t[16];
             load16(col + 16 * gi, kVec, t);
-            store16_perm(t, e, x16 + n * K + 16 * gi);
+            store16_perm<HL>(t, e, x16 + n * K + 16 * gi, lo_off);
         }
     }
 }
@@ -239,15 +251,17 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int RF, int NJ, int NXB, bool kAligned, int OCC>
+template <int RF, int NJ, int NXB, bool kAligned, int OCC, bool HL>
 __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb, const _Float16 *__restrict__ x16,
                                                           const int *__restrict__ xe, int N, int tiles_n,
-                                                          int xcd_map, int splits) {
+                                                          int xcd_map, int splits, int64_t lo_off) {
     static_assert(RF == 1 || RF == 2, "one or two row fragments per wave");
     static_assert(NJ == 2 || NJ == 4, "two or four column fragments per wave");
     static_assert(NXB == 2 || NXB == 3, "two or three x buffers");
+    static_assert(!HL || NXB == 2, "hi/lo: two x buffers");
     constexpr int TM = 128 * RF, TN = 32 * NJ, kWRows = 32 * RF, kWAreaDw = kWRows * kWRowDw;
-    __shared__ __attribute__((aligned(16))) _Float16 Bs[NXB][TN * GK];
+    constexpr int BSZ = (HL ? 2 : 1) * TN * GK;   // a buffer: the x tile (HL: its hi, then its lo halves)
+    __shared__ __attribute__((aligned(16))) _Float16 Bs[NXB][BSZ];
     __shared__ __attribute__((aligned(16))) uint32_t Wraw[4 * kWAreaDw];
 
     const int tid = threadIdx.x;
@@ -368,9 +382,14 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
     const uint32_t bs_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)&Bs[0][0];
     auto load_x = [&](int buf, int blk) {
         blk = min(blk, nbs - 1);
-        const uint32_t dst = __builtin_amdgcn_readfirstlane(bs_lds + (uint32_t)(buf * TN * GK + 8 * NJ * wave * GK) * 2u);
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(bs_lds + (uint32_t)(buf * BSZ + 8 * NJ * wave * GK) * 2u);
 #pragma unroll
         for (int q = 0; q < NJ; ++q) lds_dma16(xsrc[q] + (int64_t)blk * GK, dst + (uint32_t)(8 * q * GK * 2));
+        if (HL) {
+#pragma unroll
+            for (int q = 0; q < NJ; ++q)
+                lds_dma16(xsrc[q] + lo_off + (int64_t)blk * GK, dst + (uint32_t)((TN * GK + 8 * q * GK) * 2));
+        }
     };
 
     float16_t acc[RF][NJ];
@@ -378,6 +397,15 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
     for (int i = 0; i < RF; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = float16_t{};
+    // HL: acc holds two blocks' sums (hi and lo products, from zero); mst adds them in
+    // fp64
+    double mst[HL ? RF : 1][HL ? NJ : 1][16];
+#pragma unroll
+    for (int i = 0; i < (HL ? RF : 1); ++i)
+#pragma unroll
+        for (int j = 0; j < (HL ? NJ : 1); ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) mst[i][j][v] = 0.0;
 
     // A lane l: row l%32 of a row fragment, k-slot (l/32)*8 of each 16-k step: word kk of
     // the block, code pairs 4h..4h+3 (h = l/32; the word is shifted down 8h bits so that
@@ -418,15 +446,32 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
                                 __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, pair_qm1<2>(c, pm)) * d2),
                                 __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, pair_qm1<3>(c, pm)) * d2));
             }
-            half8_t bv[NJ];
+            half8_t bv[NJ], bl[HL ? NJ : 1];
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
+            for (int j = 0; j < NJ; ++j) {
                 bv[j] = *reinterpret_cast<const half8_t *>(&Bs[buf][(j * 32 + frow) * GK + bsw[kk]]);
+                if (HL) bl[j] = *reinterpret_cast<const half8_t *>(&Bs[buf][TN * GK + (j * 32 + frow) * GK + bsw[kk]]);
+            }
 #pragma unroll
             for (int i = 0; i < RF; ++i)
 #pragma unroll
-                for (int j = 0; j < NJ; ++j)
+                for (int j = 0; j < NJ; ++j) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], bv[j], acc[i][j], 0, 0, 0);
+                    if (HL) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], bl[HL ? j : 0], acc[i][j], 0, 0, 0);
+                }
+        }
+    };
+    // HL: every two blocks the f32 sums go into the fp64 ones and start again from zero
+    auto flush = [&]() {
+        if constexpr (HL) {
+#pragma unroll
+            for (int i = 0; i < RF; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) mst[i][j][v] += (double)acc[i][j][v];
+                    acc[i][j] = float16_t{};
+                }
         }
     };
 
@@ -470,6 +515,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
                 if (u == 3) load_raw(g + 2, wr);
             }
             if (t < nbs) step(buf, ws);
+            if (HL && (u & 1)) flush();
             if constexpr (NXB == 3) {
                 if (u == 3)
                     wait_vmcnt<NJ + kRaw>();   // tile t+1 (younger: raw group g+2, tile t+2)
@@ -496,7 +542,12 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
 #pragma unroll
         for (int i = 0; i < RF; ++i)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_amdgcn_ldexpf(acc[i][j][v], ye);
+            for (int v = 0; v < 16; ++v) {
+                if constexpr (HL)
+                    acc[i][j][v] = (float)__builtin_amdgcn_ldexp(mst[HL ? i : 0][HL ? j : 0][v], ye);   // one rounding
+                else
+                    acc[i][j][v] = __builtin_amdgcn_ldexpf(acc[i][j][v], ye);
+            }
     }
     // Stores of a 4-row run of column n at row m: float4 when in range and aligned.
     auto store4 = [&](float *col, int m, const float4_t &val) {
@@ -567,31 +618,39 @@ size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 //   C: 128 x 64, RF 1 x NJ 2, two x buffers, four workgroups per CU: the expert product,
 //      whose experts hold a few dozen columns each (half the MFMAs and x loads of A per
 //      tile there, for the same weight decode).
+//   D: C's tile with x as hi/lo pairs (fp32-grade): two x tiles per buffer, two MFMAs
+//      per operand pair (so each decoded weight fragment feeds four, as in A), the fp64
+//      sums in registers; two workgroups per CU (at three the registers spill; A's
+//      128-column tile would need 128 registers of fp64 sums per lane and spills too).
 // (256 x 64 tiles, RF 2 x NJ 2 at three workgroups per CU -- half the LDS operand reads
 // per MFMA of A, twice the decode per MFMA -- measured ~10 % slower than A at N = 512.)
-enum GemmCfg { kCfgA = 0, kCfgB = 1, kCfgC = 2 };
+enum GemmCfg { kCfgA = 0, kCfgB = 1, kCfgC = 2, kCfgD = 3 };
 constexpr int cfg_rows(int cfg) { return cfg == kCfgB ? 256 : 128; }
-constexpr int cfg_cols(int cfg) { return cfg == kCfgC ? 64 : 128; }
+constexpr int cfg_cols(int cfg) { return (cfg == kCfgC || cfg == kCfgD) ? 64 : 128; }
 
 // The GEMM kernel of a configuration, with 4-byte code loads where every matrix row is
 // 4-byte aligned.
+// lo_off: configuration D's distance (halves) from the high to the low halves of x16.
 static void launch_gemm_kernel(unsigned grid, hipStream_t s, const GemmGroup &grp, int nb, const _Float16 *x16,
-                               const int *xe, int N, int tiles_n, int xcd_map, int splits, int cfg, bool aligned) {
-#define Q2_0_GEMM_LAUNCH(RF, NJ, NXB, OCC)                                                                      \
+                               const int *xe, int N, int tiles_n, int xcd_map, int splits, int cfg, bool aligned,
+                               int64_t lo_off = 0) {
+#define Q2_0_GEMM_LAUNCH(RF, NJ, NXB, OCC, HL)                                                                   \
     do {                                                                                                        \
         if (aligned)                                                                                            \
-            gemm_f16_mfma<RF, NJ, NXB, true, OCC><<<grid, 256, 0, s>>>(grp, nb, x16, xe, N, tiles_n,      \
-                                                                             xcd_map, splits);                 \
+            gemm_f16_mfma<RF, NJ, NXB, true, OCC, HL><<<grid, 256, 0, s>>>(grp, nb, x16, xe, N, tiles_n,  \
+                                                                                 xcd_map, splits, lo_off);     \
         else                                                                                                    \
-            gemm_f16_mfma<RF, NJ, NXB, false, OCC><<<grid, 256, 0, s>>>(grp, nb, x16, xe, N, tiles_n,     \
-                                                                              xcd_map, splits);                \
+            gemm_f16_mfma<RF, NJ, NXB, false, OCC, HL><<<grid, 256, 0, s>>>(grp, nb, x16, xe, N, tiles_n, \
+                                                                                  xcd_map, splits, lo_off);    \
     } while (0)
     if (cfg == kCfgB)
-        Q2_0_GEMM_LAUNCH(2, 4, 3, 2);
+        Q2_0_GEMM_LAUNCH(2, 4, 3, 2, false);
     else if (cfg == kCfgC)
-        Q2_0_GEMM_LAUNCH(1, 2, 2, 4);
+        Q2_0_GEMM_LAUNCH(1, 2, 2, 4, false);
+    else if (cfg == kCfgD)
+        Q2_0_GEMM_LAUNCH(1, 2, 2, 2, true);
     else
-        Q2_0_GEMM_LAUNCH(1, 4, 2, 3);
+        Q2_0_GEMM_LAUNCH(1, 4, 2, 3, false);
 #undef Q2_0_GEMM_LAUNCH
 }
 
@@ -605,15 +664,18 @@ static void launch_gemm_kernel(unsigned grid, hipStream_t s, const GemmGroup &gr
 // the busiest CU's partial writes included).  Candidates: A with s in
 // {1, 2, 3, 4, 6, 8} (s dividing the blocks, at least 8 per split and, for even block
 // counts, an even number), B without a split and only for an even block count.  Ties
-// keep the earlier candidate (smaller split, A).
+// keep the earlier candidate (smaller split, A).  The fp32-grade calls (hi/lo x) have D
+// alone, with the same splits.
 struct GemmPlan {
     int cfg, splits;
 };
-constexpr double kStepUs[2][4] = {
+constexpr double kStepUs[3][4] = {
     {0.0, 0.74, 1.20, 1.75},   // A, by concurrent workgroups per CU
     {0.0, 1.00, 1.87, 0.0},    // B
+    {0.0, 0.85, 1.40, 0.0},    // D
 };
-constexpr int kPerCu[2] = {3, 2};
+constexpr int kPerCu[3] = {3, 2, 2};
+constexpr int cfg_row(int cfg) { return cfg == kCfgB ? 1 : cfg == kCfgD ? 2 : 0; }
 constexpr double kPartWriteBytesPerUs = 5.0e6, kReduceBytesPerUs = 4.5e6, kReduceLaunchUs = 2.0;
 
 static double rounds_us(int64_t wgs, int per_cu, const double *step_us, int steps) {
@@ -624,7 +686,7 @@ static double rounds_us(int64_t wgs, int per_cu, const double *step_us, int step
     return ((double)full * step_us[per_cu] + step_us[w_last]) * steps;
 }
 
-static GemmPlan gemm_plan(const q2_0_mat_vec_item *items, int64_t n_items, int nb, int64_t N) {
+static GemmPlan gemm_plan(const q2_0_mat_vec_item *items, int64_t n_items, int nb, int64_t N, bool hl) {
     int64_t rows = 0, tiles[2] = {0, 0};
     for (int64_t i = 0; i < n_items; ++i) {
         tiles[0] += (items[i].M + 127) / 128;
@@ -632,15 +694,17 @@ static GemmPlan gemm_plan(const q2_0_mat_vec_item *items, int64_t n_items, int n
         rows += items[i].M;
     }
     const double nm_bytes = 4.0 * (double)N * (double)rows;   // one f32 copy of all outputs
-    GemmPlan best{kCfgA, 1};
+    GemmPlan best{hl ? kCfgD : kCfgA, 1};
     double best_us = 1e300;
-    for (int cfg : {kCfgA, kCfgB}) {
-        if (cfg != kCfgA && nb % 2 != 0) continue;
-        const int64_t t = tiles[cfg == kCfgA ? 0 : 1] * ((N + cfg_cols(cfg) - 1) / cfg_cols(cfg));
+    const int cands[2] = {hl ? kCfgD : kCfgA, kCfgB};
+    for (int c = 0; c < (hl ? 1 : 2); ++c) {
+        const int cfg = cands[c];
+        if (cfg == kCfgB && nb % 2 != 0) continue;
+        const int64_t t = tiles[cfg == kCfgB ? 1 : 0] * ((N + cfg_cols(cfg) - 1) / cfg_cols(cfg));
         for (int sp : {1, 2, 3, 4, 6, 8}) {
             if (sp > 1 && (cfg == kCfgB || nb % sp != 0 || nb / sp < 8 || (nb % 2 == 0 && (nb / sp) % 2 != 0)))
                 continue;
-            double us = rounds_us(t * sp, kPerCu[cfg], kStepUs[cfg], nb / sp);
+            double us = rounds_us(t * sp, kPerCu[cfg_row(cfg)], kStepUs[cfg_row(cfg)], nb / sp);
             if (sp > 1)
                 us += sp * nm_bytes / kPartWriteBytesPerUs + (sp + 1) * nm_bytes / kReduceBytesPerUs + kReduceLaunchUs;
             if (us < best_us) {
@@ -652,13 +716,16 @@ static GemmPlan gemm_plan(const q2_0_mat_vec_item *items, int64_t n_items, int n
     return best;
 }
 
-// Workspace of a call: fp16 x (N*K halves), the column exponents (N ints), and with
-// a K split each matrix's partials (splits * N * M floats).
-static size_t gemm_layout(const q2_0_mat_vec_item *items, int64_t n_items, int nb, int64_t N, GemmPlan *plan,
-                          size_t *parts_off) {
-    const GemmPlan pl = gemm_plan(items, n_items, nb, N);
+// Workspace of a call: fp16 x (N*K halves; hl: the high halves, then the low ones), the
+// column exponents (N ints), and with a K split each matrix's partials (splits * N * M
+// floats).
+static size_t x16_bytes(int64_t N, int64_t K, bool hl) { return align256((size_t)N * K * 2 * (hl ? 2 : 1)); }
+
+static size_t gemm_layout(const q2_0_mat_vec_item *items, int64_t n_items, int nb, int64_t N, bool hl,
+                          GemmPlan *plan, size_t *parts_off) {
+    const GemmPlan pl = gemm_plan(items, n_items, nb, N, hl);
     const int64_t K = (int64_t)nb * kBlockWeights;
-    size_t off = align256((size_t)N * K * 2) + align256((size_t)N * 4);
+    size_t off = x16_bytes(N, K, hl) + align256((size_t)N * 4);
     *parts_off = off;
     if (pl.splits > 1)
         for (int64_t i = 0; i < n_items; ++i) off += align256((size_t)pl.splits * N * items[i].M * 4);
@@ -666,36 +733,42 @@ static size_t gemm_layout(const q2_0_mat_vec_item *items, int64_t n_items, int n
     return off;
 }
 
-size_t gemm_f16_workspace_bytes(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, int64_t N) {
+size_t gemm_f16_workspace_bytes(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, int64_t N, bool hl) {
     GemmPlan pl;
     size_t po;
-    return gemm_layout(items, n_items, (int)(K / kBlockWeights), N, &pl, &po);
+    return gemm_layout(items, n_items, (int)(K / kBlockWeights), N, hl, &pl, &po);
 }
 
-int gemm_f16_splits(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, int64_t N) {
-    return gemm_plan(items, n_items, (int)(K / kBlockWeights), N).splits;
+int gemm_f16_splits(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, int64_t N, bool hl) {
+    return gemm_plan(items, n_items, (int)(K / kBlockWeights), N, hl).splits;
 }
 
 hipError_t launch_gemm_f16_group(const q2_0_mat_vec_item *mats, int64_t n_items, int nb, const void *x, Act xt,
-                                 int64_t ldx, int64_t N, void *workspace, hipStream_t s) {
+                                 int64_t ldx, int64_t N, void *workspace, hipStream_t s, bool hl) {
     const int K = nb * kBlockWeights;
     GemmPlan plan;
     size_t parts_off;
-    gemm_layout(mats, n_items, nb, N, &plan, &parts_off);
+    gemm_layout(mats, n_items, nb, N, hl, &plan, &parts_off);
     const int splits = plan.splits, TM = cfg_rows(plan.cfg), TN = cfg_cols(plan.cfg);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     _Float16 *x16 = reinterpret_cast<_Float16 *>(ws);
-    int *xe = reinterpret_cast<int *>(ws + align256((size_t)N * K * 2));
+    int *xe = reinterpret_cast<int *>(ws + x16_bytes(N, K, hl));
+    const int64_t lo_off = hl ? N * (int64_t)K : 0;
     const int tiles_n = (int)((N + TN - 1) / TN);
 
     const bool vec = ((uintptr_t)x % (4 * act_bytes(xt)) == 0) && (ldx % 4 == 0);
     hipError_t e = with_act(xt, [&](auto tag) -> hipError_t {
         using XT = decltype(tag);
         const XT *xp = static_cast<const XT *>(x);
-        if (vec)
-            x_to_f16_perm<true, XT><<<(unsigned)N, 256, 0, s>>>(xp, ldx, K, x16, xe, XGather{nullptr, 1, 1});
+        const XGather g{nullptr, 1, 1};
+        if (vec && hl)
+            x_to_f16_perm<true, XT, true><<<(unsigned)N, 256, 0, s>>>(xp, ldx, K, x16, xe, g, lo_off);
+        else if (vec)
+            x_to_f16_perm<true, XT><<<(unsigned)N, 256, 0, s>>>(xp, ldx, K, x16, xe, g, 0);
+        else if (hl)
+            x_to_f16_perm<false, XT, true><<<(unsigned)N, 256, 0, s>>>(xp, ldx, K, x16, xe, g, lo_off);
         else
-            x_to_f16_perm<false, XT><<<(unsigned)N, 256, 0, s>>>(xp, ldx, K, x16, xe, XGather{nullptr, 1, 1});
+            x_to_f16_perm<false, XT><<<(unsigned)N, 256, 0, s>>>(xp, ldx, K, x16, xe, g, 0);
         return hipGetLastError();
     });
     if (e != hipSuccess) return e;
@@ -731,7 +804,7 @@ hipError_t launch_gemm_f16_group(const q2_0_mat_vec_item *mats, int64_t n_items,
         bool aligned = nb % 2 == 0;
         for (int k = 0; k < grp.n; ++k) aligned = aligned && ((uintptr_t)grp.p[k].w % 4 == 0);
         launch_gemm_kernel((unsigned)(tiles_m * tiles_n * splits), s, grp, nb, x16, xe, (int)N, tiles_n, xcd_map,
-                           splits, plan.cfg, aligned);
+                           splits, plan.cfg, aligned, lo_off);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (splits > 1) {
@@ -769,9 +842,9 @@ hipError_t launch_gemm_f16_moe(const uint8_t *w, int64_t M, int nb, const void *
         using XT = decltype(tag);
         const XT *xp = static_cast<const XT *>(x);
         if (vec)
-            x_to_f16_perm<true, XT><<<(unsigned)nx, 256, 0, s>>>(xp, ldx, K, x16, xe, ident);
+            x_to_f16_perm<true, XT><<<(unsigned)nx, 256, 0, s>>>(xp, ldx, K, x16, xe, ident, 0);
         else
-            x_to_f16_perm<false, XT><<<(unsigned)nx, 256, 0, s>>>(xp, ldx, K, x16, xe, ident);
+            x_to_f16_perm<false, XT><<<(unsigned)nx, 256, 0, s>>>(xp, ldx, K, x16, xe, ident, 0);
         return hipGetLastError();
     });
     if (e != hipSuccess) return e;

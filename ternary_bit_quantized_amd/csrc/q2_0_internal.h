@@ -159,11 +159,13 @@ struct GemmGroup {
     int moe_max_tiles;
     int moe_n_expert;
 };
-size_t gemm_f16_workspace_bytes(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, int64_t N);
+// hl: x as fp16 hi/lo pairs, per-block sums added in fp64 (the fp32-grade GEMM)
+size_t gemm_f16_workspace_bytes(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, int64_t N,
+                                bool hl = false);
 // the K split the call's plan picks (1: none)
-int gemm_f16_splits(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, int64_t N);
+int gemm_f16_splits(const q2_0_mat_vec_item *items, int64_t n_items, int64_t K, int64_t N, bool hl = false);
 hipError_t launch_gemm_f16_group(const q2_0_mat_vec_item *items, int64_t n_items, int nb, const void *x, Act xt,
-                                 int64_t ldx, int64_t N, void *workspace, hipStream_t s);
+                                 int64_t ldx, int64_t N, void *workspace, hipStream_t s, bool hl = false);
 hipError_t launch_gemm_f32(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx,
                            int64_t N, float *y, int64_t ldy, hipStream_t s);
 

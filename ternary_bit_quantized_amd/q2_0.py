@@ -27,6 +27,7 @@ Q2_0_ERR_HIP = 7
 Q2_0_ERR_TOO_LARGE = 8
 Q2_0_PREC_F16_MFMA = 0
 Q2_0_PREC_F32 = 1
+Q2_0_PREC_F32_MFMA = 2
 Q2_0_ACT_F32 = 0
 Q2_0_ACT_F16 = 1
 Q2_0_ACT_BF16 = 2

@@ -92,7 +92,7 @@ def test_alignment_errors():
 
 def test_unsupported():
     assert B.mul_mat_vec_raw(P16, 10, 64, P16, 64, 9, P16, 10) == B.Q2_0_ERR_UNSUPPORTED
-    assert B.mul_mat_raw(P16, 10, 64, P16, 64, 20, P16, 10, 2, 0, 0) == B.Q2_0_ERR_UNSUPPORTED
+    assert B.mul_mat_raw(P16, 10, 64, P16, 64, 20, P16, 10, 3, 0, 0) == B.Q2_0_ERR_UNSUPPORTED
     assert B.mul_mat_raw(P16, 10, 64, P16, 64, 20, P16, 10, -1, 0, 0) == B.Q2_0_ERR_UNSUPPORTED
 
 
@@ -110,6 +110,14 @@ def test_workspace_query_and_checks():
     assert B.mul_mat_raw(P16, 10, 64, P16, 64, 20, P16, 10, 0, P16, need - 1) == B.Q2_0_ERR_WORKSPACE
     assert B.mul_mat_raw(P16, 10, 64, P16, 64, 20, P16, 10, 0, 0, need) == B.Q2_0_ERR_WORKSPACE
     assert B.mul_mat_raw(P16, 10, 64, P16, 64, 20, P16, 10, 0, P16 + 8, need) == B.Q2_0_ERR_WORKSPACE
+    # the fp32-grade matrix-core GEMM stages x as two fp16 halves; N <= 8 needs nothing
+    F32M = B.Q2_0_PREC_F32_MFMA
+    assert B.mul_mat_workspace_bytes(65536, 4096, 512, F32M) == 2 * 512 * 4096 * 2 + 2048
+    assert B.mul_mat_workspace_bytes(4096, 4096, 8, F32M) == 0
+    need = B.mul_mat_workspace_bytes(10, 64, 20, F32M)
+    assert need >= 2 * 20 * 64 * 2
+    assert B.mul_mat_raw(P16, 10, 64, P16, 64, 20, P16, 10, F32M, P16, need - 1) == B.Q2_0_ERR_WORKSPACE
+    assert B.mul_mat_raw(P16, 10, 64, P16, 64, 20, P16, 10, F32M, 0, need) == B.Q2_0_ERR_WORKSPACE
 
 
 def test_group_validation():
@@ -218,7 +226,10 @@ def test_mul_mat_id_validation():
     assert call(xt=5) == B.Q2_0_ERR_UNSUPPORTED
     assert call(ids=P16 + 2) == B.Q2_0_ERR_ALIGN
     assert call(x=P16 + 2) == B.Q2_0_ERR_ALIGN
-    assert call(prec=2) == B.Q2_0_ERR_UNSUPPORTED
+    assert call(prec=3) == B.Q2_0_ERR_UNSUPPORTED
+    # the fp32-grade matrix-core precision runs as Q2_0_PREC_F32 here (same workspace)
+    assert (B.mul_mat_id_workspace_bytes(4, 10, 64, 2, 3, B.Q2_0_PREC_F32_MFMA) ==
+            B.mul_mat_id_workspace_bytes(4, 10, 64, 2, 3, F32))
     need = B.mul_mat_id_workspace_bytes(4, 10, 64, 2, 3, F16)
     assert need >= 6 * 64 * 2 and B.mul_mat_id_workspace_bytes(4, 10, 64, 2, 3, F32) > 0
     assert call(wsb=need - 1) == B.Q2_0_ERR_WORKSPACE

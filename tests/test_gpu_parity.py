@@ -308,7 +308,8 @@ def test_mat_vec_group_activation_range():
 
 # =============================================================================== GEMM
 
-@pytest.mark.parametrize("precision,rel", [(B.Q2_0_PREC_F16_MFMA, REL_F16), (B.Q2_0_PREC_F32, REL_F32)])
+@pytest.mark.parametrize("precision,rel", [(B.Q2_0_PREC_F16_MFMA, REL_F16), (B.Q2_0_PREC_F32, REL_F32),
+                                             (B.Q2_0_PREC_F32_MFMA, REL_F32)])
 @pytest.mark.parametrize("M,K,N,ldx,ldy", [
     (64, 64, 64, 64, 64), (1, 64, 9, 64, 1), (65, 192, 63, 200, 70), (200, 512, 130, 512, 203),
     (127, 2048, 65, 2050, 127), (33, 576, 100, 576, 33),
@@ -321,7 +322,8 @@ def test_mul_mat_ragged(precision, rel, M, K, N, ldx, ldy):
     assert_products(y, w, M, K, x, rel, what="p=%d M=%d K=%d N=%d" % (precision, M, K, N))
 
 
-@pytest.mark.parametrize("precision,rel", [(B.Q2_0_PREC_F16_MFMA, REL_F16), (B.Q2_0_PREC_F32, REL_F32)])
+@pytest.mark.parametrize("precision,rel", [(B.Q2_0_PREC_F16_MFMA, REL_F16), (B.Q2_0_PREC_F32, REL_F32),
+                                             (B.Q2_0_PREC_F32_MFMA, REL_F32)])
 def test_mul_mat_prefill_1p7b_workload(precision, rel):
     wl = synth.PREFILL_1P7B
     rng = np.random.default_rng(2)
@@ -333,7 +335,8 @@ def test_mul_mat_prefill_1p7b_workload(precision, rel):
         assert_products(y, w, M, K, x, rel, rows=rows, what=name)
 
 
-@pytest.mark.parametrize("precision,rel", [(B.Q2_0_PREC_F16_MFMA, REL_F16), (B.Q2_0_PREC_F32, REL_F32)])
+@pytest.mark.parametrize("precision,rel", [(B.Q2_0_PREC_F16_MFMA, REL_F16), (B.Q2_0_PREC_F32, REL_F32),
+                                             (B.Q2_0_PREC_F32_MFMA, REL_F32)])
 def test_mul_mat_stack_8b_workload(precision, rel):
     wl = synth.STACK_8B
     rng = np.random.default_rng(4)
@@ -388,7 +391,8 @@ def test_mul_mat_small_n_routes_to_mat_vec():
         assert_products(run_mul_mat(wd, M, K, x, B.Q2_0_PREC_F32), w, M, K, x, REL_F32, what="PREC_F32 N=%d" % N)
 
 
-@pytest.mark.parametrize("precision,rel", [(B.Q2_0_PREC_F16_MFMA, REL_F16), (B.Q2_0_PREC_F32, REL_F32)])
+@pytest.mark.parametrize("precision,rel", [(B.Q2_0_PREC_F16_MFMA, REL_F16), (B.Q2_0_PREC_F32, REL_F32),
+                                             (B.Q2_0_PREC_F32_MFMA, REL_F32)])
 @pytest.mark.parametrize("M,K,N", [(200, 640, 9), (1024, 4096, 27), (129, 12288, 18)])
 def test_mul_mat_activation_range(precision, rel, M, K, N):
     w = synth.weight(15, M, K // 64, M, K, "tern", synth.ScaleDist("uniform", 0.002, 0.02))
@@ -398,7 +402,7 @@ def test_mul_mat_activation_range(precision, rel, M, K, N):
         assert_products(y, w, M, K, x, rel, what="M=%d K=%d N=%d spread=%s" % (M, K, N, spread))
 
 
-@pytest.mark.parametrize("precision", [B.Q2_0_PREC_F16_MFMA, B.Q2_0_PREC_F32])
+@pytest.mark.parametrize("precision", [B.Q2_0_PREC_F16_MFMA, B.Q2_0_PREC_F32, B.Q2_0_PREC_F32_MFMA])
 def test_mul_mat_all_code_one_is_exactly_zero(precision):
     rng = np.random.default_rng(5)
     M, K, N = 130, 1024, 70
@@ -409,7 +413,7 @@ def test_mul_mat_all_code_one_is_exactly_zero(precision):
     assert np.all(y == 0.0)
 
 
-@pytest.mark.parametrize("precision", [B.Q2_0_PREC_F16_MFMA, B.Q2_0_PREC_F32])
+@pytest.mark.parametrize("precision", [B.Q2_0_PREC_F16_MFMA, B.Q2_0_PREC_F32, B.Q2_0_PREC_F32_MFMA])
 def test_mul_mat_metamorphic_scale(precision):
     rng = np.random.default_rng(6)
     M, K, N = 100, 512, 40
@@ -597,7 +601,8 @@ def run_gemm_group(mats, K, x, precision):
     return out
 
 
-@pytest.mark.parametrize("precision,rel", [(B.Q2_0_PREC_F16_MFMA, REL_F16), (B.Q2_0_PREC_F32, REL_F32)])
+@pytest.mark.parametrize("precision,rel", [(B.Q2_0_PREC_F16_MFMA, REL_F16), (B.Q2_0_PREC_F32, REL_F32),
+                                             (B.Q2_0_PREC_F32_MFMA, REL_F32)])
 @pytest.mark.parametrize("Ms,K,N", [((4096 // 8, 1024 // 8, 1024 // 8), 2048, 96), ((300, 0, 77, 129), 576, 130),
                                     ((64,) * 20, 192, 64), ((1000, 24), 4096, 9)])
 def test_mul_mat_group_matches_oracle(precision, rel, Ms, K, N):
