@@ -3,8 +3,8 @@
 Usage: python -m ternary_bit_quantized_amd.build [--sanitize]
 Every source in csrc/ is compiled for gfx950 only; object files go to _build/ at the
 repository root and the shared library next to this file.  The measurement kernels in
-ceilings/ (HBM read stream, MFMA loop, empty launch) become libq2_0_ceilings.so, which
-only the benchmark loads.
+ceilings/ (HBM read stream, MFMA loop, empty launch, and a probe of the matrix cores'
+rounding) become libq2_0_ceilings.so, which only the benchmark and the tests load.
 
 --sanitize builds a second copy, _build/sanitize/libq2_0.so, whose host code carries
 AddressSanitizer and UndefinedBehaviorSanitizer checks (device code as usual).  It is for

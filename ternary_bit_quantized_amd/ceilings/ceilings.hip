@@ -8,6 +8,8 @@
 //                             operands held in registers (no memory traffic in the loop),
 //                             four independent accumulators per wave.
 //   q2_0_ceil_empty        -- one workgroup that does nothing: the fixed cost of a launch.
+//   q2_0_probe_mfma_f16    -- one v_mfma_f32_32x32x16_f16 on given operands: how the matrix
+//                             cores round (the fp32-grade GEMM's error bound counts on it).
 //
 // All return the hipError_t of the launch.
 #include <hip/hip_runtime.h>
@@ -67,6 +69,25 @@ __global__ __launch_bounds__(256) void mfma_f16_loop(int iters, float *__restric
 
 __global__ void empty_kernel() {}
 
+// One wave: every row of A and every column of B carry the same 16 k-values a16[k] and
+// b16[k] (lane l holds k = 8 (l / 32) .. + 7, the layout of both operands), every
+// accumulator element starts at c; out receives the 16 results of every lane.
+__global__ __launch_bounds__(64) void mfma_f16_probe(const _Float16 *a16, const _Float16 *b16, float c, float *out) {
+    const int lane = threadIdx.x;
+    half8_t a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = a16[8 * (lane / 32) + e];
+        b[e] = b16[8 * (lane / 32) + e];
+    }
+    float16_t acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = c;
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) out[lane * 16 + v] = acc[v];
+}
+
 }  // namespace
 
 extern "C" {
@@ -106,6 +127,15 @@ int q2_0_ceil_mfma_f16(int grid, int iters, void *out, void *stream) {
     if (!out || grid < 1 || iters < 1) return (int)hipErrorInvalidValue;
     mfma_f16_loop<<<grid, 256, 0, static_cast<hipStream_t>(stream)>>>(iters, static_cast<float *>(out), 12345u);
     return (int)hipGetLastError();
+}
+
+// a16, b16: 16 halves each; out: 1024 floats (device memory).  Synchronous.
+int q2_0_probe_mfma_f16(const void *a16, const void *b16, float c, void *out) {
+    if (!a16 || !b16 || !out) return (int)hipErrorInvalidValue;
+    mfma_f16_probe<<<1, 64>>>(static_cast<const _Float16 *>(a16), static_cast<const _Float16 *>(b16), c,
+                              static_cast<float *>(out));
+    const hipError_t e = hipGetLastError();
+    return (int)(e != hipSuccess ? e : hipDeviceSynchronize());
 }
 
 int q2_0_ceil_empty(void *stream) {
