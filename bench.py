@@ -465,6 +465,21 @@ def main():
 
     # the decode kernel's own launch time: launches enqueued back to back, an event between
     # each two, so that the GPU finds the next launch queued (no graph launch, no gap)
+    # the expert layer's calls (two launches each) enqueued back to back, events around the
+    # run: their own time, without the ~15-20 us that a graph replay of a few launches adds
+    ms_b2b = {}
+    for name in ("expert_layer_prefill", "expert_layer_decode"):
+        if name in parts:
+            parts[name]()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(4 * args.steps):
+                parts[name]()
+            b.record()
+            torch.cuda.synchronize()
+            ms_b2b[name] = a.elapsed_time(b) / (4 * args.steps)
+
     launch_us = None
     if "decode_mat_vec" in graphs:
         run_decode_matvecs()
@@ -482,7 +497,7 @@ def main():
                     "samples": len(ev[n])}
                 for n in ("prefill_gemm", "decode_mat_vec", "decode_mat_vec_per_layer") if n in ev and ev[n]}
     if set(step_parts) != {"prefill_get_rows", "prefill_gemm", "decode_get_rows", "decode_mat_vec"}:
-        print(json.dumps({"partial_run": True, "ms": ms}), flush=True)
+        print(json.dumps({"partial_run": True, "ms": ms, "ms_back_to_back": ms_b2b}), flush=True)
         return
 
     # ---- algorithmic work
@@ -568,7 +583,7 @@ def main():
             "algorithmic_bytes": int(pre_bytes),
             "mfma_busy_frac_counters": mfma.get("mfma_busy_frac"),
         },
-        "next_rows": next_rows(ms, wl, order, VM, VK, pre_flops, MOE_E, MOE_M, MOE_K, MOE_USED),
+        "next_rows": next_rows(ms, ms_b2b, wl, order, VM, VK, pre_flops, MOE_E, MOE_M, MOE_K, MOE_USED),
         "cpu_baseline": None,
     }
     if not args.no_extra:
@@ -771,13 +786,15 @@ def measured_ceilings(torch, dev, wl, matvec_gbs, gemm_tflops):
     return out
 
 
-def next_rows(ms, wl, order, VM, VK, pre_flops, ne, mm, mk, nu):
-    """Rates of the widened rows, timed beside the step (HIP events around their graphs)."""
+def next_rows(ms, ms_b2b, wl, order, VM, VK, pre_flops, ne, mm, mk, nu):
+    """Rates of the widened rows, timed beside the step (HIP events around their graphs; the
+    expert layer's calls back to back, ms_b2b, with the graph-replay figures beside)."""
     out = {}
 
-    def rate(name, work, scale):
-        if name in ms and ms[name] > 0:
-            return round(work / (ms[name] * 1e-3) / scale, 1)
+    def rate(name, work, scale, src=None):
+        src = ms if src is None else src
+        if name in src and src[name] > 0:
+            return round(work / (src[name] * 1e-3) / scale, 1)
         return None
 
     dec16 = sum(M * (K // 64) * 18 + 2 * K + 4 * M for (_, n) in order for (M, K) in [wl.shapes[n]])
@@ -787,13 +804,20 @@ def next_rows(ms, wl, order, VM, VK, pre_flops, ne, mm, mk, nu):
     out["quantize_151936x4096_f32_GBps"] = rate("quantize_vocab_f32", VM * VK * 4 + VM * (VK // 64) * 18, 1e9)
     out["repack_g128_151936x4096_GBps"] = rate("repack_g128_vocab", VM * (VK // 128) * 34 + VM * (VK // 64) * 18,
                                               1e9)
-    out["expert_layer_prefill_TFLOPs"] = rate("expert_layer_prefill", 2.0 * mm * mk * PREFILL_N * nu, 1e12)
-    out["expert_layer_decode_GBps"] = rate("expert_layer_decode", nu * (mm * (mk // 64) * 18 + 4 * mk + 4 * mm), 1e9)
+    moe_flops = 2.0 * mm * mk * PREFILL_N * nu
+    moe_bytes = nu * (mm * (mk // 64) * 18 + 4 * mk + 4 * mm)
+    out["expert_layer_prefill_TFLOPs"] = rate("expert_layer_prefill", moe_flops, 1e12, ms_b2b)
+    out["expert_layer_decode_GBps"] = rate("expert_layer_decode", moe_bytes, 1e9, ms_b2b)
+    out["expert_layer_graph_replay"] = {"prefill_TFLOPs": rate("expert_layer_prefill", moe_flops, 1e12),
+                                        "decode_GBps": rate("expert_layer_decode", moe_bytes, 1e9),
+                                        "note": "each call as its own graph replay, whose launch (~15-20 us) "
+                                                "is timed with it"}
     out["expert_layer"] = ("%d experts of %dx%d, %d per token; prefill %d tokens (fp16 MFMA), decode 1 token "
                            "(fp32-grade mat-vec per pair)" % (ne, mm, mk, nu, PREFILL_N))
     out["ms"] = {k: round(ms[k], 4) for k in ("decode_mat_vec_f16_activations", "prefill_gemm_bf16_activations",
                                               "quantize_vocab_f32", "repack_g128_vocab", "expert_layer_prefill",
                                               "expert_layer_decode") if k in ms}
+    out["ms_expert_layer_back_to_back"] = {k: round(v, 4) for k, v in ms_b2b.items()}
     return out
 
 

@@ -259,16 +259,20 @@ int q2_0_mul_mat_id(const void *w, int64_t n_expert, int64_t M, int64_t K, const
                                                           (int)x_slots, (int)n_pairs, y, ldy, s));
     }
     q2_0::MoeRoute r;
-    st = hip_status(q2_0::launch_moe_route(ids, (int)n_pairs, (int)n_expert, (int)n_used, (int)x_slots,
-                                           moe_tile_w(precision), workspace, &r, s));
+    // the fp16 GEMM's scratch follows the routing tables; where it can, the routing launch
+    // also converts x into it
+    void *scratch = static_cast<uint8_t *>(workspace) + q2_0::moe_route_bytes(n_expert, n_pairs, moe_tile_w(precision));
+    const bool fused = precision == Q2_0_PREC_F16_MFMA && q2_0::moe_route_converts((int)n_expert);
+    if (fused)
+        st = hip_status(q2_0::launch_moe_route_convert(ids, (int)n_pairs, (int)n_expert, (int)n_used, (int)x_slots,
+                                                       moe_tile_w(precision), workspace, &r, x, xt, ldx, (int)K,
+                                                       scratch, s));
+    else
+        st = hip_status(q2_0::launch_moe_route(ids, (int)n_pairs, (int)n_expert, (int)n_used, (int)x_slots,
+                                               moe_tile_w(precision), workspace, &r, s));
     if (st) return st;
-    if (precision == Q2_0_PREC_F16_MFMA) {
-        // the fp16 GEMM's scratch follows the routing tables; its launch also fills the
-        // out-of-range pairs' columns
-        void *scratch =
-            static_cast<uint8_t *>(workspace) + q2_0::moe_route_bytes(n_expert, n_pairs, moe_tile_w(precision));
-        return hip_status(q2_0::launch_gemm_f16_moe(wb, M, nb, x, xt, ldx, r, y, ldy, scratch, s));
-    }
+    if (precision == Q2_0_PREC_F16_MFMA)   // (its launch also fills the out-of-range pairs' columns)
+        return hip_status(q2_0::launch_gemm_f16_moe(wb, M, nb, x, xt, ldx, r, y, ldy, scratch, s, fused));
     st = hip_status(q2_0::launch_gemm_f32_moe(wb, M, nb, x, xt, ldx, r, y, ldy, s));
     if (st) return st;
     return hip_status(q2_0::launch_moe_fill_bad(r, M, y, ldy, s));

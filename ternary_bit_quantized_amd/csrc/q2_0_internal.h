@@ -192,8 +192,20 @@ size_t moe_route_bytes(int64_t n_expert, int64_t n_pairs, int tile_w);
 // Lays out the routing tables in ws (moe_route_bytes bytes) and enqueues the routing.
 hipError_t launch_moe_route(const int32_t *ids, int n_pairs, int n_expert, int n_used, int x_slots, int tile_w,
                             void *ws, MoeRoute *r, hipStream_t s);
+// x rows of an expert call: one per token (x_slots == 1) or one per pair
+inline int moe_x_rows(int n_pairs, int n_used, int x_slots) { return x_slots == 1 ? n_pairs / n_used : n_pairs; }
+// The routing and, in the same launch, the fp16 GEMM's x (x16 and its row exponents at
+// scratch, laid out as launch_gemm_f16_moe reads them).  Returns false (and launches
+// nothing) when the routing takes the kernel for many experts; then launch_moe_route
+// and launch_gemm_f16_moe's own conversion do the work.
+bool moe_route_converts(int n_expert);
+hipError_t launch_moe_route_convert(const int32_t *ids, int n_pairs, int n_expert, int n_used, int x_slots,
+                                    int tile_w, void *ws, MoeRoute *r, const void *x, Act xt, int64_t ldx, int K,
+                                    void *scratch, hipStream_t s);
+// x_ready: x16 and its exponents are already in scratch (launch_moe_route_convert)
 hipError_t launch_gemm_f16_moe(const uint8_t *w, int64_t M, int nb, const void *x, Act xt, int64_t ldx,
-                               const MoeRoute &r, float *y, int64_t ldy, void *scratch, hipStream_t s);
+                               const MoeRoute &r, float *y, int64_t ldy, void *scratch, hipStream_t s,
+                               bool x_ready = false);
 size_t gemm_f16_moe_scratch_bytes(int64_t K, int64_t n_pairs);
 hipError_t launch_moe_fill_bad(const MoeRoute &r, int64_t M, float *y, int64_t ldy, hipStream_t s);
 // few tokens: one K-split mat-vec per pair, expert read from ids on the GPU; pairs with

@@ -115,6 +115,26 @@ def test_mul_mat_id_many_experts(precision, ne):
 
 
 @pytest.mark.parametrize("precision", [B.Q2_0_PREC_F16_MFMA, B.Q2_0_PREC_F32])
+@pytest.mark.parametrize("ne,nt,nu", [(239, 512, 8), (240, 512, 8), (16, 513, 8)])
+def test_mul_mat_id_routing_path_edges(precision, ne, nt, nu):
+    """The edges of the one-pass routing (at most 4096 pairs and 240 runs: 239 experts at
+    512 tokens x 8 slots) and of the chunk-by-chunk one it hands over to (240 experts:
+    241 runs; 513 tokens: 4104 pairs); every output against the oracle, and bit for bit
+    the same on a second call."""
+    rng = np.random.default_rng(ne * 3 + nt + precision)
+    M, K = 64, 128
+    wall = experts(66, ne, M, K)
+    ids = rng.integers(0, ne, size=(nt, nu)).astype(np.int32)
+    ids[0, 0], ids[nt - 1, nu - 1] = -3, ne
+    x = synth.activations(66, nt, 0, nt, K)
+    y = run_id(wall, ne, M, K, x, B.Q2_0_ACT_F32, ids, precision)
+    y2 = run_id(wall, ne, M, K, x, B.Q2_0_ACT_F32, ids, precision)
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+    y_ref, bound = oracle.mul_mat_id(wall, ne, M, K, x, ids)
+    check(y, y_ref, bound, REL[precision], "ne=%d nt=%d p%d" % (ne, nt, precision))
+
+
+@pytest.mark.parametrize("precision", [B.Q2_0_PREC_F16_MFMA, B.Q2_0_PREC_F32])
 def test_mul_mat_id_two_column_tiles_per_expert(precision):
     """256 experts with 65 pairs each: every expert's run spans two 64-column tiles, so the
     tile list is as long as it gets for this pair count and the fp16 path's scratch, laid
