@@ -162,3 +162,61 @@ def test_limbs_tolerate_far_larger_outliers_than_hilo():
     x = rng(9).standard_normal(K).astype(F32)
     ratio, _ = staging_error_ratio(stage_limbs, W, x, k0, F32(2.0 ** 32))
     assert ratio <= 1e-5 - 100 * 2.0 ** -24
+
+
+def f32_mfma_model(W16, x):
+    """Q2_0_PREC_F32_MFMA for one column: W16 (M x K, the fp16 values d*(q-1)) times x staged
+    as hi/lo, every product exact; each 16-k step's products reach the f32 accumulator as
+    two exactly summed groups of 8 (the behaviour measured on the matrix cores), hi step
+    then lo step; the accumulator restarts every 128 k and is added into fp64; one
+    rounding to f32 at the end (after the exact power-of-two unscaling)."""
+    e = pow2_exponent(float(np.max(np.abs(x))), 15)
+    v = (x.astype(F32) * F32(2.0 ** e)).astype(F32)
+    hi = v.astype(np.float16).astype(np.float64)
+    lo = (v - v.astype(np.float16).astype(F32)).astype(F32).astype(np.float16).astype(np.float64)
+    Ph, Pl = W16 * hi, W16 * lo                     # exact: 11-bit by 11-bit significands
+    M, K = W16.shape
+    mst = np.zeros(M)
+    acc = np.zeros(M, dtype=F32)
+    for k0 in range(0, K, 16):
+        for P in (Ph, Pl):
+            for g in (0, 8):
+                acc = (acc.astype(np.float64) + P[:, k0 + g:k0 + g + 8].sum(axis=1)).astype(F32)
+        if (k0 + 16) % 128 == 0 or k0 + 16 == K:
+            mst += acc.astype(np.float64)
+            acc = np.zeros(M, dtype=F32)
+    return (mst * 2.0 ** -e).astype(F32)
+
+
+@pytest.mark.parametrize("K", [4096, 16384])
+def test_f32_mfma_model_meets_its_bound_at_the_range_limit(K):
+    """The whole arithmetic of Q2_0_PREC_F32_MFMA, modelled, stays within 1e-5 * A with a
+    zero-weighted outlier at the edge of its range condition (2^21), and on plain data.
+    (The header's budget counts 4 roundings per MFMA; this model takes the measured 2.)"""
+    M, k0 = 48, 3 * 64 + 17
+    W = weights_with_zero_column(4, M, K, k0)
+    W16 = W.astype(np.float16).astype(np.float64)
+    assert np.array_equal(W16, W)                   # d*(q-1) is exact in fp16
+    x = rng(10).standard_normal(K).astype(F32)
+    x[k0] = 0
+    A0 = np.abs(W) @ np.abs(x.astype(np.float64))
+    for big in (0.0, 1e4, 0.999 * 2.0 ** 21 * float(np.min(A0 / np.abs(W).sum(axis=1)))):
+        xb = x.copy()
+        xb[k0] = F32(big)
+        xd = xb.astype(np.float64)
+        A = np.abs(W) @ np.abs(xd)
+        err = np.abs(f32_mfma_model(W16, xb).astype(np.float64) - W @ xd)
+        assert float(np.max(err / A)) <= 1e-5, "outlier %.3g: %.3g" % (big, float(np.max(err / A)))
+
+
+def test_f32_mfma_model_needs_the_range_condition():
+    """Far outside the condition (a zero-weighted outlier 2^36 above the rest) the lo
+    halves of the live activations fall below fp16's subnormals and the bound fails."""
+    M, K, k0 = 48, 4096, 3 * 64 + 17
+    W = weights_with_zero_column(5, M, K, k0)
+    x = rng(11).standard_normal(K).astype(F32)
+    x[k0] = F32(2.0 ** 36)
+    xd = x.astype(np.float64)
+    A = np.abs(W) @ np.abs(xd)
+    err = np.abs(f32_mfma_model(W.astype(np.float16).astype(np.float64), x).astype(np.float64) - W @ xd)
+    assert float(np.max(err / A)) > 1e-5
