@@ -98,22 +98,31 @@ __device__ __forceinline__ float4_t bc_block(uint32_t c0, uint32_t c1, uint32_t 
 // bytes, as dwords 0..17.  A pair is 9 dwords D0..D8 (layout in mat_vec_common.h): the
 // even block's scale is the low half of D0 and its code dwords (h0,h7) (h1,h2) (h3,h4)
 // (h5,h6), the odd block's scale the high half of D4 and its code dwords D5..D8.
-// xa: the activation operands of the 4 blocks x 4 code dwords; acc_e / acc_o accumulate
-// even / odd blocks; a quarter outside the row (the empty half of a row's last stage
-// when K/64 % 16 == 8) leaves them unchanged.
+// xs: the lane's A entry of the quarter's first block (entries of block b, code dword u at
+// xs[4 (4b + u) 2NC]), read a block at a time next to its products (all 16 held at once
+// took 32 registers and made the kernel spill); acc_e / acc_o accumulate even / odd
+// blocks; a quarter outside the row (the empty half of a row's last stage when
+// K/64 % 16 == 8) leaves them unchanged.
 template <int NC>
-__device__ __forceinline__ void bc_quarter(const uint32_t (&R)[20], const half4_t (&xa)[16], const PairMasks &pm,
+__device__ __forceinline__ void bc_quarter(const uint32_t (&R)[20], const half4_t *xs, const PairMasks &pm,
                                            bool valid, float (&acc_e)[2], float (&acc_o)[2]) {
+    constexpr int NR = 2 * NC;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
         const int o = 9 * p;
         const uint32_t h0h7 = __builtin_amdgcn_perm(R[o + 4], R[o + 0], 0x05040302u);
+        half4_t xe[4], xo[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            xe[u] = xs[4 * (8 * p + u) * NR];
+            xo[u] = xs[4 * (8 * p + 4 + u) * NR];
+        }
         // scheduling fences keep the decode of one block next to its products (hoisted
         // ahead, the decoded halves of several blocks would not fit in registers)
         __builtin_amdgcn_sched_barrier(0);
-        const float4_t se = bc_block(h0h7, R[o + 1], R[o + 2], R[o + 3], xa + 8 * p, pm);
+        const float4_t se = bc_block(h0h7, R[o + 1], R[o + 2], R[o + 3], xe, pm);
         __builtin_amdgcn_sched_barrier(0);
-        const float4_t so = bc_block(R[o + 5], R[o + 6], R[o + 7], R[o + 8], xa + 8 * p + 4, pm);
+        const float4_t so = bc_block(R[o + 5], R[o + 6], R[o + 7], R[o + 8], xo, pm);
         __builtin_amdgcn_sched_barrier(0);
         const float de = half_bits_to_float(R[o + 0] & 0xffffu);
         const float dd = half_bits_to_float(R[o + 4] >> 16);
@@ -594,9 +603,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_bcast(MvGroup grp, MvSegs s
             const int boff = valid ? sl * kBcSB + 4 * G : 0;                                   \
             bx_quarter(R, xl + xoff, lds_bs + boff, lds_bsc + boff, valid, acc_e, acc_o);      \
         } else {                                                                               \
-            half4_t xa[16];                                                                    \
-            _Pragma("unroll") for (int i = 0; i < 16; ++i) xa[i] = xl[xoff + 4 * i * NR];     \
-            bc_quarter<NC>(R, xa, pm, valid, acc_e, acc_o);                                    \
+            bc_quarter<NC>(R, xl + xoff, pm, valid, acc_e, acc_o);                             \
         }                                                                                      \
         if (cur.st == sw0 + sp - 1) {                                                          \
             const float r0 = acc_e[0] + acc_o[0], r1 = acc_e[1] + acc_o[1];                    \
