@@ -634,7 +634,7 @@ def other_workloads(torch, dev, B, synth, emb, VM, VK, check, s):
     LD = 56
     stk = Stack(torch, dev, dw, LD, synth)
     dec = {}
-    for N in (1, 8):
+    for N in (1, 2, 8):
         xs = {K: torch.from_numpy(synth.activations(dw.seed, N, 7 + K // 2048, N, K)).to(dev)
               for K in sorted({K for (_, K) in dw.shapes.values()})}
         ys = {n: torch.empty((N, LD * M), device=dev) for n, (M, K) in dw.shapes.items()}
