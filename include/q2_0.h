@@ -202,8 +202,8 @@ int q2_0_mul_mat_vec_batch(const q2_0_mat_vec_batch_item *items, int64_t n_items
  *     carries every element as an fp16 pair hi = fp16(x), lo = fp16(x - hi) (2^-22
  *     relative error within 2^17 of the column's largest |x|, at most 2^-39 of that
  *     largest |x| below).  Both halves meet the weights on the matrix cores (products
- *     exact); each 64-weight block is summed in an f32 accumulator of its own and the
- *     block sums are added in fp64.  Then
+ *     exact); every two 64-weight blocks are summed in an f32 accumulator of their own
+ *     (8 matrix-core steps) and these sums are added in fp64.  Then
  *         |y - y_exact| <= 1e-5 * A
  *     for finite x with |x| < 2^100, |d| <= 32752 and K <= 16384 whenever
  *         max_k |x[n][k]| * sum_k |W[m][k]| <= 2^21 * A     (range condition),

@@ -520,8 +520,8 @@ size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 //      whose experts hold a few dozen columns each (half the MFMAs and x loads of A per
 //      tile there, for the same weight decode).
 //   D: C's tile with x as hi/lo pairs (fp32-grade): two x tiles per buffer, two MFMAs
-//      per operand pair (so each decoded weight fragment feeds four, as in A), the fp64
-//      sums in registers; two workgroups per CU (at three the registers spill; A's
+//      per operand pair (so each decoded weight fragment feeds four, as in A), an f32
+//      accumulator per two blocks and the fp64 sums in registers; two workgroups per CU (at three the registers spill; A's
 //      128-column tile would need 128 registers of fp64 sums per lane and spills too).
 // (256 x 64 tiles, RF 2 x NJ 2 at three workgroups per CU -- half the LDS operand reads
 // per MFMA of A, twice the decode per MFMA -- measured ~10 % slower than A at N = 512.)
