@@ -34,16 +34,21 @@ def experts(seed, ne, M, K):
                      for e in range(ne)])
 
 
-def run_id(wall, ne, M, K, x_store, xt, ids, precision, ldy=None):
+def run_id(wall, ne, M, K, x_store, xt, ids, precision, ldy=None, ldx=None):
     torch = _torch()
     nt, nu = ids.shape
     ldy = ldy or M
+    ldx = ldx or K
+    if ldx > K:                                    # strided x: each row padded to ldx elements
+        pad = np.zeros((x_store.shape[0], ldx), dtype=x_store.dtype)
+        pad[:, :K] = x_store
+        x_store = pad
     wd, xd, idd = dev(wall), dev(x_store), dev(ids.astype(np.int32))
     x_slots = x_store.shape[0] // nt
     yd = torch.full((nt * nu, ldy), float("inf"), dtype=torch.float32, device="cuda")
     need = B.mul_mat_id_workspace_bytes(ne, M, K, nu, nt, precision)
     ws = torch.full((need // 4 + 1,), float("nan"), dtype=torch.float32, device="cuda")
-    st = B.mul_mat_id_raw(wd.data_ptr(), ne, M, K, xd.data_ptr(), xt, K, x_slots, idd.data_ptr(), nu, nt,
+    st = B.mul_mat_id_raw(wd.data_ptr(), ne, M, K, xd.data_ptr(), xt, ldx, x_slots, idd.data_ptr(), nu, nt,
                           yd.data_ptr(), ldy, precision, ws.data_ptr(), need, torch.cuda.current_stream().cuda_stream)
     assert st == 0, B.lib().q2_0_status_string(st)
     y = host(yd)
@@ -132,6 +137,27 @@ def test_mul_mat_id_routing_path_edges(precision, ne, nt, nu):
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
     y_ref, bound = oracle.mul_mat_id(wall, ne, M, K, x, ids)
     check(y, y_ref, bound, REL[precision], "ne=%d nt=%d p%d" % (ne, nt, precision))
+
+
+@pytest.mark.parametrize("slots", ["token", "slot"])
+@pytest.mark.parametrize("ne,nt", [(16, 60), (300, 40)])
+def test_mul_mat_id_strided_x(slots, ne, nt):
+    """x rows ldx = K + 1 elements apart (not a multiple of four: the conversion reads
+    element by element), through the one-pass routing (16 experts) and the chunked one
+    (300 experts): bit for bit the result of the same x stored contiguously, and within
+    the bound of the oracle."""
+    rng = np.random.default_rng(ne + nt + len(slots))
+    M, K, nu = 96, 512, 4
+    wall = experts(67, ne, M, K)
+    ids = rng.integers(0, ne, size=(nt, nu)).astype(np.int32)
+    rows = nt if slots == "token" else nt * nu
+    x = synth.activations(67, rows, 0, rows, K)
+    p = B.Q2_0_PREC_F16_MFMA
+    y = run_id(wall, ne, M, K, x, B.Q2_0_ACT_F32, ids, p, ldx=K + 1)
+    y0 = run_id(wall, ne, M, K, x, B.Q2_0_ACT_F32, ids, p)
+    assert np.array_equal(y.view(np.uint32), y0.view(np.uint32))
+    y_ref, bound = oracle.mul_mat_id(wall, ne, M, K, x, ids)
+    check(y, y_ref, bound, REL[p], "strided x ne=%d %s" % (ne, slots))
 
 
 @pytest.mark.parametrize("precision", [B.Q2_0_PREC_F16_MFMA, B.Q2_0_PREC_F32])
