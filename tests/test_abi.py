@@ -158,6 +158,14 @@ def test_gemm_group_validation_and_workspace():
     g = B.mul_mat_group_workspace_bytes(big, 3, 4096, 512, B.Q2_0_PREC_F16_MFMA)
     singles = [B.mul_mat_workspace_bytes(M, 4096, 512, B.Q2_0_PREC_F16_MFMA) for M in (4096, 1024, 1024)]
     assert 512 * 4096 * 2 < g < sum(singles)   # x staged once, fewer splits than the small singles
+    # the fp32-grade matrix-core precision: x as two fp16 halves for the group, nothing for N <= 8
+    F32M = B.Q2_0_PREC_F32_MFMA
+    need_m = B.mul_mat_group_workspace_bytes(ok, 3, 64, 20, F32M)
+    assert need_m >= 2 * 20 * 64 * 2
+    assert B.mul_mat_group_workspace_bytes(ok, 3, 64, 8, F32M) == 0
+    assert B.mul_mat_group_raw(ok, 3, 64, P16, 64, 20, F32M, P16, need_m - 1) == B.Q2_0_ERR_WORKSPACE
+    gm = B.mul_mat_group_workspace_bytes(big, 3, 4096, 512, F32M)
+    assert gm >= 2 * 512 * 4096 * 2
 
 
 def test_activation_type_validation():
