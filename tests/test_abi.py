@@ -261,6 +261,11 @@ def test_mul_mat_noalloc_validation():
     assert B.mul_mat_workspace_bytes(4096, 12288, 4096, 0) > B.NOALLOC_SCRATCH_BYTES
     assert nr(P16, 4096, 12288, P16, 12288, 4096, P16, 4096, 0) == B.Q2_0_ERR_TOO_LARGE
     assert B.lib().q2_0_status_string(B.Q2_0_ERR_TOO_LARGE).decode().startswith("Q2_0_ERR_TOO_LARGE")
+    # the fp32-grade matrix-core precision stages x twice over: the limit comes at half the N
+    F32M = B.Q2_0_PREC_F32_MFMA
+    assert 0 < B.mul_mat_workspace_bytes(4096, 12288, 512, F32M) <= B.NOALLOC_SCRATCH_BYTES
+    assert B.mul_mat_workspace_bytes(4096, 12288, 2048, F32M) > B.NOALLOC_SCRATCH_BYTES
+    assert nr(P16, 4096, 12288, P16, 12288, 2048, P16, 4096, F32M) == B.Q2_0_ERR_TOO_LARGE
 
 
 def test_mul_mat_vec_batch_validation():

@@ -91,6 +91,17 @@ def test_split_planned_somewhere():
     assert max(planned_splits(M, K, N) for M, K, N in [(120, 1536, 60), (256, 12288, 16), (4096, 4096, 512)]) > 1
 
 
+def test_wide_n_many_column_tiles():
+    """N = 1500: 24 column tiles of 64 (no XCD column map), a ragged last one, sampled
+    rows and every column against the oracle."""
+    M, K, N = 260, 2048, 1500
+    w = synth.weight(68, M, N, M, K, "quad", synth.ScaleDist("uniform", 0.005, 0.05))
+    x = synth.activations(68, M, N, N, K)
+    y = run_mul_mat(dev(w), M, K, x, P)
+    rows = np.unique(np.concatenate([np.arange(0, M, 17), [M - 1]]))
+    assert_products(y, w, M, K, x, REL_F32, rows=rows, what="N=%d" % N)
+
+
 def test_weights_at_two_byte_offset():
     torch = __import__("torch")
     for M, K, N in [(200, 512, 130), (333, 640, 70)]:
