@@ -1,35 +1,38 @@
 // Persistent mat-vec for N = 1, 2 on the gfx950 matrix cores' 16-block 4x4x4
 // product, with the activation broadcast from registers inside groups of 16 lanes.
 //
-// Arithmetic as in the other MFMA mat-vec kernels (bisque.today "WebGPU: add Q2_0
-// support", the matrix-vector paragraph: per 64-weight block the sum of (q - 1) * x,
-// multiplied by the block scale once): exact fp16 (q - 1) from the pair decode, the
-// activation as an fp16 hi/lo pair scaled per column by a power of two, products
-// exact, sums in f32.
+// Arithmetic (bisque.today "WebGPU: add Q2_0 support", the matrix-vector paragraph: per
+// 64-weight block the sum of (q - 1) * x, multiplied by the block scale once), in one of
+// two modes, products exact either way:
+//  * exact mode (N = 1): each block of x as four 11-bit fixed-point limbs, the codes
+//    raw; every block sum is exact (described at bx_dword below);
+//  * hi/lo mode (N = 2): exact fp16 (q - 1) from the pair decode against x as an fp16
+//    hi/lo pair, each column scaled by a power of two; sums in f32.
 //
 // The product: v_mfma_f32_4x4x4_16b_f16 runs 16 independent 4x4x4 products, block b
 // on lanes 4b..4b+3; with CBSZ = 2 the blocks form 4 groups of 4 (16 lanes each), and
 // every block of group G takes the A operand of block 4G + ABID.  Lane 16G + 4a + i
-// holds A row i of chunk a, a chunk being 4 activations, the rows x hi, x lo (N = 1;
-// rows 2, 3 repeat them) or column 0 hi, lo and column 1 hi, lo (N = 2).  One pair of
-// VGPRs thus holds, for each group, the 16 activations of one code dword, and
-// ABID = 0..3 on 4 successive products selects its chunks.  B column 16G + r is
-// weight row r of the tile, i.e. the lane: group G's lanes decode the 16 rows' blocks
-// of quarter G of the stage, and each lane accumulates its own (row, quarter) sum in
-// D items 0..3.  The four quarters of a row are added once per tile by two lane
-// exchanges.  Activation reads from LDS: one 8-byte read per code dword and lane, a
-// quarter of what the 16x16x32 form needs; decode VALU: the pair decode only.
+// holds A row i of chunk a, a chunk being 4 activations, the rows limbs 0..3 (exact
+// mode) or column 0 hi, lo and column 1 hi, lo (hi/lo mode).  One pair of VGPRs thus
+// holds, for each group, the 16 activations of one code dword, and ABID = 0..3 on 4
+// successive products selects its chunks.  B column 16G + r is weight row r of the
+// tile, i.e. the lane: group G's lanes decode the 16 rows' blocks of quarter G of the
+// stage, and each lane accumulates its own (row, quarter) sum in D items 0..3.  The
+// four quarters of a row are added once per tile by two lane exchanges.  Activation
+// reads from LDS: one 8-byte read per code dword and lane, a quarter of what the
+// 16x16x32 form needs.
 //
 // Streaming as in mat_vec_stream.hip: work items (16-row tile, stage of 16 blocks),
 // tile-major, split evenly over persistent workgroups and their waves; each wave keeps
-// one stage in flight in registers (coalesced 16-byte loads, consecutive lanes on
-// consecutive bytes of a row: 16 rows x 288 bytes, an access pattern that reads at
-// the full rate of a contiguous stream) while it decodes the previous one from a
-// wave-private LDS tile.  The park routes each 8-byte half of a loaded chunk to the
-// LDS area of its quarter (80 bytes per quarter, 16-byte aligned), from which each lane
-// reads its quarter with five 16-byte reads.  A tile whose stages are split between
-// waves is finished after one barrier at the end, in stage order, so results are
-// deterministic.
+// two stages (exact mode) or one (hi/lo mode, whose registers allow no second) in
+// flight in registers -- coalesced 16-byte loads, consecutive lanes on consecutive
+// bytes of a row: 16 rows x 288 bytes, a pattern that reads at ~96 % of a contiguous
+// stream's rate -- while it decodes the previous one from a wave-private LDS tile.
+// The park routes each 8-byte half of a loaded chunk to the LDS area of its quarter (80
+// bytes per quarter, 16-byte aligned), from which each lane reads its quarter with five
+// 16-byte reads.  The activation is staged in windows of whole stages (phases); a tile
+// whose stages are split between waves is finished after the phase's barrier, in stage
+// order, so results are deterministic.
 #include <algorithm>
 #include <atomic>
 
