@@ -9,7 +9,10 @@
 //    into LDS, laid out as the MFMA A operand, behind a single barrier; each
 //    column is first scaled by a power of two that puts its max |x| just below
 //    2^15, so the fp16 hi/lo split neither overflows nor loses bits to fp16's
-//    subnormal range (the scale is undone on the results).
+//    subnormal range (the scale is undone on the results).  Where all of K does
+//    not fit, the host runs the kernel over chunks of whole stages, one launch
+//    each: a launch reads its chunk of every row (rows rowstride bytes apart) and
+//    every chunk after the first adds its results to y, in chunk order.
 //  * Work is a list of items (16-row tile, stage of SB blocks), tile-major.  Each
 //    workgroup owns a contiguous run of tiles and each of its W waves (4 to 16,
 //    chosen per shape so that the most waves stay resident within the LDS the
