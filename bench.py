@@ -330,6 +330,7 @@ def main():
     # an expert layer: 128 experts of 768 x 2048 (random blocks with finite scales), 8 of
     # them per token; prefill 512 tokens on the fp16 GEMM, decode one token on the mat-vec
     MOE_E, MOE_M, MOE_K, MOE_USED = 128, 768, 2048, 8
+    MOE_CALLS = 20
     moe_w = torch.randint(0, 256, (MOE_E * MOE_M, MOE_K // 64, 18), dtype=torch.uint8, device=dev, generator=gen)
     moe_w[:, :, 1] &= 0x3B
     moe_ids_p = torch.stack([torch.randperm(MOE_E, device=dev, generator=gen)[:MOE_USED]
@@ -463,23 +464,26 @@ def main():
         torch.cuda.synchronize()
         graph_one = float(np.mean([a.elapsed_time(b) for a, b in gev]))
 
-    # the decode kernel's own launch time: launches enqueued back to back, an event between
-    # each two, so that the GPU finds the next launch queued (no graph launch, no gap)
-    # the expert layer's calls (two launches each) enqueued back to back, events around the
-    # run: their own time, without the ~15-20 us that a graph replay of a few launches adds
+    # the expert layer's calls, MOE_CALLS of them captured back to back in one graph: the
+    # GPU's own time per call (one call per replay would add the ~15-20 us of a graph
+    # launch; calls issued one by one from Python would time the host's issue rate, slower
+    # than the one-launch decode call itself)
     ms_b2b = {}
     for name in ("expert_layer_prefill", "expert_layer_decode"):
         if name in parts:
-            parts[name]()
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
-            for _ in range(4 * args.steps):
-                parts[name]()
-            b.record()
-            torch.cuda.synchronize()
-            ms_b2b[name] = a.elapsed_time(b) / (4 * args.steps)
+            fn = parts[name]
+            ms_b2b[name] = graph_ms(torch, lambda: [fn() for _ in range(MOE_CALLS)], args.steps) / MOE_CALLS
+    # and at 1, 16, 128 and 512 tokens (the first rows of the prefill's ids), the same way
+    moe_by_tokens = {}
+    if "expert_layer_prefill" in parts:
+        for nt in (1, 16, 128, PREFILL_N):
+            ids_nt = moe_ids_p[:nt].contiguous()
+            moe_by_tokens[nt] = round(1e3 * graph_ms(
+                torch, lambda: [run_moe(ids_nt, B.Q2_0_PREC_F16_MFMA) for _ in range(MOE_CALLS)],
+                args.steps) / MOE_CALLS, 2)
 
+    # the decode kernel's own launch time: launches enqueued back to back, an event between
+    # each two, so that the GPU finds the next launch queued (no graph launch, no gap)
     launch_us = None
     if "decode_mat_vec" in graphs:
         run_decode_matvecs()
@@ -497,7 +501,8 @@ def main():
                     "samples": len(ev[n])}
                 for n in ("prefill_gemm", "decode_mat_vec", "decode_mat_vec_per_layer") if n in ev and ev[n]}
     if set(step_parts) != {"prefill_get_rows", "prefill_gemm", "decode_get_rows", "decode_mat_vec"}:
-        print(json.dumps({"partial_run": True, "ms": ms, "ms_back_to_back": ms_b2b}), flush=True)
+        print(json.dumps({"partial_run": True, "ms": ms, "ms_back_to_back": ms_b2b,
+                          "expert_layer_us_per_call_by_tokens": moe_by_tokens}), flush=True)
         return
 
     # ---- algorithmic work
@@ -583,7 +588,8 @@ def main():
             "algorithmic_bytes": int(pre_bytes),
             "mfma_busy_frac_counters": mfma.get("mfma_busy_frac"),
         },
-        "next_rows": next_rows(ms, ms_b2b, wl, order, VM, VK, pre_flops, MOE_E, MOE_M, MOE_K, MOE_USED),
+        "next_rows": next_rows(ms, ms_b2b, moe_by_tokens, wl, order, VM, VK, pre_flops, MOE_E, MOE_M, MOE_K,
+                               MOE_USED),
         "cpu_baseline": None,
     }
     if not args.no_extra:
@@ -796,9 +802,9 @@ def measured_ceilings(torch, dev, wl, matvec_gbs, gemm_tflops):
     return out
 
 
-def next_rows(ms, ms_b2b, wl, order, VM, VK, pre_flops, ne, mm, mk, nu):
+def next_rows(ms, ms_b2b, moe_by_tokens, wl, order, VM, VK, pre_flops, ne, mm, mk, nu):
     """Rates of the widened rows, timed beside the step (HIP events around their graphs; the
-    expert layer's calls back to back, ms_b2b, with the graph-replay figures beside)."""
+    expert layer's calls 20 to a graph, ms_b2b, with one call per replay beside)."""
     out = {}
 
     def rate(name, work, scale, src=None):
@@ -828,6 +834,8 @@ def next_rows(ms, ms_b2b, wl, order, VM, VK, pre_flops, ne, mm, mk, nu):
                                               "quantize_vocab_f32", "repack_g128_vocab", "expert_layer_prefill",
                                               "expert_layer_decode") if k in ms}
     out["ms_expert_layer_back_to_back"] = {k: round(v, 4) for k, v in ms_b2b.items()}
+    out["expert_layer_back_to_back_note"] = "20 calls captured back to back in one graph, ms per call"
+    out["expert_layer_us_per_call_by_tokens"] = {str(k): v for k, v in moe_by_tokens.items()}
     return out
 
 
