@@ -754,10 +754,13 @@ hipError_t launch_mat_vec_bcast(const MvGroup &grp, const MvSegDesc *d, int nseg
         ns_max = std::max(ns_max, ns);
         items += (int64_t)(d[i].tile1 - d[i].tile0) * ns;
     }
-    // Waves per workgroup: 16 (one workgroup per CU); small launches use fewer until
-    // there is a workgroup per CU.
+    // Waves per workgroup: 16 (one workgroup per CU) while an item for every wave still
+    // leaves a workgroup per CU, else 8, and small launches then leave some waves without
+    // an item.  Not 4: the workgroup's threads stage the whole activation window, and at 4
+    // waves a 4096-long row takes each thread two rounds of loads and conversion (~2 us on
+    // every launch's path, measured; 3 % of a per-layer decode).
     int waves = kMvStreamMaxWaves;   // a power of two (the kernel splits work by shifts)
-    while (waves > 4 && (items + waves - 1) / waves < 256) waves /= 2;
+    while (waves > 8 && (items + waves - 1) / waves < 256) waves /= 2;
     // windows: whole rows where the LDS left holds them all, else at most cap_phased stages
     const int64_t per_stage = (int64_t)kBcSB * (int64_t)x_bytes_per_block(N, exact);
     const int64_t avail = (int64_t)160 * 1024 - (int64_t)waves * (kBcWaveLds + 64 * 8) - (int64_t)kMvStreamStaticLds;
@@ -786,7 +789,8 @@ hipError_t launch_mat_vec_bcast(const MvGroup &grp, const MvSegDesc *d, int nseg
     const int tacc_cap = phased ? (int)((160 * 1024 - fixed) / ((size_t)kBcRows * N * 4)) : 0;
     if (phased && tacc_cap < 1) return hipErrorInvalidValue;
     const int per_cu = std::max(1, (int)((160 * 1024) / fixed));
-    int64_t want = std::min<int64_t>((items + waves - 1) / waves, 256 * (int64_t)per_cu);
+    // at least a workgroup per CU where the tiles allow (some waves may then get no item)
+    int64_t want = std::min<int64_t>(std::max<int64_t>((items + waves - 1) / waves, 256), 256 * (int64_t)per_cu);
     int wg = 0, tacc = 0;
     for (int i = 0; i < nsegs; ++i) {
         MvSeg &g = segs.s[i];
