@@ -196,17 +196,17 @@ __global__ __launch_bounds__(256) void mat_vec_mfma(const uint8_t *__restrict__ 
     }
 }
 
-// Host-side choice of K slices: prefer whole-K waves (cheapest activation staging)
-// while the grid still has at least two workgroups per CU.  Expert pairs split K less
-// (until a pair's workgroups reach 128 / pairs): a call of 8 pairs of 768 x 2048 took
-// 5.7 us in 2 slices (192 workgroups), 6.3 us in 4 and 6.6 us in 1 -- short calls pay for
-// every wave they start.
+// Host-side choice of K slices: split K (up to 4 ways) while the grid has fewer than a
+// workgroup per CU, or, for expert pairs, until a pair's workgroups reach 128 / pairs.
+// Short calls pay for every wave they start: 8 pairs of 768 x 2048 took 5.7 us in 2
+// slices (192 workgroups), 6.3 us in 4 and 6.6 us in 1; a 12288 x 4096 matrix ~1.9 us
+// less in 2 slices (384 workgroups) than in 4.
 template <int NC, typename XT>
 static hipError_t launch_nc(const uint8_t *w, int M, int nb, const XT *x, int64_t ldx, float *y,
                             int64_t ldy, hipStream_t s, const PairRoute &route = PairRoute{}, int pairs = 1) {
     const int tiles = (M + kTile - 1) / kTile;
     int ks = 1;
-    const int want = pairs > 1 ? (128 / pairs > 0 ? 128 / pairs : 1) : 512;
+    const int want = pairs > 1 ? (128 / pairs > 0 ? 128 / pairs : 1) : 256;
     const int maxks = (NC <= 4) ? 4 : 2;
     while (ks < maxks && (tiles + (4 / ks) - 1) / (4 / ks) < want && nb % (8 * ks * 2) == 0) ks *= 2;
     const int rg = 4 / ks;
