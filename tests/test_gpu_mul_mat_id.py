@@ -226,3 +226,32 @@ def test_mul_mat_id_torch_wrapper():
     y = B.q2_0_mul_mat_id(dev(wall), ne, M, K, x, ids, precision=B.Q2_0_PREC_F32)
     y_ref, bound = oracle.mul_mat_id(wall, ne, M, K, x.cpu().numpy(), ids.cpu().numpy())
     check(host(y), y_ref, bound, 1e-5, "wrapper")
+
+
+_BENCH_EXPERTS = {}
+
+
+def bench_experts():
+    """128 experts of 768 x 2048, the expert layer the benchmark times."""
+    if "w" not in _BENCH_EXPERTS:
+        _BENCH_EXPERTS["w"] = experts(65, 128, 768, 2048)
+    return _BENCH_EXPERTS["w"]
+
+
+@pytest.mark.parametrize("nt,nu", [(1, 8), (1, 2), (3, 8), (16, 8), (128, 8), (512, 8)])
+def test_mul_mat_id_bench_expert_layer(nt, nu):
+    """The benchmark's expert layer (128 experts of 768 x 2048) at its token counts, on the
+    fast precision: up to 8 tokens one fp32-grade mat-vec per pair (1 token x 8 slots: K in
+    2 slices; 1 x 2: in 4; 3 x 8: in 1), more tokens the routed fp16 GEMM.  Sampled tokens
+    against the oracle, each at the tolerance of the path that served it."""
+    ne, M, K = 128, 768, 2048
+    rng = np.random.default_rng(65 + nt * 10 + nu)
+    wall = bench_experts()
+    ids = np.stack([rng.permutation(ne)[:nu] for _ in range(nt)]).astype(np.int32)
+    x = synth.activations(65, nt, nu, nt, K)
+    y = run_id(wall, ne, M, K, x, B.Q2_0_ACT_F32, ids, B.Q2_0_PREC_F16_MFMA)
+    pick = np.sort(rng.choice(nt, size=min(nt, 12), replace=False))
+    y_ref, bound = oracle.mul_mat_id(wall, ne, M, K, x[pick], ids[pick])
+    rows = (pick[:, None] * nu + np.arange(nu)[None, :]).reshape(-1)
+    rel = REL[B.Q2_0_PREC_F32] if nt <= 8 else REL[B.Q2_0_PREC_F16_MFMA]
+    check(y[rows], y_ref, bound, rel, "bench layer nt=%d nu=%d" % (nt, nu))
