@@ -739,7 +739,7 @@ static hipError_t launch_bcast_nc(const MvGroup &grp, const MvSegs &segs, hipStr
 
 // grp counts tiles of kMvBcastRows rows; N is 1 or 2; every segment's rows and
 // activation 16-byte aligned and nb % 8 == 0.  Workgroups go to the segments in
-// proportion to their stages of work.
+// proportion to their stages of work (a phased segment's stages weighted, below).
 hipError_t launch_mat_vec_bcast(const MvGroup &grp, const MvSegDesc *d, int nsegs, Act xt, int N, hipStream_t s) {
     if (N < 1 || N > 2 || nsegs < 1 || nsegs > kMvMaxSegs) return hipErrorInvalidValue;
     const bool exact = N == 1;
@@ -791,12 +791,24 @@ hipError_t launch_mat_vec_bcast(const MvGroup &grp, const MvSegDesc *d, int nseg
     const int per_cu = std::max(1, (int)((160 * 1024) / fixed));
     // at least a workgroup per CU where the tiles allow (some waves may then get no item)
     int64_t want = std::min<int64_t>(std::max<int64_t>((items + waves - 1) / waves, 256), 256 * (int64_t)per_cu);
+    // Workgroups go to the segments in proportion to their stages, a stage of a phased
+    // segment (several windows: its activation staged again, its tile sums kept in LDS)
+    // counted as 1.036: measured per workgroup, with equal bytes each, the decode step's
+    // K = 12288 workgroups (two windows) ended 3.6 % after its K = 4096 ones (one window),
+    // and weighting them so took that launch from 419.5 to 414.8 us.
+    constexpr int64_t kStageWeight = 1000, kPhasedStageWeight = 1036;
+    auto seg_work = [&](const MvSeg &g) {
+        const int64_t ns_ = (g.nb + kBcSB - 1) / kBcSB;
+        return (int64_t)(g.tile1 - g.tile0) * ns_ * (g.ws < ns_ ? kPhasedStageWeight : kStageWeight);
+    };
+    int64_t work = 0;
+    for (int i = 0; i < nsegs; ++i) work += seg_work(segs.s[i]);
     int wg = 0, tacc = 0;
     for (int i = 0; i < nsegs; ++i) {
         MvSeg &g = segs.s[i];
         const int T = g.tile1 - g.tile0;
         const int ns = (g.nb + kBcSB - 1) / kBcSB;
-        int64_t n = (want * T * ns + items / 2) / items;       // share of the workgroups
+        int64_t n = (want * seg_work(g) + work / 2) / work;    // share of the workgroups
         n = std::max<int64_t>(1, std::min<int64_t>(n, T));     // at least one tile each
         if (g.ws < ns) n = std::max<int64_t>(n, (T + tacc_cap - 1) / tacc_cap);
         if ((int64_t)wg + n > 0x7fffffff) return hipErrorInvalidValue;
