@@ -24,8 +24,7 @@
 //
 // Streaming as in mat_vec_stream.hip: work items (16-row tile, stage of 16 blocks),
 // tile-major, split evenly over persistent workgroups and their waves; each wave keeps
-// two stages (exact mode) or one (hi/lo mode, whose registers allow no second) in
-// flight in registers -- coalesced 16-byte loads, consecutive lanes on consecutive
+// one stage in flight in registers -- coalesced 16-byte loads, consecutive lanes on consecutive
 // bytes of a row: 16 rows x 288 bytes, a pattern that reads at ~96 % of a contiguous
 // stream's rate -- while it decodes the previous one from a wave-private LDS tile.
 // The park routes each 8-byte half of a loaded chunk to the LDS area of its quarter (80
@@ -521,11 +520,12 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_bcast(MvGroup grp, MvSegs s
         }
     };
 
-    // Stages in flight per wave: two in exact mode (its registers allow a second set),
-    // one otherwise.  Q2_0_ISSUE_NEXT loads the wave's next item of the phase, or once all
-    // are issued the last one again.
-    constexpr int DEPTH = EXACT ? 2 : 1;
-    u32x4_t ra[kBcCH], rb[kBcCH];
+    // One stage in flight per wave.  A second register set (exact mode has the registers for
+    // it) measured no faster on the 8B decode launch (419 against 415 us with one) and 7 %
+    // slower on the per-layer schedule, whose small launches leave many waves a single
+    // item that the second set then loads twice.  Q2_0_ISSUE_NEXT loads the wave's next
+    // item of the phase, or once all are issued the last one again.
+    u32x4_t ra[kBcCH];
     for (int p = 0; p < P; ++p) {   // the same trip count in every wave: the barriers need it
         const int sw0 = p * W;                               // first stage of the window
         const int sp = min(W, ns - sw0);
@@ -565,10 +565,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_bcast(MvGroup grp, MvSegs s
         const int nbw = min(sp * kBcSB, nb - blk0);
         LimbLoads xld;
         if (EXACT) limbs_load(xw, nbw, 0, tid, WAVES * 64, xld);
-        if (n > 0) {
-            Q2_0_ISSUE_NEXT(ra)
-            if (DEPTH == 2) Q2_0_ISSUE_NEXT(rb)
-        }
+        if (n > 0) Q2_0_ISSUE_NEXT(ra)
         if (EXACT) {
             limbs_convert(nbw, 0, tid, WAVES * 64, xld, lds_x, lds_bs, lds_bsc);
             for (int q0 = kLimbU * WAVES * 64; q0 < nbw * 16; q0 += kLimbU * WAVES * 64) {
@@ -628,31 +625,15 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_bcast(MvGroup grp, MvSegs s
         }                                                                                      \
     }
 
-        // Each step parks the stage that arrived in one register set, reissues that set
-        // for the item DEPTH ahead and decodes the parked stage while the other loads are
-        // in flight.  No exit in the middle of a loop, which keeps the compiler's memory
-        // wait counts exact.
-        if (DEPTH == 1) {
-            for (int k = 0; k < n; ++k) {
-                Q2_0_PARK(ra)
-                __builtin_amdgcn_wave_barrier();
-                Q2_0_ISSUE_NEXT(ra)
-                Q2_0_COMPUTE(k + 1 < n)
-                __builtin_amdgcn_wave_barrier();
-            }
-        } else {
-            for (int k = 0; k < n; k += 2) {
-                Q2_0_PARK(ra)
-                __builtin_amdgcn_wave_barrier();
-                Q2_0_ISSUE_NEXT(ra)
-                Q2_0_COMPUTE(k + 1 < n)
-                __builtin_amdgcn_wave_barrier();
-                Q2_0_PARK(rb)
-                __builtin_amdgcn_wave_barrier();
-                Q2_0_ISSUE_NEXT(rb)
-                if (k + 1 < n) Q2_0_COMPUTE(k + 2 < n)
-                __builtin_amdgcn_wave_barrier();
-            }
+        // Each step parks the stage that arrived, reissues the register set for the next
+        // item and decodes the parked stage while those loads are in flight.  No exit in the
+        // middle of a loop, which keeps the compiler's memory wait counts exact.
+        for (int k = 0; k < n; ++k) {
+            Q2_0_PARK(ra)
+            __builtin_amdgcn_wave_barrier();
+            Q2_0_ISSUE_NEXT(ra)
+            Q2_0_COMPUTE(k + 1 < n)
+            __builtin_amdgcn_wave_barrier();
         }
 #undef Q2_0_COMPUTE
 #undef Q2_0_ISSUE_NEXT
