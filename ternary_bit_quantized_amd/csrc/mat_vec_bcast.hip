@@ -456,9 +456,8 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_bcast(MvGroup grp, MvSegs s
         }                                                                                          \
         ld_tile = (TILE);                                                                          \
     }
-    // Every call issues exactly kBcCH loads (items past the wave's range of the phase
-    // reload the last one), so the wait counts before each park stay exact.  In the half
-    // stage at the end of a ragged row, chunks past its 144 bytes load its last chunk again.
+    // Every call issues kBcCH loads.  In the half stage at the end of a ragged row, chunks
+    // past its 144 bytes load its last chunk again.
 #define Q2_0_ISSUE(IT, REG)                                                                    \
     {                                                                                          \
         if ((IT).tile != ld_tile) Q2_0_SET_LOAD_TILE((IT).tile)                               \
@@ -524,7 +523,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_bcast(MvGroup grp, MvSegs s
     // it) measured no faster on the 8B decode launch (419 against 415 us with one) and 7 %
     // slower on the per-layer schedule, whose small launches leave many waves a single
     // item that the second set then loads twice.  Q2_0_ISSUE_NEXT loads the wave's next
-    // item of the phase, or once all are issued the last one again.
+    // item of the phase (the loop calls it only while one is left).
     u32x4_t ra[kBcCH];
     for (int p = 0; p < P; ++p) {   // the same trip count in every wave: the barriers need it
         const int sw0 = p * W;                               // first stage of the window
@@ -626,12 +625,15 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_bcast(MvGroup grp, MvSegs s
     }
 
         // Each step parks the stage that arrived, reissues the register set for the next
-        // item and decodes the parked stage while those loads are in flight.  No exit in the
-        // middle of a loop, which keeps the compiler's memory wait counts exact.
+        // item and decodes the parked stage while those loads are in flight.  The last step
+        // issues nothing: a wave cannot end before its loads return, and in small launches,
+        // where many waves hold one or two items, a reload of the last one (to keep a fixed
+        // number of loads in flight) landed on the launch's tail.  With one register set the
+        // park waits for all of the wave's loads in any case.
         for (int k = 0; k < n; ++k) {
             Q2_0_PARK(ra)
             __builtin_amdgcn_wave_barrier();
-            Q2_0_ISSUE_NEXT(ra)
+            if (k + 1 < n) Q2_0_ISSUE_NEXT(ra)
             Q2_0_COMPUTE(k + 1 < n)
             __builtin_amdgcn_wave_barrier();
         }

@@ -139,8 +139,8 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_stream(MvGroup grp, int nb,
         if (n.st == ns) { n.st = 0; n.tile += 1; }
         return n;
     };
-    // Every call issues exactly CH loads (items past the wave's range reload the current
-    // one), so the wait counts before each park stay exact.
+    // Every call issues CH loads; only the wave's own items are loaded (the last step issues
+    // nothing, and with one register set each park waits for all of the wave's loads).
 #define Q2_0_ISSUE(IT, REG)                                                                    \
     {                                                                                          \
         if ((IT).tile != ld_tile) Q2_0_SET_LOAD_TILE((IT).tile)                               \
@@ -229,8 +229,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_stream(MvGroup grp, int nb,
     for (int k = 0; k < n_items; ++k) {
         Q2_0_PARK(reg)
         __builtin_amdgcn_wave_barrier();
-        const Item load = (k + 1 < n_items) ? nxt : cur;
-        Q2_0_ISSUE(load, reg)
+        if (k + 1 < n_items) Q2_0_ISSUE(nxt, reg)   // nothing after the last item: its wave ends sooner
         compute_and_store(cur);
         __builtin_amdgcn_wave_barrier();
         if (k + 1 < n_items && nxt.tile != cur.tile) tr_out = cursor_tile<kMvTile>(grp, t0v, out_cur, nxt.tile);
