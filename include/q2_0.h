@@ -303,9 +303,11 @@ int q2_0_mul_mat_group_act(const q2_0_mat_vec_item *items, int64_t n_items, int6
  *             outside [0, n_expert) makes its y column quiet NaN and reads nothing.
  *   y       : f32 column (t, u) at y + (t*n_used + u)*ldy, ldy >= M.
  *   precision: as for q2_0_mul_mat: Q2_0_PREC_F16_MFMA (x rounded to fp16 as there,
- *             2e-3 bound under its range condition; few tokens, n_tokens <= 8, take
- *             the fp32-grade mat-vec, one per pair, with the mat-vec's bound and range
- *             condition) or Q2_0_PREC_F32 (the fp32 GEMM, 1e-5 bound, no range
+ *             2e-3 bound under its range condition; few pairs -- n_tokens <= 8, or
+ *             fewer pairs than twice n_expert -- take the fp32-grade mat-vec, one per
+ *             pair, with the mat-vec's bound and range condition: it streams the
+ *             experts faster than the GEMM decodes them while experts get about two
+ *             pairs or fewer) or Q2_0_PREC_F32 (the fp32 GEMM, 1e-5 bound, no range
  *             condition); Q2_0_PREC_F32_MFMA runs as Q2_0_PREC_F32, whose guarantee
  *             covers its own.
  *   workspace / ws_bytes: at least q2_0_mul_mat_id_workspace_bytes() bytes, 16-byte

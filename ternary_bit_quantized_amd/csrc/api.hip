@@ -250,9 +250,16 @@ int q2_0_mul_mat_id(const void *w, int64_t n_expert, int64_t M, int64_t K, const
     const uint8_t *wb = static_cast<const uint8_t *>(w);
     const int nb = (int)(K / Q2_0_BLOCK_WEIGHTS);
     const q2_0::Act xt = (q2_0::Act)x_type;
-    // few tokens with the fast precision (as q2_0_mul_mat with N <= 8): one fp32-grade
-    // mat-vec per pair
-    if (precision == Q2_0_PREC_F16_MFMA && n_tokens <= Q2_0_MAT_VEC_MAX_N && n_pairs <= 65535 &&
+    // Few pairs with the fast precision: one fp32-grade mat-vec per pair -- up to 8 tokens
+    // (as q2_0_mul_mat with N <= 8), and while the pairs are fewer than twice the experts.
+    // The routed GEMM reads each used expert once but is bound by decoding the weights
+    // (~1.6 TB/s of weight bytes); the per-pair mat-vec reads an expert once per pair but
+    // streams at ~4 TB/s, so it wins while the pairs number under about 2.5 times the
+    // distinct experts, whatever M and K.  Measured on 128 experts of 768 x 2048, 8 slots:
+    // 9, 16 and 32 tokens 14.8, 20.5 and 34.5 us per call against 27.7, 28.7 and 36.5 for
+    // the GEMM; 48 tokens 48.2 against 35.9.
+    const bool few_pairs = n_tokens <= Q2_0_MAT_VEC_MAX_N || n_pairs < 2 * n_expert;
+    if (precision == Q2_0_PREC_F16_MFMA && few_pairs && n_pairs <= 65535 &&
         q2_0::mat_vec_mfma_eligible(wb, M, nb, x, xt, ldx)) {
         // (out-of-range ids: NaN columns, written by the same launch)
         return hip_status(q2_0::launch_mat_vec_mfma_pairs(wb, M, nb, x, xt, ldx, ids, (int)n_expert, (int)n_used,

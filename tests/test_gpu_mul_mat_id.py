@@ -64,7 +64,8 @@ def check(y, y_ref, bound, rel, what):
         what, r["n_bad"], r["n"], rel, r["max_err_over_bound"], r["first_bad"])
 
 
-# few tokens (<= 8) take one mat-vec per pair, more tokens the expert-tiled GEMM
+# few pairs (<= 8 tokens, or fewer pairs than twice the experts) take one mat-vec per pair,
+# more the expert-tiled GEMM
 ROUTINGS = ["decode", "decode_bad_ids", "few_one_expert", "prefill", "one_expert", "bad_ids"]
 
 
@@ -140,11 +141,11 @@ def test_mul_mat_id_routing_path_edges(precision, ne, nt, nu):
 
 
 @pytest.mark.parametrize("slots", ["token", "slot"])
-@pytest.mark.parametrize("ne,nt", [(16, 60), (300, 40)])
+@pytest.mark.parametrize("ne,nt", [(16, 60), (300, 160)])
 def test_mul_mat_id_strided_x(slots, ne, nt):
     """x rows ldx = K + 1 elements apart (not a multiple of four: the conversion reads
     element by element), through the one-pass routing (16 experts) and the chunked one
-    (300 experts): bit for bit the result of the same x stored contiguously, and within
+    (300 experts; 640 pairs, enough to take the GEMM): bit for bit the result of the same x stored contiguously, and within
     the bound of the oracle."""
     rng = np.random.default_rng(ne + nt + len(slots))
     M, K, nu = 96, 512, 4
@@ -241,9 +242,10 @@ def bench_experts():
 @pytest.mark.parametrize("nt,nu", [(1, 8), (1, 2), (3, 8), (16, 8), (128, 8), (512, 8)])
 def test_mul_mat_id_bench_expert_layer(nt, nu):
     """The benchmark's expert layer (128 experts of 768 x 2048) at its token counts, on the
-    fast precision: up to 8 tokens one fp32-grade mat-vec per pair (1 token x 8 slots: K in
-    2 slices; 1 x 2: in 4; 3 x 8: in 1), more tokens the routed fp16 GEMM.  Sampled tokens
-    against the oracle, each at the tolerance of the path that served it."""
+    fast precision: one fp32-grade mat-vec per pair up to 8 tokens and while the pairs are
+    fewer than twice the experts (1 token x 8 slots: K in 2 slices; 1 x 2: in 4; 3 x 8: in
+    1; 16 x 8), more pairs the routed fp16 GEMM.  Sampled tokens against the oracle, each at
+    the tolerance of the path that served it."""
     ne, M, K = 128, 768, 2048
     rng = np.random.default_rng(65 + nt * 10 + nu)
     wall = bench_experts()
@@ -253,5 +255,25 @@ def test_mul_mat_id_bench_expert_layer(nt, nu):
     pick = np.sort(rng.choice(nt, size=min(nt, 12), replace=False))
     y_ref, bound = oracle.mul_mat_id(wall, ne, M, K, x[pick], ids[pick])
     rows = (pick[:, None] * nu + np.arange(nu)[None, :]).reshape(-1)
-    rel = REL[B.Q2_0_PREC_F32] if nt <= 8 else REL[B.Q2_0_PREC_F16_MFMA]
+    per_pair = nt <= 8 or nt * nu < 2 * ne
+    rel = REL[B.Q2_0_PREC_F32] if per_pair else REL[B.Q2_0_PREC_F16_MFMA]
     check(y[rows], y_ref, bound, rel, "bench layer nt=%d nu=%d" % (nt, nu))
+
+
+@pytest.mark.parametrize("nt,nu,ne", [(24, 8, 128), (31, 8, 128), (32, 8, 128), (40, 4, 96)])
+def test_mul_mat_id_few_pairs_per_expert(nt, nu, ne):
+    """More than 8 tokens but fewer pairs than twice the experts (24 and 31 tokens x 8 slots
+    over 128 experts, and 40 x 4 over 96) take the per-pair mat-vec on the fast precision;
+    32 x 8 = 256 pairs (exactly twice) takes the GEMM.  A few ids out of range give NaN
+    columns.  Every output against the oracle at the tolerance of the path that served it."""
+    M, K = 200, 1024
+    rng = np.random.default_rng(nt * 100 + nu + ne)
+    wall = experts(71, ne, M, K)
+    ids = rng.integers(0, ne, size=(nt, nu)).astype(np.int32)
+    ids[1, 0], ids[nt - 1, nu - 1] = -3, ne
+    x = synth.activations(71, nt, nu, nt, K)
+    y = run_id(wall, ne, M, K, x, B.Q2_0_ACT_F32, ids, B.Q2_0_PREC_F16_MFMA)
+    y_ref, bound = oracle.mul_mat_id(wall, ne, M, K, x, ids)
+    per_pair = nt * nu < 2 * ne
+    rel = REL[B.Q2_0_PREC_F32] if per_pair else REL[B.Q2_0_PREC_F16_MFMA]
+    check(y, y_ref, bound, rel, "few pairs nt=%d nu=%d ne=%d" % (nt, nu, ne))
