@@ -332,6 +332,15 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
         }
         return r;
     };
+    // Column fragments with a live column (uniform); in the expert product's configuration
+    // (NJ = 2 without hi/lo: its tiles are often part empty) the others skip their operand
+    // reads and products (128 experts of 768 x 2048 at 128 tokens: 40.8 -> 35.5 us per
+    // call).  The dense configurations keep every product: their tiles are full, and the
+    // branches measured 6-10 % slower on the prefill.
+    constexpr bool kSkipEmpty = NJ == 2 && !HL;
+    bool live[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) live[j] = !kSkipEmpty || n0 + 32 * j < Nv;
     auto step = [&](int buf, const WStep &ws) {
         const u32x4_t *wd = ws.wd;
         const half2_t *dd = ws.dd;
@@ -350,6 +359,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
             half8_t bv[NJ], bl[HL ? NJ : 1];
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
+                if (kSkipEmpty && j > 0 && !live[j]) continue;
                 bv[j] = *reinterpret_cast<const half8_t *>(&Bs[buf][(j * 32 + frow) * GK + bsw[kk]]);
                 if (HL) bl[j] = *reinterpret_cast<const half8_t *>(&Bs[buf][TN * GK + (j * 32 + frow) * GK + bsw[kk]]);
             }
@@ -357,6 +367,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_f16_mfma(GemmGroup grp, int nb,
             for (int i = 0; i < RF; ++i)
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
+                    if (kSkipEmpty && j > 0 && !live[j]) continue;
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], bv[j], acc[i][j], 0, 0, 0);
                     if (HL) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], bl[HL ? j : 0], acc[i][j], 0, 0, 0);
                 }
