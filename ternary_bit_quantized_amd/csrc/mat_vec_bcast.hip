@@ -390,15 +390,40 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_bcast(MvGroup grp, MvSegs s
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, G = lane >> 4;   // this lane's row of the tile and quarter of the stage
+    // ---- the kernel arguments this workgroup needs first, in one round trip: the tile
+    // table, and per lane one segment record (lane & 7) and one matrix record (lane), read
+    // as vectors; the workgroup's segment and its first tile's matrix are then picked with
+    // ballots and lane reads.  (Read one after another as scalars -- the segments' first
+    // workgroups, that segment's fields, then the matrix -- they were three dependent
+    // round trips on the way to the first weight load of every launch.)
     const int t0v = load_tile_table(grp);   // the tile table, one entry per lane
-
-    // ---- this workgroup's segment, activation, tiles [tb0, tb0 + nt) and phases
-    int sg = 0;
-    for (int i = 1; i < kMvMaxSegs; ++i)
-        if (i < segs.n && (int)blockIdx.x >= segs.s[i].wg0) sg = i;
-    const MvSeg &seg = segs.s[sg];
-    const XT *__restrict__ x = static_cast<const XT *>(seg.x);
-    const int64_t ldx = seg.ldx;
+    const uint8_t *const kargs = (const uint8_t *)__builtin_amdgcn_kernarg_segment_ptr();
+    constexpr size_t kSegsOff = (sizeof(MvGroup) + alignof(MvSegs) - 1) / alignof(MvSegs) * alignof(MvSegs);
+    const MvSeg *const segv = (const MvSeg *)(kargs + kSegsOff + offsetof(MvSegs, s)) + (lane & (kMvMaxSegs - 1));
+    const MvProblem *const probv = (const MvProblem *)(kargs + offsetof(MvGroup, p)) + lane;
+    const u32x4_t sv0 = *reinterpret_cast<const u32x4_t *>(segv);   // x, ldx
+    const MvSeg sv = *segv;
+    const u32x4_t pv0 = *reinterpret_cast<const u32x4_t *>(probv);  // w, y
+    const u32x4_t pv1 = *reinterpret_cast<const u32x4_t *>(reinterpret_cast<const uint8_t *>(probv) + 16);   // ldy, M, tile0
+    static_assert(offsetof(MvSeg, x) == 0 && offsetof(MvSeg, ldx) == 8, "segment record layout");
+    static_assert(offsetof(MvProblem, w) == 0 && offsetof(MvProblem, y) == 8 && offsetof(MvProblem, ldy) == 16 &&
+                  offsetof(MvProblem, M) == 24, "matrix record layout");
+    static_assert(kMvMaxSegs == 8 && offsetof(MvSegs, s) == 0, "segment table");
+    // segments hold ascending first workgroups (the first one 0): this workgroup's is the
+    // last whose first workgroup it is not before
+    const int sg = (int)__popcll(__ballot(lane < segs.n && lane < kMvMaxSegs && (int)blockIdx.x >= sv.wg0)) - 1;
+    auto rl = [&](uint32_t v) { return (uint32_t)__builtin_amdgcn_readlane((int)v, sg); };
+    // (pointers rebuilt from the lane reads pass through the global address space, so that
+    // the loads through them stay global loads rather than flat ones)
+    typedef const uint8_t __attribute__((address_space(1))) *gbytes;
+    auto gptr = [](uint32_t lo, uint32_t hi) {
+        return (const uint8_t *)(gbytes)(uintptr_t)(((uint64_t)hi << 32) | lo);
+    };
+    auto rli = [&](int v) { return __builtin_amdgcn_readlane(v, sg); };
+    const XT *__restrict__ x = reinterpret_cast<const XT *>(gptr(rl(sv0.x), rl(sv0.y)));
+    const int64_t ldx = (int64_t)(((uint64_t)rl(sv0.w) << 32) | rl(sv0.z));
+    const MvSeg seg{x, ldx, rli(sv.nb), rli(sv.ws), rli(sv.tile0), rli(sv.tile1), rli(sv.wg0), rli(sv.wgs), rli(sv.q),
+                    rli(sv.r), rl(sv.mag_w), rl(sv.mag_last)};
     const int nb = seg.nb, W = seg.ws;
     const int ns = (nb + kBcSB - 1) / kBcSB;
     const int P = (ns + W - 1) / W;
@@ -440,7 +465,15 @@ __attribute__((amdgpu_waves_per_eu(4))) void mat_vec_bcast(MvGroup grp, MvSegs s
     const uint8_t *ld_base = nullptr;   // first byte of the tile being loaded (uniform)
     int ld_tile = -1, ld_rows = -1;
     TileCursor ld_cur;
-    cursor_init(grp, t0v, ld_cur, tb0);
+    {   // the first tile's matrix from the records read above
+        ld_cur.idx = find_problem(t0v, tb0);
+        auto rp = [&](uint32_t v) { return (uint32_t)__builtin_amdgcn_readlane((int)v, ld_cur.idx); };
+        ld_cur.r = TileRef{gptr(rp(pv0.x), rp(pv0.y)),
+                           reinterpret_cast<float *>(((uint64_t)rp(pv0.w) << 32) | rp(pv0.z)),
+                           (int64_t)(((uint64_t)rp(pv1.y) << 32) | rp(pv1.x)), (int)rp(pv1.z), 0};
+        ld_cur.t0 = __builtin_amdgcn_readlane(t0v, ld_cur.idx);
+        ld_cur.t1 = ld_cur.idx + 1 < kMvMaxGroup ? __builtin_amdgcn_readlane(t0v, ld_cur.idx + 1) : 0x7fffffff;
+    }
 #define Q2_0_SET_LOAD_TILE(TILE)                                                                   \
     {                                                                                              \
         const TileRef tr_ = cursor_tile<kBcRows>(grp, t0v, ld_cur, (TILE));                        \
